@@ -1,0 +1,27 @@
+"""CPU float64 oracle for the Q8_0 block-quantized linear.
+
+Test infrastructure: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import it.  It shares no code with the HIP
+library.
+"""
+
+from .q8_oracle import (  # noqa: F401
+    QK8_0,
+    Q8_0_BLOCK_BYTES,
+    bf16_round_ref,
+    dequantize_q8_0,
+    fused_gate_up_silu_ref,
+    moe_mixture_ref,
+    moe_ref,
+    parse_q8_0,
+    q8_0_row_bytes,
+    q8_linear_bf16_operands_ref,
+    q8_linear_ref,
+    rel_err_row_max,
+    rel_err_row_norm,
+    route_topk_ref,
+    router_logits_ref,
+    sigmoid_ref,
+    silu_ref,
+    softmax_ref,
+)

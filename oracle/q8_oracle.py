@@ -1,0 +1,289 @@
+"""Plain, slow CPU reference (float64) for the Q8_0 block-quantized weight linear.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path imports this module: only
+``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py``
+may call it.  It shares no code with the HIP library (no kernels, headers,
+helpers, tables or pre/post-processing) and imports nothing from it.
+
+What it follows (sources are the four pages describing the fucina engine):
+
+* "14. Model families and example applications", section 14.1 (Conventions shared
+  by every family): LinearWeight keeps the GGUF dtype resident and the quant forms,
+  Q8_0 among them, run packed kernels with no global dequantization at load; q/k/v
+  are fused into one QKV matrix and gate/up into one gate_up matrix.
+* Same page, section 14.2 (Qwen3 - dense and MoE): SwiGLU FFN; the MoE FFN routes
+  with a softmax top-k (``routerTopK`` with ``normalize_selected = norm_topk_prob``,
+  default true) and runs the router-weighted SwiGLU mixture (``moeSwiGluFfnSeq``).
+* Same page, section 14.4 (Gemma 4 - text + MoE, "MoE expert kernels"): the combine
+  keeps each token's summation order fixed.
+
+Every step is the plain definition written out in float64: parse the blocks,
+dequantize exactly, multiply with a library matmul, apply the elementwise
+epilogue.  No blocking, fusion or reordering.
+
+Readings taken where the pages are silent (each also listed in the design notes):
+
+* Q8_0 byte layout: the GGUF Q8_0 block -- one little-endian IEEE binary16 scale
+  ``d`` followed by 32 signed 8-bit quants ``q``, 34 bytes; blocks run along K and
+  rows are contiguous.  The pages name Q8_0 but never spell the layout out.
+* Dequantization is ``w = d * q`` (no zero point, no minimum).  It is exact in
+  float64: an 11-bit significand times an 8-bit integer.
+* Orientation: ``y[m, n] = sum_k x[m, k] * W[n, k]`` (N outputs, K inputs, GGUF rows
+  with K innermost).
+* gate_up rows are concatenated: gate rows ``[0, F)`` then up rows ``[F, 2F)``.
+* SiLU is ``g * sigmoid(g)``.
+* Top-k ties go to the lower expert index; the output is ordered by descending
+  probability (equivalently, descending logit).
+* The MoE hidden activation ``SiLU(gate) * up`` stays un-requantized.
+
+Parity pins: every function here is pinned by ``tests/test_oracle_pins.py`` against
+hand-computed block values (``tests/golden/``), exact rational brute force, closed
+forms, invariants and library routines.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+QK8_0 = 32                 # quants per block
+Q8_0_BLOCK_BYTES = 34      # 2-byte binary16 scale + 32 int8 quants
+
+# One GGUF Q8_0 block, read as a packed record (no padding: itemsize 34).
+_Q8_0_RECORD = np.dtype([("d", "<f2"), ("qs", "i1", (QK8_0,))])
+assert _Q8_0_RECORD.itemsize == Q8_0_BLOCK_BYTES
+
+
+# --------------------------------------------------------------------------- Q8_0
+
+
+def q8_0_row_bytes(k: int) -> int:
+    """Bytes in one Q8_0 row of length k."""
+    if k % QK8_0:
+        raise ValueError(f"K={k} is not a multiple of {QK8_0}")
+    return (k // QK8_0) * Q8_0_BLOCK_BYTES
+
+
+def parse_q8_0(buf, n_rows: int, k: int):
+    """Split a Q8_0 byte stream into its scales and quants, both as float64.
+
+    Returns ``d`` of shape (n_rows, k/32) and ``q`` of shape (n_rows, k/32, 32).
+    Both conversions are exact (binary16 -> float64, int8 -> float64).
+    """
+    raw = np.frombuffer(memoryview(buf).cast("B"), dtype=np.uint8)
+    need = n_rows * q8_0_row_bytes(k)
+    if raw.size != need:
+        raise ValueError(f"Q8_0 buffer has {raw.size} bytes, expected {need}")
+    rec = raw.view(_Q8_0_RECORD).reshape(n_rows, k // QK8_0)
+    d = rec["d"].astype(np.float64)
+    q = rec["qs"].astype(np.float64)
+    return d, q
+
+
+def dequantize_q8_0(buf, n_rows: int, k: int) -> np.ndarray:
+    """W[n, 32*b + i] = d[n, b] * q[n, b, i] in float64 (exact)."""
+    d, q = parse_q8_0(buf, n_rows, k)
+    w = d[:, :, None] * q
+    return w.reshape(n_rows, k)
+
+
+# ------------------------------------------------------------------------- linear
+
+
+def q8_linear_ref(w_q8, n: int, k: int, x) -> np.ndarray:
+    """y = x . W^T for a Q8_0 weight W [n][k] and activation rows x [M][k].
+
+    The packed-weight linear of section 14.1 (LinearWeight), written as the plain
+    definition: dequantize, then one float64 matrix product.
+    """
+    x64 = np.asarray(x, dtype=np.float64)
+    if x64.ndim != 2 or x64.shape[1] != k:
+        raise ValueError(f"x must be [M][{k}], got {x64.shape}")
+    w = dequantize_q8_0(w_q8, n, k)
+    return x64 @ w.T
+
+
+def sigmoid_ref(g) -> np.ndarray:
+    """Logistic function in the overflow-free form for both signs of g."""
+    g = np.asarray(g, dtype=np.float64)
+    out = np.empty_like(g)
+    pos = g >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-g[pos]))
+    e = np.exp(g[~pos])
+    out[~pos] = e / (1.0 + e)
+    return out
+
+
+def silu_ref(g) -> np.ndarray:
+    """SiLU(g) = g * sigmoid(g) (the activation of the SwiGLU FFN, section 14.2)."""
+    g = np.asarray(g, dtype=np.float64)
+    return g * sigmoid_ref(g)
+
+
+def fused_gate_up_silu_ref(w_gate_up_q8, f: int, k: int, x) -> np.ndarray:
+    """h = SiLU(x . W_gate^T) * (x . W_up^T) from one fused gate_up matrix [2f][k].
+
+    Section 14.1 fuses gate and up into one gate_up matrix; section 14.2 gives the
+    SwiGLU FFN.  Gate rows are [0, f), up rows are [f, 2f).
+    """
+    y = q8_linear_ref(w_gate_up_q8, 2 * f, k, x)
+    g = y[:, :f]
+    u = y[:, f:]
+    return silu_ref(g) * u
+
+
+# ------------------------------------------------------------------------- router
+
+
+def router_logits_ref(x, w_router) -> np.ndarray:
+    """logits[m, e] = x[m] . w_router[e] in float64."""
+    return np.asarray(x, dtype=np.float64) @ np.asarray(w_router, dtype=np.float64).T
+
+
+def softmax_ref(logits) -> np.ndarray:
+    """Row softmax with the row maximum subtracted first."""
+    l = np.asarray(logits, dtype=np.float64)
+    z = l - l.max(axis=-1, keepdims=True)
+    e = np.exp(z)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def route_topk_ref(x, w_router, k: int, normalize: bool = True):
+    """Softmax top-k routing (section 14.2: routerTopK, normalize_selected = norm_topk_prob).
+
+    p = softmax(x . W_r^T); the k experts of largest p are chosen, in descending
+    order of p with ties to the lower expert index (a stable sort of -p); the chosen
+    weights are p[sel], divided by their sum when ``normalize``.
+
+    Returns (idx int32 [M][k], w float64 [M][k]).
+    """
+    logits = router_logits_ref(x, w_router)
+    m_rows, n_exp = logits.shape
+    if not 1 <= k <= n_exp:
+        raise ValueError(f"k={k} must be in [1, {n_exp}]")
+    p = softmax_ref(logits)
+    idx = np.empty((m_rows, k), dtype=np.int32)
+    wts = np.empty((m_rows, k), dtype=np.float64)
+    for m in range(m_rows):
+        order = np.argsort(-p[m], kind="stable")
+        sel = order[:k]
+        idx[m] = sel
+        chosen = p[m, sel]
+        wts[m] = chosen / chosen.sum() if normalize else chosen
+    return idx, wts
+
+
+# ---------------------------------------------------------------------------- MoE
+
+
+def _expert_slice(stack, e: int, rows: int, k: int):
+    """Bytes of expert e in a Q8_0 expert stack laid out [E][rows][k]."""
+    raw = np.frombuffer(memoryview(stack).cast("B"), dtype=np.uint8)
+    nb = rows * q8_0_row_bytes(k)
+    return raw[e * nb:(e + 1) * nb]
+
+
+def moe_mixture_ref(w_gate_up_exps, w_down_exps, n_exp: int, f: int, h: int,
+                    x, topk_idx, topk_w) -> np.ndarray:
+    """Router-weighted SwiGLU mixture for given routing (section 14.2: moeSwiGluFfnSeq).
+
+    y[m] = sum_j topk_w[m, j] * W_down[e] . (SiLU(W_gate[e] x_m) * (W_up[e] x_m)),
+    e = topk_idx[m, j], summed over slots j = 0 .. k-1 in order (section 14.4 keeps
+    each token's summation order fixed).  Expert stacks are Q8_0 [E][2f][h] (gate_up)
+    and [E][h][f] (down).
+    """
+    x64 = np.asarray(x, dtype=np.float64)
+    idx = np.asarray(topk_idx)
+    wts = np.asarray(topk_w, dtype=np.float64)
+    m_rows, k_used = idx.shape
+    y = np.zeros((m_rows, h), dtype=np.float64)
+    for m in range(m_rows):
+        for j in range(k_used):
+            e = int(idx[m, j])
+            if not 0 <= e < n_exp:
+                raise ValueError(f"expert index {e} out of range [0, {n_exp})")
+            hid = fused_gate_up_silu_ref(_expert_slice(w_gate_up_exps, e, 2 * f, h), f, h,
+                                         x64[m:m + 1])
+            out = q8_linear_ref(_expert_slice(w_down_exps, e, h, f), h, f, hid)
+            y[m] += wts[m, j] * out[0]
+    return y
+
+
+def moe_ref(w_router, w_gate_up_exps, w_down_exps, n_exp: int, f: int, h: int,
+            x, k: int, normalize: bool = True):
+    """Route (softmax top-k), then the mixture.  Returns (y, idx, w)."""
+    idx, wts = route_topk_ref(x, w_router, k, normalize)
+    y = moe_mixture_ref(w_gate_up_exps, w_down_exps, n_exp, f, h, x, idx, wts)
+    return y, idx, wts
+
+
+# ------------------------------------------------------- diagnostic (not a gate)
+
+
+def bf16_round_ref(a) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 (ties to even), returned as float64.
+
+    Goes through float32 first; each value here is already a float32 (activations,
+    or fp32(d)*q), so that step is exact.
+    """
+    a32 = np.asarray(a, dtype=np.float32)
+    bits = a32.view(np.uint32).astype(np.uint64)
+    lsb = (bits >> 16) & 1
+    rounded = ((bits + 0x7FFF + lsb) >> 16) << 16
+    return rounded.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def q8_linear_bf16_operands_ref(w_q8, n: int, k: int, x) -> np.ndarray:
+    """Diagnostic: y with both operands rounded to bfloat16 first, float64 sums.
+
+    Isolates the accumulation error of a bf16 matrix-core path from its operand
+    rounding.  Not a parity gate.
+    """
+    w = dequantize_q8_0(w_q8, n, k)
+    return bf16_round_ref(np.asarray(x, dtype=np.float32)) @ bf16_round_ref(w).T
+
+
+# ----------------------------------------------------------- error measurement
+
+
+def rel_err_row_norm(y, y_ref) -> float:
+    """max over rows of max|y - y_ref| / ||y_ref row||_2 (0 when the row is all zero)."""
+    y = np.asarray(y, dtype=np.float64)
+    r = np.asarray(y_ref, dtype=np.float64)
+    if y.shape != r.shape:
+        raise ValueError(f"shape mismatch {y.shape} vs {r.shape}")
+    if y.size == 0:
+        return 0.0
+    y2 = y.reshape(-1, y.shape[-1])
+    r2 = r.reshape(-1, r.shape[-1])
+    worst = 0.0
+    for a, b in zip(y2, r2):
+        nrm = math.sqrt(float(np.dot(b, b)))
+        d = float(np.max(np.abs(a - b)))
+        if nrm == 0.0:
+            if d != 0.0:
+                return math.inf
+            continue
+        worst = max(worst, d / nrm)
+    return worst
+
+
+def rel_err_row_max(y, y_ref) -> float:
+    """max over rows of max|y - y_ref| / max|y_ref row| (the stricter reading)."""
+    y = np.asarray(y, dtype=np.float64)
+    r = np.asarray(y_ref, dtype=np.float64)
+    if y.size == 0:
+        return 0.0
+    y2 = y.reshape(-1, y.shape[-1])
+    r2 = r.reshape(-1, r.shape[-1])
+    worst = 0.0
+    for a, b in zip(y2, r2):
+        mx = float(np.max(np.abs(b)))
+        d = float(np.max(np.abs(a - b)))
+        if mx == 0.0:
+            if d != 0.0:
+                return math.inf
+            continue
+        worst = max(worst, d / mx)
+    return worst

@@ -1,0 +1,54 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and require that the
+pins in test_oracle_pins.py catch each one.  This shows the pins are strong enough
+that a dropped term, a wrong sign, index or byte order, or a transposed operand in
+the oracle cannot pass unnoticed.
+"""
+
+from __future__ import annotations
+
+import os
+import types
+
+import pytest
+
+import test_oracle_pins as pins
+
+SRC_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "q8_oracle.py")
+
+MUTANTS = {
+    "scale_big_endian": ('("d", "<f2")', '("d", ">f2")'),
+    "quants_unsigned": ('("qs", "i1", (QK8_0,))', '("qs", "u1", (QK8_0,))'),
+    "dropped_scale": ("w = d[:, :, None] * q", "w = q + 0 * d[:, :, None]"),
+    "reversed_k": ("return w.reshape(n_rows, k)", "return w.reshape(n_rows, k)[:, ::-1]"),
+    "gate_up_swapped": ("g = y[:, :f]\n    u = y[:, f:]", "g = y[:, f:]\n    u = y[:, :f]"),
+    "silu_sign": ("return g * sigmoid_ref(g)", "return g * sigmoid_ref(-g)"),
+    "sigmoid_negative_branch": ("out[~pos] = e / (1.0 + e)", "out[~pos] = 1.0 / (1.0 + e)"),
+    "ties_to_higher_index": ('order = np.argsort(-p[m], kind="stable")', "order = np.argsort(p[m], kind=\"stable\")[::-1]"),
+    "no_renormalize": ("wts[m] = chosen / chosen.sum() if normalize else chosen", "wts[m] = chosen"),
+    "softmax_wrong_axis": ("return e / e.sum(axis=-1, keepdims=True)", "return e / e.sum(axis=0, keepdims=True)"),
+    "moe_ignores_weights": ("y[m] += wts[m, j] * out[0]", "y[m] += out[0]"),
+    "moe_wrong_expert": ("return raw[e * nb:(e + 1) * nb]", "return raw[(e ^ 1) * nb:((e ^ 1) + 1) * nb]"),
+    "router_untransposed_logits": ("@ np.asarray(w_router, dtype=np.float64).T",
+                                   "@ np.asarray(w_router, dtype=np.float64).T[::-1].T"),
+}
+
+
+def _mutant(name):
+    old, new = MUTANTS[name]
+    src = open(SRC_PATH).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique/absent"
+    mod = types.ModuleType(f"oracle_mutant_{name}")
+    exec(compile(src.replace(old, new), SRC_PATH, "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name):
+    mod = _mutant(name)
+    caught = []
+    for check in pins.ALL_CHECKS:
+        try:
+            check(mod)
+        except Exception:  # an assertion or a crash both count as caught
+            caught.append(check.__name__)
+    assert caught, f"no pin caught mutant {name}"

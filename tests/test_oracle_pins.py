@@ -1,0 +1,303 @@
+"""Pins of the CPU oracle to things other than itself (CPU only).
+
+Each check is a function of an oracle implementation ``o`` so the same checks can
+be run against deliberately broken copies of the oracle (see
+test_oracle_mutants.py): a plausible slip in the oracle must fail at least one.
+
+Pins used (the pages print no worked numbers):
+* hand-derived block values (tests/golden/q8_hand_blocks.txt);
+* exact rational brute force on tiny random shapes (fractions.Fraction);
+* closed forms and invariants: linearity in d and in x, zero-scale blocks, one-hot
+  gathers, sign symmetry;
+* library routines for special cases: scipy's expit (SiLU), scipy's softmax
+  (top-k with k = E), Python's sorted() (top-k selection);
+* the MoE mixture reducing to one dense SwiGLU FFN (k = 1, identical experts) and
+  invariance under relabelling the experts.
+"""
+
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle as O
+import workloads as wl
+from golden_io import half_bits_to_fraction, load_linear_cases, load_swiglu_router_cases
+
+LINEAR_CASES = load_linear_cases()
+FUSED_CASES, ROUTE_CASES = load_swiglu_router_cases()
+
+
+# ------------------------------------------------------------------ checks
+
+
+def check_hand_linear(o):
+    for c in LINEAR_CASES:
+        y = o.q8_linear_ref(c["w"], c["n"], c["k"], np.array(c["x"]))
+        want = np.array([[float(v) for v in r] for r in c["y"]])
+        assert y.shape == want.shape, c["name"]
+        # every case is exact in float64
+        for got, exp in zip(y.ravel(), [v for r in c["y"] for v in r]):
+            assert Fraction(float(got)) == exp, (c["name"], float(got), exp)
+
+
+def check_hand_fused(o):
+    for c in FUSED_CASES:
+        h = o.fused_gate_up_silu_ref(c["w"], 1, c["k"], np.array(c["x"]))
+        assert h.shape == (1, 1)
+        assert math.isclose(float(h[0, 0]), c["h"], rel_tol=1e-14, abs_tol=1e-300), c["name"]
+
+
+def check_hand_route(o):
+    for c in ROUTE_CASES:
+        idx, w = o.route_topk_ref(np.array(c["x"]), np.array(c["w_router"]), c["k"], c["normalize"])
+        assert idx.tolist() == c["idx"], c["name"]
+        np.testing.assert_allclose(w, np.array(c["w"]), rtol=1e-14, atol=0, err_msg=c["name"])
+
+
+def _exact_linear(q, d, x):
+    """Fraction brute force: y[m][n] = sum_k x[m][k] * d[n][k//32] * q[n][k]."""
+    n, k = q.shape
+    m = x.shape[0]
+    dq = [[half_bits_to_fraction(int(b)) for b in row] for row in d.view(np.uint16)]
+    xf = [[Fraction(float(v)) for v in row] for row in x]
+    out = [[Fraction(0)] * n for _ in range(m)]
+    for mi in range(m):
+        for ni in range(n):
+            s = Fraction(0)
+            for ki in range(k):
+                s += xf[mi][ki] * dq[ni][ki // 32] * int(q[ni, ki])
+            out[mi][ni] = s
+    return out
+
+
+def check_bruteforce_linear(o):
+    for seed, (n, k, m) in enumerate([(1, 32, 1), (3, 64, 2), (2, 256, 1), (3, 96, 2)]):
+        wb, q, d = wl.q8_weight(100 + seed, n, k)
+        x = wl.activations(200 + seed, m, k)
+        y = o.q8_linear_ref(wb, n, k, x)
+        ex = _exact_linear(q, d, x)
+        for mi in range(m):
+            for ni in range(n):
+                e = float(ex[mi][ni])
+                assert abs(y[mi, ni] - e) <= 1e-12 * max(1.0, abs(e)), (n, k, m, mi, ni)
+
+
+def check_dequant_exact(o):
+    wb, q, d = wl.q8_weight(7, 3, 128)
+    w = o.dequantize_q8_0(wb, 3, 128)
+    dq = d.view(np.uint16)
+    for n in range(3):
+        for kk in range(128):
+            assert Fraction(float(w[n, kk])) == half_bits_to_fraction(int(dq[n, kk // 32])) * int(q[n, kk])
+
+
+def check_linearity(o):
+    n, k, m = 5, 256, 3
+    _, q, d = wl.q8_weight(11, n, k)
+    x = wl.activations(12, m, k)
+    y = o.q8_linear_ref(wl.pack_blocks(q, d), n, k, x)
+    # doubling every scale doubles y exactly (power of two; no binary16 overflow here)
+    y2 = o.q8_linear_ref(wl.pack_blocks(q, (d.astype(np.float32) * 2).astype(np.float16)), n, k, x)
+    assert np.array_equal(y2, 2 * y)
+    # y(2x) = 2 y(x) exactly
+    assert np.array_equal(o.q8_linear_ref(wl.pack_blocks(q, d), n, k, 2 * x), 2 * y)
+    # additivity in x
+    x2 = wl.activations(13, m, k)
+    ya = o.q8_linear_ref(wl.pack_blocks(q, d), n, k, x.astype(np.float64) + x2)
+    yb = y + o.q8_linear_ref(wl.pack_blocks(q, d), n, k, x2)
+    np.testing.assert_allclose(ya, yb, rtol=1e-12, atol=1e-12)
+    # sign symmetry q -> -q (no -128 in the draw)
+    yneg = o.q8_linear_ref(wl.pack_blocks(-q, d), n, k, x)
+    assert np.array_equal(yneg, -y)
+
+
+def check_zero_scale(o):
+    n, k, m = 4, 256, 2
+    _, q, d = wl.q8_weight(21, n, k)
+    x = wl.activations(22, m, k)
+    rng = np.random.default_rng(5)
+    mask = rng.random(d.shape) < 0.4
+    d0 = d.copy()
+    d0[mask] = 0
+    q0 = q.copy().reshape(n, k // 32, 32)
+    q0[mask] = 0
+    ya = o.q8_linear_ref(wl.pack_blocks(q, d0), n, k, x)
+    yb = o.q8_linear_ref(wl.pack_blocks(q0.reshape(n, k), d), n, k, x)
+    np.testing.assert_allclose(ya, yb, rtol=1e-13, atol=1e-13)
+    yz = o.q8_linear_ref(wl.pack_blocks(q, np.zeros_like(d)), n, k, x)
+    assert np.all(yz == 0)
+
+
+def check_one_hot(o):
+    n, k, m = 6, 128, 3
+    perm = np.random.default_rng(3).permutation(k)[:n]
+    q = np.zeros((n, k), np.int8)
+    q[np.arange(n), perm] = 1
+    d = np.ones((n, k // 32), np.float16)
+    x = wl.activations(31, m, k)
+    y = o.q8_linear_ref(wl.pack_blocks(q, d), n, k, x)
+    assert np.array_equal(y, x[:, perm].astype(np.float64))
+
+
+def check_silu(o):
+    g = np.linspace(-40, 40, 2001)
+    np.testing.assert_allclose(o.silu_ref(g), g * scipy.special.expit(g), rtol=1e-14, atol=1e-300)
+    # silu(g) - silu(-g) = g
+    np.testing.assert_allclose(o.silu_ref(g) - o.silu_ref(-g), g, rtol=1e-13, atol=1e-13)
+    assert o.silu_ref(np.array([0.0]))[0] == 0.0
+    assert np.all(np.isfinite(o.silu_ref(np.array([-800.0, 800.0]))))
+
+
+def check_fused_split(o):
+    """gate rows [0,F), up rows [F,2F): the fused result equals two plain linears."""
+    f, k, m = 8, 256, 2
+    _, qg, dg = wl.q8_weight(41, f, k)
+    _, qu, du = wl.q8_weight(42, f, k)
+    x = wl.activations(43, m, k)
+    g = o.q8_linear_ref(wl.pack_blocks(qg, dg), f, k, x)
+    u = o.q8_linear_ref(wl.pack_blocks(qu, du), f, k, x)
+    fused = wl.pack_blocks(np.concatenate([qg, qu]), np.concatenate([dg, du]))
+    h = o.fused_gate_up_silu_ref(fused, f, k, x)
+    np.testing.assert_allclose(h, g * scipy.special.expit(g) * u, rtol=1e-13, atol=1e-13)
+
+
+def _sorted_topk(p_row, k):
+    order = sorted(range(len(p_row)), key=lambda e: (-p_row[e], e))
+    return order[:k]
+
+
+def check_route_invariants(o):
+    m, h, e = 6, 64, 16
+    x = wl.activations(51, m, h)
+    wr = wl.router_weight(52, e, h, std=0.5)
+    logits = x.astype(np.float64) @ wr.astype(np.float64).T
+    p_lib = scipy.special.softmax(logits, axis=-1)
+    for k in (1, 3, e):
+        idx, w = o.route_topk_ref(x, wr, k, True)
+        idx_raw, w_raw = o.route_topk_ref(x, wr, k, False)
+        assert np.array_equal(idx, idx_raw)
+        for mi in range(m):
+            assert idx[mi].tolist() == _sorted_topk(list(p_lib[mi]), k)
+            # renormalized weights = softmax over the selected logits
+            sel = logits[mi, idx[mi]]
+            np.testing.assert_allclose(w[mi], scipy.special.softmax(sel), rtol=1e-12)
+            assert abs(w[mi].sum() - 1.0) < 1e-14
+            np.testing.assert_allclose(w_raw[mi], p_lib[mi, idx[mi]], rtol=1e-12)
+            assert np.all(np.diff(w[mi]) <= 0)
+        if k == e:
+            np.testing.assert_allclose(np.take_along_axis(p_lib, idx.astype(np.int64), 1), w, rtol=1e-12)
+
+
+def _dense_ffn(o, gu, dn, f, h, x):
+    hid = o.fused_gate_up_silu_ref(gu, f, h, x)
+    return o.q8_linear_ref(dn, h, f, hid)
+
+
+def _stack(parts):
+    return np.concatenate([np.asarray(p, np.uint8) for p in parts])
+
+
+def check_moe(o):
+    e_n, f, h, m, k = 4, 64, 64, 3, 2
+    gus = [wl.q8_weight(60 + i, 2 * f, h) for i in range(e_n)]
+    dns = [wl.q8_weight(70 + i, h, f) for i in range(e_n)]
+    gu_stack = _stack([g[0] for g in gus])
+    dn_stack = _stack([d[0] for d in dns])
+    x = wl.activations(80, m, h)
+    # k = 1, weight 1: one dense SwiGLU FFN of the chosen expert
+    idx = np.array([[2], [0], [3]], np.int32)
+    w1 = np.ones((m, 1))
+    y = o.moe_mixture_ref(gu_stack, dn_stack, e_n, f, h, x, idx, w1)
+    for mi in range(m):
+        e = int(idx[mi, 0])
+        want = _dense_ffn(o, gus[e][0], dns[e][0], f, h, x[mi:mi + 1])[0]
+        np.testing.assert_allclose(y[mi], want, rtol=1e-13, atol=1e-13)
+    # general k: explicit weighted sum of dense FFNs, slot order
+    idx, wts = wl.random_routing(81, m, e_n, k)
+    y = o.moe_mixture_ref(gu_stack, dn_stack, e_n, f, h, x, idx, wts)
+    for mi in range(m):
+        want = np.zeros(h)
+        for j in range(k):
+            e = int(idx[mi, j])
+            want += float(wts[mi, j]) * _dense_ffn(o, gus[e][0], dns[e][0], f, h, x[mi:mi + 1])[0]
+        np.testing.assert_allclose(y[mi], want, rtol=1e-12, atol=1e-12)
+    # identical experts + renormalized routing = one FFN
+    same_gu = _stack([gus[0][0]] * e_n)
+    same_dn = _stack([dns[0][0]] * e_n)
+    wr = wl.router_weight(82, e_n, h, std=0.3)
+    ys, _, _ = o.moe_ref(wr, same_gu, same_dn, e_n, f, h, x, k, True)
+    np.testing.assert_allclose(ys, _dense_ffn(o, gus[0][0], dns[0][0], f, h, x), rtol=1e-12, atol=1e-12)
+    # relabelling experts (router rows with the stacks) leaves y unchanged
+    perm = np.array([2, 0, 3, 1])
+    ya, _, _ = o.moe_ref(wr, gu_stack, dn_stack, e_n, f, h, x, k, True)
+    yb, _, _ = o.moe_ref(wr[perm], _stack([gus[p][0] for p in perm]), _stack([dns[p][0] for p in perm]),
+                         e_n, f, h, x, k, True)
+    np.testing.assert_allclose(ya, yb, rtol=1e-13, atol=1e-13)
+
+
+def check_moe_bruteforce(o):
+    """Pure-Python loops over every index (tiny shapes, math.exp), from generator q/d."""
+    e_n, f, h, m, k = 3, 32, 32, 2, 2
+    gus = [wl.q8_weight(90 + i, 2 * f, h) for i in range(e_n)]
+    dns = [wl.q8_weight(95 + i, h, f) for i in range(e_n)]
+    x = wl.activations(99, m, h)
+    idx, wts = wl.random_routing(98, m, e_n, k)
+    y = o.moe_mixture_ref(_stack([g[0] for g in gus]), _stack([d[0] for d in dns]), e_n, f, h, x, idx, wts)
+
+    def wval(qd, r, c):
+        _, q, d = qd
+        return float(d[r, c // 32]) * int(q[r, c])
+
+    for mi in range(m):
+        acc = [0.0] * h
+        for j in range(k):
+            e = int(idx[mi, j])
+            hid = []
+            for r in range(f):
+                g = sum(float(x[mi, c]) * wval(gus[e], r, c) for c in range(h))
+                u = sum(float(x[mi, c]) * wval(gus[e], f + r, c) for c in range(h))
+                hid.append(g / (1.0 + math.exp(-g)) * u)
+            for r in range(h):
+                acc[r] += float(wts[mi, j]) * sum(hid[c] * wval(dns[e], r, c) for c in range(f))
+        np.testing.assert_allclose(y[mi], acc, rtol=1e-11, atol=1e-11)
+
+
+ALL_CHECKS = [
+    check_hand_linear, check_hand_fused, check_hand_route, check_bruteforce_linear,
+    check_dequant_exact, check_linearity, check_zero_scale, check_one_hot, check_silu,
+    check_fused_split, check_route_invariants, check_moe, check_moe_bruteforce,
+]
+
+
+@pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda c: c.__name__)
+def test_oracle_pin(check):
+    check(O)
+
+
+def test_bf16_rounding_diag():
+    # bfloat16 keeps 7 fraction bits: 1 + 2^-8 is a tie (to even: 1), 1 + 3*2^-8 is a
+    # tie between 1 + 2^-7 (odd) and 1 + 2^-6 (even), 1 + 2^-7 is representable
+    vals = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 2.0 ** 100 * (1 + 2 ** -8), 1 + 2 ** -7])
+    want = np.array([1.0, 1.0, 1 + 2 ** -6, -1.0, 2.0 ** 100, 1 + 2 ** -7])
+    got = O.bf16_round_ref(vals)
+    assert np.array_equal(got, want)
+
+
+def test_error_measures():
+    ref = np.array([[3.0, 4.0], [0.0, 0.0]])
+    assert O.rel_err_row_norm(ref, ref) == 0.0
+    assert O.rel_err_row_norm(ref + np.array([[0.5, 0.0], [0.0, 0.0]]), ref) == pytest.approx(0.1)
+    assert O.rel_err_row_max(ref + np.array([[0.5, 0.0], [0.0, 0.0]]), ref) == pytest.approx(0.125)
+    assert O.rel_err_row_norm(ref + np.array([[0.0, 0.0], [0.0, 1e-3]]), ref) == math.inf
+
+
+def test_parse_rejects_bad_sizes():
+    with pytest.raises(ValueError):
+        O.parse_q8_0(b"\x00" * 33, 1, 32)
+    with pytest.raises(ValueError):
+        O.q8_0_row_bytes(48)

@@ -1,0 +1,174 @@
+"""Seeded synthetic inputs shared by the tests, the bench and the oracle runs.
+
+This module only draws random numbers and lays them out as bytes; it holds none
+of the method's arithmetic (no dequantization, no products, no routing).  Both the
+CPU oracle and the HIP library consume what it produces; neither is imported here.
+
+Recipe (the shapes follow the Qwen3 0.6B / 8B / 30B-A3B layers whose linears the
+pages describe; the value distributions are fixed here):
+
+* Q8_0 quants ``q``: integers uniform in [-127, 127]; scales ``d``: uniform in
+  [1e-3, 2e-2], rounded to binary16 (round to nearest even).
+* Activations ``x``: float32 standard normal.
+* Router weights: float32 normal with standard deviation 0.02.
+* Per-tensor streams come from ``SeedSequence(seed).spawn`` in a fixed order.
+
+A Q8_0 row of length K is K/32 blocks of 34 bytes: a little-endian binary16 scale
+followed by 32 int8 quants; rows are contiguous.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+QK = 32
+BLOCK_BYTES = 34
+
+
+# ----------------------------------------------------------------- byte layout
+
+
+def pack_blocks(q: np.ndarray, d_f16: np.ndarray) -> np.ndarray:
+    """Lay int8 quants [N][K] and binary16 scales [N][K/32] out as Q8_0 bytes.
+
+    Returns a flat uint8 array of N*(K/32)*34 bytes.
+    """
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    d_f16 = np.ascontiguousarray(d_f16, dtype=np.float16)
+    n, k = q.shape
+    nb = k // QK
+    if k % QK or d_f16.shape != (n, nb):
+        raise ValueError(f"bad shapes q {q.shape} d {d_f16.shape}")
+    out = np.empty((n, nb, BLOCK_BYTES), dtype=np.uint8)
+    out[:, :, 0:2] = d_f16.astype("<f2").view(np.uint8).reshape(n, nb, 2)
+    out[:, :, 2:] = q.view(np.uint8).reshape(n, nb, QK)
+    return out.reshape(-1)
+
+
+def row_bytes(k: int) -> int:
+    return (k // QK) * BLOCK_BYTES
+
+
+# ------------------------------------------------------------------ generators
+
+
+def _rngs(seed: int, n: int):
+    return [np.random.Generator(np.random.PCG64(s)) for s in np.random.SeedSequence(seed).spawn(n)]
+
+
+def q8_weight(seed: int, n: int, k: int, d_lo: float = 1e-3, d_hi: float = 2e-2):
+    """Random Q8_0 matrix [n][k]: returns (bytes uint8, q int8 [n][k], d float16 [n][k/32])."""
+    rq, rd = _rngs(seed, 2)
+    q = rq.integers(-127, 128, size=(n, k), dtype=np.int8)
+    d = rd.uniform(d_lo, d_hi, size=(n, k // QK)).astype(np.float16)
+    return pack_blocks(q, d), q, d
+
+
+def q8_weight_exact(seed: int, n: int, k: int):
+    """Q8_0 matrix for exact-arithmetic checks: q in [-127, 127], d in {2^-7, 2^-8}.
+
+    With small-integer activations every partial sum is a multiple of 2^-8 far below
+    2^24 * 2^-8, so any float32 summation order gives the same, exact result.
+    """
+    rq, rd = _rngs(seed, 2)
+    q = rq.integers(-127, 128, size=(n, k), dtype=np.int8)
+    d = np.where(rd.integers(0, 2, size=(n, k // QK)) == 0, 2.0 ** -7, 2.0 ** -8).astype(np.float16)
+    return pack_blocks(q, d), q, d
+
+
+def activations(seed: int, m: int, k: int) -> np.ndarray:
+    """float32 standard-normal activation rows [m][k]."""
+    (r,) = _rngs(seed, 1)
+    return r.standard_normal((m, k), dtype=np.float32)
+
+
+def activations_exact(seed: int, m: int, k: int) -> np.ndarray:
+    """float32 activation rows with integer values in {-2, ..., 2}."""
+    (r,) = _rngs(seed, 1)
+    return r.integers(-2, 3, size=(m, k)).astype(np.float32)
+
+
+def router_weight(seed: int, n_exp: int, h: int, std: float = 0.02) -> np.ndarray:
+    """float32 router matrix [n_exp][h] ~ N(0, std^2)."""
+    (r,) = _rngs(seed, 1)
+    return (r.standard_normal((n_exp, h)) * std).astype(np.float32)
+
+
+def random_routing(seed: int, m: int, n_exp: int, k: int):
+    """Distinct expert ids per token and positive slot weights (not normalized).
+
+    For checking the expert mixture independently of the router.
+    """
+    r1, r2 = _rngs(seed, 2)
+    idx = np.stack([r1.permutation(n_exp)[:k] for _ in range(m)]).astype(np.int32)
+    w = r2.uniform(0.05, 1.0, size=(m, k)).astype(np.float32)
+    return idx, w
+
+
+# ------------------------------------------------------------------- workloads
+
+
+@dataclass(frozen=True)
+class Linear:
+    name: str
+    n: int          # output rows (for gate_up: 2F)
+    k: int          # input length
+    fused_silu: bool = False
+
+    @property
+    def weight_bytes(self) -> int:
+        return self.n * row_bytes(self.k)
+
+
+@dataclass(frozen=True)
+class BlockWorkload:
+    """The block linears of one decoder layer: QKV, fused gate_up (+SiLU*up), down."""
+    name: str
+    hidden: int
+    qkv_out: int
+    ffn: int
+    layers: int
+    rows: tuple = (1,)
+    seed: int = 0
+    linears: tuple = field(init=False)
+
+    def __post_init__(self):
+        object.__setattr__(self, "linears", (
+            Linear("qkv", self.qkv_out, self.hidden),
+            Linear("gate_up", 2 * self.ffn, self.hidden, fused_silu=True),
+            Linear("down", self.hidden, self.ffn),
+        ))
+
+    @property
+    def layer_weight_bytes(self) -> int:
+        return sum(l.weight_bytes for l in self.linears)
+
+
+@dataclass(frozen=True)
+class MoeWorkload:
+    name: str
+    hidden: int
+    ffn: int
+    n_exp: int
+    k: int
+    tokens: int
+    router_std: float = 0.02
+    seed: int = 0
+
+
+# Single linear at the Qwen3-0.6B fused-QKV shape (4096 out, 1024 in), one row.
+QWEN3_06B_QKV = Linear("qwen3-0.6b-qkv", 4096, 1024)
+# Qwen3-0.6B block linears at M=1; 28 layers (the 0.6B reference config has 28).
+QWEN3_06B_BLOCK = BlockWorkload("qwen3-0.6b-block-linears", hidden=1024, qkv_out=4096,
+                                ffn=3072, layers=28, rows=(1,), seed=1)
+# Qwen3-8B block linears (hidden 4096, 32 q heads + 8 kv heads of 128 -> QKV 6144, FFN 12288).
+QWEN3_8B_BLOCK = BlockWorkload("qwen3-8b-block-linears", hidden=4096, qkv_out=6144,
+                               ffn=12288, layers=36, rows=(1, 8), seed=2)
+# Qwen3-8B gate_up at M=16 (speculative-verify batch) and M=512 (prefill).
+QWEN3_8B_GATE_UP = Linear("qwen3-8b-gate-up", 24576, 4096)
+GATE_UP_ROWS = (16, 512)
+# Qwen3-30B-A3B MoE layer, 16 tokens.
+QWEN3_30B_A3B_MOE = MoeWorkload("qwen3-30b-a3b-moe-layer", hidden=2048, ffn=768, n_exp=128,
+                                k=8, tokens=16, seed=4)
