@@ -1,0 +1,216 @@
+"""Throughput of the Q8_0 block-quantized linear on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints ONE JSON line.  The default workload is the Qwen3-8B block linears (QKV 6144x4096,
+fused gate_up 24576x4096 with SiLU(gate)*up, down 4096x12288, Q8_0 weights, float32
+activations) at M = 1: a step is one decode token through 36 layers, each with its own
+resident copy of the weights (6.7 GB in total, far above the 256 MB Infinity Cache, so
+every step streams the weights from HBM).  `value` is the effective weight bandwidth:
+algorithmic Q8_0 bytes per step / step time.  The same stack at M = 8 is reported in
+"m8".  Other workloads (the other layer shapes) are selected with --workload.
+
+Inputs are seeded synthetic data (workloads/); the timed region starts with everything
+resident in HBM.  The CPU oracle is timed on a bounded sample of the same workload on
+the host cores ("cpu_baseline").
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix cores
+METRIC = "effective weight GB/s & % of HBM peak for Q8_0 linear at M=1/8/16; decode tok/s"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------------- workloads
+
+
+class Stack:
+    """L layers of block linears, each layer with its own device copy of the weights."""
+
+    def __init__(self, torch, dev, spec, layers, seed):
+        import workloads as wl
+        self.spec = spec
+        self.layers = layers
+        host = []
+        for lin in spec.linears:
+            wb, _, _ = wl.q8_weight(seed * 100 + len(host), lin.n, lin.k)
+            host.append(wb)
+        self.host = host
+        base = [torch.from_numpy(h).to(dev) for h in host]
+        self.w = [[b if i == 0 else b.clone() for b in base] for i in range(layers)]
+        self.bytes_per_layer = sum(int(h.size) for h in host)
+
+    def run(self, q8, x, bufs, m, events=None):
+        """One decode step through every layer: QKV, gate_up(+SiLU), down (fed by gate_up)."""
+        spec = self.spec
+        qkv, gu, dn = spec.linears
+        for l in range(self.layers):
+            wq, wg, wd = self.w[l]
+            q8.q8_linear(wq, qkv.n, qkv.k, x, out=bufs["qkv"])
+            if events is not None:
+                events[l][0].record()
+            q8.q8_linear_fused_gate_up_silu(wg, gu.n // 2, gu.k, x, out=bufs["h"])
+            if events is not None:
+                events[l][1].record()
+            q8.q8_linear(wd, dn.n, dn.k, bufs["h"], out=bufs["y"])
+
+
+def time_steps(torch, fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps  # ms per step
+
+
+def cpu_baseline_block(spec, seconds_hint=15.0):
+    """The oracle on one full layer of the stack (QKV, fused gate_up, down) at M = 1."""
+    import oracle
+    import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    hosts = [wl.q8_weight(900 + i, lin.n, lin.k)[0] for i, lin in enumerate(spec.linears)]
+    xs = [wl.activations(950 + i, 1, lin.k) for i, lin in enumerate(spec.linears)]
+    nbytes = sum(int(h.size) for h in hosts)
+    best = None
+    t_all = time.perf_counter()
+    reps = 0
+    while True:
+        t0 = time.perf_counter()
+        for lin, wb, x in zip(spec.linears, hosts, xs):
+            if lin.fused_silu:
+                oracle.fused_gate_up_silu_ref(wb, lin.n // 2, lin.k, x)
+            else:
+                oracle.q8_linear_ref(wb, lin.n, lin.k, x)
+        dt = time.perf_counter() - t0
+        reps += 1
+        best = dt if best is None else min(best, dt)
+        if reps >= 3 or time.perf_counter() - t_all > seconds_hint:
+            break
+    return {"value": round(nbytes / best / 1e9, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"one full layer ({'+'.join(l.name for l in spec.linears)}, {nbytes} Q8_0 bytes) at M=1, "
+                      f"float64 dequantize-then-matmul, best of {reps}",
+            "tok_s_per_layer": round(1.0 / best, 3)}
+
+
+def bench_block(args, torch, dev, q8, spec, m_values):
+    import workloads as wl
+    layers = args.layers or spec.layers
+    log(f"workload {spec.name}: {layers} layers, uploading weights")
+    stack = Stack(torch, dev, spec, layers, spec.seed)
+    qkv, gu, dn = spec.linears
+    out = {}
+    gate_up_bytes = gu.weight_bytes
+    for m in m_values:
+        x = torch.from_numpy(wl.activations(7 + m, m, spec.hidden)).to(dev)
+        bufs = {"qkv": torch.empty((m, qkv.n), device=dev), "h": torch.empty((m, gu.n // 2), device=dev),
+                "y": torch.empty((m, dn.n), device=dev)}
+        ms = time_steps(torch, lambda: stack.run(q8, x, bufs, m), args.steps, args.warmup)
+        bytes_step = stack.bytes_per_layer * layers
+        res = {"ms_per_step": round(ms, 5), "gbps": round(bytes_step / (ms * 1e-3) / 1e9, 2),
+               "tok_s": round(m * 1000.0 / ms, 2), "weight_bytes_per_step": bytes_step}
+        res["hbm_frac"] = round(res["gbps"] / HBM_PEAK_GBS, 4)
+        # dominant kernel: the fused gate_up; per-launch HIP events on the launching stream
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(layers)]
+        durs = []
+        for _ in range(max(1, args.steps // 4)):
+            stack.run(q8, x, bufs, m, events=evs)
+            torch.cuda.synchronize()
+            durs.extend(a.elapsed_time(b) for a, b in evs)
+        avg_ms = float(np.mean(durs))
+        res["gate_up_avg_us"] = round(avg_ms * 1e3, 3)
+        res["gate_up_gbps"] = round(gate_up_bytes / (avg_ms * 1e-3) / 1e9, 2)
+        out[m] = res
+        log(f"M={m}: {res}")
+    return stack, out, gate_up_bytes
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3-8b-block-linears",
+                    choices=["qwen3-8b-block-linears", "qwen3-0.6b-block-linears"])
+    ap.add_argument("--layers", type=int, default=0, help="override the layer count")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the sharding plan is described in the design notes, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_quantized_weight_linear_amd as q8
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    if args.workload == "qwen3-8b-block-linears":
+        spec = wl.QWEN3_8B_BLOCK
+        m_values = (1, 8)
+    else:
+        spec = wl.QWEN3_06B_BLOCK
+        m_values = (1,)
+    stack, res, gate_up_bytes = bench_block(args, torch, dev, q8, spec, m_values)
+    r1 = res[1]
+    line = {
+        "metric": METRIC,
+        "value": r1["gbps"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r1["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "m": 1, "layers": stack.layers, "weights": "Q8_0",
+                   "linears": {l.name: [l.n, l.k] for l in spec.linears},
+                   "weight_bytes_per_step": r1["weight_bytes_per_step"]},
+        "hbm_frac": r1["hbm_frac"],
+        "decode_tok_s": r1["tok_s"],
+        "roofline": {"bound": "hbm", "kernel": "fused gate_up + SiLU (gemv_q8_kernel<1,2,true>)",
+                     "achieved": r1["gate_up_gbps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(r1["gate_up_gbps"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": gate_up_bytes, "avg_launch_us": r1["gate_up_avg_us"]},
+    }
+    for m, r in res.items():
+        if m != 1:
+            line[f"m{m}"] = r
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on one layer")
+        line["cpu_baseline"] = cpu_baseline_block(spec)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

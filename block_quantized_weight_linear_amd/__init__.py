@@ -1,0 +1,18 @@
+"""MI355X (gfx950) Q8_0 block-quantized weight linear.
+
+Python binding of the C ABI in include/q8_linear.h (libq8linear.so, built in-tree by
+``python -m block_quantized_weight_linear_amd.build``).  PyTorch provides device
+memory and streams; all computation runs in the library's HIP kernels.
+"""
+
+from ._binding import (  # noqa: F401
+    LIB_PATH,
+    Q8Error,
+    abi_version,
+    lib,
+    moe_route_topk,
+    q8_linear,
+    q8_linear_fused_gate_up_silu,
+    q8_moe_grouped_linear,
+    q8_moe_workspace_bytes,
+)

@@ -1,0 +1,178 @@
+"""ctypes binding of include/q8_linear.h.
+
+Argument marshalling only: checks tensor dtypes/devices, allocates outputs with
+torch when none are given, passes raw device pointers, sizes and torch's current
+HIP stream, and turns a non-zero status into Q8Error.  Every step of the
+computation runs in the HIP library; there is no fallback.  Importing raises if
+the library has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+# torch ships its own HIP runtime (libamdhip64.so.7).  The library links the same
+# soname, and the first copy loaded serves the whole process; importing torch first
+# makes that torch's copy, so tensors, streams and our kernels share one runtime.
+import torch  # noqa: F401  (imported for its side effect on the loaded HIP runtime)
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libq8linear.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: the HIP library has not been built "
+        "(python -m block_quantized_weight_linear_amd.build)")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_i64, _i32, _vp, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+
+lib.q8_abi_version.restype = _i32
+lib.q8_abi_version.argtypes = []
+lib.q8_status_string.restype = ctypes.c_char_p
+lib.q8_status_string.argtypes = [ctypes.c_int]
+lib.q8_last_error.restype = ctypes.c_char_p
+lib.q8_last_error.argtypes = []
+lib.q8_linear.restype = ctypes.c_int
+lib.q8_linear.argtypes = [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp]
+lib.q8_linear_fused_gate_up_silu.restype = ctypes.c_int
+lib.q8_linear_fused_gate_up_silu.argtypes = [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp]
+lib.moe_route_topk.restype = ctypes.c_int
+lib.moe_route_topk.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _i32, _i32, _vp, _vp, _vp]
+lib.q8_moe_workspace_bytes.restype = _sz
+lib.q8_moe_workspace_bytes.argtypes = [_i64, _i32, _i64, _i64, _i64]
+lib.q8_moe_grouped_linear.restype = ctypes.c_int
+lib.q8_moe_grouped_linear.argtypes = [_vp, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _i32, _vp, _i64,
+                                      _vp, _sz, _vp]
+
+Q8_OK, Q8_ERR_NULL, Q8_ERR_SHAPE, Q8_ERR_ALIGN, Q8_ERR_WORKSPACE, Q8_ERR_DEVICE = range(6)
+
+
+class Q8Error(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{lib.q8_status_string(status).decode()} ({status}): {detail}")
+
+
+def check(status: int) -> None:
+    if status != Q8_OK:
+        raise Q8Error(status, lib.q8_last_error().decode())
+
+
+def abi_version() -> int:
+    return int(lib.q8_abi_version())
+
+
+def _torch():
+    return torch
+
+
+def _stream(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev(t, dtype, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _ld(x, width):
+    """Leading dimension to pass for a 2-D tensor whose rows hold `width` used values."""
+    if x.shape[0] <= 1:  # a single row: only its first `width` values are touched
+        return width + (-width % 4)
+    return x.stride(0)
+
+
+def q8_linear(w, n: int, k: int, x, out=None):
+    """y = x . W^T for a Q8_0 weight W [n][k] (uint8 bytes) and float32 x [m][k]."""
+    torch = _torch()
+    _dev(w, torch.uint8, "w")
+    _dev(x, torch.float32, "x")
+    if x.dim() != 2 or x.shape[1] != k or (x.numel() and x.stride(1) != 1):
+        raise ValueError(f"x must be [m][{k}] with contiguous rows")
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _dev(out, torch.float32, "out")
+    check(lib.q8_linear(w.data_ptr(), n, k, x.data_ptr(), m, _ld(x, k), out.data_ptr(), _ld(out, n), _stream(x)))
+    return out
+
+
+def q8_linear_fused_gate_up_silu(w, f: int, k: int, x, out=None):
+    """h = SiLU(x . W_gate^T) * (x . W_up^T); W is Q8_0 [2f][k], gate rows first."""
+    torch = _torch()
+    _dev(w, torch.uint8, "w")
+    _dev(x, torch.float32, "x")
+    if x.dim() != 2 or x.shape[1] != k or (x.numel() and x.stride(1) != 1):
+        raise ValueError(f"x must be [m][{k}] with contiguous rows")
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, f), dtype=torch.float32, device=x.device)
+    _dev(out, torch.float32, "out")
+    check(lib.q8_linear_fused_gate_up_silu(w.data_ptr(), f, k, x.data_ptr(), m, _ld(x, k), out.data_ptr(),
+                                           _ld(out, f), _stream(x)))
+    return out
+
+
+def moe_route_topk(x, w_router, k: int, normalize: bool = True, idx_out=None, w_out=None):
+    """Softmax top-k routing; returns (topk_idx int32 [m][k], topk_w float32 [m][k])."""
+    torch = _torch()
+    _dev(x, torch.float32, "x")
+    _dev(w_router, torch.float32, "w_router")
+    if not w_router.is_contiguous() or w_router.dim() != 2:
+        raise ValueError("w_router must be a contiguous [n_exp][h] tensor")
+    n_exp, h = w_router.shape
+    if x.dim() != 2 or x.shape[1] != h or (x.numel() and x.stride(1) != 1):
+        raise ValueError(f"x must be [m][{h}] with contiguous rows")
+    m = x.shape[0]
+    if idx_out is None:
+        idx_out = torch.empty((m, k), dtype=torch.int32, device=x.device)
+    if w_out is None:
+        w_out = torch.empty((m, k), dtype=torch.float32, device=x.device)
+    _dev(idx_out, torch.int32, "idx_out")
+    _dev(w_out, torch.float32, "w_out")
+    if not (idx_out.is_contiguous() and w_out.is_contiguous()):
+        raise ValueError("idx_out and w_out must be contiguous")
+    check(lib.moe_route_topk(x.data_ptr(), m, h, _ld(x, h), w_router.data_ptr(), n_exp, k, 1 if normalize else 0,
+                             idx_out.data_ptr(), w_out.data_ptr(), _stream(x)))
+    return idx_out, w_out
+
+
+def q8_moe_workspace_bytes(m: int, k: int, n_exp: int, f: int, h: int) -> int:
+    return int(lib.q8_moe_workspace_bytes(m, k, n_exp, f, h))
+
+
+def q8_moe_grouped_linear(w_gate_up_exps, w_down_exps, n_exp: int, f: int, h: int, x, topk_idx, topk_w,
+                          out=None, workspace=None):
+    """Router-weighted SwiGLU expert mixture; returns y float32 [m][h]."""
+    torch = _torch()
+    _dev(w_gate_up_exps, torch.uint8, "w_gate_up_exps")
+    _dev(w_down_exps, torch.uint8, "w_down_exps")
+    _dev(x, torch.float32, "x")
+    _dev(topk_idx, torch.int32, "topk_idx")
+    _dev(topk_w, torch.float32, "topk_w")
+    if x.dim() != 2 or x.shape[1] != h or (x.numel() and x.stride(1) != 1):
+        raise ValueError(f"x must be [m][{h}] with contiguous rows")
+    m = x.shape[0]
+    if topk_idx.dim() != 2 or topk_idx.shape[0] != m or not topk_idx.is_contiguous():
+        raise ValueError("topk_idx must be a contiguous [m][k] tensor")
+    k = topk_idx.shape[1]
+    if tuple(topk_w.shape) != (m, k) or not topk_w.is_contiguous():
+        raise ValueError("topk_w must be a contiguous [m][k] tensor")
+    if out is None:
+        out = torch.empty((m, h), dtype=torch.float32, device=x.device)
+    _dev(out, torch.float32, "out")
+    need = q8_moe_workspace_bytes(m, k, n_exp, f, h) if m else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _dev(workspace, torch.uint8, "workspace")
+    check(lib.q8_moe_grouped_linear(w_gate_up_exps.data_ptr(), w_down_exps.data_ptr(), n_exp, f, h, x.data_ptr(), m,
+                                    _ld(x, h), topk_idx.data_ptr(), topk_w.data_ptr(), k, out.data_ptr(),
+                                    _ld(out, h), workspace.data_ptr(), workspace.numel(), _stream(x)))
+    return out

@@ -1,0 +1,158 @@
+// C ABI entry points (include/q8_linear.h): validate on the host, then enqueue.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "q8_internal.h"
+#include "q8_validate.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+void set_err(const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+}
+
+q8_status device_fail(const char* where, hipError_t e) {
+    set_err("%s: HIP error %d (%s)", where, (int)e, hipGetErrorString(e));
+    return Q8_ERR_DEVICE;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_dev_mu;
+q8k::DeviceInfo g_dev[kMaxDevices];
+
+}  // namespace
+
+namespace q8k {
+
+hipError_t current_device_info(DeviceInfo* out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_dev_mu);
+    DeviceInfo& d = g_dev[dev];
+    if (d.device != dev) {
+        int cus = 0;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        int lds = 0;
+        e = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+        if (e != hipSuccess) return e;
+        d.cu_count = cus;
+        d.lds_per_block = (size_t)lds;
+        d.device = dev;
+    }
+    *out = d;
+    return hipSuccess;
+}
+
+}  // namespace q8k
+
+extern "C" {
+
+int32_t q8_abi_version(void) { return Q8_ABI_VERSION; }
+
+const char* q8_status_string(q8_status s) {
+    switch (s) {
+        case Q8_OK: return "ok";
+        case Q8_ERR_NULL: return "null pointer";
+        case Q8_ERR_SHAPE: return "invalid shape";
+        case Q8_ERR_ALIGN: return "misaligned pointer or leading dimension";
+        case Q8_ERR_WORKSPACE: return "workspace missing or too small";
+        case Q8_ERR_DEVICE: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* q8_last_error(void) { return g_err; }
+
+static q8_status linear_common(const char* name, const void* w, int64_t n_out, int64_t k, bool silu, const float* x,
+                               int64_t m, int64_t ldx, float* y, int64_t ldy, void* stream) {
+    g_err[0] = 0;
+    char msg[256];
+    q8_status s = q8v::check_linear(w, n_out, k, x, m, ldx, y, ldy, msg, sizeof msg);
+    if (s != Q8_OK) {
+        set_err("%s: %s", name, msg);
+        return s;
+    }
+    if (m == 0 || n_out == 0) return Q8_OK;
+    q8k::DeviceInfo dev;
+    hipError_t e = q8k::current_device_info(&dev);
+    if (e != hipSuccess) return device_fail(name, e);
+    e = q8k::launch_gemv_q8(dev, static_cast<const uint8_t*>(w), n_out, k, silu, x, m, ldx, y, ldy,
+                            static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_fail(name, e);
+    return Q8_OK;
+}
+
+q8_status q8_linear(const void* w_q8, int64_t n, int64_t k, const float* x, int64_t m, int64_t ldx, float* y,
+                    int64_t ldy, void* stream) {
+    return linear_common("q8_linear", w_q8, n, k, false, x, m, ldx, y, ldy, stream);
+}
+
+q8_status q8_linear_fused_gate_up_silu(const void* w_gate_up_q8, int64_t f, int64_t k, const float* x, int64_t m,
+                                       int64_t ldx, float* h, int64_t ldh, void* stream) {
+    return linear_common("q8_linear_fused_gate_up_silu", w_gate_up_q8, f, k, true, x, m, ldx, h, ldh, stream);
+}
+
+q8_status moe_route_topk(const float* x, int64_t m, int64_t h, int64_t ldx, const float* w_router, int64_t n_exp,
+                         int32_t k, int32_t normalize, int32_t* topk_idx, float* topk_w, void* stream) {
+    g_err[0] = 0;
+    char msg[256];
+    q8_status s = q8v::check_route(x, m, h, ldx, w_router, n_exp, k, topk_idx, topk_w, msg, sizeof msg);
+    if (s != Q8_OK) {
+        set_err("moe_route_topk: %s", msg);
+        return s;
+    }
+    if (m == 0) return Q8_OK;
+    q8k::DeviceInfo dev;
+    hipError_t e = q8k::current_device_info(&dev);
+    if (e != hipSuccess) return device_fail("moe_route_topk", e);
+    e = q8k::launch_route_topk(dev, x, m, h, ldx, w_router, n_exp, k, normalize != 0, topk_idx, topk_w,
+                               static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_fail("moe_route_topk", e);
+    return Q8_OK;
+}
+
+size_t q8_moe_workspace_bytes(int64_t m, int32_t k, int64_t n_exp, int64_t f, int64_t h) {
+    char msg[8];
+    if (q8v::check_dim("m", m, msg, sizeof msg) != Q8_OK || q8v::check_k("f", f, msg, sizeof msg) != Q8_OK ||
+        q8v::check_k("h", h, msg, sizeof msg) != Q8_OK || h > q8v::kMoeMaxDim || f > q8v::kMoeMaxDim || n_exp < 1 || n_exp > q8v::kMaxExperts || k < 1 ||
+        k > n_exp || m * int64_t(k) > (int64_t(1) << 24))
+        return 0;
+    return q8v::moe_workspace_layout(m, k, n_exp, f, h).total;
+}
+
+q8_status q8_moe_grouped_linear(const void* w_gate_up_exps, const void* w_down_exps, int64_t n_exp, int64_t f,
+                                int64_t h, const float* x, int64_t m, int64_t ldx, const int32_t* topk_idx,
+                                const float* topk_w, int32_t k, float* y, int64_t ldy, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    char msg[256];
+    q8_status s = q8v::check_moe(w_gate_up_exps, w_down_exps, n_exp, f, h, x, m, ldx, topk_idx, topk_w, k, y, ldy,
+                                 workspace, workspace_bytes, msg, sizeof msg);
+    if (s != Q8_OK) {
+        set_err("q8_moe_grouped_linear: %s", msg);
+        return s;
+    }
+    if (m == 0) return Q8_OK;
+    q8k::DeviceInfo dev;
+    hipError_t e = q8k::current_device_info(&dev);
+    if (e != hipSuccess) return device_fail("q8_moe_grouped_linear", e);
+    e = q8k::launch_moe_grouped(dev, static_cast<const uint8_t*>(w_gate_up_exps),
+                                static_cast<const uint8_t*>(w_down_exps), n_exp, f, h, x, m, ldx, topk_idx, topk_w, k,
+                                y, ldy, workspace, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_fail("q8_moe_grouped_linear", e);
+    return Q8_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,35 @@
+// Internal launcher interface between the C ABI (q8_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace q8k {
+
+// Per-device facts the launchers size their grids with.
+struct DeviceInfo {
+    int device = -1;
+    int cu_count = 0;
+    size_t lds_per_block = 0;
+};
+
+// Returns the cached info of the current device (queried once per device).
+hipError_t current_device_info(DeviceInfo* out);
+
+// y[m][n] = x[m] . W[n]^T for m <= 16 rows (float32 path).  When silu_pairs is true,
+// W has 2*n_out rows and the output is SiLU(gate) * up with gate row j, up row n_out+j.
+hipError_t launch_gemv_q8(const DeviceInfo& dev, const uint8_t* w, int64_t n_out, int64_t k, bool silu_pairs,
+                          const float* x, int64_t m, int64_t ldx, float* y, int64_t ldy, hipStream_t stream);
+
+// Softmax top-k router.
+hipError_t launch_route_topk(const DeviceInfo& dev, const float* x, int64_t m, int64_t h, int64_t ldx,
+                             const float* w_router, int64_t n_exp, int k, bool normalize, int32_t* idx, float* wts,
+                             hipStream_t stream);
+
+// Grouped MoE SwiGLU mixture; workspace laid out by q8v::moe_workspace_layout.
+hipError_t launch_moe_grouped(const DeviceInfo& dev, const uint8_t* wgu, const uint8_t* wdn, int64_t n_exp, int64_t f,
+                              int64_t h, const float* x, int64_t m, int64_t ldx, const int32_t* idx, const float* wts,
+                              int k, float* y, int64_t ldy, void* workspace, hipStream_t stream);
+
+}  // namespace q8k

@@ -1,0 +1,138 @@
+// Softmax top-k MoE router on the device (gfx950).
+//
+// "14. Model families and example applications" section 14.2: the MoE FFN routes with
+// routerTopK (normalize_selected = norm_topk_prob); the engine does that on the host,
+// here it stays on the device so the mixture can follow without a host round trip.
+//
+// One workgroup (4 waves) per token.  Logits: each wave takes experts e = wave, wave+4,
+// ...; a lane multiplies float4 slices k = 4*lane + 256*i and the wave sums its 64
+// partials with a fixed xor-butterfly (float32 throughout).  Softmax and selection run
+// on wave 0: the row maximum is subtracted before exp, and the k experts are picked one
+// by one as the largest remaining logit, ties to the lower expert index (selecting on
+// the logits avoids ties that rounding exp() could create; softmax is monotonic, so
+// the order is that of the probabilities).  The chosen probabilities are divided by
+// their sum, taken in selection order, when normalize is set.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "q8_internal.h"
+
+namespace q8k {
+
+constexpr int kRouteThreads = 256;
+constexpr int kMaxExperts = 256;
+
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+    return v > bv || (v == bv && i < bi);
+}
+
+__global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float* __restrict__ x, int h, int ldx,
+                                                                   const float* __restrict__ wr, int n_exp, int k,
+                                                                   int normalize, int32_t* __restrict__ out_idx,
+                                                                   float* __restrict__ out_w) {
+    __shared__ float logits[kMaxExperts];
+    const int tok = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const float* xr = x + (size_t)tok * ldx;
+
+    for (int e = wave; e < n_exp; e += kRouteThreads / 64) {
+        const float* we = wr + (size_t)e * h;
+        float acc = 0.0f;
+        for (int kk = 4 * lane; kk < h; kk += 256) {
+            const float4 a = *reinterpret_cast<const float4*>(xr + kk);
+            const float4 b = *reinterpret_cast<const float4*>(we + kk);
+            acc = __builtin_fmaf(a.x, b.x, acc);
+            acc = __builtin_fmaf(a.y, b.y, acc);
+            acc = __builtin_fmaf(a.z, b.z, acc);
+            acc = __builtin_fmaf(a.w, b.w, acc);
+        }
+        for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+        if (lane == 0) logits[e] = acc;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+
+    // Each lane owns experts lane, lane+64, lane+128, lane+192.
+    float l[4];
+    int taken = 0;  // bit c: expert lane + 64c already selected
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int e = lane + 64 * c;
+        l[c] = e < n_exp ? logits[e] : -INFINITY;
+        if (e >= n_exp) taken |= 1 << c;
+    }
+    float mx = fmaxf(fmaxf(l[0], l[1]), fmaxf(l[2], l[3]));
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+    float ex[4];
+    float sum = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        ex[c] = (lane + 64 * c < n_exp) ? expf(l[c] - mx) : 0.0f;
+        sum += ex[c];
+    }
+    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+    const float inv_sum = 1.0f / sum;
+
+    // k rounds; after each butterfly every lane holds the winner.  Lane (j % 64) keeps
+    // round j's result in its register slot j / 64; the sum of the chosen
+    // probabilities is accumulated in selection order, identically on all lanes.
+    int keep_i[4] = {0, 0, 0, 0};
+    float keep_p[4] = {0.f, 0.f, 0.f, 0.f};
+    float psum = 0.0f;
+    for (int j = 0; j < k; ++j) {
+        float bv = -INFINITY;
+        int bi = 0x7fffffff;
+        float bp = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int e = lane + 64 * c;
+            if (!(taken & (1 << c)) && (bi == 0x7fffffff || better(l[c], e, bv, bi))) {
+                bv = l[c];
+                bi = e;
+                bp = ex[c];
+            }
+        }
+        for (int off = 32; off >= 1; off >>= 1) {
+            const float ov = __shfl_xor(bv, off, 64);
+            const int oi = __shfl_xor(bi, off, 64);
+            const float op = __shfl_xor(bp, off, 64);
+            if (oi != 0x7fffffff && (bi == 0x7fffffff || better(ov, oi, bv, bi))) {
+                bv = ov;
+                bi = oi;
+                bp = op;
+            }
+        }
+        if ((bi & 63) == lane) taken |= 1 << (bi >> 6);
+        const float p = bp * inv_sum;
+        psum += p;
+        if ((j & 63) == lane) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                if ((j >> 6) == c) {
+                    keep_i[c] = bi;
+                    keep_p[c] = p;
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int j = lane + 64 * c;
+        if (j < k) {
+            out_idx[(size_t)tok * k + j] = keep_i[c];
+            out_w[(size_t)tok * k + j] = normalize ? keep_p[c] / psum : keep_p[c];
+        }
+    }
+}
+
+hipError_t launch_route_topk(const DeviceInfo&, const float* x, int64_t m, int64_t h, int64_t ldx,
+                             const float* w_router, int64_t n_exp, int k, bool normalize, int32_t* idx, float* wts,
+                             hipStream_t stream) {
+    hipLaunchKernelGGL(route_topk_kernel, dim3((unsigned)m), dim3(kRouteThreads), 0, stream, x, (int)h, (int)ldx,
+                       w_router, (int)n_exp, k, normalize ? 1 : 0, idx, wts);
+    return hipGetLastError();
+}
+
+}  // namespace q8k

@@ -1,0 +1,144 @@
+/*
+ * q8_linear.h -- C ABI of the MI355X (gfx950) Q8_0 block-quantized weight linear.
+ *
+ * What is computed (sources are the pages describing the fucina engine):
+ *   - "14. Model families and example applications", section 14.1 (Conventions shared
+ *     by every family): LinearWeight keeps the GGUF dtype resident and the quant forms,
+ *     Q8_0 among them, run packed kernels with no global dequantization at load; q/k/v
+ *     are fused into one QKV matrix and gate/up into one gate_up matrix, one wider
+ *     product per block.
+ *   - Same page, section 14.2 (Qwen3 - dense and MoE): SwiGLU FFN; lockstep batch
+ *     decode runs the trunk as one m = n pass that reads the weights once for all
+ *     streams; the MoE FFN routes with softmax top-k (routerTopK, normalize_selected =
+ *     norm_topk_prob) and runs the router-weighted SwiGLU mixture (moeSwiGluFfnSeq),
+ *     whose prefill groups tokens by expert so each expert's weights are read once.
+ *   - Same page, section 14.4 (Gemma 4 - text + MoE, "MoE expert kernels"): a
+ *     counting-sort route plan and a per-token summation order kept fixed.
+ *
+ * Q8_0 tensor layout (the GGUF Q8_0 block; the pages name the format without spelling
+ * it out): a row of length K is K/32 blocks of 34 bytes, each a little-endian IEEE
+ * binary16 scale d followed by 32 signed 8-bit quants q; the weight is w = d * q.
+ * Rows are contiguous: row n starts at byte n * (K/32) * 34.  Expert stacks are E such
+ * matrices back to back.
+ *
+ * Conventions for every call below:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; nothing is freed,
+ *     retained or allocated by the library.  Weights and inputs are only read.
+ *   - Row-major float32 activations x [M][ldx] (the first K of each row used) and
+ *     outputs [M][ld*].  Outputs are fully overwritten, never accumulated into.
+ *   - stream is a hipStream_t passed as void* (NULL = the null stream).  Calls are
+ *     asynchronous: they enqueue kernels and return; they never synchronize.
+ *   - Arguments are validated on the host before anything is enqueued; on a bad
+ *     argument the call returns an error code and enqueues nothing.  A launch failure
+ *     reported by the HIP runtime returns Q8_ERR_DEVICE.  q8_last_error() then holds a
+ *     thread-local description.
+ *   - M = 0 (no rows) and N = 0 (no outputs) are valid and enqueue nothing.
+ *   - K (and the MoE H and F) must be positive multiples of 256 (rows then stay 16-byte
+ *     aligned: 8 blocks are 272 bytes); otherwise Q8_ERR_SHAPE.
+ *   - Alignment: weight and x base pointers 16-byte aligned and ldx a multiple of 4;
+ *     output pointers 4-byte aligned; otherwise Q8_ERR_ALIGN.
+ *   - Results are deterministic: the same inputs give bit-identical outputs on every
+ *     call (fixed summation orders, no floating-point atomics).
+ *   - Calls are thread-safe; the only global state is the thread-local error text and
+ *     a per-device cache of launch sizes.
+ */
+#ifndef Q8_LINEAR_H
+#define Q8_LINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q8_ABI_VERSION 1
+
+typedef enum q8_status {
+    Q8_OK = 0,
+    Q8_ERR_NULL = 1,      /* a required pointer is NULL                                   */
+    Q8_ERR_SHAPE = 2,     /* a size is negative, too large, or breaks the block structure */
+    Q8_ERR_ALIGN = 3,     /* a pointer or leading dimension is misaligned                 */
+    Q8_ERR_WORKSPACE = 4, /* workspace missing or smaller than q8_moe_workspace_bytes()   */
+    Q8_ERR_DEVICE = 5     /* the HIP runtime reported an error                            */
+} q8_status;
+
+/* Version of this ABI (Q8_ABI_VERSION of the built library). */
+int32_t q8_abi_version(void);
+
+/* Static text for a status code. */
+const char* q8_status_string(q8_status status);
+
+/* Thread-local description of the last failure on this thread ("" if none). */
+const char* q8_last_error(void);
+
+/*
+ * y = x . W^T  -- the packed-weight linear (section 14.1, LinearWeight; the fused QKV
+ * and down projections use it directly).
+ *   w_q8 : Q8_0 [n][k]          x : float32 [m][ldx]          y : float32 [m][ldy]
+ *   n >= 0 outputs, k > 0 a multiple of 256, m >= 0 rows, ldx >= k, ldy >= n.
+ * Every row of y is computed by the same per-row arithmetic whatever m is, so a row's
+ * result does not depend on the other rows in the batch (the lockstep m = n pass of
+ * section 14.2).  Rows m >= 256 use the bf16 matrix-core path when one is built for
+ * this library version; the current version uses the float32 path for every m.
+ */
+q8_status q8_linear(const void* w_q8, int64_t n, int64_t k,
+                    const float* x, int64_t m, int64_t ldx,
+                    float* y, int64_t ldy, void* stream);
+
+/*
+ * h = SiLU(x . W_gate^T) * (x . W_up^T) from one fused gate_up matrix (section 14.1 fuses
+ * gate and up; section 14.2 gives the SwiGLU FFN).  SiLU(g) = g / (1 + exp(-g)).
+ *   w_gate_up_q8 : Q8_0 [2f][k], gate rows [0, f) then up rows [f, 2f)
+ *   x : float32 [m][ldx]          h : float32 [m][ldh], ldh >= f
+ * Same rules as q8_linear otherwise.
+ */
+q8_status q8_linear_fused_gate_up_silu(const void* w_gate_up_q8, int64_t f, int64_t k,
+                                       const float* x, int64_t m, int64_t ldx,
+                                       float* h, int64_t ldh, void* stream);
+
+/*
+ * Softmax top-k routing (section 14.2: routerTopK with normalize_selected =
+ * norm_topk_prob, run on the device here instead of on the host).
+ *   x        : float32 [m][ldx], hidden size h (h > 0 a multiple of 256, ldx >= h)
+ *   w_router : float32 [n_exp][h], row-major, 1 <= n_exp <= 256
+ *   k        : 1 <= k <= n_exp experts per token
+ *   normalize: nonzero -> the chosen probabilities are divided by their sum
+ *   topk_idx : int32 [m][k] out, descending probability, ties to the lower expert index
+ *   topk_w   : float32 [m][k] out
+ * Logits and the softmax are computed in float32.
+ */
+q8_status moe_route_topk(const float* x, int64_t m, int64_t h, int64_t ldx,
+                         const float* w_router, int64_t n_exp, int32_t k, int32_t normalize,
+                         int32_t* topk_idx, float* topk_w, void* stream);
+
+/* Workspace bytes q8_moe_grouped_linear needs for these sizes (0 on invalid sizes). */
+size_t q8_moe_workspace_bytes(int64_t m, int32_t k, int64_t n_exp, int64_t f, int64_t h);
+
+/*
+ * Router-weighted SwiGLU expert mixture (section 14.2: moeSwiGluFfnSeq; section 14.4:
+ * counting-sort route plan, fixed per-token summation order):
+ *   y[t] = sum_{j=0..k-1} topk_w[t][j] * W_down[e] . (SiLU(W_gate[e] x_t) * (W_up[e] x_t)),
+ *   e = topk_idx[t][j], summed in slot order j = 0, 1, ..., k-1.
+ *   w_gate_up_exps : Q8_0 [n_exp][2f][h] (gate rows [0,f), up rows [f,2f) per expert)
+ *   w_down_exps    : Q8_0 [n_exp][h][f]
+ *   x : float32 [m][ldx] (ldx >= h)     y : float32 [m][ldy] (ldy >= h)
+ *   topk_idx : int32 [m][k], every entry in [0, n_exp) (a precondition: entries outside
+ *              it are skipped on the device and contribute nothing)
+ *   topk_w   : float32 [m][k]
+ *   workspace: device memory of at least q8_moe_workspace_bytes(m, k, n_exp, f, h)
+ *              bytes, 256-byte aligned; its contents on entry do not matter.
+ * Each expert's weights are read once per call for all tokens routed to it.
+ */
+q8_status q8_moe_grouped_linear(const void* w_gate_up_exps, const void* w_down_exps,
+                                int64_t n_exp, int64_t f, int64_t h,
+                                const float* x, int64_t m, int64_t ldx,
+                                const int32_t* topk_idx, const float* topk_w, int32_t k,
+                                float* y, int64_t ldy,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q8_LINEAR_H */

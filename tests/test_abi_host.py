@@ -1,0 +1,144 @@
+"""The C ABI library on the host (no GPU needed): it loads, exports every function the
+header declares, and rejects bad arguments before touching the device.
+
+None of these calls reaches a kernel: every argument error is detected on the host,
+and zero-size calls return before any HIP call.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q8_linear.h")
+
+q8 = pytest.importorskip("block_quantized_weight_linear_amd")
+lib = q8.lib
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_DEVICE = range(6)
+FAKE = 0x10000  # 64 KiB: a 256-byte aligned, non-null address that is never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("q8_linear", "q8_linear_fused_gate_up_silu", "moe_route_topk", "q8_moe_grouped_linear",
+              "q8_moe_workspace_bytes", "q8_status_string", "q8_last_error", "q8_abi_version"):
+        assert n in names, names
+
+
+def test_library_exports_every_declared_symbol():
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert q8.abi_version() == 1
+
+
+def test_status_strings():
+    for s in range(6):
+        assert lib.q8_status_string(s)
+    assert lib.q8_status_string(99) == b"unknown status"
+
+
+def _lin(w=FAKE, n=64, k=256, x=FAKE, m=1, ldx=256, y=FAKE, ldy=64, fused=False):
+    fn = lib.q8_linear_fused_gate_up_silu if fused else lib.q8_linear
+    return fn(w, n, k, x, m, ldx, y, ldy, None)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_linear_argument_errors(fused):
+    assert _lin(k=0, fused=fused) == ERR_SHAPE
+    assert _lin(k=32, fused=fused) == ERR_SHAPE          # a Q8_0 multiple but not of 256
+    assert _lin(k=384, fused=fused) == ERR_SHAPE
+    assert _lin(n=-1, fused=fused) == ERR_SHAPE
+    assert _lin(m=-3, fused=fused) == ERR_SHAPE
+    assert _lin(ldx=128, fused=fused) == ERR_SHAPE
+    assert _lin(ldy=63, fused=fused) == ERR_SHAPE
+    assert _lin(w=None, fused=fused) == ERR_NULL
+    assert _lin(x=None, fused=fused) == ERR_NULL
+    assert _lin(y=None, fused=fused) == ERR_NULL
+    assert _lin(w=FAKE + 4, fused=fused) == ERR_ALIGN
+    assert _lin(x=FAKE + 8, fused=fused) == ERR_ALIGN
+    assert _lin(m=2, ldx=258, fused=fused) == ERR_ALIGN
+    assert _lin(y=FAKE + 2, fused=fused) == ERR_ALIGN
+    msg = lib.q8_last_error().decode()
+    assert "aligned" in msg
+
+
+def test_zero_sizes_enqueue_nothing():
+    # no rows or no outputs: valid, nothing enqueued, pointers may be null
+    assert _lin(m=0, w=None, x=None, y=None) == OK
+    assert _lin(n=0, w=None, x=None, y=None, ldy=0) == OK
+    assert lib.moe_route_topk(None, 0, 256, 256, None, 8, 2, 1, None, None, None) == OK
+    assert lib.q8_moe_grouped_linear(None, None, 8, 256, 256, None, 0, 256, None, None, 2, None, 256,
+                                     None, 0, None) == OK
+
+
+def test_route_argument_errors():
+    def call(x=FAKE, m=2, h=256, ldx=256, w=FAKE, e=8, k=2, idx=FAKE, wt=FAKE):
+        return lib.moe_route_topk(x, m, h, ldx, w, e, k, 1, idx, wt, None)
+
+    assert call(h=100) == ERR_SHAPE
+    assert call(e=0) == ERR_SHAPE
+    assert call(e=257) == ERR_SHAPE
+    assert call(k=0) == ERR_SHAPE
+    assert call(k=9) == ERR_SHAPE
+    assert call(ldx=128) == ERR_SHAPE
+    assert call(x=None) == ERR_NULL
+    assert call(idx=None) == ERR_NULL
+    assert call(w=FAKE + 4) == ERR_ALIGN
+    assert call(wt=FAKE + 2) == ERR_ALIGN
+
+
+def test_moe_workspace_and_errors():
+    need = lib.q8_moe_workspace_bytes(16, 8, 128, 768, 2048)
+    pairs = 16 * 8
+    assert need >= 4 * (129 + 2 * pairs) + 4 * pairs * (768 + 2048)
+    assert need % 256 == 0
+    assert lib.q8_moe_workspace_bytes(16, 9, 8, 768, 2048) == 0      # k > n_exp
+    assert lib.q8_moe_workspace_bytes(16, 2, 8, 100, 2048) == 0      # f not a multiple of 256
+    assert lib.q8_moe_workspace_bytes(16, 2, 8, 768, 32768) == 0     # h above 16384
+
+    def call(e=8, f=256, h=256, m=2, k=2, ws=FAKE, wsb=None, idx=FAKE):
+        if wsb is None:
+            wsb = lib.q8_moe_workspace_bytes(m, k, e, f, h)
+        return lib.q8_moe_grouped_linear(FAKE, FAKE, e, f, h, FAKE, m, 256, idx, FAKE, k, FAKE, 256, ws, wsb, None)
+
+    assert call(wsb=16) == ERR_WORKSPACE
+    assert call(ws=None) == ERR_WORKSPACE
+    assert call(ws=FAKE + 16) == ERR_ALIGN
+    assert call(k=9) == ERR_SHAPE
+    assert call(f=200) == ERR_SHAPE
+    assert call(idx=None) == ERR_NULL
+
+
+def test_error_text_is_thread_local():
+    import threading
+
+    assert _lin(k=32) == ERR_SHAPE
+    here = lib.q8_last_error().decode()
+    seen = {}
+
+    def other():
+        seen["t"] = lib.q8_last_error().decode()
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert "k=32" in here and seen["t"] == ""
+
+
+def test_one_hip_runtime_in_process():
+    """torch bundles a HIP runtime with the same soname as the one the library links;
+    the binding imports torch first so only one copy is ever mapped."""
+    maps = open("/proc/self/maps").read()
+    paths = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(paths) == 1, paths

@@ -1,0 +1,226 @@
+"""GPU parity of q8_linear and q8_linear_fused_gate_up_silu against the CPU oracle.
+
+Small shapes (many tiles and ragged tails) are compared element by element with the
+full oracle; the Qwen3 layer shapes at their real sizes are compared on sampled
+output rows the oracle computes one by one.  Exact-arithmetic inputs (every partial
+sum representable in float32) must match bit for bit.  Invariants: batch invariance,
+run-to-run determinism, scale doubling, sign symmetry, zero blocks, one-hot gathers.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from gpu_util import TOL, assert_close, row_slice, sample_rows, say, to_dev, torch_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q8():
+    torch, dev = torch_dev()
+    import block_quantized_weight_linear_amd as q8mod
+    return q8mod, torch, dev
+
+
+SMALL = [(1, 256), (3, 256), (37, 512), (257, 768), (1000, 1024), (4099, 1024), (513, 3072), (129, 4096),
+         (77, 12288), (64, 2048), (300, 6144)]
+
+
+@pytest.mark.parametrize("n,k", SMALL)
+@pytest.mark.parametrize("m", [1, 2, 3, 5, 8, 16, 17, 33])
+def test_linear_small_vs_oracle(q8, n, k, m):
+    lib, torch, dev = q8
+    wb, _, _ = wl.q8_weight(1000 + n + k, n, k)
+    x = wl.activations(2000 + m + k, m, k)
+    say(f"q8_linear n={n} k={k} m={m}")
+    y = lib.q8_linear(to_dev(wb, dev), n, k, to_dev(x, dev)).cpu().numpy()
+    assert_close(y, oracle.q8_linear_ref(wb, n, k, x), f"linear n={n} k={k} m={m}")
+
+
+@pytest.mark.parametrize("f,k", [(1, 256), (5, 512), (300, 1024), (1536, 1024), (129, 4096), (64, 768)])
+@pytest.mark.parametrize("m", [1, 4, 8, 16, 19])
+def test_fused_small_vs_oracle(q8, f, k, m):
+    lib, torch, dev = q8
+    wb, _, _ = wl.q8_weight(3000 + f + k, 2 * f, k)
+    x = wl.activations(4000 + m, m, k)
+    say(f"fused f={f} k={k} m={m}")
+    h = lib.q8_linear_fused_gate_up_silu(to_dev(wb, dev), f, k, to_dev(x, dev)).cpu().numpy()
+    assert_close(h, oracle.fused_gate_up_silu_ref(wb, f, k, x), f"fused f={f} k={k} m={m}")
+
+
+# ------------------------------------------------------------ real layer shapes
+
+LAYER_LINEARS = [
+    # (name, n, k, fused, rows)   n = outputs (F for fused)
+    ("0.6b qkv", 4096, 1024, False, (1,)),
+    ("0.6b gate_up", 3072, 1024, True, (1,)),
+    ("0.6b down", 1024, 3072, False, (1,)),
+    ("8b qkv", 6144, 4096, False, (1, 8)),
+    ("8b gate_up", 12288, 4096, True, (1, 8)),
+    ("8b down", 4096, 12288, False, (1, 8)),
+    ("8b gate_up plain", 24576, 4096, False, (16,)),
+]
+
+
+@pytest.mark.parametrize("name,n,k,fused,rows", LAYER_LINEARS, ids=[c[0] for c in LAYER_LINEARS])
+def test_layer_shapes_sampled(q8, name, n, k, fused, rows):
+    lib, torch, dev = q8
+    w_rows = 2 * n if fused else n
+    wb, _, _ = wl.q8_weight(11, w_rows, k)
+    wd = to_dev(wb, dev)
+    pick = sample_rows(n, 96, seed=n)
+    for m in rows:
+        x = wl.activations(12 + m, m, k)
+        say(f"{name} m={m}")
+        fn = lib.q8_linear_fused_gate_up_silu if fused else lib.q8_linear
+        y = fn(wd, n, k, to_dev(x, dev)).cpu().numpy()
+        if fused:
+            sub = np.concatenate([row_slice(wb, k, pick), row_slice(wb, k, pick + n)])
+            ref = oracle.fused_gate_up_silu_ref(sub, len(pick), k, x)
+        else:
+            ref = oracle.q8_linear_ref(row_slice(wb, k, pick), len(pick), k, x)
+        # each sampled output against its own oracle value; the row norm over the samples
+        assert_close(y[:, pick], ref, f"{name} m={m} ({len(pick)} sampled outputs)")
+        assert np.all(np.isfinite(y))
+
+
+@pytest.mark.parametrize("n,k,m", [(4096, 1024, 1), (6144, 4096, 8), (4096, 12288, 3), (24576, 4096, 16),
+                                   (1024, 3072, 1), (999, 256, 33)])
+def test_exact_arithmetic_bit_identical(q8, n, k, m):
+    """Integer activations in [-2, 2], scales 2^-7 / 2^-8: every float32 partial sum is exact."""
+    lib, torch, dev = q8
+    wb, _, _ = wl.q8_weight_exact(21 + n, n, k)
+    x = wl.activations_exact(22 + m, m, k)
+    say(f"exact n={n} k={k} m={m}")
+    y = lib.q8_linear(to_dev(wb, dev), n, k, to_dev(x, dev)).cpu().numpy()
+    if n * k > 30_000_000:
+        pick = sample_rows(n, 256, seed=3)
+        ref = oracle.q8_linear_ref(row_slice(wb, k, pick), len(pick), k, x)
+        got = y[:, pick]
+    else:
+        ref = oracle.q8_linear_ref(wb, n, k, x)
+        got = y
+    assert np.array_equal(got.astype(np.float64), ref), np.max(np.abs(got - ref))
+
+
+# ------------------------------------------------------------------- invariants
+
+
+@pytest.mark.parametrize("n,k", [(4096, 1024), (1024, 3072), (6144, 4096), (777, 12288)])
+def test_batch_invariance_and_determinism(q8, n, k):
+    lib, torch, dev = q8
+    wb, _, _ = wl.q8_weight(31, n, k)
+    wd = to_dev(wb, dev)
+    x = wl.activations(32, 40, k)
+    xd = to_dev(x, dev)
+    say(f"batch invariance n={n} k={k}")
+    y40 = lib.q8_linear(wd, n, k, xd).cpu().numpy()
+    y40b = lib.q8_linear(wd, n, k, xd).cpu().numpy()
+    assert np.array_equal(y40, y40b)  # run to run
+    for m in (1, 2, 5, 8, 16):
+        ym = lib.q8_linear(wd, n, k, xd[:m].contiguous()).cpu().numpy()
+        assert np.array_equal(ym, y40[:m]), m
+    for r in (0, 7, 15, 16, 39):
+        y1 = lib.q8_linear(wd, n, k, xd[r:r + 1].contiguous()).cpu().numpy()
+        assert np.array_equal(y1[0], y40[r]), r
+    # fused: same property
+    f = n // 2
+    h40 = lib.q8_linear_fused_gate_up_silu(wd, f, k, xd).cpu().numpy()
+    for r in (0, 9, 33):
+        h1 = lib.q8_linear_fused_gate_up_silu(wd, f, k, xd[r:r + 1].contiguous()).cpu().numpy()
+        assert np.array_equal(h1[0], h40[r]), r
+
+
+def test_scale_doubling_sign_and_zero_blocks(q8):
+    lib, torch, dev = q8
+    n, k, m = 2048, 2048, 4
+    _, q, d = wl.q8_weight(41, n, k)
+    x = wl.activations(42, m, k)
+    xd = to_dev(x, dev)
+    y = lib.q8_linear(to_dev(wl.pack_blocks(q, d), dev), n, k, xd).cpu().numpy()
+    d2 = (d.astype(np.float32) * 2).astype(np.float16)
+    y2 = lib.q8_linear(to_dev(wl.pack_blocks(q, d2), dev), n, k, xd).cpu().numpy()
+    assert np.array_equal(y2, 2 * y)
+    yx = lib.q8_linear(to_dev(wl.pack_blocks(q, d), dev), n, k, to_dev(2 * x, dev)).cpu().numpy()
+    assert np.array_equal(yx, 2 * y)
+    yn = lib.q8_linear(to_dev(wl.pack_blocks(-q, d), dev), n, k, xd).cpu().numpy()
+    assert np.array_equal(yn, -y)
+    mask = np.random.default_rng(1).random(d.shape) < 0.3
+    d0 = d.copy()
+    d0[mask] = 0
+    q0 = q.copy().reshape(n, k // 32, 32)
+    q0[mask] = 0
+    ya = lib.q8_linear(to_dev(wl.pack_blocks(q, d0), dev), n, k, xd).cpu().numpy()
+    yb = lib.q8_linear(to_dev(wl.pack_blocks(q0.reshape(n, k), d), dev), n, k, xd).cpu().numpy()
+    assert np.array_equal(ya, yb)
+    assert_close(ya, oracle.q8_linear_ref(wl.pack_blocks(q, d0), n, k, x), "zero blocks")
+    yz = lib.q8_linear(to_dev(wl.pack_blocks(q, np.zeros_like(d)), dev), n, k, xd).cpu().numpy()
+    assert np.all(yz == 0)
+
+
+def test_one_hot_gather(q8):
+    lib, torch, dev = q8
+    n, k, m = 1000, 4096, 3
+    perm = np.random.default_rng(5).permutation(k)[:n]
+    q = np.zeros((n, k), np.int8)
+    q[np.arange(n), perm] = 1
+    d = np.ones((n, k // 32), np.float16)
+    x = wl.activations(51, m, k)
+    y = lib.q8_linear(to_dev(wl.pack_blocks(q, d), dev), n, k, to_dev(x, dev)).cpu().numpy()
+    assert np.array_equal(y, x[:, perm])
+
+
+def test_hand_blocks_on_gpu(q8):
+    """The hand-derived cases, padded to K = 256 with zero blocks and zero activations."""
+    from golden_io import load_linear_cases
+    lib, torch, dev = q8
+    for c in load_linear_cases():
+        k0, n = c["k"], c["n"]
+        k = 256
+        rb0 = (k0 // 32) * 34
+        rows = np.frombuffer(c["w"], np.uint8).reshape(n, rb0)
+        pad = np.zeros((n, (k - k0) // 32 * 34), np.uint8)
+        wb = np.concatenate([rows, pad], axis=1).reshape(-1)
+        x = np.zeros((len(c["x"]), k), np.float32)
+        x[:, :k0] = np.array(c["x"], np.float32)
+        y = lib.q8_linear(to_dev(wb, dev), n, k, to_dev(x, dev)).cpu().numpy()
+        want = np.array([[float(v) for v in r] for r in c["y"]])
+        np.testing.assert_allclose(y, want, rtol=2e-7, atol=0, err_msg=c["name"])
+
+
+# ------------------------------------------------------------------- edge cases
+
+
+def test_edge_sizes_and_strides(q8):
+    lib, torch, dev = q8
+    k = 512
+    wb, _, _ = wl.q8_weight(61, 10, k)
+    wd = to_dev(wb, dev)
+    # no rows
+    y = lib.q8_linear(wd, 10, k, torch.empty((0, k), dtype=torch.float32, device=dev))
+    assert tuple(y.shape) == (0, 10)
+    # no outputs
+    y = lib.q8_linear(wd, 0, k, to_dev(wl.activations(1, 2, k), dev))
+    assert tuple(y.shape) == (2, 0)
+    # strided x and y: x rows inside a wider buffer, y written into a wider buffer
+    xb = to_dev(wl.activations(62, 5, k + 64), dev)
+    xs = xb[:, :k]
+    out = torch.full((5, 32), 7.0, dtype=torch.float32, device=dev)
+    lib.q8_linear(wd, 10, k, xs, out=out[:, :10])
+    o = out.cpu().numpy()
+    assert np.all(o[:, 10:] == 7.0)
+    assert_close(o[:, :10], oracle.q8_linear_ref(wb, 10, k, xs.cpu().numpy()), "strided")
+
+
+def test_binding_rejects_bad_arguments(q8):
+    lib, torch, dev = q8
+    wb, _, _ = wl.q8_weight(71, 8, 256)
+    wd = to_dev(wb, dev)
+    with pytest.raises(ValueError):
+        lib.q8_linear(wd, 8, 256, torch.zeros((1, 128), dtype=torch.float32, device=dev))
+    with pytest.raises(lib.Q8Error):
+        lib.q8_linear(wd[:0], 8, 96, torch.zeros((1, 96), dtype=torch.float32, device=dev))

@@ -1,0 +1,229 @@
+"""GPU parity of moe_route_topk and q8_moe_grouped_linear against the CPU oracle.
+
+Router indices must match exactly wherever the choice is unique at float32 precision:
+the oracle's float64 logits decide, and positions whose logit gap is below a bound on
+float32 rounding (`DELTA` times the row's sum of |x_i w_i|) are checked for validity
+instead (every chosen expert within that bound of the true order).  Exactly
+representable logits (small integers) must match bit for bit, ties included.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from gpu_util import TOL, assert_close, say, to_dev, torch_dev
+
+pytestmark = pytest.mark.gpu
+
+DELTA = 2.0 ** -16   # float32 logit error allowance per unit of sum |x_i w_i|
+
+
+@pytest.fixture(scope="module")
+def q8():
+    torch, dev = torch_dev()
+    import block_quantized_weight_linear_amd as q8mod
+    return q8mod, torch, dev
+
+
+def check_routing(idx_gpu, w_gpu, x, wr, k, normalize):
+    """Returns the number of tokens whose choice was ambiguous at float32 precision."""
+    ridx, rw = oracle.route_topk_ref(x, wr, k, normalize)
+    logits = oracle.router_logits_ref(x, wr)
+    scale = np.abs(x.astype(np.float64)) @ np.abs(wr.astype(np.float64)).T
+    ambiguous = 0
+    for t in range(x.shape[0]):
+        tol = DELTA * scale[t].max()
+        order = np.argsort(-logits[t], kind="stable")
+        srt = logits[t, order]
+        # the choice of position j is unique if its logit is separated from both neighbours
+        gaps = np.diff(-srt)  # >= 0
+        unique = True
+        for j in range(k):
+            left = gaps[j - 1] if j > 0 else np.inf
+            right = gaps[j] if j < len(gaps) else np.inf
+            if min(left, right) <= tol:
+                unique = False
+        if unique:
+            assert idx_gpu[t].tolist() == ridx[t].tolist(), (t, idx_gpu[t], ridx[t])
+            np.testing.assert_allclose(w_gpu[t], rw[t], rtol=TOL, atol=TOL * np.abs(rw[t]).max())
+        else:
+            ambiguous += 1
+            chosen = idx_gpu[t]
+            assert len(set(chosen.tolist())) == k
+            kth = srt[k - 1]
+            assert np.all(logits[t, chosen] >= kth - tol), t
+            assert np.all(np.diff(logits[t, chosen]) <= tol), t
+    return ambiguous
+
+
+def _pad_h(a, h=256):
+    out = np.zeros((a.shape[0], h), np.float32)
+    out[:, :a.shape[1]] = a
+    return out
+
+
+def test_hand_router_cases(q8):
+    from golden_io import load_swiglu_router_cases
+    lib, torch, dev = q8
+    _, cases = load_swiglu_router_cases()
+    for c in cases:
+        x = _pad_h(np.array(c["x"], np.float32))
+        wr = _pad_h(np.array(c["w_router"], np.float32))
+        idx, w = lib.moe_route_topk(to_dev(x, dev), to_dev(wr, dev), c["k"], c["normalize"])
+        assert idx.cpu().numpy().tolist() == c["idx"], c["name"]
+        np.testing.assert_allclose(w.cpu().numpy(), np.array(c["w"]), rtol=1e-6, err_msg=c["name"])
+
+
+def test_exact_logits_with_ties(q8):
+    """Integer activations and router rows: float32 logits are exact, ties included."""
+    lib, torch, dev = q8
+    m, h, e = 64, 512, 40
+    rng = np.random.default_rng(7)
+    x = rng.integers(-1, 2, size=(m, h)).astype(np.float32)
+    wr = rng.integers(-1, 2, size=(e, h)).astype(np.float32)
+    wr[5] = wr[3]      # guaranteed ties
+    wr[17] = wr[3]
+    for k in (1, 4, 8, e):
+        idx, w = lib.moe_route_topk(to_dev(x, dev), to_dev(wr, dev), k, True)
+        ridx, rw = oracle.route_topk_ref(x, wr, k, True)
+        assert np.array_equal(idx.cpu().numpy(), ridx), k
+        np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=1e-5, atol=1e-7)
+
+
+@pytest.mark.parametrize("m,h,e,k,normalize", [(16, 2048, 128, 8, True), (16, 2048, 128, 8, False),
+                                               (257, 1024, 64, 6, True), (3, 256, 256, 256, True),
+                                               (1, 4096, 8, 2, True), (33, 768, 7, 1, True)])
+def test_router_vs_oracle(q8, m, h, e, k, normalize):
+    lib, torch, dev = q8
+    x = wl.activations(81 + m, m, h)
+    wr = wl.router_weight(82 + e, e, h)
+    say(f"router m={m} h={h} e={e} k={k}")
+    idx, w = lib.moe_route_topk(to_dev(x, dev), to_dev(wr, dev), k, normalize)
+    amb = check_routing(idx.cpu().numpy(), w.cpu().numpy(), x, wr, k, normalize)
+    say(f"router m={m}: {amb} ambiguous tokens")
+    if k == e and normalize:
+        p = oracle.softmax_ref(oracle.router_logits_ref(x, wr))
+        got = np.zeros_like(p)
+        np.put_along_axis(got, idx.cpu().numpy().astype(np.int64), w.cpu().numpy(), axis=1)
+        assert_close(got, p, "k=E full softmax")
+
+
+# ------------------------------------------------------------------------- MoE
+
+
+def _experts(seed, e, f, h):
+    gu = np.concatenate([wl.q8_weight(seed + i, 2 * f, h)[0] for i in range(e)])
+    dn = np.concatenate([wl.q8_weight(seed + 1000 + i, h, f)[0] for i in range(e)])
+    return gu, dn
+
+
+@pytest.fixture(scope="module")
+def a3b_layer():
+    cfg = wl.QWEN3_30B_A3B_MOE
+    gu, dn = _experts(cfg.seed * 10000, cfg.n_exp, cfg.ffn, cfg.hidden)
+    x = wl.activations(cfg.seed + 1, cfg.tokens, cfg.hidden)
+    wr = wl.router_weight(cfg.seed + 2, cfg.n_exp, cfg.hidden, cfg.router_std)
+    return cfg, gu, dn, x, wr
+
+
+def test_moe_layer_given_routing(q8, a3b_layer):
+    lib, torch, dev = q8
+    cfg, gu, dn, x, wr = a3b_layer
+    ridx, rw = oracle.route_topk_ref(x, wr, cfg.k, True)
+    say("moe 30b-a3b layer, oracle routing")
+    y = lib.q8_moe_grouped_linear(to_dev(gu, dev), to_dev(dn, dev), cfg.n_exp, cfg.ffn, cfg.hidden, to_dev(x, dev),
+                                  to_dev(ridx.astype(np.int32), dev), to_dev(rw.astype(np.float32), dev)).cpu().numpy()
+    ref = oracle.moe_mixture_ref(gu, dn, cfg.n_exp, cfg.ffn, cfg.hidden, x, ridx, rw.astype(np.float32))
+    assert_close(y, ref, "moe 30b-a3b layer (given routing)")
+
+
+def test_moe_layer_end_to_end(q8, a3b_layer):
+    """Device routing then the device mixture.  Where the routing choice is unique at
+    float32 precision it equals the oracle's (checked in check_routing); the mixture is
+    compared with the oracle's mixture for the experts the device chose, weighted by the
+    oracle's float64 softmax renormalized over those experts."""
+    lib, torch, dev = q8
+    cfg, gu, dn, x, wr = a3b_layer
+    xd = to_dev(x, dev)
+    idx, w = lib.moe_route_topk(xd, to_dev(wr, dev), cfg.k, True)
+    idx_h = idx.cpu().numpy()
+    amb = check_routing(idx_h, w.cpu().numpy(), x, wr, cfg.k, True)
+    say(f"moe 30b-a3b layer: {amb} of {cfg.tokens} tokens with a float32 near-tie in routing")
+    y = lib.q8_moe_grouped_linear(to_dev(gu, dev), to_dev(dn, dev), cfg.n_exp, cfg.ffn, cfg.hidden, xd, idx,
+                                  w).cpu().numpy()
+    p = oracle.softmax_ref(oracle.router_logits_ref(x, wr))
+    w_ref = np.take_along_axis(p, idx_h.astype(np.int64), axis=1)
+    w_ref = w_ref / w_ref.sum(axis=1, keepdims=True)
+    ref = oracle.moe_mixture_ref(gu, dn, cfg.n_exp, cfg.ffn, cfg.hidden, x, idx_h, w_ref)
+    assert_close(y, ref, "moe 30b-a3b layer (device routing)")
+    y2 = lib.q8_moe_grouped_linear(to_dev(gu, dev), to_dev(dn, dev), cfg.n_exp, cfg.ffn, cfg.hidden, xd, idx,
+                                   w).cpu().numpy()
+    assert np.array_equal(y, y2)  # deterministic
+
+
+@pytest.mark.parametrize("m,e,k,f,h", [(1, 8, 2, 256, 512), (37, 16, 4, 512, 256), (64, 4, 2, 256, 1024),
+                                       (5, 3, 3, 768, 2048), (200, 32, 8, 256, 256)])
+def test_moe_shapes_vs_oracle(q8, m, e, k, f, h):
+    lib, torch, dev = q8
+    gu, dn = _experts(500 + e, e, f, h)
+    x = wl.activations(90 + m, m, h)
+    idx, w = wl.random_routing(91 + m, m, e, k)
+    say(f"moe m={m} e={e} k={k} f={f} h={h}")
+    y = lib.q8_moe_grouped_linear(to_dev(gu, dev), to_dev(dn, dev), e, f, h, to_dev(x, dev), to_dev(idx, dev),
+                                  to_dev(w, dev)).cpu().numpy()
+    assert_close(y, oracle.moe_mixture_ref(gu, dn, e, f, h, x, idx, w), f"moe m={m} e={e}")
+
+
+def test_moe_k1_equals_dense_ffn_bitwise(q8):
+    """k = 1 with weight 1: the mixture is the chosen expert's dense SwiGLU FFN, and the
+    grouped kernels do the same per-row arithmetic as the dense calls."""
+    lib, torch, dev = q8
+    e, f, h, m = 6, 768, 2048, 9
+    gu, dn = _experts(700, e, f, h)
+    x = wl.activations(701, m, h)
+    idx = np.array([[i % e] for i in range(m)], np.int32)
+    w = np.ones((m, 1), np.float32)
+    gud, dnd, xd = to_dev(gu, dev), to_dev(dn, dev), to_dev(x, dev)
+    y = lib.q8_moe_grouped_linear(gud, dnd, e, f, h, xd, to_dev(idx, dev), to_dev(w, dev)).cpu().numpy()
+    gu_b = (2 * f) * (h // 32) * 34
+    dn_b = h * (f // 32) * 34
+    for t in range(m):
+        ex = int(idx[t, 0])
+        hid = lib.q8_linear_fused_gate_up_silu(gud[ex * gu_b:(ex + 1) * gu_b], f, h, xd[t:t + 1].contiguous())
+        out = lib.q8_linear(dnd[ex * dn_b:(ex + 1) * dn_b], h, f, hid).cpu().numpy()
+        assert np.array_equal(y[t], out[0]), t
+
+
+def test_moe_relabel_and_duplicates(q8):
+    lib, torch, dev = q8
+    e, f, h, m, k = 5, 256, 512, 11, 3
+    gu, dn = _experts(800, e, f, h)
+    x = wl.activations(801, m, h)
+    idx, w = wl.random_routing(802, m, e, k)
+    xd = to_dev(x, dev)
+    y = lib.q8_moe_grouped_linear(to_dev(gu, dev), to_dev(dn, dev), e, f, h, xd, to_dev(idx, dev),
+                                  to_dev(w, dev)).cpu().numpy()
+    perm = np.array([3, 0, 4, 1, 2])           # new expert i holds old expert perm[i]
+    gu_b = (2 * f) * (h // 32) * 34
+    dn_b = h * (f // 32) * 34
+    gu_p = np.concatenate([gu[p * gu_b:(p + 1) * gu_b] for p in perm])
+    dn_p = np.concatenate([dn[p * dn_b:(p + 1) * dn_b] for p in perm])
+    inv = np.argsort(perm)
+    idx_p = inv[idx].astype(np.int32)
+    yp = lib.q8_moe_grouped_linear(to_dev(gu_p, dev), to_dev(dn_p, dev), e, f, h, xd, to_dev(idx_p, dev),
+                                   to_dev(w, dev)).cpu().numpy()
+    assert np.array_equal(y, yp)
+    # the same expert twice in one token's slots, and an out-of-range id that is skipped
+    idx2 = idx.copy()
+    idx2[:, 1] = idx2[:, 0]
+    idx2[0, 2] = e + 7
+    y2 = lib.q8_moe_grouped_linear(to_dev(gu, dev), to_dev(dn, dev), e, f, h, xd, to_dev(idx2, dev),
+                                   to_dev(w, dev)).cpu().numpy()
+    ref_idx = idx2.copy()
+    ref_w = w.copy()
+    ref_idx[0, 2] = 0
+    ref_w[0, 2] = 0.0
+    assert_close(y2, oracle.moe_mixture_ref(gu, dn, e, f, h, x, ref_idx, ref_w), "duplicates + skipped id")
