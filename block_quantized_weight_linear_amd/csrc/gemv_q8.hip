@@ -23,43 +23,7 @@ namespace q8k {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kMaxXLdsBytes = 64 * 1024;
 
-template <int M, int R, bool XL>
-__global__ __launch_bounds__(kThreads) void gemv_q8_kernel(const uint8_t* __restrict__ w, int n_out, int P, int log2S,
-                                                           const float* __restrict__ x, int ldx,
-                                                           float* __restrict__ y, int ldy) {
-    extern __shared__ float4 x_lds[];
-    typename std::conditional<XL, XLds, XGlobal>::type xs;
-    if constexpr (XL) {
-        stage_x_lds(x_lds, M, P, [&](int m) { return x + (size_t)m * ldx; }, threadIdx.x, kThreads);
-        __syncthreads();
-        xs.base = x_lds;
-        xs.P = P;
-    } else {
-        xs.x = x;
-        xs.ldx = ldx;
-    }
-    const int G = 64 >> log2S;
-    const int row_groups = (n_out + G - 1) / G;
-    const int gw = blockIdx.x * kWaves + (threadIdx.x >> 6);
-    wave_rows<M, R>(w, n_out, n_out, P, log2S, xs, gw, gridDim.x * kWaves, row_groups,
-                    [&](int n, const float(&acc)[R][M]) {
-#pragma unroll
-                        for (int m = 0; m < M; ++m) {
-                            if constexpr (R == 2)
-                                y[(size_t)m * ldy + n] = silu_mul(acc[0][m], acc[1][m]);
-                            else
-                                y[(size_t)m * ldy + n] = acc[0][m];
-                        }
-                    });
-}
-
-// Activation rows held in registers (M <= 2).  Each lane keeps the 64*M activation
-// values of every pair slot it owns (NR rounds) for the whole kernel, so the hot loop
-// reads no LDS.  Weights stream through a ring of D register buffers: the loads of
-// item it+D-1 are in flight while item it is multiplied.  Same per-output summation
-// order as wave_rows (slot chain over rounds, then the butterfly).
 // Calls f(std::integral_constant<int, 0>{}), ..., f(std::integral_constant<int, N-1>{}).
 template <class F, int... I>
 __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
@@ -76,11 +40,12 @@ struct XArr {
     __device__ __forceinline__ float4 get(int m, int, int c) const { return v[m][c]; }
 };
 
-template <int M, int R, int NR, int D>
-__global__ __launch_bounds__(kThreads) void gemv_xreg_kernel(const uint8_t* __restrict__ w, int n_out, int P, int log2S,
+template <int M, int R, int NR, int D, int WPE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, WPE))) void gemv_xreg_kernel(const uint8_t* __restrict__ w, int n_out, int P, int log2S,
                                                              const float* __restrict__ x, int ldx,
-                                                             float* __restrict__ y, int ldy) {
+                                                             float* __restrict__ y, int ldy, int ipw) {
     static_assert(D % NR == 0, "the ring depth must be a multiple of the rounds per row");
+    extern __shared__ float4 x_lds[];
     const int S = 1 << log2S;
     const int G = 64 >> log2S;
     const int lane = threadIdx.x & 63;
@@ -88,32 +53,37 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_kernel(const uint8_t* __re
     const int g = lane >> log2S;
     const size_t row_bytes = (size_t)P * 68;
 
-    const int row_groups = (n_out + G - 1) / G;
-    const int stride = gridDim.x * kWaves;
-    const int gw = blockIdx.x * kWaves + (threadIdx.x >> 6);
-    if (gw >= row_groups) return;
+    const int total = ((n_out + G - 1) / G) * NR;  // items: (row group, round)
+    const int wid = blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int nw = gridDim.x * kWaves;
 
-    float4 xr[NR][M][16];
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
+    // Wave w takes the row groups w, w + W, w + 2W, ... (W waves in the grid; `ipw` items
+    // per wave, a multiple of D and of NR), so at any time the grid streams one window of
+    // the matrix.  Every load and
+    // store below is unconditional so the compiler counts the outstanding memory
+    // operations exactly and keeps the ring's loads in flight while an item is
+    // multiplied (a load inside a branch makes it wait for all of them):
+    //  - a lane whose pair index is past the row (p >= P, only when S does not divide
+    //    P) loads pair p - P of the same row instead and skips the multiply;
+    //  - a lane whose row is past the matrix, and any item past the last one (only in
+    //    the grid's last wave), work on the last row group again and store the same
+    //    bits its owner stores.
+    // After the xor butterfly every lane of a row holds the same bits, so all of them
+    // store it.
+
+    // local item it -> row (clamped) of this lane; its round is it % NR
+    auto item_row = [&](int itl) __attribute__((always_inline)) {
+        const int it = (wid + (itl / NR) * nw) * NR + (itl % NR);
+        const int itc = it < total ? it : total - NR + (it % NR);
+        const int n = (itc / NR) * G + g;
+        return n < n_out ? n : n_out - 1;
+    };
+    auto load_item = [&](int it, int i, uint32_t(&wr)[R][17]) __attribute__((always_inline)) {
+        const int n = item_row(it);
         const int p = j + S * i;
+        const int pc = p < P ? p : p - P;
 #pragma unroll
-        for (int m = 0; m < M; ++m)
-#pragma unroll
-            for (int c = 0; c < 16; ++c)
-                xr[i][m][c] = p < P ? *reinterpret_cast<const float4*>(x + (size_t)m * ldx + 64 * p + 4 * c)
-                                    : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-
-    const int n_items = ((row_groups - 1 - gw) / stride + 1) * NR;
-    auto item_n = [&](int it) { return (gw + (it / NR) * stride) * G + g; };
-    auto load_item = [&](int it, uint32_t(&wr)[R][17]) {
-        const int n = item_n(it);
-        const int p = j + S * (it % NR);
-        if (n < n_out && p < P) {
-#pragma unroll
-            for (int r = 0; r < R; ++r) load_pair(w + (size_t)(n + r * n_out) * row_bytes + 68 * (size_t)p, wr[r]);
-        }
+        for (int r = 0; r < R; ++r) load_pair(w + (size_t)(n + r * n_out) * row_bytes + 68 * (size_t)pc, wr[r]);
     };
 
     float acc[R][M];
@@ -122,44 +92,210 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_kernel(const uint8_t* __re
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
 
+    // Activations: one coalesced pass from global into the slot-major LDS layout per
+    // block, then each lane copies the values of its own pair slots into registers.
+    stage_x_lds(x_lds, M, P, [&](int m) { return x + (size_t)m * ldx; }, threadIdx.x, kThreads);
+    __syncthreads();
+    if (wid >= total / NR) return;
+    float4 xr[NR][M][16];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        const int p = j + S * i;
+        const int pc = p < P ? p : p - P;
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int c = 0; c < 16; ++c) xr[i][m][c] = x_lds[(m * 16 + c) * P + pc];
+    }
     uint32_t ring[D][R][17];
-#pragma unroll
-    for (int s = 0; s < D - 1; ++s)
-        if (s < n_items) load_item(s, ring[s]);
+    static_for<D - 1>([&](auto sc) __attribute__((always_inline)) {
+        constexpr int s = decltype(sc)::value;
+        load_item(s, s % NR, ring[s]);
+    });
 
-    for (int it0 = 0; it0 < n_items; it0 += D) {
-        static_for<D>([&](auto sc) {
-            constexpr int s = decltype(sc)::value;
-            constexpr int i = s % NR;
-            const int it = it0 + s;
-            if (it < n_items) {
-                if (it + D - 1 < n_items) load_item(it + D - 1, ring[(s + D - 1) % D]);
-                const int n = item_n(it);
-                const int p = j + S * i;
-                if (n < n_out && p < P) mac_pair<M, R>(ring[s], XArr<M>{xr[i]}, p, acc);
-                if constexpr (i == NR - 1) {
-                    for (int off = S >> 1; off >= 1; off >>= 1) {
+    // One ring step: prefetch item it+D-1 (when LOAD), multiply item it, and finish the
+    // row after its last round.
+    auto step = [&](int it0, auto sc, auto load_tag) __attribute__((always_inline)) {
+        constexpr int s = decltype(sc)::value;
+        constexpr int i = s % NR;
+        const int it = it0 + s;
+        if constexpr (decltype(load_tag)::value) load_item(it + D - 1, (s + D - 1) % NR, ring[(s + D - 1) % D]);
+        if (j + S * i < P) mac_pair<M, R>(ring[s], XArr<M>{xr[i]}, j + S * i, acc);
+        if constexpr (i == NR - 1) {
+            for (int off = S >> 1; off >= 1; off >>= 1) {
 #pragma unroll
-                        for (int r = 0; r < R; ++r)
+                for (int r = 0; r < R; ++r)
 #pragma unroll
-                            for (int m = 0; m < M; ++m) acc[r][m] += __shfl_xor(acc[r][m], off, 64);
+                    for (int m = 0; m < M; ++m) acc[r][m] += __shfl_xor(acc[r][m], off, 64);
+            }
+            const int n = item_row(it);
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                if constexpr (R == 2)
+                    y[(size_t)m * ldy + n] = silu_mul(acc[0][m], acc[1][m]);
+                else
+                    y[(size_t)m * ldy + n] = acc[0][m];
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+        }
+    };
+    // Steady state: every step prefetches.  The last ring of the wave is straight-line
+    // code that only prefetches the wave's final item, so no load sits in a branch.
+    const int last = ipw - D;
+    for (int it0 = 0; it0 < last; it0 += D)
+        static_for<D>([&](auto sc) __attribute__((always_inline)) { step(it0, sc, std::true_type{}); });
+    static_for<D>([&](auto sc) __attribute__((always_inline)) {
+        step(last, sc, std::integral_constant<bool, decltype(sc)::value == 0>{});
+    });
+}
+
+// Several activation rows (2 <= M <= 16).  A block tile is 16*R rows (fused: R gate/up
+// row pairs) over the whole K, worked on by two groups of 4 waves: group h takes the
+// chunks h, h+2, h+4, ... of 16 pairs (1024 inputs) each.  16 lanes share a row (lane j
+// owns pair j of a chunk), 4 row slots per wave, R rows (or row pairs) per lane, so
+// each activation value read from LDS feeds R (or 2R) rows.  Each group stages its
+// chunk's activations in its own slot-major LDS buffer; the next chunk's weights are
+// loaded while the current one is multiplied.  Weights are dequantized exactly
+// (fp32(d) * q needs at most 19 significant bits), one fma per weight and activation
+// row.
+//
+// Per-output order: acc = fma(w_k, x_k, acc) over the lane's weights (its pair of each
+// of the group's chunks in increasing order, inputs in increasing order), the xor
+// butterfly over the 16 lanes (8, 4, 2, 1), then group 0's sum + group 1's sum.  It
+// depends only on K, never on M, so every row of a 2..16-row call is bit-identical to
+// the same row in any other such call.
+template <int M, int R, bool SILU>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) void gemv_tile_kernel(
+    const uint8_t* __restrict__ w, int n_out, int P, const float* __restrict__ x, int ldx, float* __restrict__ y,
+    int ldy) {
+    constexpr int RR = SILU ? 2 * R : R;  // weight rows per lane
+    __shared__ float4 xs[2][M * 16 * 16];  // per group, one chunk: [m][c][j]
+    __shared__ float part[16 * RR * M];  // group 1's row sums: [slot][r][m]
+    const int tid = threadIdx.x & 255;   // thread within the group
+    const int h = threadIdx.x >> 8;      // group
+    const int lane = tid & 63;
+    const int j = lane & 15;
+    const int g = lane >> 4;
+    const int wv = tid >> 6;
+    const size_t row_bytes = (size_t)P * 68;
+    const int nch = (P + 15) >> 4;
+    const int my_nch = (nch - h + 1) >> 1;  // chunks h, h+2, ... < nch
+    const int steps = (nch + 1) >> 1;       // both groups run the same number of steps
+
+    int rows[RR];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        int n = blockIdx.x * (16 * R) + wv * (4 * R) + g * R + r;
+        n = n < n_out ? n : n_out - 1;  // past the end: duplicate the last row (same bits)
+        rows[r] = n;
+        if constexpr (SILU) rows[R + r] = n + n_out;
+    }
+    // chunk of step s for this group, clamped to one it owns (a clamped step is not used)
+    auto chunk_of = [&](int st) __attribute__((always_inline)) {
+        const int ch = h + 2 * st;
+        return ch < nch ? ch : (my_nch > 0 ? h + 2 * (my_nch - 1) : 0);
+    };
+    auto load_chunk = [&](int ch, uint32_t(&wr)[RR][17]) __attribute__((always_inline)) {
+        const int p = 16 * ch + j;
+        const int pc = p < P ? p : p % P;  // past the row: a pair of the same row (unused)
+#pragma unroll
+        for (int r = 0; r < RR; ++r) load_pair(w + (size_t)rows[r] * row_bytes + 68 * (size_t)pc, wr[r]);
+    };
+
+    float acc[RR][M];
+#pragma unroll
+    for (int r = 0; r < RR; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+
+    uint32_t wc[RR][17], wn[RR][17];
+    load_chunk(chunk_of(0), wc);
+    for (int st = 0; st < steps; ++st) {
+        const int ch = chunk_of(st);
+        const bool active = h + 2 * st < nch;
+        __syncthreads();  // the previous step's activations are no longer read
+        for (int i = tid; i < M * 256; i += 256) {
+            const int m = i >> 8;
+            const int c = (i >> 4) & 15;
+            const int jj = i & 15;
+            const int p = 16 * ch + jj;
+            const int pc = p < P ? p : p % P;
+            xs[h][i] = *reinterpret_cast<const float4*>(x + (size_t)m * ldx + 64 * pc + 4 * c);
+        }
+        __syncthreads();
+        load_chunk(chunk_of(st + 1), wn);  // the next step's weights (clamped: reloads, unused)
+        if (active && 16 * ch + j < P) {
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+                float wf[RR][4];
+#pragma unroll
+                for (int r = 0; r < RR; ++r) {
+                    if (c < 8) {  // block 0: scale in dword 0 (low half), quants at bytes 2..33
+                        const float d = half_lo(wc[r][0]);
+                        wf[r][0] = sbyte<2>(wc[r][c]) * d;
+                        wf[r][1] = sbyte<3>(wc[r][c]) * d;
+                        wf[r][2] = sbyte<0>(wc[r][c + 1]) * d;
+                        wf[r][3] = sbyte<1>(wc[r][c + 1]) * d;
+                    } else {      // block 1: scale in dword 8 (high half), quants in dwords 9..16
+                        const float d = half_hi(wc[r][8]);
+                        const uint32_t v = wc[r][c + 1];
+                        wf[r][0] = sbyte<0>(v) * d;
+                        wf[r][1] = sbyte<1>(v) * d;
+                        wf[r][2] = sbyte<2>(v) * d;
+                        wf[r][3] = sbyte<3>(v) * d;
                     }
-                    if (j == 0 && n < n_out) {
+                }
 #pragma unroll
-                        for (int m = 0; m < M; ++m) {
-                            if constexpr (R == 2)
-                                y[(size_t)m * ldy + n] = silu_mul(acc[0][m], acc[1][m]);
-                            else
-                                y[(size_t)m * ldy + n] = acc[0][m];
-                        }
+                for (int m = 0; m < M; ++m) {
+                    const float4 xv = xs[h][(m * 16 + c) * 16 + j];
+#pragma unroll
+                    for (int r = 0; r < RR; ++r) {
+                        acc[r][m] = __builtin_fmaf(wf[r][0], xv.x, acc[r][m]);
+                        acc[r][m] = __builtin_fmaf(wf[r][1], xv.y, acc[r][m]);
+                        acc[r][m] = __builtin_fmaf(wf[r][2], xv.z, acc[r][m]);
+                        acc[r][m] = __builtin_fmaf(wf[r][3], xv.w, acc[r][m]);
                     }
-#pragma unroll
-                    for (int r = 0; r < R; ++r)
-#pragma unroll
-                        for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
                 }
             }
-        });
+        }
+#pragma unroll
+        for (int r = 0; r < RR; ++r)
+#pragma unroll
+            for (int q = 0; q < 17; ++q) wc[r][q] = wn[r][q];
+    }
+    for (int off = 8; off >= 1; off >>= 1) {
+#pragma unroll
+        for (int r = 0; r < RR; ++r)
+#pragma unroll
+            for (int m = 0; m < M; ++m) acc[r][m] += __shfl_xor(acc[r][m], off, 64);
+    }
+    // group 1 hands its sums to group 0 through LDS; lane j == 0 of each row writes
+    const int slot = wv * 4 + g;  // 16 row slots per group
+    if (h == 1 && j == 0) {
+#pragma unroll
+        for (int r = 0; r < RR; ++r)
+#pragma unroll
+            for (int m = 0; m < M; ++m) part[(slot * RR + r) * M + m] = acc[r][m];
+    }
+    __syncthreads();
+    if (h == 0) {
+#pragma unroll
+        for (int r = 0; r < RR; ++r)
+#pragma unroll
+            for (int m = 0; m < M; ++m) acc[r][m] += part[(slot * RR + r) * M + m];
+        // every lane of the 16 holds the same bits: all store
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                if constexpr (SILU)
+                    y[(size_t)m * ldy + rows[r]] = silu_mul(acc[r][m], acc[R + r][m]);
+                else
+                    y[(size_t)m * ldy + rows[r]] = acc[r][m];
+            }
     }
 }
 
@@ -181,30 +317,26 @@ inline int grid_for(const DeviceInfo& dev, int per_cu, int row_groups) {
     return blocks < 1 ? 1 : blocks;
 }
 
-template <int M, int R, bool XL>
-hipError_t launch_one(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, int log2S, const float* x, int ldx,
-                      float* y, int ldy, hipStream_t stream) {
-    const size_t lds = XL ? (size_t)M * P * 256 : 0;
-    const int G = 64 >> log2S;
-    static thread_local int cached_lds_P = -1, cached_per_cu = 1;
-    if (cached_lds_P != (int)lds) {
-        cached_per_cu = resident_blocks(gemv_q8_kernel<M, R, XL>, lds);
-        cached_lds_P = (int)lds;
-    }
-    const int blocks = grid_for(dev, cached_per_cu, (n_out + G - 1) / G);
-    hipLaunchKernelGGL((gemv_q8_kernel<M, R, XL>), dim3(blocks), dim3(kThreads), lds, stream, w, n_out, P, log2S, x,
-                       ldx, y, ldy);
-    return hipGetLastError();
-}
-
-template <int M, int R, int NR, int D>
+template <int M, int R, int NR, int D, int WPE>
 hipError_t launch_xreg(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, int log2S, const float* x, int ldx,
                        float* y, int ldy, hipStream_t stream) {
-    static const int per_cu = resident_blocks(gemv_xreg_kernel<M, R, NR, D>, 0);
+    const size_t lds = (size_t)M * P * 256;
+    static thread_local int cached_lds = -1, per_cu = 1;
+    if (cached_lds != (int)lds) {
+        per_cu = resident_blocks(gemv_xreg_kernel<M, R, NR, D, WPE>, lds);
+        cached_lds = (int)lds;
+    }
     const int G = 64 >> log2S;
-    const int blocks = grid_for(dev, per_cu, (n_out + G - 1) / G);
-    hipLaunchKernelGGL((gemv_xreg_kernel<M, R, NR, D>), dim3(blocks), dim3(kThreads), 0, stream, w, n_out, P, log2S,
-                       x, ldx, y, ldy);
+    const int total = ((n_out + G - 1) / G) * NR;
+    // items per wave: enough to cover the work with the waves that fit at once, rounded
+    // up to a multiple of the ring depth (at least one ring)
+    const int resident = dev.cu_count * per_cu * kWaves;
+    int ipw = (total + resident - 1) / resident;
+    ipw = ((ipw + D - 1) / D) * D;
+    const int waves = (total + ipw - 1) / ipw;
+    const int blocks = (waves + kWaves - 1) / kWaves;
+    hipLaunchKernelGGL((gemv_xreg_kernel<M, R, NR, D, WPE>), dim3(blocks), dim3(kThreads), lds, stream, w, n_out, P,
+                       log2S, x, ldx, y, ldy, ipw);
     return hipGetLastError();
 }
 
@@ -215,13 +347,36 @@ bool try_xreg_m(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, int l
               float* y, int ldy, hipStream_t stream, hipError_t* err) {
     const int S = 1 << log2S;
     const int NR = (P + S - 1) / S;
+    // (ring depth, waves per SIMD) per shape: the ring and the activations stay in registers
     switch (NR) {
-        case 1: *err = launch_xreg<M, R, 1, (R == 1 ? 4 : 3)>(dev, w, n_out, P, log2S, x, ldx, y, ldy, stream); return true;
-        case 2: *err = launch_xreg<M, R, 2, (R == 1 ? 4 : 2)>(dev, w, n_out, P, log2S, x, ldx, y, ldy, stream); return true;
-        case 3: *err = launch_xreg<M, R, 3, 3>(dev, w, n_out, P, log2S, x, ldx, y, ldy, stream); return true;
-        case 4: *err = launch_xreg<M, R, 4, 4>(dev, w, n_out, P, log2S, x, ldx, y, ldy, stream); return true;
+        case 1: *err = launch_xreg<M, R, 1, (R == 1 ? 4 : 3), (R == 1 ? 3 : 2)>(dev, w, n_out, P, log2S, x, ldx, y, ldy, stream); return true;
+        case 2: *err = launch_xreg<M, R, 2, (R == 1 ? 4 : 2), 2>(dev, w, n_out, P, log2S, x, ldx, y, ldy, stream); return true;
+        case 3: *err = launch_xreg<M, R, 3, 3, 1>(dev, w, n_out, P, log2S, x, ldx, y, ldy, stream); return true;
+        case 4: *err = launch_xreg<M, R, 4, 4, 1>(dev, w, n_out, P, log2S, x, ldx, y, ldy, stream); return true;
         default: return false;
     }
+}
+
+template <int M, bool SILU>
+hipError_t launch_tile(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, const float* x, int ldx, float* y,
+                       int ldy, hipStream_t stream) {
+    // R rows per lane: 2 (32 rows per block); 4 when that still gives two blocks per CU
+    if constexpr (!SILU) {
+        if (n_out >= 64 * 2 * dev.cu_count) {
+            constexpr int R = 4;
+            const int blocks = (n_out + 16 * R - 1) / (16 * R);
+            hipLaunchKernelGGL((gemv_tile_kernel<M, R, SILU>), dim3(blocks), dim3(512), 0, stream, w, n_out, P, x, ldx,
+                               y, ldy);
+            return hipGetLastError();
+        }
+    }
+    {
+        constexpr int R = 2;
+        const int blocks = (n_out + 16 * R - 1) / (16 * R);
+        hipLaunchKernelGGL((gemv_tile_kernel<M, R, SILU>), dim3(blocks), dim3(512), 0, stream, w, n_out, P, x, ldx, y,
+                           ldy);
+    }
+    return hipGetLastError();
 }
 
 template <int M, int R>
@@ -231,14 +386,7 @@ hipError_t launch_m(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, i
         hipError_t e;
         if (try_xreg_m<1, R>(dev, w, n_out, P, log2S, x, ldx, y, ldy, stream, &e)) return e;
     }
-    if constexpr (M == 2) {
-        // 128 registers of activations per round: one round only (K <= 64 * lanes per row)
-        if ((P + (1 << log2S) - 1) >> log2S == 1)
-            return launch_xreg<2, R, 1, (R == 1 ? 4 : 3)>(dev, w, n_out, P, log2S, x, ldx, y, ldy, stream);
-    }
-    if ((size_t)M * P * 256 <= (size_t)kMaxXLdsBytes)
-        return launch_one<M, R, true>(dev, w, n_out, P, log2S, x, ldx, y, ldy, stream);
-    return launch_one<M, R, false>(dev, w, n_out, P, log2S, x, ldx, y, ldy, stream);
+    return launch_tile<M, R == 2>(dev, w, n_out, P, x, ldx, y, ldy, stream);
 }
 
 template <int R>

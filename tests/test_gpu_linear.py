@@ -112,6 +112,11 @@ def test_exact_arithmetic_bit_identical(q8, n, k, m):
 
 @pytest.mark.parametrize("n,k", [(4096, 1024), (1024, 3072), (6144, 4096), (777, 12288)])
 def test_batch_invariance_and_determinism(q8, n, k):
+    """Run-to-run bit-identical.  Rows of any call with 2..16 activation rows (and the
+    16-row chunks of larger calls) are bit-identical to the same rows of any other such
+    call; a one-row call uses the single-row kernel, whose summation order differs, so
+    there rows agree to float32 reassociation (the batch-kernel threshold behaviour of
+    "14. Model families and example applications", section 14.2)."""
     lib, torch, dev = q8
     wb, _, _ = wl.q8_weight(31, n, k)
     wd = to_dev(wb, dev)
@@ -121,18 +126,28 @@ def test_batch_invariance_and_determinism(q8, n, k):
     y40 = lib.q8_linear(wd, n, k, xd).cpu().numpy()
     y40b = lib.q8_linear(wd, n, k, xd).cpu().numpy()
     assert np.array_equal(y40, y40b)  # run to run
-    for m in (1, 2, 5, 8, 16):
+    for m in (2, 5, 8, 16):
         ym = lib.q8_linear(wd, n, k, xd[:m].contiguous()).cpu().numpy()
         assert np.array_equal(ym, y40[:m]), m
-    for r in (0, 7, 15, 16, 39):
+    for r in (3, 17, 38):
+        y2 = lib.q8_linear(wd, n, k, xd[r:r + 2].contiguous()).cpu().numpy()
+        assert np.array_equal(y2, y40[r:r + 2]), r
+    ref = oracle.q8_linear_ref(wb, n, k, x[:4])
+    for r in (0, 1, 2, 3):
         y1 = lib.q8_linear(wd, n, k, xd[r:r + 1].contiguous()).cpu().numpy()
-        assert np.array_equal(y1[0], y40[r]), r
-    # fused: same property
+        y1b = lib.q8_linear(wd, n, k, xd[r:r + 1].contiguous()).cpu().numpy()
+        assert np.array_equal(y1, y1b)
+        drift = np.max(np.abs(y1[0] - y40[r])) / np.max(np.abs(ref[r]))
+        assert drift <= 1e-5, drift
+    # fused: same properties
     f = n // 2
     h40 = lib.q8_linear_fused_gate_up_silu(wd, f, k, xd).cpu().numpy()
-    for r in (0, 9, 33):
-        h1 = lib.q8_linear_fused_gate_up_silu(wd, f, k, xd[r:r + 1].contiguous()).cpu().numpy()
-        assert np.array_equal(h1[0], h40[r]), r
+    for m in (2, 9):
+        hm = lib.q8_linear_fused_gate_up_silu(wd, f, k, xd[:m].contiguous()).cpu().numpy()
+        assert np.array_equal(hm, h40[:m]), m
+    h1 = lib.q8_linear_fused_gate_up_silu(wd, f, k, xd[5:6].contiguous()).cpu().numpy()
+    href = oracle.fused_gate_up_silu_ref(row_slice(wb, k, np.arange(2 * f)), f, k, x[5:6])
+    assert np.max(np.abs(h1[0] - h40[5])) / np.max(np.abs(href)) <= 1e-5
 
 
 def test_scale_doubling_sign_and_zero_blocks(q8):
