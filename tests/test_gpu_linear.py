@@ -239,3 +239,42 @@ def test_binding_rejects_bad_arguments(q8):
         lib.q8_linear(wd, 8, 256, torch.zeros((1, 128), dtype=torch.float32, device=dev))
     with pytest.raises(lib.Q8Error):
         lib.q8_linear(wd[:0], 8, 96, torch.zeros((1, 96), dtype=torch.float32, device=dev))
+
+
+def test_graph_replay_matches_eager(q8):
+    """The three block linears captured in one HIP graph: every replay, with eager work
+    and synchronizations in between, gives the eager result bit for bit."""
+    lib, torch, dev = q8
+    k, nq, f = 1024, 4096, 3072
+    wq, _, _ = wl.q8_weight(81, nq, k)
+    wg, _, _ = wl.q8_weight(82, 2 * f, k)
+    wdn, _, _ = wl.q8_weight(83, k, f)
+    wq, wg, wdn = to_dev(wq, dev), to_dev(wg, dev), to_dev(wdn, dev)
+    for m in (1, 3):
+        x = to_dev(wl.activations(84 + m, m, k), dev)
+        yq = torch.empty((m, nq), device=dev)
+        h = torch.empty((m, f), device=dev)
+        yd = torch.empty((m, k), device=dev)
+
+        def step():
+            lib.q8_linear(wq, nq, k, x, out=yq)
+            lib.q8_linear_fused_gate_up_silu(wg, f, k, x, out=h)
+            lib.q8_linear(wdn, k, f, h, out=yd)
+
+        step()
+        torch.cuda.synchronize()
+        ref = [t.clone() for t in (yq, h, yd)]
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                step()
+        for rep in range(4):
+            for t in (yq, h, yd):
+                t.fill_(float("nan"))
+            g.replay()
+            torch.cuda.synchronize()
+            for got, want in zip((yq, h, yd), ref):
+                assert torch.equal(got, want), (m, rep)
+            step()  # eager work between replays
+            torch.cuda.synchronize()
