@@ -26,6 +26,7 @@ q8_status device_fail(const char* where, hipError_t e) {
 }
 
 constexpr int kMaxDevices = 64;
+constexpr int64_t kPrefillRows = 256;  // from this many activation rows on: bf16 matrix-core path
 std::mutex g_dev_mu;
 q8k::DeviceInfo g_dev[kMaxDevices];
 
@@ -88,8 +89,10 @@ static q8_status linear_common(const char* name, const void* w, int64_t n_out, i
     q8k::DeviceInfo dev;
     hipError_t e = q8k::current_device_info(&dev);
     if (e != hipSuccess) return device_fail(name, e);
-    e = q8k::launch_gemv_q8(dev, static_cast<const uint8_t*>(w), n_out, k, silu, x, m, ldx, y, ldy,
-                            static_cast<hipStream_t>(stream));
+    const uint8_t* wq = static_cast<const uint8_t*>(w);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    e = m >= kPrefillRows ? q8k::launch_gemm_q8_mfma(dev, wq, n_out, k, silu, x, m, ldx, y, ldy, st)
+                          : q8k::launch_gemv_q8(dev, wq, n_out, k, silu, x, m, ldx, y, ldy, st);
     if (e != hipSuccess) return device_fail(name, e);
     return Q8_OK;
 }

@@ -77,10 +77,13 @@ const char* q8_last_error(void);
  * and down projections use it directly).
  *   w_q8 : Q8_0 [n][k]          x : float32 [m][ldx]          y : float32 [m][ldy]
  *   n >= 0 outputs, k > 0 a multiple of 256, m >= 0 rows, ldx >= k, ldy >= n.
- * Every row of y is computed by the same per-row arithmetic whatever m is, so a row's
- * result does not depend on the other rows in the batch (the lockstep m = n pass of
- * section 14.2).  Rows m >= 256 use the bf16 matrix-core path when one is built for
- * this library version; the current version uses the float32 path for every m.
+ * Arithmetic by batch size (the m-dependent kernel classes of section 14.2):
+ *   m == 1      float32: w = d*q exactly, per-block chains, fixed butterfly;
+ *   2..255      float32 (16-row chunks): exact fp32 dequantization, one fma per weight
+ *               and row; every row is bit-identical whatever the other rows are (for
+ *               any m in 2..255), and agrees with the m == 1 result to reassociation;
+ *   m >= 256    bf16 matrix cores (dense prefill): weights d*q and activations rounded
+ *               to bf16 (nearest even), float32 accumulation and output.
  */
 q8_status q8_linear(const void* w_q8, int64_t n, int64_t k,
                     const float* x, int64_t m, int64_t ldx,
@@ -91,7 +94,7 @@ q8_status q8_linear(const void* w_q8, int64_t n, int64_t k,
  * gate and up; section 14.2 gives the SwiGLU FFN).  SiLU(g) = g / (1 + exp(-g)).
  *   w_gate_up_q8 : Q8_0 [2f][k], gate rows [0, f) then up rows [f, 2f)
  *   x : float32 [m][ldx]          h : float32 [m][ldh], ldh >= f
- * Same rules as q8_linear otherwise.
+ * Same rules (and the same arithmetic by batch size) as q8_linear otherwise.
  */
 q8_status q8_linear_fused_gate_up_silu(const void* w_gate_up_q8, int64_t f, int64_t k,
                                        const float* x, int64_t m, int64_t ldx,

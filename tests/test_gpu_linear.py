@@ -278,3 +278,61 @@ def test_graph_replay_matches_eager(q8):
                 assert torch.equal(got, want), (m, rep)
             step()  # eager work between replays
             torch.cuda.synchronize()
+
+
+# ------------------------------------------------------- prefill (bf16 matrix cores)
+
+PREFILL_TOL = 2e-2   # bf16 operands, float32 accumulation
+
+
+@pytest.mark.parametrize("n,k,m", [(300, 1024, 256), (129, 512, 300), (1024, 4096, 512), (77, 3072, 257),
+                                   (520, 256, 1000)])
+def test_prefill_vs_oracle(q8, n, k, m):
+    lib, torch, dev = q8
+    wb, _, _ = wl.q8_weight(91 + n, n, k)
+    x = wl.activations(92 + m, m, k)
+    say(f"prefill n={n} k={k} m={m}")
+    y = lib.q8_linear(to_dev(wb, dev), n, k, to_dev(x, dev)).cpu().numpy()
+    assert_close(y, oracle.q8_linear_ref(wb, n, k, x), f"prefill n={n} k={k} m={m}", tol=PREFILL_TOL)
+    # with both operands rounded to bf16 first, only float32 accumulation error remains
+    diag = oracle.q8_linear_bf16_operands_ref(wb, n, k, x)
+    assert_close(y, diag, f"prefill vs bf16-operand oracle n={n} m={m}", tol=1e-4)
+
+
+@pytest.mark.parametrize("f,k,m", [(64, 1024, 256), (200, 512, 300), (1536, 2048, 512)])
+def test_prefill_fused_vs_oracle(q8, f, k, m):
+    lib, torch, dev = q8
+    wb, _, _ = wl.q8_weight(93 + f, 2 * f, k)
+    x = wl.activations(94 + m, m, k)
+    say(f"prefill fused f={f} k={k} m={m}")
+    h = lib.q8_linear_fused_gate_up_silu(to_dev(wb, dev), f, k, to_dev(x, dev)).cpu().numpy()
+    assert_close(h, oracle.fused_gate_up_silu_ref(wb, f, k, x), f"prefill fused f={f} m={m}", tol=PREFILL_TOL)
+    gu = oracle.q8_linear_bf16_operands_ref(wb, 2 * f, k, x)
+    diag = oracle.silu_ref(gu[:, :f]) * gu[:, f:]
+    assert_close(h, diag, f"prefill fused vs bf16-operand oracle f={f}", tol=1e-4)
+
+
+def test_prefill_qwen3_8b_gate_up_sampled(q8):
+    """Qwen3-8B gate_up 24576x4096 at M=512 (the prefill configuration), sampled rows."""
+    lib, torch, dev = q8
+    n, k, m = 24576, 4096, 512
+    wb, _, _ = wl.q8_weight(11, n, k)
+    x = wl.activations(95, m, k)
+    y = lib.q8_linear(to_dev(wb, dev), n, k, to_dev(x, dev)).cpu().numpy()
+    pick = sample_rows(n, 128, seed=5)
+    sub = row_slice(wb, k, pick)
+    assert_close(y[:, pick], oracle.q8_linear_ref(sub, len(pick), k, x), "8b gate_up m=512 sampled",
+                 tol=PREFILL_TOL)
+    assert_close(y[:, pick], oracle.q8_linear_bf16_operands_ref(sub, len(pick), k, x),
+                 "8b gate_up m=512 vs bf16-operand oracle", tol=1e-4)
+
+
+@pytest.mark.parametrize("n,k,m", [(4096, 1024, 256), (1000, 4096, 512)])
+def test_prefill_exact_arithmetic(q8, n, k, m):
+    """Integer activations and scales 2^-7 / 2^-8: bf16 holds every operand exactly and every
+    float32 partial sum is exact, so the matrix-core result equals the oracle bit for bit."""
+    lib, torch, dev = q8
+    wb, _, _ = wl.q8_weight_exact(96 + n, n, k)
+    x = wl.activations_exact(97 + m, m, k)
+    y = lib.q8_linear(to_dev(wb, dev), n, k, to_dev(x, dev)).cpu().numpy()
+    assert np.array_equal(y.astype(np.float64), oracle.q8_linear_ref(wb, n, k, x))
