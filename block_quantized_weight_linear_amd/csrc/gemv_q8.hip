@@ -152,58 +152,101 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, WPE
     });
 }
 
-// Several activation rows (2 <= M <= 16).  A block tile is 16*R rows (fused: R gate/up
-// row pairs) over the whole K, worked on by two groups of 4 waves: group h takes the
-// chunks h, h+2, h+4, ... of 16 pairs (1024 inputs) each.  16 lanes share a row (lane j
-// owns pair j of a chunk), 4 row slots per wave, R rows (or row pairs) per lane, so
-// each activation value read from LDS feeds R (or 2R) rows.  Each group stages its
-// chunk's activations in its own slot-major LDS buffer; the next chunk's weights are
-// loaded while the current one is multiplied.  Weights are dequantized exactly
-// (fp32(d) * q needs at most 19 significant bits), one fma per weight and activation
-// row.
+// Several activation rows (1 <= M <= 8 per launch; the class used for 2..255 rows).  A
+// block tile is 8*R rows (fused: R gate/up row pairs) over the whole K, worked on by two
+// groups of 2 waves: group h takes the chunks h, h+2, h+4, ... of 16 pairs (1024 inputs)
+// each.  16 lanes share a row (lane j owns pair j of a chunk), 4 row slots per wave, R
+// rows (or row pairs) per lane, so each activation value read from LDS feeds R (or 2R)
+// rows.  Each step copies both groups' activation chunks into slot-major LDS with
+// direct-to-LDS loads (no register round trip); the weights of the step after next are
+// loaded while a step is multiplied (a ring of two steps in registers).  Weights are
+// dequantized exactly (fp32(d) * q needs at most 19 significant bits), one fma per
+// weight and activation row.
 //
 // Per-output order: acc = fma(w_k, x_k, acc) over the lane's weights (its pair of each
 // of the group's chunks in increasing order, inputs in increasing order), the xor
 // butterfly over the 16 lanes (8, 4, 2, 1), then group 0's sum + group 1's sum.  It
-// depends only on K, never on M, so every row of a 2..16-row call is bit-identical to
-// the same row in any other such call.
+// depends only on K, never on M or R, so every row of a 2..255-row call is bit-identical
+// to the same row in any other such call.
+constexpr int kRowsThreads = 256;
+
+// s_waitcnt with only vmcnt limited to n (gfx9 encoding: vmcnt in bits 3:0 and 15:14).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// One wave-wide direct-to-LDS copy: lane l copies 16 bytes from its src to
+// lds + 16*l (lds wave-uniform).  Written as inline assembly so that the compiler does
+// not serialize it against LDS reads of the other buffer: the caller waits for it with
+// wait_vmcnt (it counts as one vector-memory load, retired in order) and a barrier.
+__device__ __forceinline__ void lds_copy16(const void* src, float4* lds) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(base) : "m0");
+}
+
 template <int M, int R, bool SILU>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) void gemv_tile_kernel(
+__global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(1, 2))) void gemv_rows_kernel(
     const uint8_t* __restrict__ w, int n_out, int P, const float* __restrict__ x, int ldx, float* __restrict__ y,
     int ldy) {
     constexpr int RR = SILU ? 2 * R : R;  // weight rows per lane
-    __shared__ float4 xs[2][M * 16 * 16];  // per group, one chunk: [m][c][j]
-    __shared__ float part[16 * RR * M];  // group 1's row sums: [slot][r][m]
-    const int tid = threadIdx.x & 255;   // thread within the group
-    const int h = threadIdx.x >> 8;      // group
+    // Activations of one half chunk per group (inputs of block 0, or of block 1, of each
+    // of the chunk's 16 pairs), slot-major [m][c][j] float4 with c the quant dword 0..7 of
+    // the half.  Half 0 lives in xa and half 1 in xb: while one is multiplied the other is
+    // being filled.  Two variables rather than one array, so that the copy into one is
+    // known not to touch the other.
+    __shared__ float4 xa[2][M * 128];
+    __shared__ float4 xb[2][M * 128];
+    __shared__ float part[8 * RR * M];    // group 1's row sums: [slot][r][m]
+    const int tid = threadIdx.x;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (LDS copy bases)
+    const int h = wv >> 1;                // group
     const int lane = tid & 63;
     const int j = lane & 15;
-    const int g = lane >> 4;
-    const int wv = tid >> 6;
+    const int slot = (wv & 1) * 4 + (lane >> 4);  // row slot within the group, 0..7
     const size_t row_bytes = (size_t)P * 68;
     const int nch = (P + 15) >> 4;
-    const int my_nch = (nch - h + 1) >> 1;  // chunks h, h+2, ... < nch
-    const int steps = (nch + 1) >> 1;       // both groups run the same number of steps
+    const int steps = (nch + 1) >> 1;
+    __builtin_assume(steps >= 1);  // P >= 4 (K is a positive multiple of 256)
 
     int rows[RR];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        int n = blockIdx.x * (16 * R) + wv * (4 * R) + g * R + r;
+        int n = blockIdx.x * (8 * R) + slot * R + r;
         n = n < n_out ? n : n_out - 1;  // past the end: duplicate the last row (same bits)
         rows[r] = n;
         if constexpr (SILU) rows[R + r] = n + n_out;
     }
-    // chunk of step s for this group, clamped to one it owns (a clamped step is not used)
+    // the group's chunk at step st, clamped to a valid chunk (a clamped step is not used)
     auto chunk_of = [&](int st) __attribute__((always_inline)) {
         const int ch = h + 2 * st;
-        return ch < nch ? ch : (my_nch > 0 ? h + 2 * (my_nch - 1) : 0);
+        return ch < nch ? ch : nch - 1;
     };
-    auto load_chunk = [&](int ch, uint32_t(&wr)[RR][17]) __attribute__((always_inline)) {
-        const int p = 16 * ch + j;
-        const int pc = p < P ? p : p % P;  // past the row: a pair of the same row (unused)
+    auto load_w = [&](int st, uint32_t(&wr)[RR][17]) __attribute__((always_inline)) {
+        const int p = 16 * chunk_of(st) + j;
+        const int pc = p < P ? p : P - 1;  // past the row: a pair of the same row (unused)
 #pragma unroll
         for (int r = 0; r < RR; ++r) load_pair(w + (size_t)rows[r] * row_bytes + 68 * (size_t)pc, wr[r]);
     };
+    // Half `half` of the group's activation chunk for step st: 2*M wave-wide copies of 64
+    // float4; the group's two waves take every other one.  Copy q covers float4
+    // [64q, 64q + 64) of the buffer = (m = q/2, c = 4(q%2) + lane/16, j = lane%16), i.e.
+    // inputs 64*pair + 32*half + 4c .. + 3.
+    auto stage_x = [&](int st, int half, float4* buf) __attribute__((always_inline)) {
+        const int c_lo = lane >> 4;
+        int pc = 16 * chunk_of(st) + j;
+        pc = pc < P ? pc : P - 1;
+#pragma unroll
+        for (int qq = 0; qq < M; ++qq) {
+            const int q = 2 * qq + (wv & 1);
+            const int m = q >> 1;
+            const int c = 4 * (q & 1) + c_lo;
+            const float* src = x + (size_t)m * ldx + 64 * (size_t)pc + 32 * half + 4 * c;
+            lds_copy16(src, buf + 64 * q);
+        }
+    };
+    constexpr int kWLoads = 5 * RR;  // loads per weight step (load_pair = 5 loads a row)
 
     float acc[RR][M];
 #pragma unroll
@@ -211,35 +254,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
 
-    uint32_t wc[RR][17], wn[RR][17];
-    load_chunk(chunk_of(0), wc);
-    for (int st = 0; st < steps; ++st) {
-        const int ch = chunk_of(st);
-        const bool active = h + 2 * st < nch;
-        __syncthreads();  // the previous step's activations are no longer read
-        for (int i = tid; i < M * 256; i += 256) {
-            const int m = i >> 8;
-            const int c = (i >> 4) & 15;
-            const int jj = i & 15;
-            const int p = 16 * ch + jj;
-            const int pc = p < P ? p : p % P;
-            xs[h][i] = *reinterpret_cast<const float4*>(x + (size_t)m * ldx + 64 * pc + 4 * c);
-        }
-        __syncthreads();
-        load_chunk(chunk_of(st + 1), wn);  // the next step's weights (clamped: reloads, unused)
-        if (active && 16 * ch + j < P) {
+    // Quant dwords 8*HALF .. 8*HALF + 7 of the lane's pair against the half chunk in xs.
+    auto compute = [&](auto half, int st, const uint32_t(&wc)[RR][17], const float4* xs)
+                       __attribute__((always_inline)) {
+        constexpr int HALF = decltype(half)::value;
+        const int ch = h + 2 * st;
+        if (ch < nch && 16 * ch + j < P) {
 #pragma unroll
-            for (int c = 0; c < 16; ++c) {
+            for (int cc = 0; cc < 8; ++cc) {
+                const int c = 8 * HALF + cc;
                 float wf[RR][4];
 #pragma unroll
                 for (int r = 0; r < RR; ++r) {
-                    if (c < 8) {  // block 0: scale in dword 0 (low half), quants at bytes 2..33
+                    if constexpr (HALF == 0) {  // block 0: scale in dword 0 (low half), quants at bytes 2..33
                         const float d = half_lo(wc[r][0]);
                         wf[r][0] = sbyte<2>(wc[r][c]) * d;
                         wf[r][1] = sbyte<3>(wc[r][c]) * d;
                         wf[r][2] = sbyte<0>(wc[r][c + 1]) * d;
                         wf[r][3] = sbyte<1>(wc[r][c + 1]) * d;
-                    } else {      // block 1: scale in dword 8 (high half), quants in dwords 9..16
+                    } else {  // block 1: scale in dword 8 (high half), quants in dwords 9..16
                         const float d = half_hi(wc[r][8]);
                         const uint32_t v = wc[r][c + 1];
                         wf[r][0] = sbyte<0>(v) * d;
@@ -250,7 +283,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
                 }
 #pragma unroll
                 for (int m = 0; m < M; ++m) {
-                    const float4 xv = xs[h][(m * 16 + c) * 16 + j];
+                    const float4 xv = xs[(m * 8 + cc) * 16 + j];
 #pragma unroll
                     for (int r = 0; r < RR; ++r) {
                         acc[r][m] = __builtin_fmaf(wf[r][0], xv.x, acc[r][m]);
@@ -261,11 +294,46 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
                 }
             }
         }
+    };
+
+    uint32_t wc[RR][17], wn[RR][17];
+    stage_x(0, 0, xa[h]);
+    load_w(0, wc);
+    __builtin_amdgcn_sched_barrier(0);  // the loads stay above the wait
+    wait_vmcnt<0>();
+    __syncthreads();
+    // Step st, half 0: copy half 1 into xb and load step st + 1's weights into wn while
+    // multiplying half 0 (xa); wait for the copy only (the weights may stay in flight).
+    // Half 1: copy step st + 1's half 0 into xa while multiplying half 1 (xb); wait for
+    // everything, wc = wn.  A barrier ends each half.
+    for (int st = 0; st < steps; ++st) {
+        const bool more = st + 1 < steps;
+        stage_x(st, 1, xb[h]);
+        if (more) load_w(st + 1, wn);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(std::integral_constant<int, 0>{}, st, wc, xa[h]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) {
+            wait_vmcnt<kWLoads>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        __syncthreads();
+        if (more) stage_x(st + 1, 0, xa[h]);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(std::integral_constant<int, 1>{}, st, wc, xb[h]);
+        if (more) {
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vmcnt<0>();
 #pragma unroll
-        for (int r = 0; r < RR; ++r)
+            for (int r = 0; r < RR; ++r)
 #pragma unroll
-            for (int q = 0; q < 17; ++q) wc[r][q] = wn[r][q];
+                for (int q = 0; q < 17; ++q) wc[r][q] = wn[r][q];
+            __syncthreads();
+        }
     }
+
+#pragma unroll
     for (int off = 8; off >= 1; off >>= 1) {
 #pragma unroll
         for (int r = 0; r < RR; ++r)
@@ -273,7 +341,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
             for (int m = 0; m < M; ++m) acc[r][m] += __shfl_xor(acc[r][m], off, 64);
     }
     // group 1 hands its sums to group 0 through LDS; lane j == 0 of each row writes
-    const int slot = wv * 4 + g;  // 16 row slots per group
     if (h == 1 && j == 0) {
 #pragma unroll
         for (int r = 0; r < RR; ++r)
@@ -357,36 +424,31 @@ bool try_xreg_m(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, int l
     }
 }
 
-template <int M, bool SILU>
-hipError_t launch_tile(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, const float* x, int ldx, float* y,
-                       int ldy, hipStream_t stream) {
-    // R rows per lane: 2 (32 rows per block); 4 when that still gives two blocks per CU
-    if constexpr (!SILU) {
-        if (n_out >= 64 * 2 * dev.cu_count) {
-            constexpr int R = 4;
-            const int blocks = (n_out + 16 * R - 1) / (16 * R);
-            hipLaunchKernelGGL((gemv_tile_kernel<M, R, SILU>), dim3(blocks), dim3(512), 0, stream, w, n_out, P, x, ldx,
-                               y, ldy);
-            return hipGetLastError();
-        }
-    }
-    {
-        constexpr int R = 2;
-        const int blocks = (n_out + 16 * R - 1) / (16 * R);
-        hipLaunchKernelGGL((gemv_tile_kernel<M, R, SILU>), dim3(blocks), dim3(512), 0, stream, w, n_out, P, x, ldx, y,
-                           ldy);
-    }
+template <int M, int R, bool SILU>
+hipError_t launch_rows_r(int n_out, int P, const uint8_t* w, const float* x, int ldx, float* y, int ldy,
+                         hipStream_t stream) {
+    const int blocks = (n_out + 8 * R - 1) / (8 * R);
+    hipLaunchKernelGGL((gemv_rows_kernel<M, R, SILU>), dim3(blocks), dim3(kRowsThreads), 0, stream, w, n_out, P, x,
+                       ldx, y, ldy);
     return hipGetLastError();
+}
+
+template <int M, bool SILU>
+hipError_t launch_rows(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, const float* x, int ldx, float* y,
+                       int ldy, hipStream_t stream) {
+    // R rows (row pairs) per lane: the largest that still gives two blocks per CU
+    const int64_t want = 2 * (int64_t)dev.cu_count;
+    if constexpr (!SILU) {
+        if ((n_out + 31) / 32 >= want) return launch_rows_r<M, 4, SILU>(n_out, P, w, x, ldx, y, ldy, stream);
+    }
+    if ((n_out + 15) / 16 >= want) return launch_rows_r<M, 2, SILU>(n_out, P, w, x, ldx, y, ldy, stream);
+    return launch_rows_r<M, 1, SILU>(n_out, P, w, x, ldx, y, ldy, stream);
 }
 
 template <int M, int R>
 hipError_t launch_m(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, int log2S, const float* x, int ldx,
                     float* y, int ldy, hipStream_t stream) {
-    if constexpr (M == 1) {
-        hipError_t e;
-        if (try_xreg_m<1, R>(dev, w, n_out, P, log2S, x, ldx, y, ldy, stream, &e)) return e;
-    }
-    return launch_tile<M, R == 2>(dev, w, n_out, P, x, ldx, y, ldy, stream);
+    return launch_rows<M, R == 2>(dev, w, n_out, P, x, ldx, y, ldy, stream);
 }
 
 template <int R>
@@ -396,7 +458,6 @@ hipError_t launch_r(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, i
 #define Q8_CASE(MM) \
     case MM: return launch_m<MM, R>(dev, w, n_out, P, log2S, x, ldx, y, ldy, stream);
         Q8_CASE(1) Q8_CASE(2) Q8_CASE(3) Q8_CASE(4) Q8_CASE(5) Q8_CASE(6) Q8_CASE(7) Q8_CASE(8)
-        Q8_CASE(9) Q8_CASE(10) Q8_CASE(11) Q8_CASE(12) Q8_CASE(13) Q8_CASE(14) Q8_CASE(15) Q8_CASE(16)
 #undef Q8_CASE
         default: return hipErrorInvalidValue;
     }
@@ -408,8 +469,15 @@ hipError_t launch_gemv_q8(const DeviceInfo& dev, const uint8_t* w, int64_t n_out
                           const float* x, int64_t m, int64_t ldx, float* y, int64_t ldy, hipStream_t stream) {
     const int P = (int)(k / 64);
     const int log2S = slots_log2(P);
-    for (int64_t m0 = 0; m0 < m; m0 += 16) {
-        const int mm = (int)((m - m0) < 16 ? (m - m0) : 16);
+    if (m == 1) {  // one row: the register-ring kernel when K fits it
+        hipError_t e;
+        if (silu_pairs ? try_xreg_m<1, 2>(dev, w, (int)n_out, P, log2S, x, (int)ldx, y, (int)ldy, stream, &e)
+                       : try_xreg_m<1, 1>(dev, w, (int)n_out, P, log2S, x, (int)ldx, y, (int)ldy, stream, &e))
+            return e;
+    }
+    // several rows (or one row with K beyond the register kernel): 8-row launches
+    for (int64_t m0 = 0; m0 < m; m0 += 8) {
+        const int mm = (int)((m - m0) < 8 ? (m - m0) : 8);
         const float* xc = x + m0 * ldx;
         float* yc = y + m0 * ldy;
         hipError_t e = silu_pairs ? launch_r<2>(dev, w, (int)n_out, P, log2S, xc, (int)ldx, mm, yc, (int)ldy, stream)

@@ -17,7 +17,7 @@ struct DeviceInfo {
 // Returns the cached info of the current device (queried once per device).
 hipError_t current_device_info(DeviceInfo* out);
 
-// y[m][n] = x[m] . W[n]^T for m <= 16 rows (float32 path).  When silu_pairs is true,
+// y[m][n] = x[m] . W[n]^T for m < 256 rows (float32 path, 8-row launches).  When silu_pairs is true,
 // W has 2*n_out rows and the output is SiLU(gate) * up with gate row j, up row n_out+j.
 hipError_t launch_gemv_q8(const DeviceInfo& dev, const uint8_t* w, int64_t n_out, int64_t k, bool silu_pairs,
                           const float* x, int64_t m, int64_t ldx, float* y, int64_t ldy, hipStream_t stream);
