@@ -197,7 +197,7 @@ def main():
     dev = torch.device("cuda:0")
     if args.workload == "qwen3-8b-block-linears":
         spec = wl.QWEN3_8B_BLOCK
-        m_values = (1, 8)
+        m_values = (1, 8, 16)
     else:
         spec = wl.QWEN3_06B_BLOCK
         m_values = (1,)

@@ -178,12 +178,22 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // One wave-wide direct-to-LDS copy: lane l copies 16 bytes from its src to
-// lds + 16*l (lds wave-uniform).  Written as inline assembly so that the compiler does
-// not serialize it against LDS reads of the other buffer: the caller waits for it with
-// wait_vmcnt (it counts as one vector-memory load, retired in order) and a barrier.
+// lds + 16*l (lds wave-uniform, taken from M0 when the load issues).  Written as inline
+// assembly so that the compiler does not serialize it against LDS reads of the other
+// buffer: the caller waits for it with wait_vmcnt (it counts as one vector-memory load,
+// retired in order) and a barrier.  M0 is saved and restored around it; a write of M0
+// needs one wait state before an LDS-DMA load reads it.
 __device__ __forceinline__ void lds_copy16(const void* src, float4* lds) {
     const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(base) : "m0");
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(base));
 }
 
 template <int M, int R, bool SILU>
@@ -208,26 +218,33 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(1,
     const size_t row_bytes = (size_t)P * 68;
     const int nch = (P + 15) >> 4;
     const int steps = (nch + 1) >> 1;
+    const int tiles = (n_out + 8 * R - 1) / (8 * R);
+    // this block's tiles: blockIdx.x, + gridDim.x, ...; its items: (tile, step) in order
+    const int my_tiles = (tiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int items = my_tiles * steps;
     __builtin_assume(steps >= 1);  // P >= 4 (K is a positive multiple of 256)
+    __builtin_assume(items >= 1);  // the grid has at most `tiles` blocks
 
-    int rows[RR];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        int n = blockIdx.x * (8 * R) + slot * R + r;
-        n = n < n_out ? n : n_out - 1;  // past the end: duplicate the last row (same bits)
-        rows[r] = n;
-        if constexpr (SILU) rows[R + r] = n + n_out;
-    }
+    // first output row of the lane's slot in tile i of this block (past the end: clamped,
+    // so the lane duplicates the last row, same bits)
+    auto out_row = [&](int i, int r) __attribute__((always_inline)) {
+        const int n = ((int)blockIdx.x + i * (int)gridDim.x) * (8 * R) + slot * R + r;
+        return n < n_out ? n : n_out - 1;
+    };
     // the group's chunk at step st, clamped to a valid chunk (a clamped step is not used)
     auto chunk_of = [&](int st) __attribute__((always_inline)) {
         const int ch = h + 2 * st;
         return ch < nch ? ch : nch - 1;
     };
-    auto load_w = [&](int st, uint32_t(&wr)[RR][17]) __attribute__((always_inline)) {
+    auto load_w = [&](int i, int st, uint32_t(&wr)[RR][17]) __attribute__((always_inline)) {
         const int p = 16 * chunk_of(st) + j;
         const int pc = p < P ? p : P - 1;  // past the row: a pair of the same row (unused)
 #pragma unroll
-        for (int r = 0; r < RR; ++r) load_pair(w + (size_t)rows[r] * row_bytes + 68 * (size_t)pc, wr[r]);
+        for (int r = 0; r < R; ++r) {
+            const int n = out_row(i, r);
+            load_pair(w + (size_t)n * row_bytes + 68 * (size_t)pc, wr[r]);
+            if constexpr (SILU) load_pair(w + (size_t)(n + n_out) * row_bytes + 68 * (size_t)pc, wr[R + r]);
+        }
     };
     // Half `half` of the group's activation chunk for step st: 2*M wave-wide copies of 64
     // float4; the group's two waves take every other one.  Copy q covers float4
@@ -295,21 +312,66 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(1,
             }
         }
     };
+    // Tile i done: butterfly over the 16 lanes, group 1 hands its sums to group 0
+    // through LDS (lane j == 0 of each row writes), group 0 adds and stores.
+    auto finish_tile = [&](int i) __attribute__((always_inline)) {
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) {
+#pragma unroll
+            for (int r = 0; r < RR; ++r)
+#pragma unroll
+                for (int m = 0; m < M; ++m) acc[r][m] += __shfl_xor(acc[r][m], off, 64);
+        }
+        if (h == 1 && j == 0) {
+#pragma unroll
+            for (int r = 0; r < RR; ++r)
+#pragma unroll
+                for (int m = 0; m < M; ++m) part[(slot * RR + r) * M + m] = acc[r][m];
+        }
+        __syncthreads();
+        if (h == 0) {
+#pragma unroll
+            for (int r = 0; r < RR; ++r)
+#pragma unroll
+                for (int m = 0; m < M; ++m) acc[r][m] += part[(slot * RR + r) * M + m];
+            // every lane of the 16 holds the same bits: all store
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int n = out_row(i, r);
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    if constexpr (SILU)
+                        y[(size_t)m * ldy + n] = silu_mul(acc[r][m], acc[R + r][m]);
+                    else
+                        y[(size_t)m * ldy + n] = acc[r][m];
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < RR; ++r)
+#pragma unroll
+            for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+    };
 
     uint32_t wc[RR][17], wn[RR][17];
     stage_x(0, 0, xa[h]);
-    load_w(0, wc);
+    load_w(0, 0, wc);
     __builtin_amdgcn_sched_barrier(0);  // the loads stay above the wait
     wait_vmcnt<0>();
     __syncthreads();
-    // Step st, half 0: copy half 1 into xb and load step st + 1's weights into wn while
-    // multiplying half 0 (xa); wait for the copy only (the weights may stay in flight).
-    // Half 1: copy step st + 1's half 0 into xa while multiplying half 1 (xb); wait for
-    // everything, wc = wn.  A barrier ends each half.
-    for (int st = 0; st < steps; ++st) {
-        const bool more = st + 1 < steps;
+    // Item (tile i, step st), half 0: copy half 1 into xb and load the next item's
+    // weights into wn while multiplying half 0 (xa); wait for the copy only (the weights
+    // may stay in flight).  Half 1: copy the next item's half 0 into xa while multiplying
+    // half 1 (xb); finish the tile after its last step; wait for everything, wc = wn.  A
+    // barrier ends each half.  The part array of finish_tile is not touched by the copies.
+    int i = 0, st = 0;
+    for (int it = 0; it < items; ++it) {
+        const bool more = it + 1 < items;
+        const bool last_step = st + 1 == steps;
+        const int ni = last_step ? i + 1 : i;
+        const int nst = last_step ? 0 : st + 1;
         stage_x(st, 1, xb[h]);
-        if (more) load_w(st + 1, wn);
+        if (more) load_w(ni, nst, wn);
         __builtin_amdgcn_sched_barrier(0);
         compute(std::integral_constant<int, 0>{}, st, wc, xa[h]);
         __builtin_amdgcn_sched_barrier(0);
@@ -319,9 +381,10 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(1,
             wait_vmcnt<0>();
         }
         __syncthreads();
-        if (more) stage_x(st + 1, 0, xa[h]);
+        if (more) stage_x(nst, 0, xa[h]);
         __builtin_amdgcn_sched_barrier(0);
         compute(std::integral_constant<int, 1>{}, st, wc, xb[h]);
+        if (last_step) finish_tile(i);
         if (more) {
             __builtin_amdgcn_sched_barrier(0);
             wait_vmcnt<0>();
@@ -331,38 +394,8 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(1,
                 for (int q = 0; q < 17; ++q) wc[r][q] = wn[r][q];
             __syncthreads();
         }
-    }
-
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) {
-#pragma unroll
-        for (int r = 0; r < RR; ++r)
-#pragma unroll
-            for (int m = 0; m < M; ++m) acc[r][m] += __shfl_xor(acc[r][m], off, 64);
-    }
-    // group 1 hands its sums to group 0 through LDS; lane j == 0 of each row writes
-    if (h == 1 && j == 0) {
-#pragma unroll
-        for (int r = 0; r < RR; ++r)
-#pragma unroll
-            for (int m = 0; m < M; ++m) part[(slot * RR + r) * M + m] = acc[r][m];
-    }
-    __syncthreads();
-    if (h == 0) {
-#pragma unroll
-        for (int r = 0; r < RR; ++r)
-#pragma unroll
-            for (int m = 0; m < M; ++m) acc[r][m] += part[(slot * RR + r) * M + m];
-        // every lane of the 16 holds the same bits: all store
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                if constexpr (SILU)
-                    y[(size_t)m * ldy + rows[r]] = silu_mul(acc[r][m], acc[R + r][m]);
-                else
-                    y[(size_t)m * ldy + rows[r]] = acc[r][m];
-            }
+        i = ni;
+        st = nst;
     }
 }
 
@@ -424,25 +457,57 @@ bool try_xreg_m(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, int l
     }
 }
 
+// Blocks of gemv_rows_kernel<M, R, SILU> resident per CU (queried once per kernel).
 template <int M, int R, bool SILU>
-hipError_t launch_rows_r(int n_out, int P, const uint8_t* w, const float* x, int ldx, float* y, int ldy,
-                         hipStream_t stream) {
-    const int blocks = (n_out + 8 * R - 1) / (8 * R);
+int rows_per_cu() {
+    static const int per_cu = [] {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemv_rows_kernel<M, R, SILU>, kRowsThreads, 0) !=
+                hipSuccess ||
+            n < 1)
+            n = 1;
+        return n;
+    }();
+    return per_cu;
+}
+
+template <int M, int R, bool SILU>
+hipError_t launch_rows_r(const DeviceInfo& dev, int n_out, int P, const uint8_t* w, const float* x, int ldx, float* y,
+                         int ldy, hipStream_t stream) {
+    // persistent grid: one block per resident slot (at most one per tile); each walks
+    // its tiles at a stride of the grid
+    const int tiles = (n_out + 8 * R - 1) / (8 * R);
+    const int64_t slots = (int64_t)dev.cu_count * rows_per_cu<M, R, SILU>();
+    const int blocks = (int)(tiles < slots ? tiles : slots);
     hipLaunchKernelGGL((gemv_rows_kernel<M, R, SILU>), dim3(blocks), dim3(kRowsThreads), 0, stream, w, n_out, P, x,
                        ldx, y, ldy);
     return hipGetLastError();
 }
 
+// Fraction of a persistent grid's block-steps that do work: tiles spread over `slots`
+// blocks, the busiest taking ceil(tiles / slots).
+inline double round_fill(int64_t tiles, int64_t slots) {
+    const int64_t per = (tiles + slots - 1) / slots;
+    const int64_t used = tiles < slots ? tiles : slots;
+    return (double)tiles / (double)(per * (used > 0 ? slots : 1));
+}
+
 template <int M, bool SILU>
 hipError_t launch_rows(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, const float* x, int ldx, float* y,
                        int ldy, hipStream_t stream) {
-    // R rows (row pairs) per lane: the largest that still gives two blocks per CU
-    const int64_t want = 2 * (int64_t)dev.cu_count;
+    // R rows (row pairs) per lane: more rows per lane share each activation read, fewer
+    // spread the tiles more evenly.  Take the largest R within 5% of the best fill.
+    const int64_t cus = dev.cu_count;
+    const double f1 = round_fill((n_out + 7) / 8, cus * rows_per_cu<M, 1, SILU>());
+    const double f2 = round_fill((n_out + 15) / 16, cus * rows_per_cu<M, 2, SILU>());
+    double f4 = 0.0;
+    if constexpr (!SILU) f4 = round_fill((n_out + 31) / 32, cus * rows_per_cu<M, 4, SILU>());
+    const double best = f1 > f2 ? (f1 > f4 ? f1 : f4) : (f2 > f4 ? f2 : f4);
     if constexpr (!SILU) {
-        if ((n_out + 31) / 32 >= want) return launch_rows_r<M, 4, SILU>(n_out, P, w, x, ldx, y, ldy, stream);
+        if (f4 >= 0.95 * best) return launch_rows_r<M, 4, SILU>(dev, n_out, P, w, x, ldx, y, ldy, stream);
     }
-    if ((n_out + 15) / 16 >= want) return launch_rows_r<M, 2, SILU>(n_out, P, w, x, ldx, y, ldy, stream);
-    return launch_rows_r<M, 1, SILU>(n_out, P, w, x, ldx, y, ldy, stream);
+    if (f2 >= 0.95 * best) return launch_rows_r<M, 2, SILU>(dev, n_out, P, w, x, ldx, y, ldy, stream);
+    return launch_rows_r<M, 1, SILU>(dev, n_out, P, w, x, ldx, y, ldy, stream);
 }
 
 template <int M, int R>
