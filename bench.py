@@ -20,6 +20,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -36,6 +37,27 @@ METRIC = "effective weight GB/s & % of HBM peak for Q8_0 linear at M=1/8/16; dec
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def measured_traffic():
+    """HBM bytes per launch of the M=1 fused gate_up kernel from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE summary, or None once the kernel sources differ from the ones
+    the counters were taken with."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic_gemv_q8_qwen3_8b_shapes.md")
+    src = os.path.join(ROOT, "block_quantized_weight_linear_amd", "csrc")
+    try:
+        text = open(path).read()
+        h = hashlib.sha256()
+        for name in ("gemv_q8.hip", "gemv_core.h"):
+            with open(os.path.join(src, name), "rb") as f:
+                h.update(f.read())
+        want = re.search(r"sources_sha256: ([0-9a-f]{64})", text).group(1)
+        if want != h.hexdigest():
+            return None
+        return int(re.search(r"gate_up_m1_traffic_bytes: (\d+)", text).group(1))
+    except (OSError, AttributeError):
+        return None
 
 
 # --------------------------------------------------------------------- workloads
@@ -224,7 +246,8 @@ def main():
         "execution": "HIP graph replay of the step (eager per-call timing in ms_per_step_eager)",
         "roofline": {"bound": "hbm", "kernel": "fused gate_up + SiLU, one activation row (gemv_xreg_kernel)",
                      "achieved": r1["gate_up_gbps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(r1["gate_up_gbps"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(r1["gate_up_gbps"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE)",
                      "algorithmic_bytes_per_launch": gate_up_bytes, "avg_launch_us": r1["gate_up_avg_us"]},
     }
     for m, r in res.items():
