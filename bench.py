@@ -169,20 +169,10 @@ def bench_block(args, torch, dev, q8, spec, m_values):
             if not torch.equal(bufs["y"], eager_y):
                 raise RuntimeError("graph replay differs from the eager step")
             ms = time_steps(torch, graph.replay, args.steps, args.warmup)
-            # dominant kernel: the fused gate_up of every layer launched back to back (distinct
-            # weights, so each launch streams from HBM), HIP events on the launching stream
-            reps = max(1, args.steps // 5)
-            for _ in range(2):
-                stack.run_gate_up(q8, x, bufs)
-            torch.cuda.synchronize()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(reps):
-                stack.run_gate_up(q8, x, bufs)
-            e1.record()
-            torch.cuda.synchronize()
-            durs = [e0.elapsed_time(e1) / (reps * layers)]
+        # dominant kernel: the fused gate_up of every layer launched back to back (distinct
+        # weights, so each launch streams from HBM), as a graph timed on its stream
+        durs = [graph_launch_ms(torch, lambda: stack.run_gate_up(q8, x, bufs), layers,
+                                replays=max(2, args.steps // 5))]
         res = {"ms_per_step": round(ms, 5), "gbps": round(bytes_step / (ms * 1e-3) / 1e9, 2),
                "tok_s": round(m * 1000.0 / ms, 2), "weight_bytes_per_step": bytes_step,
                "ms_per_step_eager": round(ms_eager, 5),
@@ -196,6 +186,117 @@ def bench_block(args, torch, dev, q8, spec, m_values):
     return stack, out, gate_up_bytes
 
 
+def graph_launch_ms(torch, seq, launches, replays=5):
+    """Average ms per launch of a launch sequence: seq() (which makes `launches` library
+    calls) is captured once as a HIP graph on a side stream and replayed back to back,
+    timed with HIP events on that stream, so host call overhead does not hide short
+    kernels."""
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        seq()  # warm (and the eager reference for the graph check below)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            seq()
+        graph.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(replays):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (replays * launches)
+
+
+def bench_linear(torch, dev, q8, name, n, k, m, fused, reps, min_bytes=600e6):
+    """One linear launched back to back over distinct resident weight copies (enough of
+    them to exceed the 256 MB Infinity Cache twice)."""
+    import workloads as wl
+    wb, _, _ = wl.q8_weight(31, n, k)
+    base = torch.from_numpy(wb).to(dev)
+    copies = [base] + [base.clone() for _ in range(max(1, int(min_bytes // wb.size)))]
+    x = torch.from_numpy(wl.activations(37, m, k)).to(dev)
+    nout = n // 2 if fused else n
+    y = torch.empty((m, nout), device=dev)
+    launches = max(reps, len(copies))
+
+    def seq():
+        for i in range(launches):
+            w = copies[i % len(copies)]
+            if fused:
+                q8.q8_linear_fused_gate_up_silu(w, nout, k, x, out=y)
+            else:
+                q8.q8_linear(w, n, k, x, out=y)
+
+    ms = graph_launch_ms(torch, seq, launches)
+    flops = 2.0 * m * n * k
+    res = {"shape": [n, k], "m": m, "fused_silu": fused, "us_per_launch": round(ms * 1e3, 3),
+           "weight_bytes": int(wb.size), "gbps": round(wb.size / (ms * 1e-3) / 1e9, 2),
+           "hbm_frac": round(wb.size / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "tflops": round(flops / (ms * 1e-3) / 1e12, 2), "distinct_weight_copies": len(copies)}
+    if m >= 256:
+        res["mfma_bf16_frac"] = round(res["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)
+    log(f"{name}: {res}")
+    del copies
+    return res
+
+
+def bench_moe(torch, dev, q8, layers, steps, warmup):
+    """Qwen3-30B-A3B MoE layers at 16 tokens: device router (softmax top-8, renormalized)
+    then the grouped SwiGLU expert mixture, each layer with its own resident experts."""
+    import workloads as wl
+    cfg = wl.QWEN3_30B_A3B_MOE
+    e, f, hd, k, t = cfg.n_exp, cfg.ffn, cfg.hidden, cfg.k, cfg.tokens
+    distinct = 8  # experts generated on the host; the device stacks repeat them (timing only)
+    gu_h = np.concatenate([wl.q8_weight(cfg.seed * 100 + i, 2 * f, hd)[0] for i in range(distinct)])
+    dn_h = np.concatenate([wl.q8_weight(cfg.seed * 100 + 50 + i, hd, f)[0] for i in range(distinct)])
+    gu1, dn1 = torch.from_numpy(gu_h).to(dev), torch.from_numpy(dn_h).to(dev)
+    gu_stack = torch.cat([gu1] * (e // distinct))
+    dn_stack = torch.cat([dn1] * (e // distinct))
+    gu = [gu_stack] + [gu_stack.clone() for _ in range(layers - 1)]
+    dn = [dn_stack] + [dn_stack.clone() for _ in range(layers - 1)]
+    del gu1, dn1
+    wr = [torch.from_numpy(wl.router_weight(cfg.seed + 2 + l, e, hd, cfg.router_std)).to(dev) for l in range(layers)]
+    x = torch.from_numpy(wl.activations(cfg.seed + 1, t, hd)).to(dev)
+    idx = [torch.empty((t, k), dtype=torch.int32, device=dev) for _ in range(layers)]
+    wts = [torch.empty((t, k), dtype=torch.float32, device=dev) for _ in range(layers)]
+    y = torch.empty((t, hd), device=dev)
+    ws = torch.empty(q8.q8_moe_workspace_bytes(t, k, e, f, hd), dtype=torch.uint8, device=dev)
+    per_expert = (gu_h.size + dn_h.size) // distinct
+
+    def step():
+        for l in range(layers):
+            q8.moe_route_topk(x, wr[l], k, True, idx_out=idx[l], w_out=wts[l])
+            q8.q8_moe_grouped_linear(gu[l], dn[l], e, f, hd, x, idx[l], wts[l], out=y, workspace=ws)
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        ms_eager = time_steps(torch, step, steps, warmup)
+        y_eager = y.clone()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(y, y_eager):
+            raise RuntimeError("MoE graph replay differs from the eager step")
+        ms = time_steps(torch, graph.replay, steps, warmup)
+    used = [int(torch.unique(i).numel()) for i in idx]
+    expert_bytes = sum(used) * per_expert
+    router_bytes = layers * e * hd * 4
+    res = {"workload": cfg.name, "tokens": t, "layers": layers, "experts": e, "top_k": k,
+           "ms_per_step": round(ms, 5), "ms_per_step_eager": round(ms_eager, 5),
+           "us_per_layer": round(ms * 1e3 / layers, 3), "tok_s": round(t * 1000.0 / ms, 1),
+           "experts_used_per_layer": used, "bytes_per_expert": per_expert,
+           "weight_bytes_per_step": expert_bytes + router_bytes,
+           "gbps": round((expert_bytes + router_bytes) / (ms * 1e-3) / 1e9, 2)}
+    res["hbm_frac"] = round(res["gbps"] / HBM_PEAK_GBS, 4)
+    log(f"moe: {res}")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -205,6 +306,8 @@ def main():
                     choices=["qwen3-8b-block-linears", "qwen3-0.6b-block-linears"])
     ap.add_argument("--layers", type=int, default=0, help="override the layer count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the other workloads (0.6B, gate_up M=16/M=512, MoE layer)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -253,6 +356,17 @@ def main():
     for m, r in res.items():
         if m != 1:
             line[f"m{m}"] = r
+    if not args.no_extras and args.workload == "qwen3-8b-block-linears":
+        extras = {}
+        reps = max(20, args.steps)
+        extras["qwen3-0.6b-qkv-m1"] = bench_linear(torch, dev, q8, "0.6b qkv m1", 4096, 1024, 1, False, reps * 4)
+        _, r06, _ = bench_block(args, torch, dev, q8, wl.QWEN3_06B_BLOCK, (1,))
+        extras["qwen3-0.6b-block-linears-m1"] = r06[1]
+        extras["qwen3-8b-gate-up-m16"] = bench_linear(torch, dev, q8, "8b gate_up m16", 24576, 4096, 16, True, reps)
+        extras["qwen3-8b-gate-up-m512-prefill"] = bench_linear(torch, dev, q8, "8b gate_up m512", 24576, 4096, 512,
+                                                               True, reps)
+        extras["qwen3-30b-a3b-moe-16tok"] = bench_moe(torch, dev, q8, 4, args.steps, args.warmup)
+        line["configs"] = extras
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on one layer")
         line["cpu_baseline"] = cpu_baseline_block(spec)

@@ -188,13 +188,17 @@ __device__ __forceinline__ void wave_rows(const uint8_t* __restrict__ w, int n_o
         n = rg * G + g;
         p = j + S * (it % n_rounds);
     };
-    auto load_item = [&](int it, uint32_t(&wr)[R][17]) {
+    // Loads are unconditional so the compiler keeps the next item's loads in flight
+    // (a load inside a branch makes it wait for all of them): a row past the matrix
+    // loads the last row, a pair past the row loads a pair of the same row; neither is
+    // multiplied or stored under its own index.
+    auto load_item = [&](int it, uint32_t(&wr)[R][17]) __attribute__((always_inline)) {
         int n, p;
         item(it, n, p);
-        if (n < n_out && p < P) {
+        const int nc = n < n_out ? n : n_out - 1;
+        const int pc = p < P ? p : p % P;
 #pragma unroll
-            for (int r = 0; r < R; ++r) load_pair(w + (size_t)(n + r * r_off) * row_bytes + 68 * (size_t)p, wr[r]);
-        }
+        for (int r = 0; r < R; ++r) load_pair(w + (size_t)(nc + r * r_off) * row_bytes + 68 * (size_t)pc, wr[r]);
     };
 
     float acc[R][M];
@@ -203,10 +207,11 @@ __device__ __forceinline__ void wave_rows(const uint8_t* __restrict__ w, int n_o
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
 
-    auto finish_item = [&](int it, const uint32_t(&wr)[R][17]) {
+    auto finish_item = [&](int it, const uint32_t(&wr)[R][17]) __attribute__((always_inline)) {
         int n, p;
         item(it, n, p);
-        if (n < n_out && p < P) mac_pair<M, R>(wr, xs, p, acc);
+        const int nc = n < n_out ? n : n_out - 1;
+        if (p < P) mac_pair<M, R>(wr, xs, p, acc);
         if (it % n_rounds == n_rounds - 1) {
             for (int off = S >> 1; off >= 1; off >>= 1) {
 #pragma unroll
@@ -214,7 +219,10 @@ __device__ __forceinline__ void wave_rows(const uint8_t* __restrict__ w, int n_o
 #pragma unroll
                     for (int m = 0; m < M; ++m) acc[r][m] += __shfl_xor(acc[r][m], off, 64);
             }
-            if (j == 0 && n < n_out) out(n, acc);
+            // after the butterfly every lane of the row holds the same bits: all store
+            // (a lane past the matrix multiplies the last row and stores what its owner
+            // stores)
+            out(nc, acc);
 #pragma unroll
             for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -229,7 +237,7 @@ __device__ __forceinline__ void wave_rows(const uint8_t* __restrict__ w, int n_o
     for (; it + 1 < n_items; it += 2) {
         load_item(it + 1, wb);
         finish_item(it, wa);
-        if (it + 2 < n_items) load_item(it + 2, wa);
+        load_item(it + 2 < n_items ? it + 2 : it + 1, wa);  // past the end: a reload, unused
         finish_item(it + 1, wb);
     }
     if (it < n_items) finish_item(it, wa);

@@ -92,6 +92,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, WPE
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
 
+    // The ring's first weight loads are issued before the activations are staged, so the
+    // weights' HBM latency runs under the staging instead of after it (with one round per
+    // row; with more, the extra live registers cost the ring its overlap).
+    uint32_t ring[D][R][17];
+    auto ring_prologue = [&]() __attribute__((always_inline)) {
+        static_for<D - 1>([&](auto sc) __attribute__((always_inline)) {
+            constexpr int s = decltype(sc)::value;
+            load_item(s, s % NR, ring[s]);
+        });
+    };
+    if constexpr (NR == 1) ring_prologue();
     // Activations: one coalesced pass from global into the slot-major LDS layout per
     // block, then each lane copies the values of its own pair slots into registers.
     stage_x_lds(x_lds, M, P, [&](int m) { return x + (size_t)m * ldx; }, threadIdx.x, kThreads);
@@ -107,11 +118,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, WPE
 #pragma unroll
             for (int c = 0; c < 16; ++c) xr[i][m][c] = x_lds[(m * 16 + c) * P + pc];
     }
-    uint32_t ring[D][R][17];
-    static_for<D - 1>([&](auto sc) __attribute__((always_inline)) {
-        constexpr int s = decltype(sc)::value;
-        load_item(s, s % NR, ring[s]);
-    });
+    if constexpr (NR > 1) ring_prologue();
 
     // One ring step: prefetch item it+D-1 (when LOAD), multiply item it, and finish the
     // row after its last round.
@@ -449,7 +456,16 @@ bool try_xreg_m(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, int l
     const int NR = (P + S - 1) / S;
     // (ring depth, waves per SIMD) per shape: the ring and the activations stay in registers
     switch (NR) {
-        case 1: *err = launch_xreg<M, R, 1, (R == 1 ? 4 : 3), (R == 1 ? 3 : 2)>(dev, w, n_out, P, log2S, x, ldx, y, ldy, stream); return true;
+        case 1: {
+            // A matrix with few row groups would leave most SIMDs idle if every wave had to
+            // fill a whole ring: shallower rings give one wave per SIMD first.
+            const int items = (n_out + (64 >> log2S) - 1) / (64 >> log2S);
+            const int simds = dev.cu_count * kWaves;
+            if (items <= simds) *err = launch_xreg<M, R, 1, 1, 4>(dev, w, n_out, P, log2S, x, ldx, y, ldy, stream);
+            else if (items <= 2 * simds) *err = launch_xreg<M, R, 1, 2, 3>(dev, w, n_out, P, log2S, x, ldx, y, ldy, stream);
+            else *err = launch_xreg<M, R, 1, (R == 1 ? 4 : 3), (R == 1 ? 3 : 2)>(dev, w, n_out, P, log2S, x, ldx, y, ldy, stream);
+            return true;
+        }
         case 2: *err = launch_xreg<M, R, 2, (R == 1 ? 4 : 2), 2>(dev, w, n_out, P, log2S, x, ldx, y, ldy, stream); return true;
         case 3: *err = launch_xreg<M, R, 3, 3, 1>(dev, w, n_out, P, log2S, x, ldx, y, ldy, stream); return true;
         case 4: *err = launch_xreg<M, R, 4, 4, 1>(dev, w, n_out, P, log2S, x, ldx, y, ldy, stream); return true;

@@ -11,16 +11,19 @@
 //                expert, stable in pair order; offsets[e], sorted pair list, and the
 //                inverse map pair -> position.
 //   2. gate_up   grid (expert, row tile): an expert with no pairs exits at once;
-//                otherwise its tokens' activation rows are staged in LDS (up to 8 at a
-//                time) and one pass over the tile's gate/up rows serves all of them
-//                (same per-row arithmetic as the dense fused gate_up call).  Output:
-//                hidden[position][f] = SiLU(gate) * up.
-//   3. down      grid (expert, row tile): hidden rows of the expert's positions are
-//                contiguous; out[position][h] = W_down[e] . hidden[position].
-//   4. combine   one workgroup per token: y[t] = sum_j w[t][j] * out[pos(t, j)] in slot
-//                order j = 0..k-1 (float32 fma chain, no atomics).
+//                otherwise its tokens' activation rows are staged in LDS (up to 4 at a
+//                time) and one pass over the tile's rows serves all of them (same
+//                per-row arithmetic as the dense one-row call).  The 2f gate and up rows
+//                run as separate rows: hidden[position][0..2f) = gate sums, up sums.
+//   3. down      grid (expert, row tile): the activation row of a position is
+//                SiLU(gate) * up, formed from its hidden row while staging (hidden rows
+//                of an expert's positions are contiguous); out[position][h].
+//   4. combine   grid (token, 256 columns): y[t] = sum_j w[t][j] * out[pos(t, j)] in
+//                slot order j = 0..k-1 (float32 fma chain, no atomics).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <utility>
 
 #include "gemv_core.h"
 #include "q8_internal.h"
@@ -31,7 +34,7 @@ namespace q8k {
 constexpr int kMoeThreads = 256;
 constexpr int kMoeWaves = kMoeThreads / 64;
 constexpr int kMoeGroupsPerWave = 4;  // row groups each wave takes in one tile
-constexpr int kMoeMaxRows = 8;        // activation rows staged per pass
+constexpr int kMoeMaxRows = 4;        // activation rows staged per pass
 constexpr int kPlanThreads = 256;
 
 // ---------------------------------------------------------------- 1. route plan
@@ -39,10 +42,10 @@ constexpr int kPlanThreads = 256;
 __global__ __launch_bounds__(kPlanThreads) void moe_plan_kernel(const int32_t* __restrict__ idx, int n_pairs,
                                                                 int n_exp, int32_t* __restrict__ offsets,
                                                                 int32_t* __restrict__ sorted,
-                                                                int32_t* __restrict__ inv) {
+                                                                int32_t* __restrict__ inv,
+                                                                int32_t* __restrict__ active) {
     __shared__ int counts[q8v::kMaxExperts + 1];
     __shared__ int running[q8v::kMaxExperts + 1];
-    __shared__ int chunk_e[kPlanThreads];
     const int tid = threadIdx.x;
     for (int e = tid; e <= n_exp; e += kPlanThreads) counts[e] = 0;
     __syncthreads();
@@ -51,19 +54,51 @@ __global__ __launch_bounds__(kPlanThreads) void moe_plan_kernel(const int32_t* _
         if (e >= 0 && e < n_exp) atomicAdd(&counts[e], 1);
     }
     __syncthreads();
-    if (tid == 0) {
-        int acc = 0;
-        for (int e = 0; e < n_exp; ++e) {
-            running[e] = acc;
-            offsets[e] = acc;
-            acc += counts[e];
+    {
+        // exclusive scan of the counts (thread e takes expert e; n_exp <= kPlanThreads):
+        // a shuffle scan per wave, then the totals of the waves before it
+        __shared__ int wave_total[kPlanThreads / 64];
+        const int lane = tid & 63;
+        const int c = tid < n_exp ? counts[tid] : 0;
+        int incl = c;
+        for (int off = 1; off < 64; off <<= 1) {
+            const int v = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += v;
         }
-        offsets[n_exp] = acc;
+        if (lane == 63) wave_total[tid >> 6] = incl;
+        __syncthreads();
+        int base = 0;
+        for (int w = 0; w < (tid >> 6); ++w) base += wave_total[w];
+        const int excl = base + incl - c;
+        if (tid < n_exp) {
+            running[tid] = excl;
+            offsets[tid] = excl;
+        }
+        if (tid == n_exp - 1) offsets[n_exp] = excl + c;
+        // the experts with pairs, in expert order, and their number at active[n_exp]
+        const int has = c > 0 ? 1 : 0;
+        int aincl = has;
+        for (int off = 1; off < 64; off <<= 1) {
+            const int v = __shfl_up(aincl, off, 64);
+            if (lane >= off) aincl += v;
+        }
+        __shared__ int wave_active[kPlanThreads / 64];
+        if (lane == 63) wave_active[tid >> 6] = aincl;
+        __syncthreads();
+        int abase = 0;
+        for (int w = 0; w < (tid >> 6); ++w) abase += wave_active[w];
+        if (has) active[abase + aincl - 1] = tid;
+        if (tid == kPlanThreads - 1) active[n_exp] = abase + aincl;
     }
     __syncthreads();
     // Stable scatter, one chunk of kPlanThreads pairs at a time: a pair's place is the
     // running count of its expert plus the number of earlier pairs of the chunk with
-    // the same expert.
+    // the same expert.  Within a wave the lanes holding the same expert are found with
+    // eight ballots (one per bit of the id, ids < 256); earlier waves' counts come
+    // through LDS.
+    __shared__ int wave_cnt[kPlanThreads / 64][q8v::kMaxExperts];
+    const int lane = tid & 63;
+    const int wv = tid >> 6;
     for (int base = 0; base < n_pairs; base += kPlanThreads) {
         const int i = base + tid;
         int e = -1;
@@ -71,90 +106,129 @@ __global__ __launch_bounds__(kPlanThreads) void moe_plan_kernel(const int32_t* _
             e = idx[i];
             if (e < 0 || e >= n_exp) e = -1;
         }
-        chunk_e[tid] = e;
-        __syncthreads();
-        int rank = 0;
-        bool last = true;
-        if (e >= 0) {
-            for (int t = 0; t < tid; ++t) rank += (chunk_e[t] == e);
-            for (int t = tid + 1; t < kPlanThreads; ++t) last = last && (chunk_e[t] != e);
+        uint64_t same = __ballot(e >= 0);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const uint64_t set = __ballot(e >= 0 && ((e >> b) & 1));
+            same &= ((e >> b) & 1) ? set : ~set;
         }
+        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        const int rank_in_wave = __popcll(same & below);
+        // the highest lane of each group publishes the wave's count for that expert
+        for (int x = tid; x < (kPlanThreads / 64) * q8v::kMaxExperts; x += kPlanThreads) (&wave_cnt[0][0])[x] = 0;
+        __syncthreads();
+        if (e >= 0 && (same >> lane) == 1ull) wave_cnt[wv][e] = __popcll(same);
+        __syncthreads();
+        int rank = rank_in_wave;
+        if (e >= 0)
+            for (int w = 0; w < wv; ++w) rank += wave_cnt[w][e];
         const int pos = (e >= 0) ? running[e] + rank : -1;
         if (i < n_pairs) {
             inv[i] = pos;
             if (pos >= 0) sorted[pos] = i;
         }
         __syncthreads();
-        if (e >= 0 && last) running[e] = pos + 1;
+        // the chunk's last pair of each expert advances its running count
+        if (e >= 0) {
+            int later = 0;
+            for (int w = wv + 1; w < kPlanThreads / 64; ++w) later += wave_cnt[w][e];
+            if (later == 0 && (same >> lane) == 1ull) running[e] = pos + 1;
+        }
         __syncthreads();
     }
 }
 
 // ------------------------------------------------------- 2./3. expert GEMV passes
 
-// R = 2: gate_up (rows n and n + n_out, SiLU(gate)*up into `out`);  R = 1: down.
-// GATHER: activation row i of the expert is x[sorted[pos] / k] (token rows); else it
-// is row `pos` of x (the hidden rows, contiguous per expert).
-template <int R, bool GATHER>
+// One pass of the experts' rows, one row per lane group (the lane layout and per-row
+// order of the one-row dense kernel: S lanes per row, lane j takes the pairs j, j + S,
+// ..., block chains in mac_pair, then the xor butterfly).
+// GATE_UP: the rows are the 2f gate and up rows of the expert, the activation rows the
+//          tokens' x rows (x[sorted[pos] / k]); out[pos][n] for n < 2f.
+// else (down): the activation row of position pos is SiLU(gate) * up of that position's
+//          gate_up output (row pos of `x`, gate in [0, ldx/2), up in [ldx/2, ldx)),
+//          formed while staging; out[pos][n] for n < h.
+// Computing the gate and up rows as separate rows keeps one weight row per lane (the
+// fused two-row form needs twice the registers); SiLU(gate) * up is formed from the
+// same two row sums, with the same function, as in the dense fused call.
+template <bool GATE_UP>
 __global__ __launch_bounds__(kMoeThreads) void moe_expert_kernel(const uint8_t* __restrict__ w_stack,
                                                                  size_t expert_bytes, int n_out, int P, int log2S,
                                                                  const float* __restrict__ x, int ldx,
                                                                  const int32_t* __restrict__ offsets,
-                                                                 const int32_t* __restrict__ sorted, int k,
-                                                                 float* __restrict__ out, int ldo, int rows_per_pass) {
+                                                                 const int32_t* __restrict__ sorted,
+                                                                 const int32_t* __restrict__ active, int n_exp,
+                                                                 int k, float* __restrict__ out, int ldo,
+                                                                 int rows_per_pass, int tiles) {
     extern __shared__ float4 x_lds[];
-    const int e = blockIdx.x;
-    const int pos0 = offsets[e];
-    const int cnt = offsets[e + 1] - pos0;
-    if (cnt == 0) return;
-    const uint8_t* w = w_stack + (size_t)e * expert_bytes;
     const int G = 64 >> log2S;
     const int row_groups = (n_out + G - 1) / G;
     const int tile_groups = kMoeWaves * kMoeGroupsPerWave;
-    const int g_begin = blockIdx.y * tile_groups;
-    const int g_end = min(row_groups, g_begin + tile_groups);
     const int wave = threadIdx.x >> 6;
     const XLds xs{x_lds, P};
-
-    for (int c0 = 0; c0 < cnt; c0 += rows_per_pass) {
-        const int cc = min(rows_per_pass, cnt - c0);
-        const int mt = cc <= 1 ? 1 : cc <= 2 ? 2 : cc <= 4 ? 4 : 8;
-        stage_x_lds(x_lds, mt, P,
-                    [&](int m) -> const float* {
-                        if (m >= cc) return nullptr;
-                        const int pos = pos0 + c0 + m;
-                        if constexpr (GATHER)
-                            return x + (size_t)(sorted[pos] / k) * ldx;
-                        else
-                            return x + (size_t)pos * ldx;
-                    },
-                    threadIdx.x, kMoeThreads);
-        __syncthreads();
-        float* o = out + (size_t)(pos0 + c0) * ldo;
-        auto run = [&](auto mtag) {
-            constexpr int MT = decltype(mtag)::value;
-            wave_rows<MT, R>(w, n_out, n_out, P, log2S, xs, g_begin + wave, kMoeWaves, g_end,
-                             [&](int n, const float(&acc)[R][MT]) {
+    const int k4 = P * 16;  // float4 per activation row
+    // units (active expert, row tile), expert-major, over a grid of resident blocks
+    const int units = active[n_exp] * tiles;
+    for (int u = blockIdx.x; u < units; u += gridDim.x) {
+        const int e = active[u / tiles];
+        const int tile = u - (u / tiles) * tiles;
+        const int pos0 = offsets[e];
+        const int cnt = offsets[e + 1] - pos0;
+        const uint8_t* w = w_stack + (size_t)e * expert_bytes;
+        const int g_begin = tile * tile_groups;
+        const int g_end = min(row_groups, g_begin + tile_groups);
+        for (int c0 = 0; c0 < cnt; c0 += rows_per_pass) {
+            const int cc = min(rows_per_pass, cnt - c0);
+            const int mt = cc <= 1 ? 1 : cc <= 2 ? 2 : 4;
+            // activation rows of this pass: the row addresses first (one load each, the
+            // same for every thread), then the row loads, then LDS (slot-major)
+            const float* rowp[kMoeMaxRows];
 #pragma unroll
-                                 for (int m = 0; m < MT; ++m) {
-                                     if (m < cc) {
-                                         if constexpr (R == 2)
-                                             o[(size_t)m * ldo + n] = silu_mul(acc[0][m], acc[1][m]);
-                                         else
-                                             o[(size_t)m * ldo + n] = acc[0][m];
-                                     }
-                                 }
-                             });
-        };
-        if (mt == 1)
-            run(std::integral_constant<int, 1>{});
-        else if (mt == 2)
-            run(std::integral_constant<int, 2>{});
-        else if (mt == 4)
-            run(std::integral_constant<int, 4>{});
-        else
-            run(std::integral_constant<int, 8>{});
-        __syncthreads();
+            for (int m = 0; m < kMoeMaxRows; ++m) {
+                const int pos = pos0 + c0 + (m < cc ? m : 0);
+                if constexpr (GATE_UP)
+                    rowp[m] = x + (size_t)(sorted[pos] / k) * ldx;
+                else
+                    rowp[m] = x + (size_t)pos * ldx;
+            }
+#pragma unroll
+            for (int m = 0; m < kMoeMaxRows; ++m) {
+                if (m < mt) {
+                    for (int i = threadIdx.x; i < k4; i += kMoeThreads) {
+                        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+                        if (m < cc) {
+                            if constexpr (GATE_UP) {
+                                v = *reinterpret_cast<const float4*>(rowp[m] + 4 * i);
+                            } else {
+                                const float4 gt = *reinterpret_cast<const float4*>(rowp[m] + 4 * i);
+                                const float4 up = *reinterpret_cast<const float4*>(rowp[m] + (ldx >> 1) + 4 * i);
+                                v = make_float4(silu_mul(gt.x, up.x), silu_mul(gt.y, up.y), silu_mul(gt.z, up.z),
+                                                silu_mul(gt.w, up.w));
+                            }
+                        }
+                        x_lds[(m * 16 + (i & 15)) * P + (i >> 4)] = v;
+                    }
+                }
+            }
+            __syncthreads();
+            float* o = out + (size_t)(pos0 + c0) * ldo;
+            auto run = [&](auto mtag) {
+                constexpr int MT = decltype(mtag)::value;
+                wave_rows<MT, 1>(w, n_out, n_out, P, log2S, xs, g_begin + wave, kMoeWaves, g_end,
+                                 [&](int n, const float(&acc)[1][MT]) {
+#pragma unroll
+                                     for (int m = 0; m < MT; ++m)
+                                         if (m < cc) o[(size_t)m * ldo + n] = acc[0][m];
+                                 });
+            };
+            if (mt == 1)
+                run(std::integral_constant<int, 1>{});
+            else if (mt == 2)
+                run(std::integral_constant<int, 2>{});
+            else
+                run(std::integral_constant<int, 4>{});
+            __syncthreads();  // the next pass or unit overwrites the staged rows
+        }
     }
 }
 
@@ -164,29 +238,58 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
                                                           const int32_t* __restrict__ inv,
                                                           const float* __restrict__ wts, int k,
                                                           float* __restrict__ y, int ldy) {
+    // block (token t, 256 columns): each thread one column, the k slot loads issued
+    // together, then the fma chain in slot order
     const int t = blockIdx.x;
-    for (int c = threadIdx.x; c < h; c += blockDim.x) {
-        float acc = 0.0f;
-        for (int j = 0; j < k; ++j) {
+    const int c = blockIdx.y * 256 + threadIdx.x;
+    if (c >= h) return;
+    float acc = 0.0f;
+    for (int j0 = 0; j0 < k; j0 += 8) {
+        float v[8], wj[8];
+        bool use[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            const int j = j0 + jj < k ? j0 + jj : k - 1;
             const int pos = inv[(size_t)t * k + j];
-            if (pos >= 0) acc = __builtin_fmaf(wts[(size_t)t * k + j], o[(size_t)pos * h + c], acc);
+            use[jj] = j0 + jj < k && pos >= 0;  // a skipped expert id contributes nothing
+            wj[jj] = wts[(size_t)t * k + j];
+            v[jj] = o[(size_t)(pos >= 0 ? pos : 0) * h + c];
         }
-        y[(size_t)t * ldy + c] = acc;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+            if (use[jj]) acc = __builtin_fmaf(wj[jj], v[jj], acc);
     }
+    y[(size_t)t * ldy + c] = acc;
 }
 
 // ------------------------------------------------------------------- launcher
 
-// Activation rows staged per pass: the largest power of two <= 8 whose rows fit in
-// 64 KB of LDS (a row of K floats takes P*256 bytes).  Passes use 1, 2, 4 or 8 rows,
-// never more than this.
+// Activation rows staged per pass: the largest power of two <= 4 whose rows fit in
+// 64 KB of LDS (a row of K floats takes P*256 bytes).
 static int staged_rows(int P) {
     int rows = kMoeMaxRows;
     while (rows > 1 && (size_t)rows * P * 256 > 65536) rows >>= 1;
     return rows;
 }
 
-hipError_t launch_moe_grouped(const DeviceInfo&, const uint8_t* wgu, const uint8_t* wdn, int64_t n_exp, int64_t f,
+// Blocks of moe_expert_kernel resident per CU for an LDS size (queried once per size).
+template <bool GATE_UP>
+static int moe_blocks_per_cu(size_t lds) {
+    static thread_local size_t cached_lds = (size_t)-1;
+    static thread_local int per_cu = 1;
+    if (cached_lds != lds) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, moe_expert_kernel<GATE_UP>, kMoeThreads, lds) !=
+                hipSuccess ||
+            n < 1)
+            n = 1;
+        per_cu = n;
+        cached_lds = lds;
+    }
+    return per_cu;
+}
+
+hipError_t launch_moe_grouped(const DeviceInfo& dev, const uint8_t* wgu, const uint8_t* wdn, int64_t n_exp, int64_t f,
                               int64_t h, const float* x, int64_t m, int64_t ldx, const int32_t* idx, const float* wts,
                               int k, float* y, int64_t ldy, void* workspace, hipStream_t stream) {
     const q8v::MoeWorkspace L = q8v::moe_workspace_layout(m, k, n_exp, f, h);
@@ -194,49 +297,49 @@ hipError_t launch_moe_grouped(const DeviceInfo&, const uint8_t* wgu, const uint8
     int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets_off);
     int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.sorted_off);
     int32_t* inv = reinterpret_cast<int32_t*>(ws + L.inv_off);
+    int32_t* active = reinterpret_cast<int32_t*>(ws + L.active_off);
     float* hidden = reinterpret_cast<float*>(ws + L.hidden_off);
     float* outp = reinterpret_cast<float*>(ws + L.out_off);
     const int n_pairs = (int)(m * k);
 
     hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, idx, n_pairs, (int)n_exp, offsets,
-                       sorted, inv);
+                       sorted, inv, active);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
-    // gate_up: K = h, rows 2f per expert
-    {
-        const int P = (int)(h / 64);
+    // gate_up: K = h, the 2f gate and up rows of each expert as separate rows; down: K = f,
+    // rows h per expert, activation row of a position = SiLU(gate) * up of its gate_up
+    // output (hidden rows are contiguous per expert).  Persistent grids of resident
+    // blocks walk the (active expert, row tile) units.
+    for (int pass = 0; pass < 2; ++pass) {
+        const bool gate_up = pass == 0;
+        const int K = (int)(gate_up ? h : f);
+        const int rows_out = (int)(gate_up ? 2 * f : h);
+        const int P = K / 64;
         const int log2S = slots_log2(P);
         const int G = 64 >> log2S;
-        const int groups = ((int)f + G - 1) / G;
+        const int groups = (rows_out + G - 1) / G;
         const int tiles = (groups + kMoeWaves * kMoeGroupsPerWave - 1) / (kMoeWaves * kMoeGroupsPerWave);
         const int rows = staged_rows(P);
         const size_t lds = (size_t)rows * P * 256;
-        const size_t expert_bytes = (size_t)(2 * f) * (size_t)(h / 32) * 34;
-        hipLaunchKernelGGL((moe_expert_kernel<2, true>), dim3((unsigned)n_exp, (unsigned)tiles), dim3(kMoeThreads),
-                           lds, stream, wgu, expert_bytes, (int)f, P, log2S, x, (int)ldx, offsets, sorted, k, hidden,
-                           (int)f, rows);
+        const size_t expert_bytes = (size_t)rows_out * (size_t)(K / 32) * 34;
+        const int64_t max_units = n_exp * (int64_t)tiles;
+        const int per_cu = gate_up ? moe_blocks_per_cu<true>(lds) : moe_blocks_per_cu<false>(lds);
+        const int64_t slots = (int64_t)dev.cu_count * per_cu;
+        const unsigned grid = (unsigned)(max_units < slots ? max_units : slots);
+        if (gate_up)
+            hipLaunchKernelGGL((moe_expert_kernel<true>), dim3(grid), dim3(kMoeThreads), lds, stream, wgu, expert_bytes,
+                               rows_out, P, log2S, x, (int)ldx, offsets, sorted, active, (int)n_exp, k, hidden,
+                               (int)(2 * f), rows, tiles);
+        else
+            hipLaunchKernelGGL((moe_expert_kernel<false>), dim3(grid), dim3(kMoeThreads), lds, stream, wdn,
+                               expert_bytes, rows_out, P, log2S, hidden, (int)(2 * f), offsets, sorted, active,
+                               (int)n_exp, k, outp, (int)h, rows, tiles);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    // down: K = f, rows h per expert, activation rows = hidden (contiguous per expert)
-    {
-        const int P = (int)(f / 64);
-        const int log2S = slots_log2(P);
-        const int G = 64 >> log2S;
-        const int groups = ((int)h + G - 1) / G;
-        const int tiles = (groups + kMoeWaves * kMoeGroupsPerWave - 1) / (kMoeWaves * kMoeGroupsPerWave);
-        const int rows = staged_rows(P);
-        const size_t lds = (size_t)rows * P * 256;
-        const size_t expert_bytes = (size_t)h * (size_t)(f / 32) * 34;
-        hipLaunchKernelGGL((moe_expert_kernel<1, false>), dim3((unsigned)n_exp, (unsigned)tiles), dim3(kMoeThreads),
-                           lds, stream, wdn, expert_bytes, (int)h, P, log2S, hidden, (int)f, offsets, sorted, k, outp,
-                           (int)h, rows);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)m), dim3(256), 0, stream, outp, (int)h, inv, wts, k, y,
-                       (int)ldy);
+    hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)m, (unsigned)((h + 255) / 256)), dim3(256), 0, stream, outp,
+                       (int)h, inv, wts, k, y, (int)ldy);
     return hipGetLastError();
 }
 

@@ -82,7 +82,7 @@ inline q8_status check_route(const float* x, int64_t m, int64_t h, int64_t ldx, 
 
 // Workspace of the grouped MoE call: a route plan plus the hidden activations.
 struct MoeWorkspace {
-    size_t offsets_off, sorted_off, inv_off, hidden_off, out_off, total;
+    size_t offsets_off, sorted_off, inv_off, active_off, hidden_off, out_off, total;
 };
 
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -94,7 +94,8 @@ inline MoeWorkspace moe_workspace_layout(int64_t m, int32_t k, int64_t n_exp, in
     w.offsets_off = off; off = round_up(off + sizeof(int32_t) * size_t(n_exp + 1), 256);
     w.sorted_off = off;  off = round_up(off + sizeof(int32_t) * pairs, 256);
     w.inv_off = off;     off = round_up(off + sizeof(int32_t) * pairs, 256);
-    w.hidden_off = off;  off = round_up(off + sizeof(float) * pairs * size_t(f), 256);
+    w.active_off = off;  off = round_up(off + sizeof(int32_t) * size_t(n_exp + 1), 256);
+    w.hidden_off = off;  off = round_up(off + sizeof(float) * pairs * 2 * size_t(f), 256);  // gate and up rows
     w.out_off = off;     off = round_up(off + sizeof(float) * pairs * size_t(h), 256);
     w.total = off;
     return w;

@@ -4,14 +4,15 @@
 // routerTopK (normalize_selected = norm_topk_prob); the engine does that on the host,
 // here it stays on the device so the mixture can follow without a host round trip.
 //
-// One workgroup (4 waves) per token.  Logits: each wave takes experts e = wave, wave+4,
-// ...; a lane multiplies float4 slices k = 4*lane + 256*i and the wave sums its 64
-// partials with a fixed xor-butterfly (float32 throughout).  Softmax and selection run
-// on wave 0: the row maximum is subtracted before exp, and the k experts are picked one
-// by one as the largest remaining logit, ties to the lower expert index (selecting on
-// the logits avoids ties that rounding exp() could create; softmax is monotonic, so
-// the order is that of the probabilities).  The chosen probabilities are divided by
-// their sum, taken in selection order, when normalize is set.
+// One workgroup (16 waves) per token.  Logits: each wave takes experts e = wave,
+// wave+16, ..., four at a time so that many loads are in flight; a lane multiplies
+// float4 slices k = 4*lane + 256*i (i ascending) and the wave sums its 64 partials with
+// a fixed xor-butterfly (float32 throughout).  Softmax and selection run on wave 0: the
+// row maximum is subtracted before exp, and the k experts are picked one by one as the
+// largest remaining logit, ties to the lower expert index (selecting on the logits
+// avoids ties that rounding exp() could create; softmax is monotonic, so the order is
+// that of the probabilities).  The chosen probabilities are divided by their sum, taken
+// in selection order, when normalize is set.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -20,7 +21,9 @@
 
 namespace q8k {
 
-constexpr int kRouteThreads = 256;
+constexpr int kRouteThreads = 1024;
+constexpr int kRouteWaves = kRouteThreads / 64;
+constexpr int kRouteBatch = 4;  // experts a wave multiplies together
 constexpr int kMaxExperts = 256;
 
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
@@ -37,19 +40,46 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float* 
     const int wave = threadIdx.x >> 6;
     const float* xr = x + (size_t)tok * ldx;
 
-    for (int e = wave; e < n_exp; e += kRouteThreads / 64) {
-        const float* we = wr + (size_t)e * h;
-        float acc = 0.0f;
-        for (int kk = 4 * lane; kk < h; kk += 256) {
-            const float4 a = *reinterpret_cast<const float4*>(xr + kk);
-            const float4 b = *reinterpret_cast<const float4*>(we + kk);
-            acc = __builtin_fmaf(a.x, b.x, acc);
-            acc = __builtin_fmaf(a.y, b.y, acc);
-            acc = __builtin_fmaf(a.z, b.z, acc);
-            acc = __builtin_fmaf(a.w, b.w, acc);
+    for (int e0 = wave; e0 < n_exp; e0 += kRouteWaves * kRouteBatch) {
+        // experts e0, e0 + 16, e0 + 32, e0 + 48 (past n_exp: expert e0 again, not stored)
+        const float* we[kRouteBatch];
+#pragma unroll
+        for (int b = 0; b < kRouteBatch; ++b) {
+            const int e = e0 + kRouteWaves * b;
+            we[b] = wr + (size_t)(e < n_exp ? e : e0) * h;
         }
-        for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-        if (lane == 0) logits[e] = acc;
+        float acc[kRouteBatch] = {0.0f, 0.0f, 0.0f, 0.0f};
+        // chunks of 1024 inputs (h is a multiple of 256; a partial chunk clamps its
+        // loads and skips the multiply): every load of a chunk is issued before its fmas
+        for (int k0 = 0; k0 < h; k0 += 1024) {
+            float4 a[4], v[kRouteBatch][4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int kk = k0 + 4 * lane + 256 * i;
+                const int kc = kk < h ? kk : 4 * lane;
+                a[i] = *reinterpret_cast<const float4*>(xr + kc);
+#pragma unroll
+                for (int b = 0; b < kRouteBatch; ++b) v[b][i] = *reinterpret_cast<const float4*>(we[b] + kc);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (k0 + 256 * i < h) {
+#pragma unroll
+                    for (int b = 0; b < kRouteBatch; ++b) {
+                        acc[b] = __builtin_fmaf(a[i].x, v[b][i].x, acc[b]);
+                        acc[b] = __builtin_fmaf(a[i].y, v[b][i].y, acc[b]);
+                        acc[b] = __builtin_fmaf(a[i].z, v[b][i].z, acc[b]);
+                        acc[b] = __builtin_fmaf(a[i].w, v[b][i].w, acc[b]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < kRouteBatch; ++b) {
+            for (int off = 32; off >= 1; off >>= 1) acc[b] += __shfl_xor(acc[b], off, 64);
+            const int e = e0 + kRouteWaves * b;
+            if (lane == 0 && e < n_exp) logits[e] = acc[b];
+        }
     }
     __syncthreads();
     if (wave != 0) return;
