@@ -244,6 +244,63 @@ def q8_linear_bf16_operands_ref(w_q8, n: int, k: int, x) -> np.ndarray:
     return bf16_round_ref(np.asarray(x, dtype=np.float32)) @ bf16_round_ref(w).T
 
 
+# ---------------------------------- integer q8 x q8 path (quantized activations)
+#
+# The DGX Spark README (Features; Architecture) names GEMV kernels that read Q8_0
+# directly through int8 dot products (dp4a), and the qwen3 runner README (the q8_0
+# KV cache example; the --cache-type flag) names an integer q8 x q8 dot path over
+# quantized blocks.  No page defines the activation code; the reading taken here
+# (parity unpinned against the pages themselves, pinned by hand values, properties
+# and exact identities): per block of 32 inputs, amax = max |x|; the scale is
+# dx = amax / 127 and the codes are q = round-half-even(x * (127 / amax)), both
+# quotients and the product rounded to float32, so that the integer codes are decided
+# in float32 exactly as on the device; an all-zero block has dx = 0, q = 0.
+
+
+def quantize_act_q8_ref(x):
+    """Per-32-input int8 codes and float32 scales of float32 activation rows.
+
+    Returns (q int8 [m][k], dx float32 [m][k/32]); |q| <= 127.
+    """
+    x32 = np.asarray(x, dtype=np.float32)
+    m, k = x32.shape
+    if k % QK8_0:
+        raise ValueError("k must be a multiple of 32")
+    blocks = x32.reshape(m, k // QK8_0, QK8_0)
+    amax = np.max(np.abs(blocks), axis=2)
+    nz = amax > 0
+    safe = np.where(nz, amax, np.float32(1)).astype(np.float32)
+    inv = np.where(nz, np.float32(127) / safe, np.float32(0)).astype(np.float32)
+    dx = np.where(nz, safe / np.float32(127), np.float32(0)).astype(np.float32)
+    prod = (blocks * inv[:, :, None]).astype(np.float32)
+    q = np.clip(np.rint(prod), -127, 127).astype(np.int8)
+    return q.reshape(m, k), dx
+
+
+def q8_linear_q8act_ref(w_q8, n: int, k: int, x) -> np.ndarray:
+    """y[m, n] = sum_b d_w[n, b] * dx[m, b] * (sum_i q_w[n, b, i] * q_x[m, b, i]).
+
+    The block dot products are exact integers (int64); the scaling and the sum over
+    blocks run in float64.
+    """
+    dw, qwf = parse_q8_0(w_q8, n, k)                      # [n][nb], [n][nb][32]
+    qw = qwf.astype(np.int64)                             # exact: the quants are integers
+    qx, dx = quantize_act_q8_ref(x)
+    m = qx.shape[0]
+    qx = qx.reshape(m, k // QK8_0, QK8_0).astype(np.int64)
+    out = np.empty((m, n), dtype=np.float64)
+    for mi in range(m):
+        isum = np.einsum("nbi,bi->nb", qw, qx[mi])       # exact integer block dots
+        out[mi] = (dw * dx[mi].astype(np.float64)[None, :] * isum).sum(axis=1)
+    return out
+
+
+def fused_gate_up_silu_q8act_ref(w_gate_up_q8, f: int, k: int, x) -> np.ndarray:
+    """SiLU(gate) * up with both products on quantized activations (gate rows [0, f))."""
+    y = q8_linear_q8act_ref(w_gate_up_q8, 2 * f, k, x)
+    return silu_ref(y[:, :f]) * y[:, f:]
+
+
 # ----------------------------------------------------------- error measurement
 
 

@@ -125,3 +125,26 @@ def load_swiglu_router_cases():
             else:
                 raise ValueError(line)
     return fused, route
+
+
+def load_act_quant_cases(path=None):
+    """Cases of tests/golden/q8_act_hand.txt: dicts with x (32 floats), q (32 ints), dx."""
+    path = path or os.path.join(GOLDEN, "q8_act_hand.txt")
+    cases, cur = [], None
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        head, *rest = line.split()
+        if head == "case":
+            cur = {"name": rest[0]}
+            cases.append(cur)
+        elif head == "x":
+            vals = [float(v) for v in rest]
+            cur["x"] = vals + [0.0] * (32 - len(vals))
+        elif head == "q":
+            vals = [int(v) for v in rest]
+            cur["q"] = vals + [0] * (32 - len(vals))
+        elif head == "dx":
+            cur["dx"] = float(rest[0])
+    return cases

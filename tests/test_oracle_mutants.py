@@ -30,6 +30,14 @@ MUTANTS = {
     "moe_wrong_expert": ("return raw[e * nb:(e + 1) * nb]", "return raw[(e ^ 1) * nb:((e ^ 1) + 1) * nb]"),
     "router_untransposed_logits": ("@ np.asarray(w_router, dtype=np.float64).T",
                                    "@ np.asarray(w_router, dtype=np.float64).T[::-1].T"),
+    "act_round_floor": ("q = np.clip(np.rint(prod), -127, 127)", "q = np.clip(np.floor(prod), -127, 127)"),
+    "act_round_half_away": ("q = np.clip(np.rint(prod), -127, 127)",
+                            "q = np.clip(np.trunc(prod + np.copysign(np.float32(0.5), prod)), -127, 127)"),
+    "act_scale_inverted": ("dx = np.where(nz, safe / np.float32(127), np.float32(0))",
+                           "dx = np.where(nz, np.float32(127) / safe, np.float32(0))"),
+    "act_amax_signed": ("amax = np.max(np.abs(blocks), axis=2)", "amax = np.max(blocks, axis=2)"),
+    "q8act_drops_dx": ("(dw * dx[mi].astype(np.float64)[None, :] * isum)", "(dw * isum)"),
+    "q8act_wrong_block": ('isum = np.einsum("nbi,bi->nb", qw, qx[mi])', 'isum = np.einsum("nbi,bi->nb", qw, qx[mi][::-1])'),
 }
 
 

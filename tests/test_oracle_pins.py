@@ -26,10 +26,11 @@ import scipy.special
 
 import oracle as O
 import workloads as wl
-from golden_io import half_bits_to_fraction, load_linear_cases, load_swiglu_router_cases
+from golden_io import half_bits_to_fraction, load_act_quant_cases, load_linear_cases, load_swiglu_router_cases
 
 LINEAR_CASES = load_linear_cases()
 FUSED_CASES, ROUTE_CASES = load_swiglu_router_cases()
+ACT_CASES = load_act_quant_cases()
 
 
 # ------------------------------------------------------------------ checks
@@ -267,10 +268,86 @@ def check_moe_bruteforce(o):
         np.testing.assert_allclose(y[mi], acc, rtol=1e-11, atol=1e-11)
 
 
+# ------------------------------------------- integer q8 x q8 path (quantized activations)
+
+
+def check_act_quant_hand(o):
+    """Hand-derived codes and scales (tests/golden/q8_act_hand.txt): ties to even,
+    the clamp at 127, powers-of-two scales, an all-zero block."""
+    x = np.array([c["x"] for c in ACT_CASES], dtype=np.float32)
+    q, dx = o.quantize_act_q8_ref(x)
+    for i, c in enumerate(ACT_CASES):
+        assert q[i].tolist() == c["q"], c["name"]
+        assert float(dx[i, 0]) == c["dx"], c["name"]
+
+
+def check_act_quant_props(o):
+    """Codes within [-127, 127], 127 reached in every non-zero block, |x - q*dx| <= dx/2
+    up to float32 rounding, zero blocks exact, and invariance under scaling by 2^j."""
+    x = wl.activations(40, 5, 512)
+    x[1, 64:96] = 0.0                       # one all-zero block
+    x[2, 0:32] *= 1e-30                     # a block of tiny values
+    q, dx = o.quantize_act_q8_ref(x)
+    qb = q.reshape(5, 16, 32).astype(np.int64)
+    xb = x.reshape(5, 16, 32).astype(np.float64)
+    assert np.abs(qb).max() <= 127
+    nz = np.abs(xb).max(axis=2) > 0
+    assert np.all(np.abs(qb).max(axis=2)[nz] == 127)
+    assert np.all(dx[~nz] == 0) and np.all(qb[~nz] == 0)
+    err = np.abs(xb - qb * dx.astype(np.float64)[:, :, None])
+    assert np.all(err <= 0.5 * dx.astype(np.float64)[:, :, None] * (1 + 1e-5) + 1e-45)
+    for j in (-3, 5):
+        q2, dx2 = o.quantize_act_q8_ref(x * np.float32(2.0 ** j))
+        assert np.array_equal(q2, q)
+        assert np.array_equal(dx2, (dx * np.float32(2.0 ** j)).astype(np.float32))
+
+
+def check_q8act_linear(o):
+    """The integer block-dot form equals dequantize-then-matmul of the quantized
+    activations; lossless activations (x = q0 * 2^-3 with 127 in every block) give
+    the plain linear; Fraction brute force on a tiny case."""
+    n, k, m = 6, 256, 3
+    wb, qw, dw = wl.q8_weight(41, n, k)
+    x = wl.activations(42, m, k)
+    y = o.q8_linear_q8act_ref(wb, n, k, x)
+    qx, dx = o.quantize_act_q8_ref(x)
+    xdq = (qx.reshape(m, k // 32, 32).astype(np.float64) * dx.astype(np.float64)[:, :, None]).reshape(m, k)
+    np.testing.assert_allclose(y, o.q8_linear_ref(wb, n, k, xdq), rtol=1e-12, atol=1e-12)
+    rng = np.random.default_rng(43)
+    q0 = rng.integers(-127, 128, size=(m, k // 32, 32))
+    q0[:, :, 7] = 127
+    xl = (q0 * 2.0 ** -3).reshape(m, k).astype(np.float32)
+    np.testing.assert_allclose(o.q8_linear_q8act_ref(wb, n, k, xl), o.q8_linear_ref(wb, n, k, xl),
+                               rtol=1e-12, atol=1e-12)
+    # brute force: n = 2, k = 64, m = 1, every product written out in rationals
+    wb2, qw2, dw2 = wl.q8_weight(44, 2, 64)
+    x2 = wl.activations(45, 1, 64)
+    y2 = o.q8_linear_q8act_ref(wb2, 2, 64, x2)
+    qx2, dx2 = o.quantize_act_q8_ref(x2)
+    for ni in range(2):
+        exact = Fraction(0)
+        for kk in range(64):
+            b = kk // 32
+            exact += (half_bits_to_fraction(int(dw2.view(np.uint16)[ni, b])) * int(qw2[ni, kk])
+                      * Fraction(float(dx2[0, b])) * int(qx2[0, kk]))
+        assert abs(y2[0, ni] - float(exact)) <= 1e-12 * max(1.0, abs(float(exact)))
+
+
+def check_q8act_fused(o):
+    """The fused q8act SwiGLU is SiLU of the gate half times the up half."""
+    f, k, m = 4, 256, 2
+    wb, _, _ = wl.q8_weight(46, 2 * f, k)
+    x = wl.activations(47, m, k)
+    h = o.fused_gate_up_silu_q8act_ref(wb, f, k, x)
+    y = o.q8_linear_q8act_ref(wb, 2 * f, k, x)
+    np.testing.assert_allclose(h, scipy.special.expit(y[:, :f]) * y[:, :f] * y[:, f:], rtol=1e-12, atol=1e-15)
+
+
 ALL_CHECKS = [
     check_hand_linear, check_hand_fused, check_hand_route, check_bruteforce_linear,
     check_dequant_exact, check_linearity, check_zero_scale, check_one_hot, check_silu,
     check_fused_split, check_route_invariants, check_moe, check_moe_bruteforce,
+    check_act_quant_hand, check_act_quant_props, check_q8act_linear, check_q8act_fused,
 ]
 
 
