@@ -6,10 +6,12 @@ library.
 """
 
 from .q8_oracle import (  # noqa: F401
+    ACT_ZERO_BELOW,
     QK8_0,
     Q8_0_BLOCK_BYTES,
     bf16_round_ref,
     dequantize_q8_0,
+    fused_gate_up_silu_codes_ref,
     fused_gate_up_silu_q8act_ref,
     fused_gate_up_silu_ref,
     moe_mixture_ref,
@@ -18,6 +20,7 @@ from .q8_oracle import (  # noqa: F401
     quantize_act_q8_ref,
     q8_0_row_bytes,
     q8_linear_bf16_operands_ref,
+    q8_linear_codes_ref,
     q8_linear_q8act_ref,
     q8_linear_ref,
     rel_err_row_max,

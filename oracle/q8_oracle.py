@@ -250,11 +250,14 @@ def q8_linear_bf16_operands_ref(w_q8, n: int, k: int, x) -> np.ndarray:
 # directly through int8 dot products (dp4a), and the qwen3 runner README (the q8_0
 # KV cache example; the --cache-type flag) names an integer q8 x q8 dot path over
 # quantized blocks.  No page defines the activation code; the reading taken here
-# (parity unpinned against the pages themselves, pinned by hand values, properties
-# and exact identities): per block of 32 inputs, amax = max |x|; the scale is
-# dx = amax / 127 and the codes are q = round-half-even(x * (127 / amax)), both
-# quotients and the product rounded to float32, so that the integer codes are decided
-# in float32 exactly as on the device; an all-zero block has dx = 0, q = 0.
+# (pinned by hand values, properties and exact identities, not by a page's numbers):
+# per block of 32 inputs, amax = max |x|; the scale is dx = amax / 127 and the codes
+# are q = round-half-even(x * (127 / amax)), both quotients and the product rounded
+# to float32, so that the integer codes are decided in float32 exactly as on the
+# device.  A block with amax below 2^-120 (all zeros included) gets dx = 0, q = 0:
+# there 127 / amax would leave the float32 range.  Inputs are finite.
+
+ACT_ZERO_BELOW = np.float32(2.0 ** -120)   # smaller block maxima are coded as zero
 
 
 def quantize_act_q8_ref(x):
@@ -268,7 +271,7 @@ def quantize_act_q8_ref(x):
         raise ValueError("k must be a multiple of 32")
     blocks = x32.reshape(m, k // QK8_0, QK8_0)
     amax = np.max(np.abs(blocks), axis=2)
-    nz = amax > 0
+    nz = amax >= ACT_ZERO_BELOW
     safe = np.where(nz, amax, np.float32(1)).astype(np.float32)
     inv = np.where(nz, np.float32(127) / safe, np.float32(0)).astype(np.float32)
     dx = np.where(nz, safe / np.float32(127), np.float32(0)).astype(np.float32)
@@ -277,28 +280,42 @@ def quantize_act_q8_ref(x):
     return q.reshape(m, k), dx
 
 
-def q8_linear_q8act_ref(w_q8, n: int, k: int, x) -> np.ndarray:
+def q8_linear_codes_ref(w_q8, n: int, k: int, qx, dx) -> np.ndarray:
     """y[m, n] = sum_b d_w[n, b] * dx[m, b] * (sum_i q_w[n, b, i] * q_x[m, b, i]).
 
-    The block dot products are exact integers (int64); the scaling and the sum over
-    blocks run in float64.
+    qx: int8 codes [m][k] (any int8 value), dx: float32 scales [m][k/32].  The block
+    dot products are exact integers (int64); the scaling and the sum over blocks run in
+    float64.
     """
     dw, qwf = parse_q8_0(w_q8, n, k)                      # [n][nb], [n][nb][32]
     qw = qwf.astype(np.int64)                             # exact: the quants are integers
-    qx, dx = quantize_act_q8_ref(x)
+    qx = np.asarray(qx, dtype=np.int64)
+    dx = np.asarray(dx, dtype=np.float32).astype(np.float64)
     m = qx.shape[0]
-    qx = qx.reshape(m, k // QK8_0, QK8_0).astype(np.int64)
+    qx = qx.reshape(m, k // QK8_0, QK8_0)
     out = np.empty((m, n), dtype=np.float64)
     for mi in range(m):
         isum = np.einsum("nbi,bi->nb", qw, qx[mi])       # exact integer block dots
-        out[mi] = (dw * dx[mi].astype(np.float64)[None, :] * isum).sum(axis=1)
+        out[mi] = (dw * dx[mi][None, :] * isum).sum(axis=1)
     return out
 
 
-def fused_gate_up_silu_q8act_ref(w_gate_up_q8, f: int, k: int, x) -> np.ndarray:
-    """SiLU(gate) * up with both products on quantized activations (gate rows [0, f))."""
-    y = q8_linear_q8act_ref(w_gate_up_q8, 2 * f, k, x)
+def q8_linear_q8act_ref(w_q8, n: int, k: int, x) -> np.ndarray:
+    """The linear on activations quantized by quantize_act_q8_ref."""
+    qx, dx = quantize_act_q8_ref(x)
+    return q8_linear_codes_ref(w_q8, n, k, qx, dx)
+
+
+def fused_gate_up_silu_codes_ref(w_gate_up_q8, f: int, k: int, qx, dx) -> np.ndarray:
+    """SiLU(gate) * up with both products on the given codes (gate rows [0, f))."""
+    y = q8_linear_codes_ref(w_gate_up_q8, 2 * f, k, qx, dx)
     return silu_ref(y[:, :f]) * y[:, f:]
+
+
+def fused_gate_up_silu_q8act_ref(w_gate_up_q8, f: int, k: int, x) -> np.ndarray:
+    """SiLU(gate) * up on activations quantized by quantize_act_q8_ref."""
+    qx, dx = quantize_act_q8_ref(x)
+    return fused_gate_up_silu_codes_ref(w_gate_up_q8, f, k, qx, dx)
 
 
 # ----------------------------------------------------------- error measurement

@@ -36,7 +36,8 @@ MUTANTS = {
     "act_scale_inverted": ("dx = np.where(nz, safe / np.float32(127), np.float32(0))",
                            "dx = np.where(nz, np.float32(127) / safe, np.float32(0))"),
     "act_amax_signed": ("amax = np.max(np.abs(blocks), axis=2)", "amax = np.max(blocks, axis=2)"),
-    "q8act_drops_dx": ("(dw * dx[mi].astype(np.float64)[None, :] * isum)", "(dw * isum)"),
+    "q8act_drops_dx": ("(dw * dx[mi][None, :] * isum)", "(dw * isum)"),
+    "act_zero_only_exact_zero": ("nz = amax >= ACT_ZERO_BELOW", "nz = amax > 0"),
     "q8act_wrong_block": ('isum = np.einsum("nbi,bi->nb", qw, qx[mi])', 'isum = np.einsum("nbi,bi->nb", qw, qx[mi][::-1])'),
 }
 

@@ -319,6 +319,12 @@ def check_q8act_linear(o):
     xl = (q0 * 2.0 ** -3).reshape(m, k).astype(np.float32)
     np.testing.assert_allclose(o.q8_linear_q8act_ref(wb, n, k, xl), o.q8_linear_ref(wb, n, k, xl),
                                rtol=1e-12, atol=1e-12)
+    # arbitrary codes (the full int8 range, -128 included) against dequantize-then-matmul
+    qa = rng.integers(-128, 128, size=(m, k)).astype(np.int8)
+    da = (rng.random((m, k // 32)) * 0.01).astype(np.float32)
+    xa = (qa.reshape(m, k // 32, 32).astype(np.float64) * da.astype(np.float64)[:, :, None]).reshape(m, k)
+    np.testing.assert_allclose(o.q8_linear_codes_ref(wb, n, k, qa, da), o.q8_linear_ref(wb, n, k, xa),
+                               rtol=1e-12, atol=1e-12)
     # brute force: n = 2, k = 64, m = 1, every product written out in rationals
     wb2, qw2, dw2 = wl.q8_weight(44, 2, 64)
     x2 = wl.activations(45, 1, 64)
