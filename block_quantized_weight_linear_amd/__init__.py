@@ -13,6 +13,9 @@ from ._binding import (  # noqa: F401
     moe_route_topk,
     q8_linear,
     q8_linear_fused_gate_up_silu,
+    q8_linear_fused_gate_up_silu_q8act,
+    q8_linear_q8act,
     q8_moe_grouped_linear,
     q8_moe_workspace_bytes,
+    q8_quantize_act,
 )

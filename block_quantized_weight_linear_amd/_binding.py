@@ -39,6 +39,12 @@ lib.q8_linear.restype = ctypes.c_int
 lib.q8_linear.argtypes = [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp]
 lib.q8_linear_fused_gate_up_silu.restype = ctypes.c_int
 lib.q8_linear_fused_gate_up_silu.argtypes = [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp]
+lib.q8_quantize_act.restype = ctypes.c_int
+lib.q8_quantize_act.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp]
+lib.q8_linear_q8act.restype = ctypes.c_int
+lib.q8_linear_q8act.argtypes = [_vp, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _vp]
+lib.q8_linear_fused_gate_up_silu_q8act.restype = ctypes.c_int
+lib.q8_linear_fused_gate_up_silu_q8act.argtypes = [_vp, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _vp]
 lib.moe_route_topk.restype = ctypes.c_int
 lib.moe_route_topk.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _i32, _i32, _vp, _vp, _vp]
 lib.q8_moe_workspace_bytes.restype = _sz
@@ -117,6 +123,63 @@ def q8_linear_fused_gate_up_silu(w, f: int, k: int, x, out=None):
     _dev(out, torch.float32, "out")
     check(lib.q8_linear_fused_gate_up_silu(w.data_ptr(), f, k, x.data_ptr(), m, _ld(x, k), out.data_ptr(),
                                            _ld(out, f), _stream(x)))
+    return out
+
+
+def q8_quantize_act(x, xq=None, xd=None):
+    """Int8 codes [m][k] and float32 scales [m][k/32] of float32 activation rows x [m][k]."""
+    torch = _torch()
+    _dev(x, torch.float32, "x")
+    if x.dim() != 2 or (x.numel() and x.stride(1) != 1):
+        raise ValueError("x must be [m][k] with contiguous rows")
+    m, k = x.shape
+    if xq is None:
+        xq = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    if xd is None:
+        xd = torch.empty((m, k // 32), dtype=torch.float32, device=x.device)
+    _dev(xq, torch.int8, "xq")
+    _dev(xd, torch.float32, "xd")
+    if tuple(xq.shape) != (m, k) or tuple(xd.shape) != (m, k // 32) or not (xq.is_contiguous() and xd.is_contiguous()):
+        raise ValueError("xq must be a contiguous [m][k] tensor and xd a contiguous [m][k/32] tensor")
+    check(lib.q8_quantize_act(x.data_ptr(), m, k, _ld(x, k), xq.data_ptr(), xd.data_ptr(), _stream(x)))
+    return xq, xd
+
+
+def _codes(xq, xd, k):
+    torch = _torch()
+    _dev(xq, torch.int8, "xq")
+    _dev(xd, torch.float32, "xd")
+    if xq.dim() != 2 or xq.shape[1] != k or not xq.is_contiguous():
+        raise ValueError(f"xq must be a contiguous [m][{k}] tensor")
+    m = xq.shape[0]
+    if tuple(xd.shape) != (m, k // 32) or not xd.is_contiguous():
+        raise ValueError(f"xd must be a contiguous [m][{k // 32}] tensor")
+    return m
+
+
+def q8_linear_q8act(w, n: int, k: int, xq, xd, out=None):
+    """y = the Q8_0 weight W [n][k] against int8 activation codes xq [m][k] with scales xd."""
+    torch = _torch()
+    _dev(w, torch.uint8, "w")
+    m = _codes(xq, xd, k)
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=xq.device)
+    _dev(out, torch.float32, "out")
+    check(lib.q8_linear_q8act(w.data_ptr(), n, k, xq.data_ptr(), xd.data_ptr(), m, out.data_ptr(), _ld(out, n),
+                              _stream(xq)))
+    return out
+
+
+def q8_linear_fused_gate_up_silu_q8act(w, f: int, k: int, xq, xd, out=None):
+    """h = SiLU(gate) * up from a fused Q8_0 gate_up matrix [2f][k] on int8 activation codes."""
+    torch = _torch()
+    _dev(w, torch.uint8, "w")
+    m = _codes(xq, xd, k)
+    if out is None:
+        out = torch.empty((m, f), dtype=torch.float32, device=xq.device)
+    _dev(out, torch.float32, "out")
+    check(lib.q8_linear_fused_gate_up_silu_q8act(w.data_ptr(), f, k, xq.data_ptr(), xd.data_ptr(), m,
+                                                 out.data_ptr(), _ld(out, f), _stream(xq)))
     return out
 
 

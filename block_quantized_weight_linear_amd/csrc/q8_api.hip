@@ -107,6 +107,51 @@ q8_status q8_linear_fused_gate_up_silu(const void* w_gate_up_q8, int64_t f, int6
     return linear_common("q8_linear_fused_gate_up_silu", w_gate_up_q8, f, k, true, x, m, ldx, h, ldh, stream);
 }
 
+q8_status q8_quantize_act(const float* x, int64_t m, int64_t k, int64_t ldx, int8_t* xq, float* xd, void* stream) {
+    g_err[0] = 0;
+    char msg[256];
+    q8_status s = q8v::check_quantize_act(x, m, k, ldx, xq, xd, msg, sizeof msg);
+    if (s != Q8_OK) {
+        set_err("q8_quantize_act: %s", msg);
+        return s;
+    }
+    if (m == 0) return Q8_OK;
+    hipError_t e = q8k::launch_quantize_act(x, m, k, ldx, xq, xd, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_fail("q8_quantize_act", e);
+    return Q8_OK;
+}
+
+static q8_status linear_q8act_common(const char* name, const void* w, int64_t n_out, int64_t k, bool silu,
+                                     const int8_t* xq, const float* xd, int64_t m, float* y, int64_t ldy,
+                                     void* stream) {
+    g_err[0] = 0;
+    char msg[256];
+    q8_status s = q8v::check_linear_q8act(w, n_out, k, xq, xd, m, y, ldy, msg, sizeof msg);
+    if (s != Q8_OK) {
+        set_err("%s: %s", name, msg);
+        return s;
+    }
+    if (m == 0 || n_out == 0) return Q8_OK;
+    q8k::DeviceInfo dev;
+    hipError_t e = q8k::current_device_info(&dev);
+    if (e != hipSuccess) return device_fail(name, e);
+    e = q8k::launch_gemv_q8act(dev, static_cast<const uint8_t*>(w), n_out, k, silu, xq, xd, m, y, ldy,
+                               static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_fail(name, e);
+    return Q8_OK;
+}
+
+q8_status q8_linear_q8act(const void* w_q8, int64_t n, int64_t k, const int8_t* xq, const float* xd, int64_t m,
+                          float* y, int64_t ldy, void* stream) {
+    return linear_q8act_common("q8_linear_q8act", w_q8, n, k, false, xq, xd, m, y, ldy, stream);
+}
+
+q8_status q8_linear_fused_gate_up_silu_q8act(const void* w_gate_up_q8, int64_t f, int64_t k, const int8_t* xq,
+                                             const float* xd, int64_t m, float* h, int64_t ldh, void* stream) {
+    return linear_q8act_common("q8_linear_fused_gate_up_silu_q8act", w_gate_up_q8, f, k, true, xq, xd, m, h, ldh,
+                               stream);
+}
+
 q8_status moe_route_topk(const float* x, int64_t m, int64_t h, int64_t ldx, const float* w_router, int64_t n_exp,
                          int32_t k, int32_t normalize, int32_t* topk_idx, float* topk_w, void* stream) {
     g_err[0] = 0;

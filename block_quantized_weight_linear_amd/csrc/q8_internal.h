@@ -27,6 +27,15 @@ hipError_t launch_gemv_q8(const DeviceInfo& dev, const uint8_t* w, int64_t n_out
 hipError_t launch_gemm_q8_mfma(const DeviceInfo& dev, const uint8_t* w, int64_t n_out, int64_t k, bool silu_pairs,
                                const float* x, int64_t m, int64_t ldx, float* y, int64_t ldy, hipStream_t stream);
 
+// Int8 activation codes and scales of float32 rows: xq [m][k], xd [m][k/32] (contiguous).
+hipError_t launch_quantize_act(const float* x, int64_t m, int64_t k, int64_t ldx, int8_t* xq, float* xd,
+                               hipStream_t stream);
+
+// y[m][n] from int8 activation codes xq [m][k] and scales xd [m][k/32] (contiguous rows),
+// 16-row launches; silu_pairs as for launch_gemv_q8.
+hipError_t launch_gemv_q8act(const DeviceInfo& dev, const uint8_t* w, int64_t n_out, int64_t k, bool silu_pairs,
+                             const int8_t* xq, const float* xd, int64_t m, float* y, int64_t ldy, hipStream_t stream);
+
 // Softmax top-k router.
 hipError_t launch_route_topk(const DeviceInfo& dev, const float* x, int64_t m, int64_t h, int64_t ldx,
                              const float* w_router, int64_t n_exp, int k, bool normalize, int32_t* idx, float* wts,

@@ -64,6 +64,39 @@ inline q8_status check_linear(const void* w, int64_t n_out, int64_t k, const flo
     return Q8_OK;
 }
 
+// The integer q8 x q8 linears: codes xq [m][k] and scales xd [m][k/32], contiguous.
+inline q8_status check_linear_q8act(const void* w, int64_t n_out, int64_t k, const void* xq, const void* xd,
+                                    int64_t m, const float* y, int64_t ldy, char* msg, size_t cap) {
+    q8_status s;
+    if ((s = check_dim("n", n_out, msg, cap)) != Q8_OK) return s;
+    if ((s = check_dim("m", m, msg, cap)) != Q8_OK) return s;
+    if ((s = check_k("k", k, msg, cap)) != Q8_OK) return s;
+    if (ldy < n_out) return fail(msg, cap, Q8_ERR_SHAPE, "ldy=%lld < n=%lld", ldy, n_out);
+    if (ldy > kMaxDim) return fail(msg, cap, Q8_ERR_SHAPE, "leading dimension above 2^30");
+    if (m * k > (int64_t(1) << 40)) return fail(msg, cap, Q8_ERR_SHAPE, "m*k=%lld above 2^40", m * k);
+    if (m == 0 || n_out == 0) return Q8_OK;
+    if (!w || !xq || !xd || !y) return fail(msg, cap, Q8_ERR_NULL, "null pointer (w, xq, xd or y)");
+    if (!aligned(w, 16)) return fail(msg, cap, Q8_ERR_ALIGN, "weight pointer not 16-byte aligned");
+    if (!aligned(xq, 16) || !aligned(xd, 16)) return fail(msg, cap, Q8_ERR_ALIGN, "xq or xd not 16-byte aligned");
+    if (!aligned(y, 4)) return fail(msg, cap, Q8_ERR_ALIGN, "output pointer not 4-byte aligned");
+    return Q8_OK;
+}
+
+inline q8_status check_quantize_act(const float* x, int64_t m, int64_t k, int64_t ldx, const void* xq,
+                                    const void* xd, char* msg, size_t cap) {
+    q8_status s;
+    if ((s = check_dim("m", m, msg, cap)) != Q8_OK) return s;
+    if ((s = check_k("k", k, msg, cap)) != Q8_OK) return s;
+    if (ldx < k || ldx > kMaxDim) return fail(msg, cap, Q8_ERR_SHAPE, "ldx=%lld < k=%lld", ldx, k);
+    if (m * k > (int64_t(1) << 40)) return fail(msg, cap, Q8_ERR_SHAPE, "m*k=%lld above 2^40", m * k);
+    if (m == 0) return Q8_OK;
+    if (!x || !xq || !xd) return fail(msg, cap, Q8_ERR_NULL, "null pointer (x, xq or xd)");
+    if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(xd, 16))
+        return fail(msg, cap, Q8_ERR_ALIGN, "x, xq or xd not 16-byte aligned");
+    if (ldx % 4 != 0) return fail(msg, cap, Q8_ERR_ALIGN, "ldx=%lld not a multiple of 4", ldx);
+    return Q8_OK;
+}
+
 inline q8_status check_route(const float* x, int64_t m, int64_t h, int64_t ldx, const float* w_router, int64_t n_exp,
                              int32_t k, const int32_t* idx, const float* wts, char* msg, size_t cap) {
     q8_status s;

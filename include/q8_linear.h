@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define Q8_ABI_VERSION 1
+#define Q8_ABI_VERSION 2
 
 typedef enum q8_status {
     Q8_OK = 0,
@@ -99,6 +99,46 @@ q8_status q8_linear(const void* w_q8, int64_t n, int64_t k,
 q8_status q8_linear_fused_gate_up_silu(const void* w_gate_up_q8, int64_t f, int64_t k,
                                        const float* x, int64_t m, int64_t ldx,
                                        float* h, int64_t ldh, void* stream);
+
+/*
+ * Integer q8 x q8 path.  The DGX Spark README (Features; Architecture) names GEMV kernels
+ * that read Q8_0 directly through int8 dot products, and the qwen3 runner README (q8_0 KV
+ * cache; --cache-type) names an integer q8 x q8 dot path over quantized blocks.  No page
+ * defines the activation code; the one used here:
+ *   per block of 32 inputs, amax = max |x|;  dx = amax / 127;
+ *   q = round-half-even(x * (127 / amax)) clamped to [-127, 127],
+ *   each quotient and the product rounded to float32 (IEEE, subnormals kept);
+ *   a block with amax < 2^-120 (an all-zero block among them) gets dx = 0 and q = 0.
+ * Inputs must be finite (a NaN or infinity gives unspecified codes, never a fault).
+ *
+ * q8_quantize_act: codes and scales of float32 activation rows.
+ *   x  : float32 [m][ldx], k > 0 a multiple of 256, ldx >= k (multiple of 4)
+ *   xq : int8 [m][k] out, contiguous (row stride k bytes)
+ *   xd : float32 [m][k/32] out, contiguous (row stride k/32)
+ * x, xq and xd 16-byte aligned.  The result is bit-exact (a pure function of x).
+ */
+q8_status q8_quantize_act(const float* x, int64_t m, int64_t k, int64_t ldx,
+                          int8_t* xq, float* xd, void* stream);
+
+/*
+ * y[t][n] = sum over blocks b of (d_w[n][b] * xd[t][b]) * sum_i q_w[n][b][i] * xq[t][b][i]
+ * -- the packed-weight linear on int8 activation codes (any int8 value is accepted and
+ * multiplied exactly; q8_quantize_act produces [-127, 127]).
+ *   w_q8 : Q8_0 [n][k]     xq : int8 [m][k] contiguous     xd : float32 [m][k/32] contiguous
+ *   y : float32 [m][ldy], ldy >= n
+ * xq and xd 16-byte aligned; other rules as for q8_linear.  Block dot products are exact
+ * 32-bit integers; per output, acc = fma(d_w * dx, float(isum), acc) over the blocks in a
+ * fixed order that depends only on k, so every row is bit-identical whatever m is.
+ */
+q8_status q8_linear_q8act(const void* w_q8, int64_t n, int64_t k,
+                          const int8_t* xq, const float* xd, int64_t m,
+                          float* y, int64_t ldy, void* stream);
+
+/* SiLU(gate) * up from one fused gate_up matrix [2f][k] on int8 activation codes (the
+ * fused SwiGLU of q8_linear_fused_gate_up_silu with the arithmetic of q8_linear_q8act). */
+q8_status q8_linear_fused_gate_up_silu_q8act(const void* w_gate_up_q8, int64_t f, int64_t k,
+                                             const int8_t* xq, const float* xd, int64_t m,
+                                             float* h, int64_t ldh, void* stream);
 
 /*
  * Softmax top-k routing (section 14.2: routerTopK with normalize_selected =

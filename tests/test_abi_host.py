@@ -32,14 +32,15 @@ def declared_functions():
 def test_header_declares_the_four_calls():
     names = declared_functions()
     for n in ("q8_linear", "q8_linear_fused_gate_up_silu", "moe_route_topk", "q8_moe_grouped_linear",
-              "q8_moe_workspace_bytes", "q8_status_string", "q8_last_error", "q8_abi_version"):
+              "q8_moe_workspace_bytes", "q8_status_string", "q8_last_error", "q8_abi_version",
+              "q8_quantize_act", "q8_linear_q8act", "q8_linear_fused_gate_up_silu_q8act"):
         assert n in names, names
 
 
 def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert q8.abi_version() == 1
+    assert q8.abi_version() == 2
 
 
 def test_status_strings():
@@ -71,6 +72,46 @@ def test_linear_argument_errors(fused):
     assert _lin(y=FAKE + 2, fused=fused) == ERR_ALIGN
     msg = lib.q8_last_error().decode()
     assert "aligned" in msg
+
+
+def _lin8(w=FAKE, n=64, k=256, xq=FAKE, xd=FAKE, m=1, y=FAKE, ldy=64, fused=False):
+    fn = lib.q8_linear_fused_gate_up_silu_q8act if fused else lib.q8_linear_q8act
+    return fn(w, n, k, xq, xd, m, y, ldy, None)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_q8act_linear_argument_errors(fused):
+    assert _lin8(fused=fused, k=0) == ERR_SHAPE
+    assert _lin8(fused=fused, k=320) == ERR_SHAPE
+    assert _lin8(fused=fused, n=-1) == ERR_SHAPE
+    assert _lin8(fused=fused, m=-1) == ERR_SHAPE
+    assert _lin8(fused=fused, ldy=63) == ERR_SHAPE
+    assert _lin8(fused=fused, xq=None) == ERR_NULL
+    assert _lin8(fused=fused, xd=None) == ERR_NULL
+    assert _lin8(fused=fused, w=None) == ERR_NULL
+    assert _lin8(fused=fused, xq=FAKE + 8) == ERR_ALIGN
+    assert _lin8(fused=fused, xd=FAKE + 4) == ERR_ALIGN
+    assert _lin8(fused=fused, w=FAKE + 4) == ERR_ALIGN
+    assert _lin8(fused=fused, y=FAKE + 1) == ERR_ALIGN
+    assert _lin8(fused=fused, m=0, w=None, xq=None, xd=None, y=None) == OK
+    assert _lin8(fused=fused, n=0, ldy=0, w=None, xq=None, xd=None, y=None) == OK
+
+
+def test_quantize_act_argument_errors():
+    def call(x=FAKE, m=2, k=256, ldx=256, xq=FAKE, xd=FAKE):
+        return lib.q8_quantize_act(x, m, k, ldx, xq, xd, None)
+
+    assert call(k=96) == ERR_SHAPE
+    assert call(m=-1) == ERR_SHAPE
+    assert call(ldx=255) == ERR_SHAPE
+    assert call(x=None) == ERR_NULL
+    assert call(xq=None) == ERR_NULL
+    assert call(xd=None) == ERR_NULL
+    assert call(x=FAKE + 4) == ERR_ALIGN
+    assert call(xq=FAKE + 4) == ERR_ALIGN
+    assert call(ldx=258) == ERR_ALIGN
+    assert call(m=0, x=None, xq=None, xd=None) == OK
+    assert "q8_quantize_act" in lib.q8_last_error().decode() or lib.q8_last_error() == b""
 
 
 def test_zero_sizes_enqueue_nothing():
