@@ -88,6 +88,26 @@ class Stack:
             q8.q8_linear_fused_gate_up_silu(wg, gu.n // 2, gu.k, x, out=bufs["h"])
             q8.q8_linear(wd, dn.n, dn.k, bufs["h"], out=bufs["y"])
 
+    def run_q8act(self, q8, x, bufs, m):
+        """The same step on the integer q8 x q8 path: each linear's input is quantized to
+        int8 codes per 32-block on the device (QKV's and gate_up's separately, as their
+        inputs differ in a real block), then multiplied with v_dot4 block dot products."""
+        qkv, gu, dn = self.spec.linears
+        for l in range(self.layers):
+            wq, wg, wd = self.w[l]
+            q8.q8_quantize_act(x, bufs["xq"], bufs["xd"])
+            q8.q8_linear_q8act(wq, qkv.n, qkv.k, bufs["xq"], bufs["xd"], out=bufs["qkv"])
+            q8.q8_quantize_act(x, bufs["xq"], bufs["xd"])
+            q8.q8_linear_fused_gate_up_silu_q8act(wg, gu.n // 2, gu.k, bufs["xq"], bufs["xd"], out=bufs["h"])
+            q8.q8_quantize_act(bufs["h"], bufs["hq"], bufs["hd"])
+            q8.q8_linear_q8act(wd, dn.n, dn.k, bufs["hq"], bufs["hd"], out=bufs["y"])
+
+    def run_gate_up_q8act(self, q8, bufs):
+        gu = self.spec.linears[1]
+        for l in range(self.layers):
+            q8.q8_linear_fused_gate_up_silu_q8act(self.w[l][1], gu.n // 2, gu.k, bufs["xq"], bufs["xd"],
+                                                  out=bufs["h"])
+
     def run_gate_up(self, q8, x, bufs):
         """The fused gate_up of every layer only (the dominant kernel)."""
         gu = self.spec.linears[1]
@@ -184,6 +204,48 @@ def bench_block(args, torch, dev, q8, spec, m_values):
         out[m] = res
         log(f"M={m}: {res}")
     return stack, out, gate_up_bytes
+
+
+def bench_block_q8act(args, torch, dev, q8, stack, m_values):
+    """The block step on the integer q8 x q8 path (quantize + int8-dot linears), captured
+    as a HIP graph like the float32 step."""
+    import workloads as wl
+    qkv, gu, dn = stack.spec.linears
+    out = {}
+    bytes_step = stack.bytes_per_layer * stack.layers
+    stream = torch.cuda.Stream()
+    for m in m_values:
+        x = torch.from_numpy(wl.activations(7 + m, m, stack.spec.hidden)).to(dev)
+        f = gu.n // 2
+        bufs = {"qkv": torch.empty((m, qkv.n), device=dev), "h": torch.empty((m, f), device=dev),
+                "y": torch.empty((m, dn.n), device=dev),
+                "xq": torch.empty((m, qkv.k), dtype=torch.int8, device=dev),
+                "xd": torch.empty((m, qkv.k // 32), device=dev),
+                "hq": torch.empty((m, f), dtype=torch.int8, device=dev),
+                "hd": torch.empty((m, f // 32), device=dev)}
+        with torch.cuda.stream(stream):
+            stack.run_q8act(q8, x, bufs, m)
+            torch.cuda.synchronize()
+            eager_y = bufs["y"].clone()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                stack.run_q8act(q8, x, bufs, m)
+            graph.replay()
+            torch.cuda.synchronize()
+            if not torch.equal(bufs["y"], eager_y):
+                raise RuntimeError("graph replay differs from the eager q8act step")
+            ms = time_steps(torch, graph.replay, args.steps, args.warmup)
+        gu_ms = graph_launch_ms(torch, lambda: stack.run_gate_up_q8act(q8, bufs), stack.layers,
+                                replays=max(2, args.steps // 5))
+        res = {"path": "q8 x q8 (int8 activation codes per 32-block, v_dot4)",
+               "ms_per_step": round(ms, 5), "gbps": round(bytes_step / (ms * 1e-3) / 1e9, 2),
+               "tok_s": round(m * 1000.0 / ms, 2), "weight_bytes_per_step": bytes_step,
+               "hbm_frac": round(bytes_step / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+               "gate_up_avg_us": round(gu_ms * 1e3, 3),
+               "gate_up_gbps": round(gu.weight_bytes / (gu_ms * 1e-3) / 1e9, 2)}
+        out[m] = res
+        log(f"q8act M={m}: {res}")
+    return out
 
 
 def graph_launch_ms(torch, seq, launches, replays=5):
@@ -307,7 +369,7 @@ def main():
     ap.add_argument("--layers", type=int, default=0, help="override the layer count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the other workloads (0.6B, gate_up M=16/M=512, MoE layer)")
+                    help="skip the other workloads (q8 x q8 step, 0.6B, gate_up M=16/M=512, MoE layer)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -359,6 +421,8 @@ def main():
     if not args.no_extras and args.workload == "qwen3-8b-block-linears":
         extras = {}
         reps = max(20, args.steps)
+        for m, r in bench_block_q8act(args, torch, dev, q8, stack, m_values).items():
+            extras[f"qwen3-8b-block-linears-q8act-m{m}"] = r
         extras["qwen3-0.6b-qkv-m1"] = bench_linear(torch, dev, q8, "0.6b qkv m1", 4096, 1024, 1, False, reps * 4)
         _, r06, _ = bench_block(args, torch, dev, q8, wl.QWEN3_06B_BLOCK, (1,))
         extras["qwen3-0.6b-block-linears-m1"] = r06[1]
