@@ -41,15 +41,15 @@ def log(*a):
 
 def measured_traffic():
     """HBM bytes per launch of the M=1 fused gate_up kernel from the committed rocprofv3
-    FETCH_SIZE/WRITE_SIZE summary, or None once the kernel sources differ from the ones
-    the counters were taken with."""
+    FETCH_SIZE/WRITE_SIZE summary, or None once the kernel sources (gemv_q8.hip, gemv_core.h,
+    lds_dma.h, hashed in that order) differ from the ones the counters were taken with."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic_gemv_q8_qwen3_8b_shapes.md")
     src = os.path.join(ROOT, "block_quantized_weight_linear_amd", "csrc")
     try:
         text = open(path).read()
         h = hashlib.sha256()
-        for name in ("gemv_q8.hip", "gemv_core.h"):
+        for name in ("gemv_q8.hip", "gemv_core.h", "lds_dma.h"):
             with open(os.path.join(src, name), "rb") as f:
                 h.update(f.read())
         want = re.search(r"sources_sha256: ([0-9a-f]{64})", text).group(1)
@@ -359,6 +359,45 @@ def bench_moe(torch, dev, q8, layers, steps, warmup):
     return res
 
 
+PROFILE_LINEARS = {"qkv": (6144, 4096, False), "gate_up": (24576, 4096, True), "down": (4096, 12288, False)}
+
+
+def kernel_driver(which, m, q8act):
+    """Short launch sequence for rocprofv3 counter and trace runs: a plain 256 MiB
+    device-to-device copy (the calibration dispatch for FETCH_SIZE / WRITE_SIZE), then one
+    Qwen3-8B linear at m rows on 12 distinct resident weight copies (each launch streams
+    its weights from HBM)."""
+    import torch
+
+    import block_quantized_weight_linear_amd as q8
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    src = torch.ones(64 << 20, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    n, k, fused = PROFILE_LINEARS[which]
+    wb, _, _ = wl.q8_weight(1, n, k)
+    base = torch.from_numpy(wb).to(dev)
+    ws = [base] + [base.clone() for _ in range(11)]
+    x = torch.from_numpy(wl.activations(2, m, k)).to(dev)
+    nout = n // 2 if fused else n
+    if q8act:
+        xq, xd = q8.q8_quantize_act(x)
+    for w in ws:
+        if q8act:
+            fn = q8.q8_linear_fused_gate_up_silu_q8act if fused else q8.q8_linear_q8act
+            fn(w, nout, k, xq, xd)
+        else:
+            fn = q8.q8_linear_fused_gate_up_silu if fused else q8.q8_linear
+            fn(w, nout, k, x)
+    torch.cuda.synchronize()
+    log(f"kernel driver: {which} m={m} q8act={q8act} done")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -370,7 +409,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the other workloads (q8 x q8 step, 0.6B, gate_up M=16/M=512, MoE layer)")
+    ap.add_argument("--kernel-driver", nargs=2, metavar=("LINEAR", "M"),
+                    help="profiling driver only: a 256 MiB copy, then the Qwen3-8B LINEAR "
+                         "(qkv | gate_up | down) at M rows on 12 distinct weight copies")
+    ap.add_argument("--q8act", action="store_true", help="with --kernel-driver: the q8 x q8 path")
     args = ap.parse_args()
+    if args.kernel_driver:
+        kernel_driver(args.kernel_driver[0], int(args.kernel_driver[1]), args.q8act)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(the sharding plan is described in the design notes, not built)", file=sys.stderr)
