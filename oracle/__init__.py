@@ -25,6 +25,7 @@ from .q8_oracle import (  # noqa: F401
     q8_linear_ref,
     rel_err_row_max,
     rel_err_row_norm,
+    route_topk_p_ref,
     route_topk_ref,
     router_logits_ref,
     sigmoid_ref,

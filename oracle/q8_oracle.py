@@ -174,6 +174,41 @@ def route_topk_ref(x, w_router, k: int, normalize: bool = True):
     return idx, wts
 
 
+def route_topk_p_ref(x, w_router, k: int, normalize: bool = True, top_p: float = 1.0):
+    """Softmax top-k routing followed by adaptive expert top-p (section 14.2 Config:
+    moe_expert_top_p, 1.0 = full top-k; applyExpertTopP).
+
+    The pages give the knob and its neutral value only; the reading taken here (parity
+    pinned by hand values, the p = 1 identity and brute force, not by a page's numbers):
+    with the chosen probabilities p_0 >= p_1 >= ... >= p_{k-1} (the top-k of the softmax,
+    in selection order) and c_j = (p_0 + ... + p_j) / (p_0 + ... + p_{k-1}), slot 0 is
+    always kept and slot j >= 1 is kept while c_{j-1} < top_p; top_p >= 1 keeps all k.
+    Kept weights are p_j, divided by the kept sum when ``normalize``; a dropped slot gets
+    expert index -1 and weight 0.
+
+    Returns (idx int32 [M][k], w float64 [M][k]).
+    """
+    logits = router_logits_ref(x, w_router)
+    m_rows, n_exp = logits.shape
+    if not 1 <= k <= n_exp:
+        raise ValueError(f"k={k} must be in [1, {n_exp}]")
+    if not 0.0 < top_p <= 1.0:
+        raise ValueError("top_p must be in (0, 1]")
+    p = softmax_ref(logits)
+    idx = np.full((m_rows, k), -1, dtype=np.int32)
+    wts = np.zeros((m_rows, k), dtype=np.float64)
+    for m in range(m_rows):
+        sel = np.argsort(-p[m], kind="stable")[:k]
+        chosen = p[m, sel]
+        total = chosen.sum()
+        kept = 1
+        while kept < k and (top_p >= 1.0 or chosen[:kept].sum() / total < top_p):
+            kept += 1
+        idx[m, :kept] = sel[:kept]
+        wts[m, :kept] = chosen[:kept] / chosen[:kept].sum() if normalize else chosen[:kept]
+    return idx, wts
+
+
 # ---------------------------------------------------------------------------- MoE
 
 
@@ -191,7 +226,8 @@ def moe_mixture_ref(w_gate_up_exps, w_down_exps, n_exp: int, f: int, h: int,
     y[m] = sum_j topk_w[m, j] * W_down[e] . (SiLU(W_gate[e] x_m) * (W_up[e] x_m)),
     e = topk_idx[m, j], summed over slots j = 0 .. k-1 in order (section 14.4 keeps
     each token's summation order fixed).  Expert stacks are Q8_0 [E][2f][h] (gate_up)
-    and [E][h][f] (down).
+    and [E][h][f] (down).  An index of -1 marks a slot that expert top-p dropped: it
+    contributes nothing.
     """
     x64 = np.asarray(x, dtype=np.float64)
     idx = np.asarray(topk_idx)
@@ -201,6 +237,8 @@ def moe_mixture_ref(w_gate_up_exps, w_down_exps, n_exp: int, f: int, h: int,
     for m in range(m_rows):
         for j in range(k_used):
             e = int(idx[m, j])
+            if e == -1:
+                continue
             if not 0 <= e < n_exp:
                 raise ValueError(f"expert index {e} out of range [0, {n_exp})")
             hid = fused_gate_up_silu_ref(_expert_slice(w_gate_up_exps, e, 2 * f, h), f, h,

@@ -30,6 +30,10 @@ MUTANTS = {
     "moe_wrong_expert": ("return raw[e * nb:(e + 1) * nb]", "return raw[(e ^ 1) * nb:((e ^ 1) + 1) * nb]"),
     "router_untransposed_logits": ("@ np.asarray(w_router, dtype=np.float64).T",
                                    "@ np.asarray(w_router, dtype=np.float64).T[::-1].T"),
+    "top_p_cut_inclusive": ("chosen[:kept].sum() / total < top_p", "chosen[:kept].sum() / total <= top_p"),
+    "top_p_full_softmax_cumulative": ("chosen[:kept].sum() / total < top_p", "chosen[:kept].sum() < top_p"),
+    "top_p_normalize_by_topk_total": ("chosen[:kept] / chosen[:kept].sum() if normalize", "chosen[:kept] / total if normalize"),
+    "top_p_ignores_knob": ("kept = 1\n", "kept = k\n"),
     "act_round_floor": ("q = np.clip(np.rint(prod), -127, 127)", "q = np.clip(np.floor(prod), -127, 127)"),
     "act_round_half_away": ("q = np.clip(np.rint(prod), -127, 127)",
                             "q = np.clip(np.trunc(prod + np.copysign(np.float32(0.5), prod)), -127, 127)"),

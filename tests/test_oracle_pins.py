@@ -349,11 +349,86 @@ def check_q8act_fused(o):
     np.testing.assert_allclose(h, scipy.special.expit(y[:, :f]) * y[:, :f] * y[:, f:], rtol=1e-12, atol=1e-15)
 
 
+# ----------------------------------------------------- adaptive expert top-p routing
+
+
+def _logit_router(logits):
+    """x = logits, W_r = identity: the router's logits are exactly the given values."""
+    logits = np.asarray(logits, dtype=np.float64)
+    return logits, np.eye(logits.shape[1])
+
+
+def check_top_p_exact_boundaries(o):
+    """Equal logits give exact probabilities 1/E: the cut at c_{j-1} < top_p is checked
+    exactly at the boundaries, and the cumulative is over the chosen k, not all E."""
+    x, wr = _logit_router(np.zeros((1, 8)))
+    for top_p, kept in ((0.25, 1), (0.26, 2), (0.5, 2), (0.51, 3), (0.75, 3), (0.76, 4), (1.0, 4)):
+        idx, w = o.route_topk_p_ref(x, wr, 4, True, top_p)
+        assert idx[0].tolist() == [0, 1, 2, 3][:kept] + [-1] * (4 - kept), (top_p, idx)
+        np.testing.assert_allclose(w[0, :kept], 1.0 / kept, rtol=0, atol=1e-15)
+        assert np.all(w[0, kept:] == 0)
+    idx, w = o.route_topk_p_ref(x, wr, 4, False, 0.5)
+    np.testing.assert_allclose(w[0], [0.125, 0.125, 0, 0], rtol=0, atol=1e-15)
+
+
+def check_top_p_hand_and_identity(o):
+    """Hand case p = (1/2, 1/4, 1/8, 1/8); top_p = 1 is plain top-k routing."""
+    x, wr = _logit_router(np.log([[0.125, 0.5, 0.125, 0.25]]))
+    for top_p, kept, wexp in ((0.4, 1, [1.0]), (0.6, 2, [2 / 3, 1 / 3]), (0.8, 3, [4 / 7, 2 / 7, 1 / 7]),
+                              (0.9, 4, [0.5, 0.25, 0.125, 0.125])):
+        idx, w = o.route_topk_p_ref(x, wr, 4, True, top_p)
+        assert idx[0].tolist() == [1, 3, 0, 2][:kept] + [-1] * (4 - kept), (top_p, idx)
+        np.testing.assert_allclose(w[0, :kept], wexp, rtol=1e-12)
+    xr = wl.activations(71, 9, 256)
+    w_r = wl.router_weight(72, 16, 256, std=0.1)
+    for k in (1, 3, 8):
+        for norm in (True, False):
+            i1, w1 = o.route_topk_p_ref(xr, w_r, k, norm, 1.0)
+            i0, w0 = o.route_topk_ref(xr, w_r, k, norm)
+            assert np.array_equal(i1, i0)
+            np.testing.assert_allclose(w1, w0, rtol=1e-14)
+
+
+def check_top_p_properties(o):
+    """Kept slots are a prefix, their count is 1 + #{j < k-1 : c_j < top_p} and grows
+    with top_p; normalized kept weights sum to 1; the mixture of a top-p routing equals
+    the mixture over the kept slots only."""
+    xr = wl.activations(73, 12, 256)
+    w_r = wl.router_weight(74, 32, 256, std=0.15)
+    k = 6
+    p_all = o.softmax_ref(o.router_logits_ref(xr, w_r))
+    prev = None
+    for top_p in (0.05, 0.3, 0.5, 0.7, 0.9, 0.99):
+        idx, w = o.route_topk_p_ref(xr, w_r, k, True, top_p)
+        kept = (idx >= 0).sum(axis=1)
+        for m in range(12):
+            assert np.all(idx[m, :kept[m]] >= 0) and np.all(idx[m, kept[m]:] == -1)
+            chosen = np.sort(p_all[m])[::-1][:k]
+            c = np.cumsum(chosen) / chosen.sum()
+            assert kept[m] == 1 + int(np.sum(c[:k - 1] < top_p)), (m, top_p)
+            assert abs(w[m, :kept[m]].sum() - 1.0) < 1e-12
+        if prev is not None:
+            assert np.all(kept >= prev)
+        prev = kept
+    # mixture: dropped slots contribute nothing
+    e_n, hd, ff = 4, 256, 256
+    gu = np.concatenate([wl.q8_weight(80 + e, 2 * ff, hd)[0] for e in range(e_n)])
+    dn = np.concatenate([wl.q8_weight(90 + e, hd, ff)[0] for e in range(e_n)])
+    xm = wl.activations(75, 2, hd)
+    idx = np.array([[2, 0, -1], [1, -1, -1]], dtype=np.int32)
+    wts = np.array([[0.75, 0.25, 0.0], [1.0, 0.0, 0.0]])
+    y = o.moe_mixture_ref(gu, dn, e_n, ff, hd, xm, idx, wts)
+    y0 = o.moe_mixture_ref(gu, dn, e_n, ff, hd, xm[:1], idx[:1, :2], wts[:1, :2])
+    y1 = o.moe_mixture_ref(gu, dn, e_n, ff, hd, xm[1:], idx[1:, :1], wts[1:, :1])
+    np.testing.assert_allclose(y, np.concatenate([y0, y1]), rtol=1e-14)
+
+
 ALL_CHECKS = [
     check_hand_linear, check_hand_fused, check_hand_route, check_bruteforce_linear,
     check_dequant_exact, check_linearity, check_zero_scale, check_one_hot, check_silu,
     check_fused_split, check_route_invariants, check_moe, check_moe_bruteforce,
     check_act_quant_hand, check_act_quant_props, check_q8act_linear, check_q8act_fused,
+    check_top_p_exact_boundaries, check_top_p_hand_and_identity, check_top_p_properties,
 ]
 
 
