@@ -47,6 +47,8 @@ lib.q8_linear_fused_gate_up_silu_q8act.restype = ctypes.c_int
 lib.q8_linear_fused_gate_up_silu_q8act.argtypes = [_vp, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _vp]
 lib.moe_route_topk.restype = ctypes.c_int
 lib.moe_route_topk.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _i32, _i32, _vp, _vp, _vp]
+lib.moe_route_topk_top_p.restype = ctypes.c_int
+lib.moe_route_topk_top_p.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _i32, _i32, ctypes.c_float, _vp, _vp, _vp]
 lib.q8_moe_workspace_bytes.restype = _sz
 lib.q8_moe_workspace_bytes.argtypes = [_i64, _i32, _i64, _i64, _i64]
 lib.q8_moe_grouped_linear.restype = ctypes.c_int
@@ -183,8 +185,11 @@ def q8_linear_fused_gate_up_silu_q8act(w, f: int, k: int, xq, xd, out=None):
     return out
 
 
-def moe_route_topk(x, w_router, k: int, normalize: bool = True, idx_out=None, w_out=None):
-    """Softmax top-k routing; returns (topk_idx int32 [m][k], topk_w float32 [m][k])."""
+def moe_route_topk(x, w_router, k: int, normalize: bool = True, idx_out=None, w_out=None, top_p=None):
+    """Softmax top-k routing; returns (topk_idx int32 [m][k], topk_w float32 [m][k]).
+
+    With top_p (in (0, 1]) the adaptive expert top-p cut follows (moe_route_topk_top_p):
+    dropped slots hold expert -1 and weight 0."""
     torch = _torch()
     _dev(x, torch.float32, "x")
     _dev(w_router, torch.float32, "w_router")
@@ -202,8 +207,13 @@ def moe_route_topk(x, w_router, k: int, normalize: bool = True, idx_out=None, w_
     _dev(w_out, torch.float32, "w_out")
     if not (idx_out.is_contiguous() and w_out.is_contiguous()):
         raise ValueError("idx_out and w_out must be contiguous")
-    check(lib.moe_route_topk(x.data_ptr(), m, h, _ld(x, h), w_router.data_ptr(), n_exp, k, 1 if normalize else 0,
-                             idx_out.data_ptr(), w_out.data_ptr(), _stream(x)))
+    if top_p is None:
+        check(lib.moe_route_topk(x.data_ptr(), m, h, _ld(x, h), w_router.data_ptr(), n_exp, k,
+                                 1 if normalize else 0, idx_out.data_ptr(), w_out.data_ptr(), _stream(x)))
+    else:
+        check(lib.moe_route_topk_top_p(x.data_ptr(), m, h, _ld(x, h), w_router.data_ptr(), n_exp, k,
+                                       1 if normalize else 0, float(top_p), idx_out.data_ptr(), w_out.data_ptr(),
+                                       _stream(x)))
     return idx_out, w_out
 
 

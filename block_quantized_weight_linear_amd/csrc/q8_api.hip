@@ -152,23 +152,41 @@ q8_status q8_linear_fused_gate_up_silu_q8act(const void* w_gate_up_q8, int64_t f
                                stream);
 }
 
-q8_status moe_route_topk(const float* x, int64_t m, int64_t h, int64_t ldx, const float* w_router, int64_t n_exp,
-                         int32_t k, int32_t normalize, int32_t* topk_idx, float* topk_w, void* stream) {
+static q8_status route_common(const char* name, const float* x, int64_t m, int64_t h, int64_t ldx,
+                              const float* w_router, int64_t n_exp, int32_t k, int32_t normalize, float top_p,
+                              int32_t* topk_idx, float* topk_w, void* stream) {
     g_err[0] = 0;
     char msg[256];
     q8_status s = q8v::check_route(x, m, h, ldx, w_router, n_exp, k, topk_idx, topk_w, msg, sizeof msg);
+    if (s == Q8_OK && !(top_p > 0.0f && top_p <= 1.0f)) {
+        snprintf(msg, sizeof msg, "top_p must be in (0, 1]");
+        s = Q8_ERR_SHAPE;
+    }
     if (s != Q8_OK) {
-        set_err("moe_route_topk: %s", msg);
+        set_err("%s: %s", name, msg);
         return s;
     }
     if (m == 0) return Q8_OK;
     q8k::DeviceInfo dev;
     hipError_t e = q8k::current_device_info(&dev);
-    if (e != hipSuccess) return device_fail("moe_route_topk", e);
-    e = q8k::launch_route_topk(dev, x, m, h, ldx, w_router, n_exp, k, normalize != 0, topk_idx, topk_w,
+    if (e != hipSuccess) return device_fail(name, e);
+    e = q8k::launch_route_topk(dev, x, m, h, ldx, w_router, n_exp, k, normalize != 0, top_p, topk_idx, topk_w,
                                static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return device_fail("moe_route_topk", e);
+    if (e != hipSuccess) return device_fail(name, e);
     return Q8_OK;
+}
+
+q8_status moe_route_topk(const float* x, int64_t m, int64_t h, int64_t ldx, const float* w_router, int64_t n_exp,
+                         int32_t k, int32_t normalize, int32_t* topk_idx, float* topk_w, void* stream) {
+    return route_common("moe_route_topk", x, m, h, ldx, w_router, n_exp, k, normalize, 1.0f, topk_idx, topk_w,
+                        stream);
+}
+
+q8_status moe_route_topk_top_p(const float* x, int64_t m, int64_t h, int64_t ldx, const float* w_router,
+                               int64_t n_exp, int32_t k, int32_t normalize, float top_p, int32_t* topk_idx,
+                               float* topk_w, void* stream) {
+    return route_common("moe_route_topk_top_p", x, m, h, ldx, w_router, n_exp, k, normalize, top_p, topk_idx,
+                        topk_w, stream);
 }
 
 size_t q8_moe_workspace_bytes(int64_t m, int32_t k, int64_t n_exp, int64_t f, int64_t h) {

@@ -13,6 +13,12 @@
 // avoids ties that rounding exp() could create; softmax is monotonic, so the order is
 // that of the probabilities).  The chosen probabilities are divided by their sum, taken
 // in selection order, when normalize is set.
+//
+// Adaptive expert top-p (the Config knob moe_expert_top_p of section 14.2; 1.0 = full
+// top-k): with c_j the running sum of the chosen probabilities through slot j (float32,
+// selection order) and S the sum over all k, slot 0 is kept and slot j >= 1 while
+// c_{j-1} < top_p * S; top_p >= 1 keeps all k.  Kept weights are divided by the kept sum
+// when normalize is set; a dropped slot gets expert -1 and weight 0.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -32,7 +38,8 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
 
 __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float* __restrict__ x, int h, int ldx,
                                                                    const float* __restrict__ wr, int n_exp, int k,
-                                                                   int normalize, int32_t* __restrict__ out_idx,
+                                                                   int normalize, float top_p,
+                                                                   int32_t* __restrict__ out_idx,
                                                                    float* __restrict__ out_w) {
     __shared__ float logits[kMaxExperts];
     const int tok = blockIdx.x;
@@ -110,6 +117,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float* 
     // probabilities is accumulated in selection order, identically on all lanes.
     int keep_i[4] = {0, 0, 0, 0};
     float keep_p[4] = {0.f, 0.f, 0.f, 0.f};
+    float keep_cb[4] = {0.f, 0.f, 0.f, 0.f};  // running sum before the slot
+    float keep_ca[4] = {0.f, 0.f, 0.f, 0.f};  // running sum through the slot
     float psum = 0.0f;
     for (int j = 0; j < k; ++j) {
         float bv = -INFINITY;
@@ -136,6 +145,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float* 
         }
         if ((bi & 63) == lane) taken |= 1 << (bi >> 6);
         const float p = bp * inv_sum;
+        const float before = psum;
         psum += p;
         if ((j & 63) == lane) {
 #pragma unroll
@@ -143,25 +153,41 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float* 
                 if ((j >> 6) == c) {
                     keep_i[c] = bi;
                     keep_p[c] = p;
+                    keep_cb[c] = before;
+                    keep_ca[c] = psum;
                 }
             }
         }
     }
+    // top-p cut: every lane holds the same running sums for its slots, so the kept sum is
+    // the largest running sum through a kept slot (the sums only grow)
+    const bool all = !(top_p < 1.0f);
+    const float thr = top_p * psum;
+    bool kept[4];
+    float ksum = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int j = lane + 64 * c;
+        kept[c] = j < k && (all || j == 0 || keep_cb[c] < thr);
+        if (kept[c]) ksum = fmaxf(ksum, keep_ca[c]);
+    }
+    for (int off = 32; off >= 1; off >>= 1) ksum = fmaxf(ksum, __shfl_xor(ksum, off, 64));
+    if (all) ksum = psum;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         const int j = lane + 64 * c;
         if (j < k) {
-            out_idx[(size_t)tok * k + j] = keep_i[c];
-            out_w[(size_t)tok * k + j] = normalize ? keep_p[c] / psum : keep_p[c];
+            out_idx[(size_t)tok * k + j] = kept[c] ? keep_i[c] : -1;
+            out_w[(size_t)tok * k + j] = kept[c] ? (normalize ? keep_p[c] / ksum : keep_p[c]) : 0.0f;
         }
     }
 }
 
 hipError_t launch_route_topk(const DeviceInfo&, const float* x, int64_t m, int64_t h, int64_t ldx,
-                             const float* w_router, int64_t n_exp, int k, bool normalize, int32_t* idx, float* wts,
-                             hipStream_t stream) {
+                             const float* w_router, int64_t n_exp, int k, bool normalize, float top_p, int32_t* idx,
+                             float* wts, hipStream_t stream) {
     hipLaunchKernelGGL(route_topk_kernel, dim3((unsigned)m), dim3(kRouteThreads), 0, stream, x, (int)h, (int)ldx,
-                       w_router, (int)n_exp, k, normalize ? 1 : 0, idx, wts);
+                       w_router, (int)n_exp, k, normalize ? 1 : 0, top_p, idx, wts);
     return hipGetLastError();
 }
 

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define Q8_ABI_VERSION 2
+#define Q8_ABI_VERSION 3
 
 typedef enum q8_status {
     Q8_OK = 0,
@@ -155,6 +155,21 @@ q8_status moe_route_topk(const float* x, int64_t m, int64_t h, int64_t ldx,
                          const float* w_router, int64_t n_exp, int32_t k, int32_t normalize,
                          int32_t* topk_idx, float* topk_w, void* stream);
 
+/*
+ * Softmax top-k routing followed by adaptive expert top-p (section 14.2 Config:
+ * moe_expert_top_p, 1.0 = full top-k; applyExpertTopP).  The pages give only the knob
+ * and its neutral value; the cut used here: with the chosen probabilities p_j in
+ * selection order, c_j their running float32 sum through slot j and S the sum over all
+ * k slots, slot 0 is kept and slot j >= 1 while c_{j-1} < top_p * S; top_p = 1 keeps
+ * all k (and then equals moe_route_topk bit for bit).  Kept weights are divided by the
+ * kept sum when normalize is set; a dropped slot gets topk_idx = -1 and topk_w = 0,
+ * which q8_moe_grouped_linear skips.
+ *   top_p : in (0, 1], else Q8_ERR_SHAPE; other arguments as for moe_route_topk.
+ */
+q8_status moe_route_topk_top_p(const float* x, int64_t m, int64_t h, int64_t ldx,
+                               const float* w_router, int64_t n_exp, int32_t k, int32_t normalize,
+                               float top_p, int32_t* topk_idx, float* topk_w, void* stream);
+
 /* Workspace bytes q8_moe_grouped_linear needs for these sizes (0 on invalid sizes). */
 size_t q8_moe_workspace_bytes(int64_t m, int32_t k, int64_t n_exp, int64_t f, int64_t h);
 
@@ -166,8 +181,9 @@ size_t q8_moe_workspace_bytes(int64_t m, int32_t k, int64_t n_exp, int64_t f, in
  *   w_gate_up_exps : Q8_0 [n_exp][2f][h] (gate rows [0,f), up rows [f,2f) per expert)
  *   w_down_exps    : Q8_0 [n_exp][h][f]
  *   x : float32 [m][ldx] (ldx >= h)     y : float32 [m][ldy] (ldy >= h)
- *   topk_idx : int32 [m][k], every entry in [0, n_exp) (a precondition: entries outside
- *              it are skipped on the device and contribute nothing)
+ *   topk_idx : int32 [m][k], entries in [0, n_exp), or -1 for a slot dropped by
+ *              moe_route_topk_top_p (skipped: it contributes nothing; any other entry
+ *              outside [0, n_exp) is skipped the same way, but is a caller error)
  *   topk_w   : float32 [m][k]
  *   workspace: device memory of at least q8_moe_workspace_bytes(m, k, n_exp, f, h)
  *              bytes, 256-byte aligned; its contents on entry do not matter.

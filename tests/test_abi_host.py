@@ -33,14 +33,15 @@ def test_header_declares_the_four_calls():
     names = declared_functions()
     for n in ("q8_linear", "q8_linear_fused_gate_up_silu", "moe_route_topk", "q8_moe_grouped_linear",
               "q8_moe_workspace_bytes", "q8_status_string", "q8_last_error", "q8_abi_version",
-              "q8_quantize_act", "q8_linear_q8act", "q8_linear_fused_gate_up_silu_q8act"):
+              "q8_quantize_act", "q8_linear_q8act", "q8_linear_fused_gate_up_silu_q8act",
+              "moe_route_topk_top_p"):
         assert n in names, names
 
 
 def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert q8.abi_version() == 2
+    assert q8.abi_version() == 3
 
 
 def test_status_strings():
@@ -137,6 +138,20 @@ def test_route_argument_errors():
     assert call(idx=None) == ERR_NULL
     assert call(w=FAKE + 4) == ERR_ALIGN
     assert call(wt=FAKE + 2) == ERR_ALIGN
+
+
+def test_route_top_p_argument_errors():
+    def call(top_p, x=FAKE, m=2, k=2):
+        return lib.moe_route_topk_top_p(x, m, 256, 256, FAKE, 8, k, 1, ctypes.c_float(top_p), FAKE, FAKE, None)
+
+    assert call(0.0) == ERR_SHAPE
+    assert call(-0.5) == ERR_SHAPE
+    assert call(1.5) == ERR_SHAPE
+    assert call(float("nan")) == ERR_SHAPE
+    assert "top_p" in lib.q8_last_error().decode()
+    assert call(0.5, k=9) == ERR_SHAPE
+    assert call(0.5, x=None) == ERR_NULL
+    assert call(0.5, m=0, x=None) == OK
 
 
 def test_moe_workspace_and_errors():

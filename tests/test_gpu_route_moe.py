@@ -227,3 +227,95 @@ def test_moe_relabel_and_duplicates(q8):
     ref_idx[0, 2] = 0
     ref_w[0, 2] = 0.0
     assert_close(y2, oracle.moe_mixture_ref(gu, dn, e, f, h, x, ref_idx, ref_w), "duplicates + skipped id")
+
+
+# ------------------------------------------------------ adaptive expert top-p routing
+
+
+def check_top_p(idx_gpu, w_gpu, x, wr, k, normalize, top_p, eps=1e-5):
+    """Kept slots are a prefix with expert -1 / weight 0 after it; the kept count equals
+    the oracle's wherever no cumulative share c_j lies within eps of top_p (else it lies in
+    the band the float32 rounding allows); kept experts are the top-k's leading ones."""
+    ridx, rw = oracle.route_topk_p_ref(x, wr, k, normalize, top_p)
+    tidx, _ = oracle.route_topk_ref(x, wr, k, normalize)
+    p = oracle.softmax_ref(oracle.router_logits_ref(x, wr))
+    for t in range(x.shape[0]):
+        kept = int((idx_gpu[t] >= 0).sum())
+        assert kept >= 1 and np.all(idx_gpu[t, :kept] >= 0) and np.all(idx_gpu[t, kept:] == -1), t
+        assert np.all(w_gpu[t, kept:] == 0), t
+        chosen = p[t, tidx[t]]
+        c = np.cumsum(chosen) / chosen.sum()
+        lo = 1 + int(np.sum(c[:k - 1] < top_p - eps))
+        hi = 1 + int(np.sum(c[:k - 1] < top_p + eps))
+        if top_p >= 1.0:
+            lo = hi = k
+        assert lo <= kept <= hi, (t, kept, lo, hi)
+        if lo == hi:
+            rk = int((ridx[t] >= 0).sum())
+            assert kept == rk
+        if normalize:
+            assert abs(float(w_gpu[t, :kept].sum()) - 1.0) < 1e-5, t
+        else:
+            np.testing.assert_allclose(w_gpu[t, :kept], chosen[:kept], rtol=TOL)
+
+
+def test_top_p_one_is_plain_topk(q8):
+    lib, torch, dev = q8
+    x = wl.activations(201, 33, 2048)
+    wr = wl.router_weight(202, 128, 2048)
+    xd, wd = to_dev(x, dev), to_dev(wr, dev)
+    for k, norm in ((8, True), (8, False), (1, True), (128, True)):
+        i0, w0 = lib.moe_route_topk(xd, wd, k, norm)
+        i1, w1 = lib.moe_route_topk(xd, wd, k, norm, top_p=1.0)
+        assert torch.equal(i0, i1) and torch.equal(w0, w1), k
+
+
+def test_top_p_exact_boundaries(q8):
+    """Zero activations: every logit is 0 and every probability exactly 1/E (E a power of
+    two), so the cut is decided exactly, at the boundaries included."""
+    lib, torch, dev = q8
+    x = np.zeros((3, 256), np.float32)
+    wr = wl.router_weight(203, 8, 256)
+    for top_p, kept in ((0.25, 1), (0.26, 2), (0.5, 2), (0.51, 3), (0.75, 3), (0.76, 4), (1.0, 4)):
+        idx, w = lib.moe_route_topk(to_dev(x, dev), to_dev(wr, dev), 4, True, top_p=top_p)
+        ridx, rw = oracle.route_topk_p_ref(x, wr, 4, True, top_p)
+        assert np.array_equal(idx.cpu().numpy(), ridx), (top_p, idx)
+        assert int((ridx[0] >= 0).sum()) == kept
+        np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=1e-6)
+    idx, w = lib.moe_route_topk(to_dev(x, dev), to_dev(wr, dev), 4, False, top_p=0.5)
+    assert np.array_equal(w.cpu().numpy()[0], np.array([0.125, 0.125, 0, 0], np.float32))
+
+
+@pytest.mark.parametrize("top_p", [0.05, 0.3, 0.6, 0.9, 0.97])
+@pytest.mark.parametrize("normalize", [True, False])
+def test_top_p_vs_oracle(q8, top_p, normalize):
+    lib, torch, dev = q8
+    m, h, e, k = 64, 2048, 128, 8
+    x = wl.activations(204, m, h)
+    wr = wl.router_weight(205, e, h, std=0.05)   # spread logits: cuts at varied depths
+    say(f"top-p router top_p={top_p} normalize={normalize}")
+    idx, w = lib.moe_route_topk(to_dev(x, dev), to_dev(wr, dev), k, normalize, top_p=top_p)
+    idx, w = idx.cpu().numpy(), w.cpu().numpy()
+    check_top_p(idx, w, x, wr, k, normalize, top_p)
+    # the kept experts are the leading ones of the device's plain top-k
+    i0, _ = lib.moe_route_topk(to_dev(x, dev), to_dev(wr, dev), k, normalize)
+    i0 = i0.cpu().numpy()
+    kept = (idx >= 0)
+    assert np.array_equal(idx[kept], i0[kept])
+    say(f"top-p {top_p}: mean experts kept {kept.sum(axis=1).mean():.2f} of {k}")
+
+
+def test_top_p_mixture(q8):
+    """The grouped mixture on a top-p routing (dropped slots: expert -1) matches the oracle
+    mixture on the same routing."""
+    lib, torch, dev = q8
+    m, e, f, h, k = 16, 16, 256, 512, 8
+    gu, dn = _experts(300, e, f, h)
+    x = wl.activations(206, m, h)
+    wr = wl.router_weight(207, e, h, std=0.1)
+    xd = to_dev(x, dev)
+    idx, w = lib.moe_route_topk(xd, to_dev(wr, dev), k, True, top_p=0.6)
+    assert int((idx < 0).sum()) > 0      # some slots were dropped
+    y = lib.q8_moe_grouped_linear(to_dev(gu, dev), to_dev(dn, dev), e, f, h, xd, idx, w).cpu().numpy()
+    ref = oracle.moe_mixture_ref(gu, dn, e, f, h, x, idx.cpu().numpy(), w.cpu().numpy().astype(np.float64))
+    assert_close(y, ref, "top-p mixture")
