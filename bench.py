@@ -305,9 +305,10 @@ def bench_linear(torch, dev, q8, name, n, k, m, fused, reps, min_bytes=600e6):
     return res
 
 
-def bench_moe(torch, dev, q8, layers, steps, warmup):
-    """Qwen3-30B-A3B MoE layers at 16 tokens: device router (softmax top-8, renormalized)
-    then the grouped SwiGLU expert mixture, each layer with its own resident experts."""
+def bench_moe(torch, dev, q8, layers, steps, warmup, top_p=None):
+    """Qwen3-30B-A3B MoE layers at 16 tokens: device router (softmax top-8, renormalized;
+    with top_p, the adaptive expert top-p cut after it; the two-pass form) then the grouped
+    SwiGLU expert mixture, each layer with its own resident experts."""
     import workloads as wl
     cfg = wl.QWEN3_30B_A3B_MOE
     e, f, hd, k, t = cfg.n_exp, cfg.ffn, cfg.hidden, cfg.k, cfg.tokens
@@ -326,11 +327,12 @@ def bench_moe(torch, dev, q8, layers, steps, warmup):
     wts = [torch.empty((t, k), dtype=torch.float32, device=dev) for _ in range(layers)]
     y = torch.empty((t, hd), device=dev)
     ws = torch.empty(q8.q8_moe_workspace_bytes(t, k, e, f, hd), dtype=torch.uint8, device=dev)
+    ws_route = torch.empty(q8.moe_route_workspace_bytes(t, e), dtype=torch.uint8, device=dev)
     per_expert = (gu_h.size + dn_h.size) // distinct
 
     def step():
         for l in range(layers):
-            q8.moe_route_topk(x, wr[l], k, True, idx_out=idx[l], w_out=wts[l])
+            q8.moe_route_topk(x, wr[l], k, True, idx_out=idx[l], w_out=wts[l], top_p=top_p, workspace=ws_route)
             q8.q8_moe_grouped_linear(gu[l], dn[l], e, f, hd, x, idx[l], wts[l], out=y, workspace=ws)
 
     stream = torch.cuda.Stream()
@@ -345,16 +347,19 @@ def bench_moe(torch, dev, q8, layers, steps, warmup):
         if not torch.equal(y, y_eager):
             raise RuntimeError("MoE graph replay differs from the eager step")
         ms = time_steps(torch, graph.replay, steps, warmup)
-    used = [int(torch.unique(i).numel()) for i in idx]
+    used = [int(torch.unique(i[i >= 0]).numel()) for i in idx]
+    slots = [int((i >= 0).sum()) for i in idx]
     expert_bytes = sum(used) * per_expert
     router_bytes = layers * e * hd * 4
     res = {"workload": cfg.name, "tokens": t, "layers": layers, "experts": e, "top_k": k,
            "ms_per_step": round(ms, 5), "ms_per_step_eager": round(ms_eager, 5),
            "us_per_layer": round(ms * 1e3 / layers, 3), "tok_s": round(t * 1000.0 / ms, 1),
-           "experts_used_per_layer": used, "bytes_per_expert": per_expert,
+           "experts_used_per_layer": used, "routed_slots_per_layer": slots, "bytes_per_expert": per_expert,
            "weight_bytes_per_step": expert_bytes + router_bytes,
            "gbps": round((expert_bytes + router_bytes) / (ms * 1e-3) / 1e9, 2)}
     res["hbm_frac"] = round(res["gbps"] / HBM_PEAK_GBS, 4)
+    if top_p is not None:
+        res["expert_top_p"] = top_p
     log(f"moe: {res}")
     return res
 
@@ -476,6 +481,8 @@ def main():
         extras["qwen3-8b-gate-up-m512-prefill"] = bench_linear(torch, dev, q8, "8b gate_up m512", 24576, 4096, 512,
                                                                True, reps)
         extras["qwen3-30b-a3b-moe-16tok"] = bench_moe(torch, dev, q8, 4, args.steps, args.warmup)
+        extras["qwen3-30b-a3b-moe-16tok-expert-top-p-0.9"] = bench_moe(torch, dev, q8, 4, args.steps, args.warmup,
+                                                                        top_p=0.9)
         line["configs"] = extras
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on one layer")

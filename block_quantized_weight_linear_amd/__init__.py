@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     abi_version,
     lib,
     moe_route_topk,
+    moe_route_workspace_bytes,
     q8_linear,
     q8_linear_fused_gate_up_silu,
     q8_linear_fused_gate_up_silu_q8act,

@@ -49,6 +49,11 @@ lib.moe_route_topk.restype = ctypes.c_int
 lib.moe_route_topk.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _i32, _i32, _vp, _vp, _vp]
 lib.moe_route_topk_top_p.restype = ctypes.c_int
 lib.moe_route_topk_top_p.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _i32, _i32, ctypes.c_float, _vp, _vp, _vp]
+lib.moe_route_workspace_bytes.restype = _sz
+lib.moe_route_workspace_bytes.argtypes = [_i64, _i64]
+lib.moe_route_topk_ws.restype = ctypes.c_int
+lib.moe_route_topk_ws.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _i32, _i32, ctypes.c_float, _vp, _vp, _vp, _sz,
+                                  _vp]
 lib.q8_moe_workspace_bytes.restype = _sz
 lib.q8_moe_workspace_bytes.argtypes = [_i64, _i32, _i64, _i64, _i64]
 lib.q8_moe_grouped_linear.restype = ctypes.c_int
@@ -185,11 +190,14 @@ def q8_linear_fused_gate_up_silu_q8act(w, f: int, k: int, xq, xd, out=None):
     return out
 
 
-def moe_route_topk(x, w_router, k: int, normalize: bool = True, idx_out=None, w_out=None, top_p=None):
+def moe_route_topk(x, w_router, k: int, normalize: bool = True, idx_out=None, w_out=None, top_p=None,
+                   workspace=None):
     """Softmax top-k routing; returns (topk_idx int32 [m][k], topk_w float32 [m][k]).
 
     With top_p (in (0, 1]) the adaptive expert top-p cut follows (moe_route_topk_top_p):
-    dropped slots hold expert -1 and weight 0."""
+    dropped slots hold expert -1 and weight 0.  With a workspace (uint8 device tensor of
+    at least moe_route_workspace_bytes(m, n_exp) bytes; True allocates one) the two-pass
+    form runs (moe_route_topk_ws), bit-identical to the one-pass calls."""
     torch = _torch()
     _dev(x, torch.float32, "x")
     _dev(w_router, torch.float32, "w_router")
@@ -207,7 +215,16 @@ def moe_route_topk(x, w_router, k: int, normalize: bool = True, idx_out=None, w_
     _dev(w_out, torch.float32, "w_out")
     if not (idx_out.is_contiguous() and w_out.is_contiguous()):
         raise ValueError("idx_out and w_out must be contiguous")
-    if top_p is None:
+    if workspace is not None:
+        if workspace is True:
+            workspace = torch.empty(max(moe_route_workspace_bytes(m, n_exp), 1), dtype=torch.uint8,
+                                    device=x.device)
+        _dev(workspace, torch.uint8, "workspace")
+        check(lib.moe_route_topk_ws(x.data_ptr(), m, h, _ld(x, h), w_router.data_ptr(), n_exp, k,
+                                    1 if normalize else 0, 1.0 if top_p is None else float(top_p),
+                                    idx_out.data_ptr(), w_out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                    _stream(x)))
+    elif top_p is None:
         check(lib.moe_route_topk(x.data_ptr(), m, h, _ld(x, h), w_router.data_ptr(), n_exp, k,
                                  1 if normalize else 0, idx_out.data_ptr(), w_out.data_ptr(), _stream(x)))
     else:
@@ -215,6 +232,10 @@ def moe_route_topk(x, w_router, k: int, normalize: bool = True, idx_out=None, w_
                                        1 if normalize else 0, float(top_p), idx_out.data_ptr(), w_out.data_ptr(),
                                        _stream(x)))
     return idx_out, w_out
+
+
+def moe_route_workspace_bytes(m: int, n_exp: int) -> int:
+    return int(lib.moe_route_workspace_bytes(m, n_exp))
 
 
 def q8_moe_workspace_bytes(m: int, k: int, n_exp: int, f: int, h: int) -> int:

@@ -154,7 +154,8 @@ q8_status q8_linear_fused_gate_up_silu_q8act(const void* w_gate_up_q8, int64_t f
 
 static q8_status route_common(const char* name, const float* x, int64_t m, int64_t h, int64_t ldx,
                               const float* w_router, int64_t n_exp, int32_t k, int32_t normalize, float top_p,
-                              int32_t* topk_idx, float* topk_w, void* stream) {
+                              int32_t* topk_idx, float* topk_w, bool with_ws, void* workspace,
+                              size_t workspace_bytes, void* stream) {
     g_err[0] = 0;
     char msg[256];
     q8_status s = q8v::check_route(x, m, h, ldx, w_router, n_exp, k, topk_idx, topk_w, msg, sizeof msg);
@@ -162,6 +163,7 @@ static q8_status route_common(const char* name, const float* x, int64_t m, int64
         snprintf(msg, sizeof msg, "top_p must be in (0, 1]");
         s = Q8_ERR_SHAPE;
     }
+    if (s == Q8_OK && with_ws && m > 0) s = q8v::check_route_workspace(m, n_exp, workspace, workspace_bytes, msg, sizeof msg);
     if (s != Q8_OK) {
         set_err("%s: %s", name, msg);
         return s;
@@ -171,7 +173,7 @@ static q8_status route_common(const char* name, const float* x, int64_t m, int64
     hipError_t e = q8k::current_device_info(&dev);
     if (e != hipSuccess) return device_fail(name, e);
     e = q8k::launch_route_topk(dev, x, m, h, ldx, w_router, n_exp, k, normalize != 0, top_p, topk_idx, topk_w,
-                               static_cast<hipStream_t>(stream));
+                               with_ws ? static_cast<float*>(workspace) : nullptr, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return device_fail(name, e);
     return Q8_OK;
 }
@@ -179,14 +181,26 @@ static q8_status route_common(const char* name, const float* x, int64_t m, int64
 q8_status moe_route_topk(const float* x, int64_t m, int64_t h, int64_t ldx, const float* w_router, int64_t n_exp,
                          int32_t k, int32_t normalize, int32_t* topk_idx, float* topk_w, void* stream) {
     return route_common("moe_route_topk", x, m, h, ldx, w_router, n_exp, k, normalize, 1.0f, topk_idx, topk_w,
-                        stream);
+                        false, nullptr, 0, stream);
 }
 
 q8_status moe_route_topk_top_p(const float* x, int64_t m, int64_t h, int64_t ldx, const float* w_router,
                                int64_t n_exp, int32_t k, int32_t normalize, float top_p, int32_t* topk_idx,
                                float* topk_w, void* stream) {
     return route_common("moe_route_topk_top_p", x, m, h, ldx, w_router, n_exp, k, normalize, top_p, topk_idx,
-                        topk_w, stream);
+                        topk_w, false, nullptr, 0, stream);
+}
+
+size_t moe_route_workspace_bytes(int64_t m, int64_t n_exp) {
+    if (m < 0 || m > q8v::kMaxDim || n_exp < 1 || n_exp > q8v::kMaxExperts) return 0;
+    return q8v::route_workspace_bytes(m, n_exp);
+}
+
+q8_status moe_route_topk_ws(const float* x, int64_t m, int64_t h, int64_t ldx, const float* w_router, int64_t n_exp,
+                            int32_t k, int32_t normalize, float top_p, int32_t* topk_idx, float* topk_w,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    return route_common("moe_route_topk_ws", x, m, h, ldx, w_router, n_exp, k, normalize, top_p, topk_idx, topk_w,
+                        true, workspace, workspace_bytes, stream);
 }
 
 size_t q8_moe_workspace_bytes(int64_t m, int32_t k, int64_t n_exp, int64_t f, int64_t h) {

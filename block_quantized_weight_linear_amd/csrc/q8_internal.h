@@ -36,10 +36,12 @@ hipError_t launch_quantize_act(const float* x, int64_t m, int64_t k, int64_t ldx
 hipError_t launch_gemv_q8act(const DeviceInfo& dev, const uint8_t* w, int64_t n_out, int64_t k, bool silu_pairs,
                              const int8_t* xq, const float* xd, int64_t m, float* y, int64_t ldy, hipStream_t stream);
 
-// Softmax top-k router with adaptive expert top-p (top_p >= 1: plain top-k).
+// Softmax top-k router with adaptive expert top-p (top_p >= 1: plain top-k).  logits ==
+// nullptr: one kernel, one block per token; else a [m][n_exp] float32 workspace for the
+// two-pass form (logits over many CUs, then selection), bit-identical results.
 hipError_t launch_route_topk(const DeviceInfo& dev, const float* x, int64_t m, int64_t h, int64_t ldx,
                              const float* w_router, int64_t n_exp, int k, bool normalize, float top_p, int32_t* idx,
-                             float* wts, hipStream_t stream);
+                             float* wts, float* logits, hipStream_t stream);
 
 // Grouped MoE SwiGLU mixture; workspace laid out by q8v::moe_workspace_layout.
 hipError_t launch_moe_grouped(const DeviceInfo& dev, const uint8_t* wgu, const uint8_t* wdn, int64_t n_exp, int64_t f,

@@ -113,6 +113,21 @@ inline q8_status check_route(const float* x, int64_t m, int64_t h, int64_t ldx, 
     return Q8_OK;
 }
 
+// Workspace of the two-pass router: the float32 logits [m][n_exp].
+inline size_t route_workspace_bytes(int64_t m, int64_t n_exp) {
+    const size_t b = sizeof(float) * size_t(m) * size_t(n_exp);
+    return b ? (b + 255) / 256 * 256 : 256;
+}
+
+inline q8_status check_route_workspace(int64_t m, int64_t n_exp, const void* ws, size_t ws_bytes, char* msg,
+                                       size_t cap) {
+    if (!ws) return fail(msg, cap, Q8_ERR_WORKSPACE, "workspace is NULL");
+    const size_t need = route_workspace_bytes(m, n_exp);
+    if (ws_bytes < need) return fail(msg, cap, Q8_ERR_WORKSPACE, "workspace %lld bytes < required %lld", (long long)ws_bytes, (long long)need);
+    if (!aligned(ws, 16)) return fail(msg, cap, Q8_ERR_ALIGN, "workspace not 16-byte aligned");
+    return Q8_OK;
+}
+
 // Workspace of the grouped MoE call: a route plan plus the hidden activations.
 struct MoeWorkspace {
     size_t offsets_off, sorted_off, inv_off, active_off, hidden_off, out_off, total;

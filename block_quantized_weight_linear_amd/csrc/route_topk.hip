@@ -23,6 +23,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "q8_internal.h"
 
 namespace q8k {
@@ -34,6 +36,162 @@ constexpr int kMaxExperts = 256;
 
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
     return v > bv || (v == bv && i < bi);
+}
+
+// Cross-lane steps on the DPP network (no LDS round trip): within each row of 16 lanes,
+// xor 1 and xor 2 (quad permutes), then the half-row and row mirrors; the four rows are
+// then combined from lanes 0, 16, 32, 48 with readlane, in row order.
+constexpr int kDppXor1 = 0xB1;        // quad_perm(1, 0, 3, 2)
+constexpr int kDppXor2 = 0x4E;        // quad_perm(2, 3, 0, 1)
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    const int b = __builtin_bit_cast(int, v);
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
+// Every lane gets the wave's best (value, index) under better().
+__device__ __forceinline__ void wave_best(float& v, int& i) {
+    auto step = [&](auto c) __attribute__((always_inline)) {
+        constexpr int C = decltype(c)::value;
+        const float ov = dpp_f<C>(v);
+        const int oi = dpp_i<C>(i);
+        if (better(ov, oi, v, i)) {
+            v = ov;
+            i = oi;
+        }
+    };
+    step(std::integral_constant<int, kDppXor1>{});
+    step(std::integral_constant<int, kDppXor2>{});
+    step(std::integral_constant<int, kDppHalfMirror>{});
+    step(std::integral_constant<int, kDppMirror>{});
+    float bv = lane_f(v, 0);
+    int bi = __builtin_amdgcn_readlane(i, 0);
+#pragma unroll
+    for (int r = 1; r < 4; ++r) {
+        const float rv = lane_f(v, 16 * r);
+        const int ri = __builtin_amdgcn_readlane(i, 16 * r);
+        if (better(rv, ri, bv, bi)) {
+            bv = rv;
+            bi = ri;
+        }
+    }
+    v = bv;
+    i = bi;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp_f<kDppXor1>(v));
+    v = fmaxf(v, dpp_f<kDppXor2>(v));
+    v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp_f<kDppMirror>(v));
+    return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+}
+
+// Fixed order: the DPP tree within each row, then ((row0 + row1) + row2) + row3.
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp_f<kDppXor1>(v);
+    v += dpp_f<kDppXor2>(v);
+    v += dpp_f<kDppHalfMirror>(v);
+    v += dpp_f<kDppMirror>(v);
+    return ((lane_f(v, 0) + lane_f(v, 16)) + lane_f(v, 32)) + lane_f(v, 48);
+}
+
+// Softmax, top-k selection and the top-p cut for one token on one wave; logit_of(e)
+// returns expert e's float32 logit (e < n_exp).  Lane l owns experts l, l+64, l+128, l+192.
+template <class LogitOf>
+__device__ __forceinline__ void select_topk(LogitOf&& logit_of, int lane, int tok, int n_exp, int k, int normalize,
+                                            float top_p, int32_t* __restrict__ out_idx,
+                                            float* __restrict__ out_w) {
+    float l[4];
+    int taken = 0;  // bit c: expert lane + 64c already selected
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int e = lane + 64 * c;
+        l[c] = e < n_exp ? logit_of(e) : -INFINITY;
+        if (e >= n_exp) taken |= 1 << c;
+    }
+    const float mx = wave_max(fmaxf(fmaxf(l[0], l[1]), fmaxf(l[2], l[3])));
+    float ex[4];
+    float part = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        ex[c] = (lane + 64 * c < n_exp) ? expf(l[c] - mx) : 0.0f;
+        part += ex[c];
+    }
+    const float inv_sum = 1.0f / wave_sum(part);
+
+    // k rounds; each picks the wave's best untaken expert (every lane learns it) and the
+    // owner lane's probability by readlane.  Lane (j % 64) keeps round j's result in its
+    // register slot j / 64; the chosen probabilities are summed in selection order,
+    // identically on all lanes.
+    int keep_i[4] = {0, 0, 0, 0};
+    float keep_p[4] = {0.f, 0.f, 0.f, 0.f};
+    float keep_cb[4] = {0.f, 0.f, 0.f, 0.f};  // running sum before the slot
+    float keep_ca[4] = {0.f, 0.f, 0.f, 0.f};  // running sum through the slot
+    float psum = 0.0f;
+    for (int j = 0; j < k; ++j) {
+        float bv = -INFINITY;
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int e = lane + 64 * c;
+            if (!(taken & (1 << c)) && better(l[c], e, bv, bi)) {
+                bv = l[c];
+                bi = e;
+            }
+        }
+        wave_best(bv, bi);
+        const int wl = bi & 63, wc = bi >> 6;
+        const float mine = wc == 0 ? ex[0] : wc == 1 ? ex[1] : wc == 2 ? ex[2] : ex[3];
+        const float bp = lane_f(mine, wl);
+        if (lane == wl) taken |= 1 << wc;
+        const float p = bp * inv_sum;
+        const float before = psum;
+        psum += p;
+        if ((j & 63) == lane) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                if ((j >> 6) == c) {
+                    keep_i[c] = bi;
+                    keep_p[c] = p;
+                    keep_cb[c] = before;
+                    keep_ca[c] = psum;
+                }
+            }
+        }
+    }
+    // top-p cut: every lane holds the same running sums for its slots, so the kept sum is
+    // the largest running sum through a kept slot (the sums only grow)
+    const bool all = !(top_p < 1.0f);
+    const float thr = top_p * psum;
+    bool kept[4];
+    float ksum = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int j = lane + 64 * c;
+        kept[c] = j < k && (all || j == 0 || keep_cb[c] < thr);
+        if (kept[c]) ksum = fmaxf(ksum, keep_ca[c]);
+    }
+    ksum = wave_max(ksum);
+    if (all) ksum = psum;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int j = lane + 64 * c;
+        if (j < k) {
+            out_idx[(size_t)tok * k + j] = kept[c] ? keep_i[c] : -1;
+            out_w[(size_t)tok * k + j] = kept[c] ? (normalize ? keep_p[c] / ksum : keep_p[c]) : 0.0f;
+        }
+    }
 }
 
 __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float* __restrict__ x, int h, int ldx,
@@ -90,102 +248,84 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float* 
     }
     __syncthreads();
     if (wave != 0) return;
+    select_topk([&](int e) { return logits[e]; }, lane, tok, n_exp, k, normalize, top_p, out_idx, out_w);
+}
 
-    // Each lane owns experts lane, lane+64, lane+128, lane+192.
-    float l[4];
-    int taken = 0;  // bit c: expert lane + 64c already selected
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const int e = lane + 64 * c;
-        l[c] = e < n_exp ? logits[e] : -INFINITY;
-        if (e >= n_exp) taken |= 1 << c;
-    }
-    float mx = fmaxf(fmaxf(l[0], l[1]), fmaxf(l[2], l[3]));
-    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-    float ex[4];
-    float sum = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        ex[c] = (lane + 64 * c < n_exp) ? expf(l[c] - mx) : 0.0f;
-        sum += ex[c];
-    }
-    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
-    const float inv_sum = 1.0f / sum;
+// Two-pass router for many experts or tokens: the logits of a token are spread over
+// many CUs (one CU reading the whole router matrix per token is bound by its own L1
+// rate), then one wave per token selects.  Pass 1: block (token group t, expert group
+// g) stages the x rows of kLogitTokens tokens in LDS; wave w multiplies expert
+// 4g + w against them with the same lane slices and butterfly as route_topk_kernel, so
+// the logits, and everything selected from them, are bit-identical to the one-kernel
+// router's.
+constexpr int kLogitThreads = 256;
+constexpr int kLogitTokens = 4;
+constexpr int kLogitChunk = 2048;  // inputs staged per pass (h is split into such chunks)
 
-    // k rounds; after each butterfly every lane holds the winner.  Lane (j % 64) keeps
-    // round j's result in its register slot j / 64; the sum of the chosen
-    // probabilities is accumulated in selection order, identically on all lanes.
-    int keep_i[4] = {0, 0, 0, 0};
-    float keep_p[4] = {0.f, 0.f, 0.f, 0.f};
-    float keep_cb[4] = {0.f, 0.f, 0.f, 0.f};  // running sum before the slot
-    float keep_ca[4] = {0.f, 0.f, 0.f, 0.f};  // running sum through the slot
-    float psum = 0.0f;
-    for (int j = 0; j < k; ++j) {
-        float bv = -INFINITY;
-        int bi = 0x7fffffff;
-        float bp = 0.0f;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int e = lane + 64 * c;
-            if (!(taken & (1 << c)) && (bi == 0x7fffffff || better(l[c], e, bv, bi))) {
-                bv = l[c];
-                bi = e;
-                bp = ex[c];
-            }
+__global__ __launch_bounds__(kLogitThreads) void route_logits_kernel(const float* __restrict__ x, int m, int h,
+                                                                     int ldx, const float* __restrict__ wr,
+                                                                     int n_exp, float* __restrict__ logits) {
+    __shared__ float4 xs[kLogitTokens][kLogitChunk / 4];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int e = blockIdx.y * 4 + wave;
+    const int t0 = blockIdx.x * kLogitTokens;
+    const int ec = e < n_exp ? e : n_exp - 1;  // a wave past the experts repeats the last one, not stored
+    const float* we = wr + (size_t)ec * h;
+    float acc[kLogitTokens] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int c0 = 0; c0 < h; c0 += kLogitChunk) {
+        const int len = h - c0 < kLogitChunk ? h - c0 : kLogitChunk;  // a multiple of 256
+        __syncthreads();
+        for (int i = threadIdx.x; i < kLogitTokens * (len / 4); i += kLogitThreads) {
+            const int t = i / (len / 4);
+            const int q = i - t * (len / 4);
+            const int tc = t0 + t < m ? t0 + t : m - 1;
+            xs[t][q] = *reinterpret_cast<const float4*>(x + (size_t)tc * ldx + c0 + 4 * q);
         }
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off, 64);
-            const int oi = __shfl_xor(bi, off, 64);
-            const float op = __shfl_xor(bp, off, 64);
-            if (oi != 0x7fffffff && (bi == 0x7fffffff || better(ov, oi, bv, bi))) {
-                bv = ov;
-                bi = oi;
-                bp = op;
-            }
-        }
-        if ((bi & 63) == lane) taken |= 1 << (bi >> 6);
-        const float p = bp * inv_sum;
-        const float before = psum;
-        psum += p;
-        if ((j & 63) == lane) {
+        __syncthreads();
+        for (int i = 0; i < len / 256; ++i) {
+            const float4 v = *reinterpret_cast<const float4*>(we + c0 + 4 * lane + 256 * i);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                if ((j >> 6) == c) {
-                    keep_i[c] = bi;
-                    keep_p[c] = p;
-                    keep_cb[c] = before;
-                    keep_ca[c] = psum;
-                }
+            for (int t = 0; t < kLogitTokens; ++t) {
+                const float4 a = xs[t][lane + 64 * i];
+                acc[t] = __builtin_fmaf(a.x, v.x, acc[t]);
+                acc[t] = __builtin_fmaf(a.y, v.y, acc[t]);
+                acc[t] = __builtin_fmaf(a.z, v.z, acc[t]);
+                acc[t] = __builtin_fmaf(a.w, v.w, acc[t]);
             }
         }
     }
-    // top-p cut: every lane holds the same running sums for its slots, so the kept sum is
-    // the largest running sum through a kept slot (the sums only grow)
-    const bool all = !(top_p < 1.0f);
-    const float thr = top_p * psum;
-    bool kept[4];
-    float ksum = 0.0f;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const int j = lane + 64 * c;
-        kept[c] = j < k && (all || j == 0 || keep_cb[c] < thr);
-        if (kept[c]) ksum = fmaxf(ksum, keep_ca[c]);
+    for (int t = 0; t < kLogitTokens; ++t) {
+        for (int off = 32; off >= 1; off >>= 1) acc[t] += __shfl_xor(acc[t], off, 64);
+        if (lane == 0 && e < n_exp && t0 + t < m) logits[(size_t)(t0 + t) * n_exp + e] = acc[t];
     }
-    for (int off = 32; off >= 1; off >>= 1) ksum = fmaxf(ksum, __shfl_xor(ksum, off, 64));
-    if (all) ksum = psum;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const int j = lane + 64 * c;
-        if (j < k) {
-            out_idx[(size_t)tok * k + j] = kept[c] ? keep_i[c] : -1;
-            out_w[(size_t)tok * k + j] = kept[c] ? (normalize ? keep_p[c] / ksum : keep_p[c]) : 0.0f;
-        }
-    }
+}
+
+// Pass 2: one wave per token.
+__global__ __launch_bounds__(256) void route_select_kernel(const float* __restrict__ logits, int m, int n_exp, int k,
+                                                           int normalize, float top_p,
+                                                           int32_t* __restrict__ out_idx,
+                                                           float* __restrict__ out_w) {
+    const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (tok >= m) return;
+    const float* lg = logits + (size_t)tok * n_exp;
+    select_topk([&](int e) { return lg[e]; }, threadIdx.x & 63, tok, n_exp, k, normalize, top_p, out_idx, out_w);
 }
 
 hipError_t launch_route_topk(const DeviceInfo&, const float* x, int64_t m, int64_t h, int64_t ldx,
                              const float* w_router, int64_t n_exp, int k, bool normalize, float top_p, int32_t* idx,
-                             float* wts, hipStream_t stream) {
+                             float* wts, float* logits, hipStream_t stream) {
+    if (logits) {
+        const dim3 grid((unsigned)((m + kLogitTokens - 1) / kLogitTokens), (unsigned)((n_exp + 3) / 4));
+        hipLaunchKernelGGL(route_logits_kernel, grid, dim3(kLogitThreads), 0, stream, x, (int)m, (int)h, (int)ldx,
+                           w_router, (int)n_exp, logits);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(route_select_kernel, dim3((unsigned)((m + 3) / 4)), dim3(256), 0, stream, logits, (int)m,
+                           (int)n_exp, k, normalize ? 1 : 0, top_p, idx, wts);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(route_topk_kernel, dim3((unsigned)m), dim3(kRouteThreads), 0, stream, x, (int)h, (int)ldx,
                        w_router, (int)n_exp, k, normalize ? 1 : 0, top_p, idx, wts);
     return hipGetLastError();

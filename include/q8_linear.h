@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define Q8_ABI_VERSION 3
+#define Q8_ABI_VERSION 4
 
 typedef enum q8_status {
     Q8_OK = 0,
@@ -169,6 +169,25 @@ q8_status moe_route_topk(const float* x, int64_t m, int64_t h, int64_t ldx,
 q8_status moe_route_topk_top_p(const float* x, int64_t m, int64_t h, int64_t ldx,
                                const float* w_router, int64_t n_exp, int32_t k, int32_t normalize,
                                float top_p, int32_t* topk_idx, float* topk_w, void* stream);
+
+/* Workspace bytes moe_route_topk_ws needs for m tokens and n_exp experts (0 on invalid sizes). */
+size_t moe_route_workspace_bytes(int64_t m, int64_t n_exp);
+
+/*
+ * moe_route_topk_top_p in two passes that spread each token's logits over many CUs (one
+ * kernel block per token is bound by one CU's load rate for the whole router matrix):
+ * the logits go to the workspace, then one wave per token selects.  The logits are
+ * summed in the same order as in the one-pass calls, so the results are bit-identical
+ * to moe_route_topk_top_p (and to moe_route_topk when top_p = 1).
+ *   workspace : device memory of at least moe_route_workspace_bytes(m, n_exp) bytes,
+ *               16-byte aligned (Q8_ERR_WORKSPACE / Q8_ERR_ALIGN otherwise); its contents
+ *               on entry do not matter and are overwritten.
+ * Other arguments as for moe_route_topk_top_p.
+ */
+q8_status moe_route_topk_ws(const float* x, int64_t m, int64_t h, int64_t ldx,
+                            const float* w_router, int64_t n_exp, int32_t k, int32_t normalize,
+                            float top_p, int32_t* topk_idx, float* topk_w,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes q8_moe_grouped_linear needs for these sizes (0 on invalid sizes). */
 size_t q8_moe_workspace_bytes(int64_t m, int32_t k, int64_t n_exp, int64_t f, int64_t h);

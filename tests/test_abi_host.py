@@ -34,14 +34,14 @@ def test_header_declares_the_four_calls():
     for n in ("q8_linear", "q8_linear_fused_gate_up_silu", "moe_route_topk", "q8_moe_grouped_linear",
               "q8_moe_workspace_bytes", "q8_status_string", "q8_last_error", "q8_abi_version",
               "q8_quantize_act", "q8_linear_q8act", "q8_linear_fused_gate_up_silu_q8act",
-              "moe_route_topk_top_p"):
+              "moe_route_topk_top_p", "moe_route_topk_ws", "moe_route_workspace_bytes"):
         assert n in names, names
 
 
 def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert q8.abi_version() == 3
+    assert q8.abi_version() == 4
 
 
 def test_status_strings():
@@ -152,6 +152,25 @@ def test_route_top_p_argument_errors():
     assert call(0.5, k=9) == ERR_SHAPE
     assert call(0.5, x=None) == ERR_NULL
     assert call(0.5, m=0, x=None) == OK
+
+
+def test_route_ws_argument_errors():
+    need = lib.moe_route_workspace_bytes(16, 128)
+    assert need >= 16 * 128 * 4 and need % 256 == 0
+    assert lib.moe_route_workspace_bytes(16, 0) == 0
+    assert lib.moe_route_workspace_bytes(-1, 8) == 0
+
+    def call(ws=FAKE, wsb=None, m=2, top_p=1.0, x=FAKE):
+        if wsb is None:
+            wsb = lib.moe_route_workspace_bytes(m, 8)
+        return lib.moe_route_topk_ws(x, m, 256, 256, FAKE, 8, 2, 1, ctypes.c_float(top_p), FAKE, FAKE, ws, wsb, None)
+
+    assert call(ws=None) == ERR_WORKSPACE
+    assert call(wsb=8) == ERR_WORKSPACE
+    assert call(ws=FAKE + 4) == ERR_ALIGN
+    assert call(top_p=0.0) == ERR_SHAPE
+    assert call(x=None) == ERR_NULL
+    assert call(m=0, x=None, ws=None) == OK
 
 
 def test_moe_workspace_and_errors():

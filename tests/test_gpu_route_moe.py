@@ -319,3 +319,29 @@ def test_top_p_mixture(q8):
     y = lib.q8_moe_grouped_linear(to_dev(gu, dev), to_dev(dn, dev), e, f, h, xd, idx, w).cpu().numpy()
     ref = oracle.moe_mixture_ref(gu, dn, e, f, h, x, idx.cpu().numpy(), w.cpu().numpy().astype(np.float64))
     assert_close(y, ref, "top-p mixture")
+
+
+# ------------------------------------------------------------- two-pass router
+
+
+@pytest.mark.parametrize("m,h,e,k", [(16, 2048, 128, 8), (1, 4096, 8, 2), (257, 1024, 64, 6), (3, 256, 256, 256),
+                                     (5, 6144, 7, 1), (33, 768, 130, 9)])
+def test_two_pass_router_bit_identical(q8, m, h, e, k):
+    """moe_route_topk_ws (logits over many CUs, then selection) equals the one-pass router
+    bit for bit, with and without the top-p cut, and stays within the oracle's checks."""
+    lib, torch, dev = q8
+    x = wl.activations(401 + m, m, h)
+    wr = wl.router_weight(402 + e, e, h, std=0.05)
+    xd, wd = to_dev(x, dev), to_dev(wr, dev)
+    say(f"two-pass router m={m} h={h} e={e} k={k}")
+    ws = torch.full((lib.moe_route_workspace_bytes(m, e),), 255, dtype=torch.uint8, device=dev)
+    for norm in (True, False):
+        i1, w1 = lib.moe_route_topk(xd, wd, k, norm)
+        i2, w2 = lib.moe_route_topk(xd, wd, k, norm, workspace=ws)
+        assert torch.equal(i1, i2) and torch.equal(w1, w2), norm
+        for top_p in (0.3, 0.8):
+            i1, w1 = lib.moe_route_topk(xd, wd, k, norm, top_p=top_p)
+            i2, w2 = lib.moe_route_topk(xd, wd, k, norm, top_p=top_p, workspace=ws)
+            assert torch.equal(i1, i2) and torch.equal(w1, w2), (norm, top_p)
+    i2, w2 = lib.moe_route_topk(xd, wd, k, True, workspace=True)
+    check_routing(i2.cpu().numpy(), w2.cpu().numpy(), x, wr, k, True)
