@@ -33,7 +33,11 @@ namespace q8k {
 
 constexpr int kMoeThreads = 256;
 constexpr int kMoeWaves = kMoeThreads / 64;
-constexpr int kMoeGroupsPerWave = 4;  // row groups each wave takes in one tile
+// Row groups each wave takes in one (expert, tile) unit: longer units amortize the
+// per-unit staging and pipeline start; measured on the A3B layer, 8 suits the gate_up
+// pass (2f rows of K = h) and 4 the down pass (h rows of K = f).
+template <bool GATE_UP>
+constexpr int moe_groups_per_wave() { return GATE_UP ? 8 : 4; }
 constexpr int kMoeMaxRows = 4;        // activation rows staged per pass
 constexpr int kPlanThreads = 256;
 
@@ -163,7 +167,7 @@ __global__ __launch_bounds__(kMoeThreads) void moe_expert_kernel(const uint8_t* 
     extern __shared__ float4 x_lds[];
     const int G = 64 >> log2S;
     const int row_groups = (n_out + G - 1) / G;
-    const int tile_groups = kMoeWaves * kMoeGroupsPerWave;
+    const int tile_groups = kMoeWaves * moe_groups_per_wave<GATE_UP>();
     const int wave = threadIdx.x >> 6;
     const XLds xs{x_lds, P};
     const int k4 = P * 16;  // float4 per activation row
@@ -319,7 +323,8 @@ hipError_t launch_moe_grouped(const DeviceInfo& dev, const uint8_t* wgu, const u
         const int log2S = slots_log2(P);
         const int G = 64 >> log2S;
         const int groups = (rows_out + G - 1) / G;
-        const int tiles = (groups + kMoeWaves * kMoeGroupsPerWave - 1) / (kMoeWaves * kMoeGroupsPerWave);
+        const int tile_groups = kMoeWaves * (gate_up ? moe_groups_per_wave<true>() : moe_groups_per_wave<false>());
+        const int tiles = (groups + tile_groups - 1) / tile_groups;
         const int rows = staged_rows(P);
         const size_t lds = (size_t)rows * P * 256;
         const size_t expert_bytes = (size_t)rows_out * (size_t)(K / 32) * 34;
