@@ -10,13 +10,20 @@ from .q8_oracle import (  # noqa: F401
     QK8_0,
     Q8_0_BLOCK_BYTES,
     bf16_round_ref,
+    Q4_0_BLOCK_BYTES,
+    QK4_0,
+    dequantize_q4_0,
     dequantize_q8_0,
+    fused_gate_up_silu_q4_0_ref,
     fused_gate_up_silu_codes_ref,
     fused_gate_up_silu_q8act_ref,
     fused_gate_up_silu_ref,
     moe_mixture_ref,
     moe_ref,
+    parse_q4_0,
     parse_q8_0,
+    q4_0_linear_ref,
+    q4_0_row_bytes,
     quantize_act_q8_ref,
     q8_0_row_bytes,
     q8_linear_bf16_operands_ref,

@@ -88,6 +88,61 @@ def dequantize_q8_0(buf, n_rows: int, k: int) -> np.ndarray:
     return w.reshape(n_rows, k)
 
 
+# --------------------------------------------------------------------------- Q4_0
+#
+# The DGX Spark README (Features; Models) names Q4_0 among the formats read directly by
+# the quantized GEMV/GEMM (the Gemma 4 QAT checkpoints), and "14. Model families and
+# example applications" section 14.1 says the other ggml quant forms run their own
+# packed kernels; neither spells the layout out.  Reading: the GGUF Q4_0 block -- a
+# little-endian binary16 scale d, then 16 bytes; weight j (0..15) is the low nibble of
+# byte j and weight j + 16 its high nibble, both unsigned 0..15; w = d * (q - 8).  18
+# bytes per 32 weights, blocks along K, rows contiguous.
+
+QK4_0 = 32
+Q4_0_BLOCK_BYTES = 18
+_Q4_0_RECORD = np.dtype([("d", "<f2"), ("qs", "u1", (QK4_0 // 2,))])
+assert _Q4_0_RECORD.itemsize == Q4_0_BLOCK_BYTES
+
+
+def q4_0_row_bytes(k: int) -> int:
+    """Bytes in one Q4_0 row of length k."""
+    if k % QK4_0:
+        raise ValueError(f"K={k} is not a multiple of {QK4_0}")
+    return (k // QK4_0) * Q4_0_BLOCK_BYTES
+
+
+def parse_q4_0(buf, n_rows: int, k: int):
+    """Scales d (n_rows, k/32) and unsigned quants q (n_rows, k/32, 32), as float64."""
+    raw = np.frombuffer(memoryview(buf).cast("B"), dtype=np.uint8)
+    need = n_rows * q4_0_row_bytes(k)
+    if raw.size != need:
+        raise ValueError(f"Q4_0 buffer has {raw.size} bytes, expected {need}")
+    rec = raw.view(_Q4_0_RECORD).reshape(n_rows, k // QK4_0)
+    d = rec["d"].astype(np.float64)
+    qs = rec["qs"]
+    q = np.empty((n_rows, k // QK4_0, QK4_0), dtype=np.float64)
+    q[:, :, :16] = qs & 0x0F
+    q[:, :, 16:] = qs >> 4
+    return d, q
+
+
+def dequantize_q4_0(buf, n_rows: int, k: int) -> np.ndarray:
+    """W[n, 32*b + i] = d[n, b] * (q[n, b, i] - 8) in float64 (exact)."""
+    d, q = parse_q4_0(buf, n_rows, k)
+    return (d[:, :, None] * (q - 8.0)).reshape(n_rows, k)
+
+
+def q4_0_linear_ref(w_q4, n: int, k: int, x) -> np.ndarray:
+    """y[m, n] = sum_k x[m, k] * W[n, k] with W the dequantized Q4_0 matrix (float64)."""
+    return np.asarray(x, dtype=np.float64) @ dequantize_q4_0(w_q4, n, k).T
+
+
+def fused_gate_up_silu_q4_0_ref(w_gate_up_q4, f: int, k: int, x) -> np.ndarray:
+    """SiLU(x . W_gate^T) * (x . W_up^T) from one Q4_0 [2f][k] matrix, gate rows first."""
+    y = q4_0_linear_ref(w_gate_up_q4, 2 * f, k, x)
+    return silu_ref(y[:, :f]) * y[:, f:]
+
+
 # ------------------------------------------------------------------------- linear
 
 

@@ -148,3 +148,22 @@ def load_act_quant_cases(path=None):
         elif head == "dx":
             cur["dx"] = float(rest[0])
     return cases
+
+
+def load_q4_0_cases(path=None):
+    """Cases of tests/golden/q4_0_hand.txt: dicts with name, bytes (18 uint8), w (32 floats)."""
+    path = path or os.path.join(GOLDEN, "q4_0_hand.txt")
+    cases, cur = [], None
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        head, *rest = line.split()
+        if head == "case":
+            cur = {"name": rest[0]}
+            cases.append(cur)
+        elif head == "bytes":
+            cur["bytes"] = bytes(int(v, 16) for v in rest)
+        elif head == "w":
+            cur["w"] = [float(v) for v in rest]
+    return cases

@@ -16,7 +16,8 @@ import test_oracle_pins as pins
 SRC_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "q8_oracle.py")
 
 MUTANTS = {
-    "scale_big_endian": ('("d", "<f2")', '("d", ">f2")'),
+    "scale_big_endian": ('("d", "<f2"), ("qs", "i1"', '("d", ">f2"), ("qs", "i1"'),
+    "q4_0_scale_big_endian": ('("d", "<f2"), ("qs", "u1"', '("d", ">f2"), ("qs", "u1"'),
     "quants_unsigned": ('("qs", "i1", (QK8_0,))', '("qs", "u1", (QK8_0,))'),
     "dropped_scale": ("w = d[:, :, None] * q", "w = q + 0 * d[:, :, None]"),
     "reversed_k": ("return w.reshape(n_rows, k)", "return w.reshape(n_rows, k)[:, ::-1]"),
@@ -34,6 +35,12 @@ MUTANTS = {
     "top_p_full_softmax_cumulative": ("chosen[:kept].sum() / total < top_p", "chosen[:kept].sum() < top_p"),
     "top_p_normalize_by_topk_total": ("chosen[:kept] / chosen[:kept].sum() if normalize", "chosen[:kept] / total if normalize"),
     "top_p_ignores_knob": ("kept = 1\n", "kept = k\n"),
+    "q4_0_nibbles_interleaved": ("q[:, :, :16] = qs & 0x0F\n    q[:, :, 16:] = qs >> 4",
+                                 "q[:, :, 0::2] = qs & 0x0F\n    q[:, :, 1::2] = qs >> 4"),
+    "q4_0_nibbles_swapped": ("q[:, :, :16] = qs & 0x0F\n    q[:, :, 16:] = qs >> 4",
+                             "q[:, :, :16] = qs >> 4\n    q[:, :, 16:] = qs & 0x0F"),
+    "q4_0_no_offset": ("(d[:, :, None] * (q - 8.0))", "(d[:, :, None] * q)"),
+    "q4_0_signed_nibbles": ("(d[:, :, None] * (q - 8.0))", "(d[:, :, None] * np.where(q > 7, q - 16.0, q))"),
     "act_round_floor": ("q = np.clip(np.rint(prod), -127, 127)", "q = np.clip(np.floor(prod), -127, 127)"),
     "act_round_half_away": ("q = np.clip(np.rint(prod), -127, 127)",
                             "q = np.clip(np.trunc(prod + np.copysign(np.float32(0.5), prod)), -127, 127)"),

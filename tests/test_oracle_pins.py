@@ -26,11 +26,13 @@ import scipy.special
 
 import oracle as O
 import workloads as wl
-from golden_io import half_bits_to_fraction, load_act_quant_cases, load_linear_cases, load_swiglu_router_cases
+from golden_io import (half_bits_to_fraction, load_act_quant_cases, load_linear_cases, load_q4_0_cases,
+                       load_swiglu_router_cases)
 
 LINEAR_CASES = load_linear_cases()
 FUSED_CASES, ROUTE_CASES = load_swiglu_router_cases()
 ACT_CASES = load_act_quant_cases()
+Q4_CASES = load_q4_0_cases()
 
 
 # ------------------------------------------------------------------ checks
@@ -423,12 +425,55 @@ def check_top_p_properties(o):
     np.testing.assert_allclose(y, np.concatenate([y0, y1]), rtol=1e-14)
 
 
+# ------------------------------------------------------------------------- Q4_0
+
+
+def check_q4_0_hand(o):
+    """Hand-derived blocks (tests/golden/q4_0_hand.txt): nibble order, the -8 offset, the
+    sign and size of d; and a linear over those blocks against the hand weights."""
+    for c in Q4_CASES:
+        w = o.dequantize_q4_0(c["bytes"], 1, 32)
+        assert w[0].tolist() == c["w"], c["name"]
+    raw = b"".join(c["bytes"] for c in Q4_CASES)       # 4 rows of one block each
+    x = wl.activations(91, 3, 32)
+    wh = np.array([c["w"] for c in Q4_CASES])
+    np.testing.assert_allclose(o.q4_0_linear_ref(raw, len(Q4_CASES), 32, x), x.astype(np.float64) @ wh.T,
+                               rtol=1e-13)
+
+
+def check_q4_0_properties(o):
+    """Linearity in d, zero d gives zero, nibble 8 everywhere gives zero, Fraction brute
+    force on a small case, and the fused split."""
+    n, k = 5, 256
+    wb, q, d = wl.q4_0_weight(92, n, k)
+    x = wl.activations(93, 2, k)
+    y = o.q4_0_linear_ref(wb, n, k, x)
+    y2 = o.q4_0_linear_ref(wl.pack_q4_0(q, (d.astype(np.float32) * 2).astype(np.float16)), n, k, x)
+    np.testing.assert_allclose(y2, 2 * y, rtol=1e-13)
+    assert np.all(o.q4_0_linear_ref(wl.pack_q4_0(q, np.zeros_like(d)), n, k, x) == 0)
+    assert np.all(o.q4_0_linear_ref(wl.pack_q4_0(np.full_like(q, 8), d), n, k, x) == 0)
+    # brute force: one row, one block pair, every product in rationals
+    wb1, q1, d1 = wl.q4_0_weight(94, 1, 64)
+    x1 = wl.activations(95, 1, 64)
+    exact = Fraction(0)
+    for kk in range(64):
+        dd = half_bits_to_fraction(int(d1.view(np.uint16)[0, kk // 32]))
+        exact += dd * (int(q1[0, kk]) - 8) * Fraction(float(x1[0, kk]))
+    assert abs(o.q4_0_linear_ref(wb1, 1, 64, x1)[0, 0] - float(exact)) <= 1e-12 * max(1.0, abs(float(exact)))
+    f = 3
+    wg, _, _ = wl.q4_0_weight(96, 2 * f, k)
+    h = o.fused_gate_up_silu_q4_0_ref(wg, f, k, x)
+    yy = o.q4_0_linear_ref(wg, 2 * f, k, x)
+    np.testing.assert_allclose(h, scipy.special.expit(yy[:, :f]) * yy[:, :f] * yy[:, f:], rtol=1e-12, atol=1e-15)
+
+
 ALL_CHECKS = [
     check_hand_linear, check_hand_fused, check_hand_route, check_bruteforce_linear,
     check_dequant_exact, check_linearity, check_zero_scale, check_one_hot, check_silu,
     check_fused_split, check_route_invariants, check_moe, check_moe_bruteforce,
     check_act_quant_hand, check_act_quant_props, check_q8act_linear, check_q8act_fused,
     check_top_p_exact_boundaries, check_top_p_hand_and_identity, check_top_p_properties,
+    check_q4_0_hand, check_q4_0_properties,
 ]
 
 

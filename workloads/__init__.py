@@ -51,6 +51,28 @@ def row_bytes(k: int) -> int:
     return (k // QK) * BLOCK_BYTES
 
 
+Q4_BLOCK_BYTES = 18
+
+
+def pack_q4_0(q: np.ndarray, d_f16: np.ndarray) -> np.ndarray:
+    """Lay unsigned 4-bit quants [N][K] (values 0..15) and binary16 scales [N][K/32] out as
+    GGUF Q4_0 bytes: per block the scale, then byte j = q[j] | q[j + 16] << 4.
+
+    Returns a flat uint8 array of N*(K/32)*18 bytes.
+    """
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    d_f16 = np.ascontiguousarray(d_f16, dtype=np.float16)
+    n, k = q.shape
+    nb = k // QK
+    if k % QK or d_f16.shape != (n, nb) or q.max(initial=0) > 15:
+        raise ValueError(f"bad shapes or values q {q.shape} d {d_f16.shape}")
+    qb = q.reshape(n, nb, QK)
+    out = np.empty((n, nb, Q4_BLOCK_BYTES), dtype=np.uint8)
+    out[:, :, 0:2] = d_f16.astype("<f2").view(np.uint8).reshape(n, nb, 2)
+    out[:, :, 2:] = qb[:, :, :16] | (qb[:, :, 16:] << 4)
+    return out.reshape(-1)
+
+
 # ------------------------------------------------------------------ generators
 
 
@@ -76,6 +98,22 @@ def q8_weight_exact(seed: int, n: int, k: int):
     q = rq.integers(-127, 128, size=(n, k), dtype=np.int8)
     d = np.where(rd.integers(0, 2, size=(n, k // QK)) == 0, 2.0 ** -7, 2.0 ** -8).astype(np.float16)
     return pack_blocks(q, d), q, d
+
+
+def q4_0_weight(seed: int, n: int, k: int, d_lo: float = 1e-3, d_hi: float = 2e-2):
+    """Random Q4_0 matrix [n][k]: returns (bytes uint8, q uint8 [n][k] in 0..15, d float16)."""
+    rq, rd = _rngs(seed, 2)
+    q = rq.integers(0, 16, size=(n, k), dtype=np.uint8)
+    d = rd.uniform(d_lo, d_hi, size=(n, k // QK)).astype(np.float16)
+    return pack_q4_0(q, d), q, d
+
+
+def q4_0_weight_exact(seed: int, n: int, k: int):
+    """Q4_0 matrix for exact-arithmetic checks: d in {2^-7, 2^-8} (see q8_weight_exact)."""
+    rq, rd = _rngs(seed, 2)
+    q = rq.integers(0, 16, size=(n, k), dtype=np.uint8)
+    d = np.where(rd.integers(0, 2, size=(n, k // QK)) == 0, 2.0 ** -7, 2.0 ** -8).astype(np.float16)
+    return pack_q4_0(q, d), q, d
 
 
 def activations(seed: int, m: int, k: int) -> np.ndarray:
