@@ -11,6 +11,8 @@ from ._binding import (  # noqa: F401
     abi_version,
     lib,
     moe_route_topk,
+    q4_0_linear,
+    q4_0_linear_fused_gate_up_silu,
     moe_route_workspace_bytes,
     q8_linear,
     q8_linear_fused_gate_up_silu,

@@ -39,6 +39,10 @@ lib.q8_linear.restype = ctypes.c_int
 lib.q8_linear.argtypes = [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp]
 lib.q8_linear_fused_gate_up_silu.restype = ctypes.c_int
 lib.q8_linear_fused_gate_up_silu.argtypes = [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp]
+lib.q4_0_linear.restype = ctypes.c_int
+lib.q4_0_linear.argtypes = [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp]
+lib.q4_0_linear_fused_gate_up_silu.restype = ctypes.c_int
+lib.q4_0_linear_fused_gate_up_silu.argtypes = [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp]
 lib.q8_quantize_act.restype = ctypes.c_int
 lib.q8_quantize_act.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp]
 lib.q8_linear_q8act.restype = ctypes.c_int
@@ -130,6 +134,37 @@ def q8_linear_fused_gate_up_silu(w, f: int, k: int, x, out=None):
     _dev(out, torch.float32, "out")
     check(lib.q8_linear_fused_gate_up_silu(w.data_ptr(), f, k, x.data_ptr(), m, _ld(x, k), out.data_ptr(),
                                            _ld(out, f), _stream(x)))
+    return out
+
+
+def q4_0_linear(w, n: int, k: int, x, out=None):
+    """y = x . W^T for a GGUF Q4_0 weight W [n][k] (uint8 bytes) and float32 x [m][k]."""
+    torch = _torch()
+    _dev(w, torch.uint8, "w")
+    _dev(x, torch.float32, "x")
+    if x.dim() != 2 or x.shape[1] != k or (x.numel() and x.stride(1) != 1):
+        raise ValueError(f"x must be [m][{k}] with contiguous rows")
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _dev(out, torch.float32, "out")
+    check(lib.q4_0_linear(w.data_ptr(), n, k, x.data_ptr(), m, _ld(x, k), out.data_ptr(), _ld(out, n), _stream(x)))
+    return out
+
+
+def q4_0_linear_fused_gate_up_silu(w, f: int, k: int, x, out=None):
+    """h = SiLU(x . W_gate^T) * (x . W_up^T); W is GGUF Q4_0 [2f][k], gate rows first."""
+    torch = _torch()
+    _dev(w, torch.uint8, "w")
+    _dev(x, torch.float32, "x")
+    if x.dim() != 2 or x.shape[1] != k or (x.numel() and x.stride(1) != 1):
+        raise ValueError(f"x must be [m][{k}] with contiguous rows")
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, f), dtype=torch.float32, device=x.device)
+    _dev(out, torch.float32, "out")
+    check(lib.q4_0_linear_fused_gate_up_silu(w.data_ptr(), f, k, x.data_ptr(), m, _ld(x, k), out.data_ptr(),
+                                             _ld(out, f), _stream(x)))
     return out
 
 

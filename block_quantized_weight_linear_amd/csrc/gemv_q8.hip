@@ -160,6 +160,63 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, WPE
     });
 }
 
+// Block-pair formats of the rows kernel.  A "pair" is two consecutive blocks (64
+// weights); rows are 16-byte aligned, so pairs start on dword boundaries.  weights<HALF>
+// gives the 4 weights, as exact float32, of inputs 4*cc .. 4*cc+3 of block HALF.
+struct FmtQ8_0 {  // 68 bytes: [d0 | 32 q] [d1 | 32 q]
+    static constexpr int kPairBytes = 68, kDwords = 17, kLoads = 5;
+    static __device__ __forceinline__ void load(const uint8_t* p, uint32_t (&w)[kDwords]) { load_pair(p, w); }
+    template <int HALF>
+    static __device__ __forceinline__ void weights(const uint32_t (&w)[kDwords], int cc, float (&wf)[4]) {
+        if constexpr (HALF == 0) {  // block 0: scale in dword 0 (low half), quants at bytes 2..33
+            const float d = half_lo(w[0]);
+            wf[0] = sbyte<2>(w[cc]) * d;
+            wf[1] = sbyte<3>(w[cc]) * d;
+            wf[2] = sbyte<0>(w[cc + 1]) * d;
+            wf[3] = sbyte<1>(w[cc + 1]) * d;
+        } else {  // block 1: scale in dword 8 (high half), quants in dwords 9..16
+            const float d = half_hi(w[8]);
+            const uint32_t v = w[9 + cc];
+            wf[0] = sbyte<0>(v) * d;
+            wf[1] = sbyte<1>(v) * d;
+            wf[2] = sbyte<2>(v) * d;
+            wf[3] = sbyte<3>(v) * d;
+        }
+    }
+};
+
+// GGUF Q4_0: 36 bytes a pair, [d0 | 16 bytes] [d1 | 16 bytes]; weight j < 16 of a block is
+// the low nibble of its byte j, weight j + 16 the high nibble; w = d * (nibble - 8), exact
+// in float32 (a 4-bit integer times an 11-bit scale).
+struct FmtQ4_0 {
+    static constexpr int kPairBytes = 36, kDwords = 9, kLoads = 3;
+    static __device__ __forceinline__ void load(const uint8_t* p, uint32_t (&w)[kDwords]) {
+        const u32x4_a4 a = *reinterpret_cast<const u32x4_a4*>(p);
+        const u32x4_a4 b = *reinterpret_cast<const u32x4_a4*>(p + 16);
+        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+        w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+        w[8] = *reinterpret_cast<const uint32_t*>(p + 32);
+    }
+    template <int HALF>
+    static __device__ __forceinline__ void weights(const uint32_t (&w)[kDwords], int cc, float (&wf)[4]) {
+        const int c4 = cc & 3;  // quant dword of the block: bytes 4*c4 .. 4*c4+3
+        float d;
+        uint32_t v;
+        if constexpr (HALF == 0) {  // scale = low half of dword 0, quant bytes at 2..17
+            d = half_lo(w[0]);
+            v = __builtin_amdgcn_alignbyte(w[c4 + 1], w[c4], 2);
+        } else {  // scale = high half of dword 4, quant bytes in dwords 5..8
+            d = half_hi(w[4]);
+            v = w[5 + c4];
+        }
+        const uint32_t nib = (cc < 4 ? v : v >> 4) & 0x0F0F0F0Fu;  // inputs 4cc..: low nibbles, then high
+        wf[0] = ((float)(nib & 0xFFu) - 8.0f) * d;
+        wf[1] = ((float)((nib >> 8) & 0xFFu) - 8.0f) * d;
+        wf[2] = ((float)((nib >> 16) & 0xFFu) - 8.0f) * d;
+        wf[3] = ((float)(nib >> 24) - 8.0f) * d;
+    }
+};
+
 // Several activation rows (1 <= M <= 8 per launch; the class used for 2..255 rows).  A
 // block tile is 8*R rows (fused: R gate/up row pairs) over the whole K, worked on by two
 // groups of 2 waves: group h takes the chunks h, h+2, h+4, ... of 16 pairs (1024 inputs)
@@ -178,7 +235,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, WPE
 // to the same row in any other such call.
 constexpr int kRowsThreads = 256;
 
-template <int M, int R, bool SILU>
+template <class Fmt, int M, int R, bool SILU>
 __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(1, 2))) void gemv_rows_kernel(
     const uint8_t* __restrict__ w, int n_out, int P, const float* __restrict__ x, int ldx, float* __restrict__ y,
     int ldy) {
@@ -197,7 +254,7 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(1,
     const int lane = tid & 63;
     const int j = lane & 15;
     const int slot = (wv & 1) * 4 + (lane >> 4);  // row slot within the group, 0..7
-    const size_t row_bytes = (size_t)P * 68;
+    const size_t row_bytes = (size_t)P * Fmt::kPairBytes;
     const int nch = (P + 15) >> 4;
     const int steps = (nch + 1) >> 1;
     const int tiles = (n_out + 8 * R - 1) / (8 * R);
@@ -218,14 +275,14 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(1,
         const int ch = h + 2 * st;
         return ch < nch ? ch : nch - 1;
     };
-    auto load_w = [&](int i, int st, uint32_t(&wr)[RR][17]) __attribute__((always_inline)) {
+    auto load_w = [&](int i, int st, uint32_t(&wr)[RR][Fmt::kDwords]) __attribute__((always_inline)) {
         const int p = 16 * chunk_of(st) + j;
         const int pc = p < P ? p : P - 1;  // past the row: a pair of the same row (unused)
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int n = out_row(i, r);
-            load_pair(w + (size_t)n * row_bytes + 68 * (size_t)pc, wr[r]);
-            if constexpr (SILU) load_pair(w + (size_t)(n + n_out) * row_bytes + 68 * (size_t)pc, wr[R + r]);
+            Fmt::load(w + (size_t)n * row_bytes + Fmt::kPairBytes * (size_t)pc, wr[r]);
+            if constexpr (SILU) Fmt::load(w + (size_t)(n + n_out) * row_bytes + Fmt::kPairBytes * (size_t)pc, wr[R + r]);
         }
     };
     // Half `half` of the group's activation chunk for step st: 2*M wave-wide copies of 64
@@ -245,7 +302,7 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(1,
             lds_copy16(src, buf + 64 * q);
         }
     };
-    constexpr int kWLoads = 5 * RR;  // loads per weight step (load_pair = 5 loads a row)
+    constexpr int kWLoads = Fmt::kLoads * RR;  // loads per weight step
 
     float acc[RR][M];
 #pragma unroll
@@ -254,32 +311,16 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(1,
         for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
 
     // Quant dwords 8*HALF .. 8*HALF + 7 of the lane's pair against the half chunk in xs.
-    auto compute = [&](auto half, int st, const uint32_t(&wc)[RR][17], const float4* xs)
+    auto compute = [&](auto half, int st, const uint32_t(&wc)[RR][Fmt::kDwords], const float4* xs)
                        __attribute__((always_inline)) {
         constexpr int HALF = decltype(half)::value;
         const int ch = h + 2 * st;
         if (ch < nch && 16 * ch + j < P) {
 #pragma unroll
             for (int cc = 0; cc < 8; ++cc) {
-                const int c = 8 * HALF + cc;
                 float wf[RR][4];
 #pragma unroll
-                for (int r = 0; r < RR; ++r) {
-                    if constexpr (HALF == 0) {  // block 0: scale in dword 0 (low half), quants at bytes 2..33
-                        const float d = half_lo(wc[r][0]);
-                        wf[r][0] = sbyte<2>(wc[r][c]) * d;
-                        wf[r][1] = sbyte<3>(wc[r][c]) * d;
-                        wf[r][2] = sbyte<0>(wc[r][c + 1]) * d;
-                        wf[r][3] = sbyte<1>(wc[r][c + 1]) * d;
-                    } else {  // block 1: scale in dword 8 (high half), quants in dwords 9..16
-                        const float d = half_hi(wc[r][8]);
-                        const uint32_t v = wc[r][c + 1];
-                        wf[r][0] = sbyte<0>(v) * d;
-                        wf[r][1] = sbyte<1>(v) * d;
-                        wf[r][2] = sbyte<2>(v) * d;
-                        wf[r][3] = sbyte<3>(v) * d;
-                    }
-                }
+                for (int r = 0; r < RR; ++r) Fmt::template weights<HALF>(wc[r], cc, wf[r]);
 #pragma unroll
                 for (int m = 0; m < M; ++m) {
                     const float4 xv = xs[(m * 8 + cc) * 16 + j];
@@ -335,7 +376,7 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(1,
             for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
     };
 
-    uint32_t wc[RR][17], wn[RR][17];
+    uint32_t wc[RR][Fmt::kDwords], wn[RR][Fmt::kDwords];
     stage_x(0, 0, xa[h]);
     load_w(0, 0, wc);
     __builtin_amdgcn_sched_barrier(0);  // the loads stay above the wait
@@ -373,7 +414,7 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(1,
 #pragma unroll
             for (int r = 0; r < RR; ++r)
 #pragma unroll
-                for (int q = 0; q < 17; ++q) wc[r][q] = wn[r][q];
+                for (int q = 0; q < Fmt::kDwords; ++q) wc[r][q] = wn[r][q];
             __syncthreads();
         }
         i = ni;
@@ -448,12 +489,12 @@ bool try_xreg_m(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, int l
     }
 }
 
-// Blocks of gemv_rows_kernel<M, R, SILU> resident per CU (queried once per kernel).
-template <int M, int R, bool SILU>
+// Blocks of gemv_rows_kernel<Fmt, M, R, SILU> resident per CU (queried once per kernel).
+template <class Fmt, int M, int R, bool SILU>
 int rows_per_cu() {
     static const int per_cu = [] {
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemv_rows_kernel<M, R, SILU>, kRowsThreads, 0) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemv_rows_kernel<Fmt, M, R, SILU>, kRowsThreads, 0) !=
                 hipSuccess ||
             n < 1)
             n = 1;
@@ -462,15 +503,15 @@ int rows_per_cu() {
     return per_cu;
 }
 
-template <int M, int R, bool SILU>
+template <class Fmt, int M, int R, bool SILU>
 hipError_t launch_rows_r(const DeviceInfo& dev, int n_out, int P, const uint8_t* w, const float* x, int ldx, float* y,
                          int ldy, hipStream_t stream) {
     // persistent grid: one block per resident slot (at most one per tile); each walks
     // its tiles at a stride of the grid
     const int tiles = (n_out + 8 * R - 1) / (8 * R);
-    const int64_t slots = (int64_t)dev.cu_count * rows_per_cu<M, R, SILU>();
+    const int64_t slots = (int64_t)dev.cu_count * rows_per_cu<Fmt, M, R, SILU>();
     const int blocks = (int)(tiles < slots ? tiles : slots);
-    hipLaunchKernelGGL((gemv_rows_kernel<M, R, SILU>), dim3(blocks), dim3(kRowsThreads), 0, stream, w, n_out, P, x,
+    hipLaunchKernelGGL((gemv_rows_kernel<Fmt, M, R, SILU>), dim3(blocks), dim3(kRowsThreads), 0, stream, w, n_out, P, x,
                        ldx, y, ldy);
     return hipGetLastError();
 }
@@ -483,28 +524,28 @@ inline double round_fill(int64_t tiles, int64_t slots) {
     return (double)tiles / (double)(per * (used > 0 ? slots : 1));
 }
 
-template <int M, bool SILU>
+template <class Fmt, int M, bool SILU>
 hipError_t launch_rows(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, const float* x, int ldx, float* y,
                        int ldy, hipStream_t stream) {
     // R rows (row pairs) per lane: more rows per lane share each activation read, fewer
     // spread the tiles more evenly.  Take the largest R within 5% of the best fill.
     const int64_t cus = dev.cu_count;
-    const double f1 = round_fill((n_out + 7) / 8, cus * rows_per_cu<M, 1, SILU>());
-    const double f2 = round_fill((n_out + 15) / 16, cus * rows_per_cu<M, 2, SILU>());
+    const double f1 = round_fill((n_out + 7) / 8, cus * rows_per_cu<Fmt, M, 1, SILU>());
+    const double f2 = round_fill((n_out + 15) / 16, cus * rows_per_cu<Fmt, M, 2, SILU>());
     double f4 = 0.0;
-    if constexpr (!SILU) f4 = round_fill((n_out + 31) / 32, cus * rows_per_cu<M, 4, SILU>());
+    if constexpr (!SILU) f4 = round_fill((n_out + 31) / 32, cus * rows_per_cu<Fmt, M, 4, SILU>());
     const double best = f1 > f2 ? (f1 > f4 ? f1 : f4) : (f2 > f4 ? f2 : f4);
     if constexpr (!SILU) {
-        if (f4 >= 0.95 * best) return launch_rows_r<M, 4, SILU>(dev, n_out, P, w, x, ldx, y, ldy, stream);
+        if (f4 >= 0.95 * best) return launch_rows_r<Fmt, M, 4, SILU>(dev, n_out, P, w, x, ldx, y, ldy, stream);
     }
-    if (f2 >= 0.95 * best) return launch_rows_r<M, 2, SILU>(dev, n_out, P, w, x, ldx, y, ldy, stream);
-    return launch_rows_r<M, 1, SILU>(dev, n_out, P, w, x, ldx, y, ldy, stream);
+    if (f2 >= 0.95 * best) return launch_rows_r<Fmt, M, 2, SILU>(dev, n_out, P, w, x, ldx, y, ldy, stream);
+    return launch_rows_r<Fmt, M, 1, SILU>(dev, n_out, P, w, x, ldx, y, ldy, stream);
 }
 
 template <int M, int R>
 hipError_t launch_m(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, int log2S, const float* x, int ldx,
                     float* y, int ldy, hipStream_t stream) {
-    return launch_rows<M, R == 2>(dev, w, n_out, P, x, ldx, y, ldy, stream);
+    return launch_rows<FmtQ8_0, M, R == 2>(dev, w, n_out, P, x, ldx, y, ldy, stream);
 }
 
 template <int R>
@@ -519,7 +560,33 @@ hipError_t launch_r(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, i
     }
 }
 
+template <bool SILU>
+hipError_t launch_q4_0_m(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, const float* x, int ldx, int m,
+                         float* y, int ldy, hipStream_t stream) {
+    switch (m) {
+#define Q4_CASE(MM) \
+    case MM: return launch_rows<FmtQ4_0, MM, SILU>(dev, w, n_out, P, x, ldx, y, ldy, stream);
+        Q4_CASE(1) Q4_CASE(2) Q4_CASE(3) Q4_CASE(4) Q4_CASE(5) Q4_CASE(6) Q4_CASE(7) Q4_CASE(8)
+#undef Q4_CASE
+        default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_gemv_q4_0(const DeviceInfo& dev, const uint8_t* w, int64_t n_out, int64_t k, bool silu_pairs,
+                            const float* x, int64_t m, int64_t ldx, float* y, int64_t ldy, hipStream_t stream) {
+    const int P = (int)(k / 64);
+    for (int64_t m0 = 0; m0 < m; m0 += 8) {
+        const int mm = (int)((m - m0) < 8 ? (m - m0) : 8);
+        const float* xc = x + m0 * ldx;
+        float* yc = y + m0 * ldy;
+        hipError_t e = silu_pairs ? launch_q4_0_m<true>(dev, w, (int)n_out, P, xc, (int)ldx, mm, yc, (int)ldy, stream)
+                                  : launch_q4_0_m<false>(dev, w, (int)n_out, P, xc, (int)ldx, mm, yc, (int)ldy, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
 
 hipError_t launch_gemv_q8(const DeviceInfo& dev, const uint8_t* w, int64_t n_out, int64_t k, bool silu_pairs,
                           const float* x, int64_t m, int64_t ldx, float* y, int64_t ldy, hipStream_t stream) {

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define Q8_ABI_VERSION 4
+#define Q8_ABI_VERSION 5
 
 typedef enum q8_status {
     Q8_OK = 0,
@@ -99,6 +99,27 @@ q8_status q8_linear(const void* w_q8, int64_t n, int64_t k,
 q8_status q8_linear_fused_gate_up_silu(const void* w_gate_up_q8, int64_t f, int64_t k,
                                        const float* x, int64_t m, int64_t ldx,
                                        float* h, int64_t ldh, void* stream);
+
+/*
+ * GGUF Q4_0 weights (the DGX Spark README, Features and Models: Q4_0 is read directly by
+ * the quantized GEMV; section 14.1: the other ggml quant forms run their own packed
+ * kernels).  The layout is the ggml one (the pages name the format only): per block of
+ * 32 weights a little-endian binary16 scale d, then 16 bytes; weight j < 16 is the low
+ * nibble of byte j, weight j + 16 the high nibble; w = d * (nibble - 8).  18 bytes per
+ * block, rows of k/32 blocks back to back.
+ *   q4_0_linear                     : y[m][n] = x . W^T,  W = Q4_0 [n][k]
+ *   q4_0_linear_fused_gate_up_silu  : h = SiLU(x . W_gate^T) * (x . W_up^T), W = Q4_0 [2f][k]
+ * Arguments, rules and errors as for q8_linear / q8_linear_fused_gate_up_silu.  Every m
+ * runs on the float32 rows kernel in 8-row launches (weights w = d*(q-8) exact in
+ * float32, one fma per weight and row, the per-output order depends only on k: every row
+ * is bit-identical whatever m is).
+ */
+q8_status q4_0_linear(const void* w_q4_0, int64_t n, int64_t k,
+                      const float* x, int64_t m, int64_t ldx,
+                      float* y, int64_t ldy, void* stream);
+q8_status q4_0_linear_fused_gate_up_silu(const void* w_gate_up_q4_0, int64_t f, int64_t k,
+                                         const float* x, int64_t m, int64_t ldx,
+                                         float* h, int64_t ldh, void* stream);
 
 /*
  * Integer q8 x q8 path.  The DGX Spark README (Features; Architecture) names GEMV kernels

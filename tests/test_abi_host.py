@@ -34,14 +34,15 @@ def test_header_declares_the_four_calls():
     for n in ("q8_linear", "q8_linear_fused_gate_up_silu", "moe_route_topk", "q8_moe_grouped_linear",
               "q8_moe_workspace_bytes", "q8_status_string", "q8_last_error", "q8_abi_version",
               "q8_quantize_act", "q8_linear_q8act", "q8_linear_fused_gate_up_silu_q8act",
-              "moe_route_topk_top_p", "moe_route_topk_ws", "moe_route_workspace_bytes"):
+              "moe_route_topk_top_p", "moe_route_topk_ws", "moe_route_workspace_bytes",
+              "q4_0_linear", "q4_0_linear_fused_gate_up_silu"):
         assert n in names, names
 
 
 def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert q8.abi_version() == 4
+    assert q8.abi_version() == 5
 
 
 def test_status_strings():
@@ -50,13 +51,20 @@ def test_status_strings():
     assert lib.q8_status_string(99) == b"unknown status"
 
 
-def _lin(w=FAKE, n=64, k=256, x=FAKE, m=1, ldx=256, y=FAKE, ldy=64, fused=False):
-    fn = lib.q8_linear_fused_gate_up_silu if fused else lib.q8_linear
+def _lin_base(w=FAKE, n=64, k=256, x=FAKE, m=1, ldx=256, y=FAKE, ldy=64, fused=False, q4=False):
+    if q4:
+        fn = lib.q4_0_linear_fused_gate_up_silu if fused else lib.q4_0_linear
+    else:
+        fn = lib.q8_linear_fused_gate_up_silu if fused else lib.q8_linear
     return fn(w, n, k, x, m, ldx, y, ldy, None)
 
 
+@pytest.mark.parametrize("q4", [False, True])
 @pytest.mark.parametrize("fused", [False, True])
-def test_linear_argument_errors(fused):
+def test_linear_argument_errors(fused, q4):
+    def _lin(**kw):
+        return _lin_base(q4=q4, **kw)
+
     assert _lin(k=0, fused=fused) == ERR_SHAPE
     assert _lin(k=32, fused=fused) == ERR_SHAPE          # a Q8_0 multiple but not of 256
     assert _lin(k=384, fused=fused) == ERR_SHAPE
@@ -73,6 +81,9 @@ def test_linear_argument_errors(fused):
     assert _lin(y=FAKE + 2, fused=fused) == ERR_ALIGN
     msg = lib.q8_last_error().decode()
     assert "aligned" in msg
+
+
+_lin = _lin_base
 
 
 def _lin8(w=FAKE, n=64, k=256, xq=FAKE, xd=FAKE, m=1, y=FAKE, ldy=64, fused=False):

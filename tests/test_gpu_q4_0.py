@@ -1,0 +1,117 @@
+"""GPU parity of q4_0_linear and q4_0_linear_fused_gate_up_silu (GGUF Q4_0 weights)
+against the CPU oracle: small shapes element by element (tiles, ragged chunks, row
+counts that are not a launch size), the Gemma 4 12B FFN shape on sampled outputs, hand
+blocks, exact-arithmetic inputs bit for bit, batch invariance."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from gpu_util import assert_close, say, sample_rows, to_dev, torch_dev
+
+pytestmark = pytest.mark.gpu
+
+Q4_BLOCK = 18
+
+
+@pytest.fixture(scope="module")
+def q8():
+    torch, dev = torch_dev()
+    import block_quantized_weight_linear_amd as q8mod
+    return q8mod, torch, dev
+
+
+def q4_rows(wbytes, k, rows):
+    rb = (k // 32) * Q4_BLOCK
+    return np.ascontiguousarray(wbytes.reshape(-1, rb)[np.asarray(rows)]).reshape(-1)
+
+
+SMALL = [(1, 256), (3, 256), (37, 512), (257, 768), (1000, 1024), (513, 3072), (129, 3840), (77, 12288), (64, 2048)]
+
+
+@pytest.mark.parametrize("n,k", SMALL)
+@pytest.mark.parametrize("m", [1, 2, 3, 8, 9, 17])
+def test_q4_0_linear_small_vs_oracle(q8, n, k, m):
+    lib, torch, dev = q8
+    wb, _, _ = wl.q4_0_weight(1100 + n + k, n, k)
+    x = wl.activations(1200 + m + k, m, k)
+    say(f"q4_0_linear n={n} k={k} m={m}")
+    y = lib.q4_0_linear(to_dev(wb, dev), n, k, to_dev(x, dev)).cpu().numpy()
+    assert_close(y, oracle.q4_0_linear_ref(wb, n, k, x), f"q4_0 n={n} k={k} m={m}")
+
+
+@pytest.mark.parametrize("f,k", [(1, 256), (5, 512), (300, 1024), (129, 3840), (64, 768)])
+@pytest.mark.parametrize("m", [1, 4, 8, 11])
+def test_q4_0_fused_small_vs_oracle(q8, f, k, m):
+    lib, torch, dev = q8
+    wb, _, _ = wl.q4_0_weight(1300 + f + k, 2 * f, k)
+    x = wl.activations(1400 + m, m, k)
+    say(f"q4_0 fused f={f} k={k} m={m}")
+    h = lib.q4_0_linear_fused_gate_up_silu(to_dev(wb, dev), f, k, to_dev(x, dev)).cpu().numpy()
+    assert_close(h, oracle.fused_gate_up_silu_q4_0_ref(wb, f, k, x), f"q4_0 fused f={f} k={k} m={m}")
+
+
+def test_q4_0_hand_blocks(q8):
+    """The hand-derived blocks, each the first block of a K = 256 row padded with zero
+    blocks (d = 0), against activations chosen so that every product is exact."""
+    from golden_io import load_q4_0_cases
+    lib, torch, dev = q8
+    cases = load_q4_0_cases()
+    k = 256
+    zero = bytes(Q4_BLOCK)
+    raw = np.frombuffer(b"".join(c["bytes"] + zero * 7 for c in cases), dtype=np.uint8)
+    x = np.zeros((2, k), np.float32)
+    x[0, :32] = 1.0
+    x[1, :32] = np.arange(32) % 5 - 2
+    y = lib.q4_0_linear(to_dev(raw, dev), len(cases), k, to_dev(x, dev)).cpu().numpy()
+    wh = np.array([c["w"] for c in cases])
+    assert np.array_equal(y.astype(np.float64), x[:, :32].astype(np.float64) @ wh.T)
+
+
+@pytest.mark.parametrize("n,k,m", [(4096, 1024, 1), (6144, 3840, 8), (999, 256, 33), (2048, 12288, 3)])
+def test_q4_0_exact_arithmetic_bit_identical(q8, n, k, m):
+    """Scales 2^-7 / 2^-8, activations in {-2..2}: every float32 partial sum is exact."""
+    lib, torch, dev = q8
+    wb, _, _ = wl.q4_0_weight_exact(1500 + n, n, k)
+    x = wl.activations_exact(1600 + m, m, k)
+    say(f"q4_0 exact n={n} k={k} m={m}")
+    y = lib.q4_0_linear(to_dev(wb, dev), n, k, to_dev(x, dev)).cpu().numpy()
+    assert np.array_equal(y.astype(np.float64), oracle.q4_0_linear_ref(wb, n, k, x))
+
+
+def test_q4_0_gemma4_12b_ffn_sampled(q8):
+    """Gemma 4 12B FFN (hidden 3840, intermediate 15360): fused gate_up 30720 x 3840 and
+    down 3840 x 15360 at m = 1 and 8, sampled outputs against the oracle."""
+    lib, torch, dev = q8
+    hid, ff = 3840, 15360
+    wg, _, _ = wl.q4_0_weight(1700, 2 * ff, hid)
+    wd, _, _ = wl.q4_0_weight(1701, hid, ff)
+    wgd, wdd = to_dev(wg, dev), to_dev(wd, dev)
+    pick_g = sample_rows(ff, 96, seed=5)
+    pick_d = sample_rows(hid, 96, seed=6)
+    for m in (1, 8):
+        x = wl.activations(1702 + m, m, hid)
+        say(f"gemma-4-12b q4_0 gate_up m={m}")
+        h = lib.q4_0_linear_fused_gate_up_silu(wgd, ff, hid, to_dev(x, dev)).cpu().numpy()
+        sub = np.concatenate([q4_rows(wg, hid, pick_g), q4_rows(wg, hid, pick_g + ff)])
+        assert_close(h[:, pick_g], oracle.fused_gate_up_silu_q4_0_ref(sub, len(pick_g), hid, x), f"gate_up m={m}")
+        xh = wl.activations(1704 + m, m, ff)
+        y = lib.q4_0_linear(wdd, hid, ff, to_dev(xh, dev)).cpu().numpy()
+        assert_close(y[:, pick_d], oracle.q4_0_linear_ref(q4_rows(wd, ff, pick_d), len(pick_d), ff, xh), f"down m={m}")
+
+
+@pytest.mark.parametrize("n,k", [(4096, 1024), (777, 3840)])
+def test_q4_0_batch_invariance(q8, n, k):
+    """One kernel class for every m: any row of any call is bit-identical to the same row
+    of any other call, one-row calls included; run to run identical."""
+    lib, torch, dev = q8
+    wb, _, _ = wl.q4_0_weight(1800, n, k)
+    wd = to_dev(wb, dev)
+    xd = to_dev(wl.activations(1801, 20, k), dev)
+    y20 = lib.q4_0_linear(wd, n, k, xd).cpu().numpy()
+    assert np.array_equal(y20, lib.q4_0_linear(wd, n, k, xd).cpu().numpy())
+    for r0, r1 in ((0, 1), (3, 4), (0, 5), (7, 19)):
+        assert np.array_equal(lib.q4_0_linear(wd, n, k, xd[r0:r1].contiguous()).cpu().numpy(), y20[r0:r1]), (r0, r1)
