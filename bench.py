@@ -272,11 +272,11 @@ def graph_launch_ms(torch, seq, launches, replays=5):
     return e0.elapsed_time(e1) / (replays * launches)
 
 
-def bench_linear(torch, dev, q8, name, n, k, m, fused, reps, min_bytes=600e6):
+def bench_linear(torch, dev, q8, name, n, k, m, fused, reps, min_bytes=600e6, fmt="q8_0"):
     """One linear launched back to back over distinct resident weight copies (enough of
-    them to exceed the 256 MB Infinity Cache twice)."""
+    them to exceed the 256 MB Infinity Cache twice).  fmt: "q8_0" or "q4_0" weights."""
     import workloads as wl
-    wb, _, _ = wl.q8_weight(31, n, k)
+    wb, _, _ = (wl.q4_0_weight if fmt == "q4_0" else wl.q8_weight)(31, n, k)
     base = torch.from_numpy(wb).to(dev)
     copies = [base] + [base.clone() for _ in range(max(1, int(min_bytes // wb.size)))]
     x = torch.from_numpy(wl.activations(37, m, k)).to(dev)
@@ -287,14 +287,19 @@ def bench_linear(torch, dev, q8, name, n, k, m, fused, reps, min_bytes=600e6):
     def seq():
         for i in range(launches):
             w = copies[i % len(copies)]
-            if fused:
+            if fmt == "q4_0":
+                if fused:
+                    q8.q4_0_linear_fused_gate_up_silu(w, nout, k, x, out=y)
+                else:
+                    q8.q4_0_linear(w, n, k, x, out=y)
+            elif fused:
                 q8.q8_linear_fused_gate_up_silu(w, nout, k, x, out=y)
             else:
                 q8.q8_linear(w, n, k, x, out=y)
 
     ms = graph_launch_ms(torch, seq, launches)
     flops = 2.0 * m * n * k
-    res = {"shape": [n, k], "m": m, "fused_silu": fused, "us_per_launch": round(ms * 1e3, 3),
+    res = {"shape": [n, k], "m": m, "fused_silu": fused, "weights": fmt.upper(), "us_per_launch": round(ms * 1e3, 3),
            "weight_bytes": int(wb.size), "gbps": round(wb.size / (ms * 1e-3) / 1e9, 2),
            "hbm_frac": round(wb.size / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
            "tflops": round(flops / (ms * 1e-3) / 1e12, 2), "distinct_weight_copies": len(copies)}
@@ -480,6 +485,11 @@ def main():
         extras["qwen3-8b-gate-up-m16"] = bench_linear(torch, dev, q8, "8b gate_up m16", 24576, 4096, 16, True, reps)
         extras["qwen3-8b-gate-up-m512-prefill"] = bench_linear(torch, dev, q8, "8b gate_up m512", 24576, 4096, 512,
                                                                True, reps)
+        # GGUF Q4_0 weights: the Gemma 4 12B FFN (hidden 3840, intermediate 15360), one token
+        extras["gemma-4-12b-ffn-gate-up-q4_0-m1"] = bench_linear(torch, dev, q8, "gemma4 12b gate_up q4_0 m1",
+                                                                 30720, 3840, 1, True, reps, fmt="q4_0")
+        extras["gemma-4-12b-ffn-down-q4_0-m1"] = bench_linear(torch, dev, q8, "gemma4 12b down q4_0 m1",
+                                                              3840, 15360, 1, False, reps, fmt="q4_0")
         extras["qwen3-30b-a3b-moe-16tok"] = bench_moe(torch, dev, q8, 4, args.steps, args.warmup)
         extras["qwen3-30b-a3b-moe-16tok-expert-top-p-0.9"] = bench_moe(torch, dev, q8, 4, args.steps, args.warmup,
                                                                         top_p=0.9)

@@ -210,10 +210,12 @@ struct FmtQ4_0 {
             v = w[5 + c4];
         }
         const uint32_t nib = (cc < 4 ? v : v >> 4) & 0x0F0F0F0Fu;  // inputs 4cc..: low nibbles, then high
-        wf[0] = ((float)(nib & 0xFFu) - 8.0f) * d;
-        wf[1] = ((float)((nib >> 8) & 0xFFu) - 8.0f) * d;
-        wf[2] = ((float)((nib >> 16) & 0xFFu) - 8.0f) * d;
-        wf[3] = ((float)(nib >> 24) - 8.0f) * d;
+        // q*d - 8d in one fma: the exact value (q - 8)*d has at most 15 significant bits
+        const float m8d = -8.0f * d;
+        wf[0] = __builtin_fmaf((float)(nib & 0xFFu), d, m8d);
+        wf[1] = __builtin_fmaf((float)((nib >> 8) & 0xFFu), d, m8d);
+        wf[2] = __builtin_fmaf((float)((nib >> 16) & 0xFFu), d, m8d);
+        wf[3] = __builtin_fmaf((float)(nib >> 24), d, m8d);
     }
 };
 
