@@ -71,10 +71,25 @@ struct Q8Pair {  // 9 dwords of one Q8_0 block as it sits in its pair (see the l
     uint32_t dw[9];
 };
 
-template <int BN, bool SILU>
+// Expert-grouped tiles (the MoE prefill form): tile t of the grid's tile list belongs to
+// the expert e with tile_start[e] <= t < tile_start[e + 1]; its activation rows are the
+// positions offsets[e] + 128 * (t - tile_start[e]) + r of the expert-sorted pair list.
+// gather: row of position pos is x[sorted[pos] / k] (the token's input); else x[pos].
+// The output row of position pos is y[pos].
+struct GroupArgs {
+    const int32_t* offsets;     // [n_exp + 1] pair positions per expert
+    const int32_t* tile_start;  // [n_exp + 1] first 128-row tile of each expert
+    const int32_t* sorted;      // [pairs] pair index (token * k + slot) at each position
+    int n_exp, k, n_tiles;      // n_tiles: output tiles per expert (grid = tiles x n_tiles)
+    size_t expert_bytes;        // bytes of one expert's Q8_0 matrix
+    bool gather;
+};
+
+template <int BN, bool SILU, bool GROUPED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_q8_mfma_kernel(const uint8_t* __restrict__ w, int n_out, int P,
                                                            const float* __restrict__ x, int M, int ldx,
-                                                           float* __restrict__ y, int ldy, int m_tiles) {
+                                                           float* __restrict__ y, int ldy, int m_tiles,
+                                                           GroupArgs g) {
     constexpr int TJ = BN / 32;        // 16x16 tiles per wave along n
     constexpr int SPLIT = 128 / BN;    // threads per Q8_0 block (1: whole block, 2: 16 quants each)
     static_assert(SPLIT == 1 || SPLIT == 2, "2*BN blocks per step over 256 threads");
@@ -84,8 +99,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int lane = tid & 63;
     const int wv = tid >> 6;
     const int wm = wv & 1, wn = wv >> 1;
-    const int mt = blockIdx.x % m_tiles;  // m tiles of one n tile run side by side (shared weights)
-    const int nt = blockIdx.x / m_tiles;
+    int mt = blockIdx.x % m_tiles;  // m tiles of one n tile run side by side (shared weights)
+    int nt = blockIdx.x / m_tiles;
+    int mbase = 0;  // grouped: first position of the tile (its rows are positions mbase + r)
+    if constexpr (GROUPED) {
+        const int t = blockIdx.x / g.n_tiles;
+        nt = blockIdx.x - t * g.n_tiles;
+        if (t >= g.tile_start[g.n_exp]) return;  // past the tile list (block-uniform, no barrier yet)
+        int lo = 0, hi = g.n_exp;  // tile_start[lo] <= t < tile_start[hi]: the expert is the largest such lo
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (g.tile_start[mid] <= t) lo = mid;
+            else hi = mid;
+        }
+        mbase = g.offsets[lo] + kBM * (t - g.tile_start[lo]);
+        const int rows = g.offsets[lo + 1] - mbase;
+        M = rows < kBM ? rows : kBM;
+        mt = 0;
+        w += (size_t)lo * g.expert_bytes;
+    }
     const size_t row_bytes = (size_t)P * 68;
 
     // weight role: block wb of the pair of tile column wc (part hh of it when SPLIT = 2).
@@ -98,7 +130,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int xr = tid >> 1, xh = tid & 1;
     int xm = mt * kBM + xr;
     xm = xm < M ? xm : M - 1;
-    const float* xrow = x + (size_t)xm * ldx + 32 * xh;
+    size_t xoff = (size_t)xm;
+    if constexpr (GROUPED) xoff = g.gather ? (size_t)(g.sorted[mbase + xm] / g.k) : (size_t)(mbase + xm);
+    const float* xrow = x + xoff * ldx + 32 * xh;
 
     f32x4 acc[4][TJ];
 #pragma unroll
@@ -200,6 +234,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 
     // ---- epilogue: lane holds D[m = 4*(lane/16) + e][n = lane%16] of each 16 x 16 tile
+    if constexpr (GROUPED) y += (size_t)mbase * ldy;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -231,16 +266,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 template <int BN>
 hipError_t launch_tiles(const uint8_t* w, int64_t n_out, int P, bool silu, const float* x, int64_t m, int64_t ldx,
                         float* y, int64_t ldy, hipStream_t stream) {
+    const GroupArgs none{};
     const int m_tiles = (int)((m + kBM - 1) / kBM);
     const int64_t cols = silu ? BN / 2 : BN;  // outputs per tile
     const int64_t blocks = (n_out + cols - 1) / cols * m_tiles;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     if (silu)
-        hipLaunchKernelGGL((gemm_q8_mfma_kernel<BN, true>), dim3((unsigned)blocks), dim3(256), 0, stream, w,
-                           (int)n_out, P, x, (int)m, (int)ldx, y, (int)ldy, m_tiles);
+        hipLaunchKernelGGL((gemm_q8_mfma_kernel<BN, true, false>), dim3((unsigned)blocks), dim3(256), 0, stream, w,
+                           (int)n_out, P, x, (int)m, (int)ldx, y, (int)ldy, m_tiles, none);
     else
-        hipLaunchKernelGGL((gemm_q8_mfma_kernel<BN, false>), dim3((unsigned)blocks), dim3(256), 0, stream, w,
-                           (int)n_out, P, x, (int)m, (int)ldx, y, (int)ldy, m_tiles);
+        hipLaunchKernelGGL((gemm_q8_mfma_kernel<BN, false, false>), dim3((unsigned)blocks), dim3(256), 0, stream, w,
+                           (int)n_out, P, x, (int)m, (int)ldx, y, (int)ldy, m_tiles, none);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_q8_mfma_grouped(const uint8_t* w_stack, size_t expert_bytes, int64_t n_out, int64_t k,
+                                       bool silu_pairs, const float* x, int64_t ldx, float* y, int64_t ldy,
+                                       const int32_t* offsets, const int32_t* tile_start, const int32_t* sorted,
+                                       int n_exp, int top_k, bool gather, int64_t max_tiles, hipStream_t stream) {
+    const int P = (int)(k / kBK);
+    const int64_t cols = silu_pairs ? 64 : 128;  // outputs per 128 x 128 tile
+    const int n_tiles = (int)((n_out + cols - 1) / cols);
+    const int64_t blocks = max_tiles * n_tiles;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    const GroupArgs g{offsets, tile_start, sorted, n_exp, top_k, n_tiles, expert_bytes, gather};
+    if (silu_pairs)
+        hipLaunchKernelGGL((gemm_q8_mfma_kernel<128, true, true>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                           w_stack, (int)n_out, P, x, 0, (int)ldx, y, (int)ldy, 1, g);
+    else
+        hipLaunchKernelGGL((gemm_q8_mfma_kernel<128, false, true>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                           w_stack, (int)n_out, P, x, 0, (int)ldx, y, (int)ldy, 1, g);
     return hipGetLastError();
 }
 

@@ -47,7 +47,8 @@ __global__ __launch_bounds__(kPlanThreads) void moe_plan_kernel(const int32_t* _
                                                                 int n_exp, int32_t* __restrict__ offsets,
                                                                 int32_t* __restrict__ sorted,
                                                                 int32_t* __restrict__ inv,
-                                                                int32_t* __restrict__ active) {
+                                                                int32_t* __restrict__ active,
+                                                                int32_t* __restrict__ tile_start) {
     __shared__ int counts[q8v::kMaxExperts + 1];
     __shared__ int running[q8v::kMaxExperts + 1];
     const int tid = threadIdx.x;
@@ -93,6 +94,20 @@ __global__ __launch_bounds__(kPlanThreads) void moe_plan_kernel(const int32_t* _
         for (int w = 0; w < (tid >> 6); ++w) abase += wave_active[w];
         if (has) active[abase + aincl - 1] = tid;
         if (tid == kPlanThreads - 1) active[n_exp] = abase + aincl;
+        // the first 128-row tile of each expert in the grouped matrix-core form
+        const int nt = (c + 127) / 128;
+        int tincl = nt;
+        for (int off = 1; off < 64; off <<= 1) {
+            const int v = __shfl_up(tincl, off, 64);
+            if (lane >= off) tincl += v;
+        }
+        __shared__ int wave_tiles[kPlanThreads / 64];
+        if (lane == 63) wave_tiles[tid >> 6] = tincl;
+        __syncthreads();
+        int tbase = 0;
+        for (int w = 0; w < (tid >> 6); ++w) tbase += wave_tiles[w];
+        if (tid < n_exp) tile_start[tid] = tbase + tincl - nt;
+        if (tid == n_exp - 1) tile_start[n_exp] = tbase + tincl;
     }
     __syncthreads();
     // Stable scatter, one chunk of kPlanThreads pairs at a time: a pair's place is the
@@ -306,10 +321,27 @@ hipError_t launch_moe_grouped(const DeviceInfo& dev, const uint8_t* wgu, const u
     float* outp = reinterpret_cast<float*>(ws + L.out_off);
     const int n_pairs = (int)(m * k);
 
+    int32_t* tile_start = reinterpret_cast<int32_t*>(ws + L.tiles_off);
     hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, idx, n_pairs, (int)n_exp, offsets,
-                       sorted, inv, active);
+                       sorted, inv, active, tile_start);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+
+    if (q8v::moe_uses_matrix_cores(n_pairs, n_exp)) {
+        // Prefill: expert-grouped bf16 matrix-core tiles.  gate_up (K = h) writes
+        // SiLU(gate) * up straight into hidden [pairs][f]; down (K = f) reads it and writes
+        // the per-pair outputs; the grid covers the largest possible tile list.
+        const int64_t max_tiles = (n_pairs + 127) / 128 + n_exp;
+        e = launch_gemm_q8_mfma_grouped(wgu, (size_t)(2 * f) * (size_t)(h / 32) * 34, f, h, true, x, ldx, hidden, f,
+                                        offsets, tile_start, sorted, (int)n_exp, k, true, max_tiles, stream);
+        if (e != hipSuccess) return e;
+        e = launch_gemm_q8_mfma_grouped(wdn, (size_t)h * (size_t)(f / 32) * 34, h, f, false, hidden, f, outp, h,
+                                        offsets, tile_start, sorted, (int)n_exp, k, false, max_tiles, stream);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)m, (unsigned)((h + 255) / 256)), dim3(256), 0, stream,
+                           outp, (int)h, inv, wts, k, y, (int)ldy);
+        return hipGetLastError();
+    }
 
     // gate_up: K = h, the 2f gate and up rows of each expert as separate rows; down: K = f,
     // rows h per expert, activation row of a position = SiLU(gate) * up of its gate_up

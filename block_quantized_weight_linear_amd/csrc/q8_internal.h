@@ -40,6 +40,14 @@ hipError_t launch_quantize_act(const float* x, int64_t m, int64_t k, int64_t ldx
 hipError_t launch_gemv_q8act(const DeviceInfo& dev, const uint8_t* w, int64_t n_out, int64_t k, bool silu_pairs,
                              const int8_t* xq, const float* xd, int64_t m, float* y, int64_t ldy, hipStream_t stream);
 
+// Expert-grouped form of the matrix-core tiles (MoE prefill): tiles from the route plan's
+// offsets / tile_start / sorted lists; gather: activation row of a position is
+// x[sorted[pos] / top_k], else x[pos]; output row of a position is y[pos].
+hipError_t launch_gemm_q8_mfma_grouped(const uint8_t* w_stack, size_t expert_bytes, int64_t n_out, int64_t k,
+                                       bool silu_pairs, const float* x, int64_t ldx, float* y, int64_t ldy,
+                                       const int32_t* offsets, const int32_t* tile_start, const int32_t* sorted,
+                                       int n_exp, int top_k, bool gather, int64_t max_tiles, hipStream_t stream);
+
 // Softmax top-k router with adaptive expert top-p (top_p >= 1: plain top-k).  logits ==
 // nullptr: one kernel, one block per token; else a [m][n_exp] float32 workspace for the
 // two-pass form (logits over many CUs, then selection), bit-identical results.

@@ -128,9 +128,17 @@ inline q8_status check_route_workspace(int64_t m, int64_t n_exp, const void* ws,
     return Q8_OK;
 }
 
+// The grouped MoE call runs on the bf16 matrix cores (expert-grouped 128-row tiles) when
+// the routed pairs average at least this many per expert (prefill), else on the float32
+// GEMV passes (decode).
+constexpr int64_t kMoeMatrixCorePairsPerExpert = 64;
+inline bool moe_uses_matrix_cores(int64_t n_pairs, int64_t n_exp) {
+    return n_pairs >= kMoeMatrixCorePairsPerExpert * n_exp;
+}
+
 // Workspace of the grouped MoE call: a route plan plus the hidden activations.
 struct MoeWorkspace {
-    size_t offsets_off, sorted_off, inv_off, active_off, hidden_off, out_off, total;
+    size_t offsets_off, sorted_off, inv_off, active_off, tiles_off, hidden_off, out_off, total;
 };
 
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -143,6 +151,7 @@ inline MoeWorkspace moe_workspace_layout(int64_t m, int32_t k, int64_t n_exp, in
     w.sorted_off = off;  off = round_up(off + sizeof(int32_t) * pairs, 256);
     w.inv_off = off;     off = round_up(off + sizeof(int32_t) * pairs, 256);
     w.active_off = off;  off = round_up(off + sizeof(int32_t) * size_t(n_exp + 1), 256);
+    w.tiles_off = off;   off = round_up(off + sizeof(int32_t) * size_t(n_exp + 1), 256);
     w.hidden_off = off;  off = round_up(off + sizeof(float) * pairs * 2 * size_t(f), 256);  // gate and up rows
     w.out_off = off;     off = round_up(off + sizeof(float) * pairs * size_t(h), 256);
     w.total = off;

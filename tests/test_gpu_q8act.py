@@ -202,3 +202,42 @@ def test_zero_rows_and_outputs(q8):
     assert lib.q8_linear_q8act(to_dev(wb, dev), 8, k, qx, dx).shape == (0, 8)
     xq, xd = lib.q8_quantize_act(torch.empty((0, k), dtype=torch.float32, device=dev))
     assert xq.shape == (0, k) and xd.shape == (0, k // 32)
+
+
+def test_q8act_graph_replay_matches_eager(q8):
+    """Quantize + the int8-dot linears captured in one HIP graph: every replay, with eager
+    work in between, gives the eager result bit for bit."""
+    lib, torch, dev = q8
+    k, n, f = 1024, 4096, 1536
+    wq = to_dev(wl.q8_weight(91, n, k)[0], dev)
+    wg = to_dev(wl.q8_weight(92, 2 * f, k)[0], dev)
+    for m in (1, 9):
+        x = to_dev(wl.activations(93 + m, m, k), dev)
+        xq = torch.empty((m, k), dtype=torch.int8, device=dev)
+        xd = torch.empty((m, k // 32), device=dev)
+        y = torch.empty((m, n), device=dev)
+        h = torch.empty((m, f), device=dev)
+
+        def step():
+            lib.q8_quantize_act(x, xq, xd)
+            lib.q8_linear_q8act(wq, n, k, xq, xd, out=y)
+            lib.q8_linear_fused_gate_up_silu_q8act(wg, f, k, xq, xd, out=h)
+
+        step()
+        torch.cuda.synchronize()
+        ref = [t.clone() for t in (xq, xd, y, h)]
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                step()
+        for rep in range(4):
+            for t in (xd, y, h):
+                t.fill_(float("nan"))
+            xq.fill_(0)
+            g.replay()
+            torch.cuda.synchronize()
+            for got, want in zip((xq, xd, y, h), ref):
+                assert torch.equal(got, want), (m, rep)
+            step()
+            torch.cuda.synchronize()

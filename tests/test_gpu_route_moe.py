@@ -345,3 +345,89 @@ def test_two_pass_router_bit_identical(q8, m, h, e, k):
             assert torch.equal(i1, i2) and torch.equal(w1, w2), (norm, top_p)
     i2, w2 = lib.moe_route_topk(xd, wd, k, True, workspace=True)
     check_routing(i2.cpu().numpy(), w2.cpu().numpy(), x, wr, k, True)
+
+
+def test_moe_graph_replay_matches_eager(q8):
+    """Two-pass routing (with a top-p cut) and the grouped mixture captured in one HIP
+    graph: every replay, with eager work and synchronizations in between, gives the eager
+    result bit for bit (the route plan clears its counters with kernels, no memsets)."""
+    lib, torch, dev = q8
+    m, e, f, h, k = 16, 32, 256, 512, 4
+    gu, dn = _experts(500, e, f, h)
+    gud, dnd = to_dev(gu, dev), to_dev(dn, dev)
+    xd = to_dev(wl.activations(501, m, h), dev)
+    wrd = to_dev(wl.router_weight(502, e, h, std=0.1), dev)
+    idx = torch.empty((m, k), dtype=torch.int32, device=dev)
+    wts = torch.empty((m, k), device=dev)
+    y = torch.empty((m, h), device=dev)
+    ws_r = torch.empty(lib.moe_route_workspace_bytes(m, e), dtype=torch.uint8, device=dev)
+    ws_m = torch.empty(lib.q8_moe_workspace_bytes(m, k, e, f, h), dtype=torch.uint8, device=dev)
+
+    def step():
+        lib.moe_route_topk(xd, wrd, k, True, idx_out=idx, w_out=wts, top_p=0.7, workspace=ws_r)
+        lib.q8_moe_grouped_linear(gud, dnd, e, f, h, xd, idx, wts, out=y, workspace=ws_m)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (idx, wts, y)]
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            step()
+    for rep in range(4):
+        y.fill_(float("nan"))
+        idx.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((idx, wts, y), ref):
+            assert torch.equal(got, want), rep
+        step()
+        torch.cuda.synchronize()
+
+
+# ------------------------------------------- MoE prefill: expert-grouped matrix-core tiles
+
+MOE_PREFILL_TOL = 2e-2   # bf16 operands (x, d*q, and the hidden SiLU*up), float32 accumulation
+
+
+@pytest.mark.parametrize("m,e,k,f,h", [(300, 8, 2, 256, 512), (700, 16, 4, 512, 1024), (129, 2, 1, 768, 256),
+                                       (520, 4, 3, 256, 2048)])
+def test_moe_prefill_vs_oracle(q8, m, e, k, f, h):
+    """At least 64 routed pairs per expert: the expert-grouped bf16 tiles run (ragged last
+    tile of every expert, experts with fewer rows than a tile)."""
+    lib, torch, dev = q8
+    assert m * k >= 64 * e
+    gu, dn = _experts(900 + e, e, f, h)
+    x = wl.activations(901 + m, m, h)
+    idx, w = wl.random_routing(902 + m, m, e, k)
+    say(f"moe prefill m={m} e={e} k={k} f={f} h={h}")
+    y = lib.q8_moe_grouped_linear(to_dev(gu, dev), to_dev(dn, dev), e, f, h, to_dev(x, dev), to_dev(idx, dev),
+                                  to_dev(w, dev)).cpu().numpy()
+    assert_close(y, oracle.moe_mixture_ref(gu, dn, e, f, h, x, idx, w), f"moe prefill m={m} e={e}",
+                 tol=MOE_PREFILL_TOL)
+    y2 = lib.q8_moe_grouped_linear(to_dev(gu, dev), to_dev(dn, dev), e, f, h, to_dev(x, dev), to_dev(idx, dev),
+                                   to_dev(w, dev)).cpu().numpy()
+    assert np.array_equal(y, y2)  # deterministic
+
+
+def test_moe_prefill_a3b_sampled(q8):
+    """Qwen3-30B-A3B layer at 1024 tokens (8192 routed pairs, 64 per expert on average):
+    device routing, the grouped tiles, 24 sampled tokens against the oracle; dropped slots
+    of a top-p routing are skipped on this path too."""
+    lib, torch, dev = q8
+    cfg = wl.QWEN3_30B_A3B_MOE
+    e, f, h, k, m = cfg.n_exp, cfg.ffn, cfg.hidden, cfg.k, 1024
+    gu, dn = _experts(950, e, f, h)
+    x = wl.activations(951, m, h)
+    wr = wl.router_weight(952, e, h, cfg.router_std)
+    gud, dnd, xd = to_dev(gu, dev), to_dev(dn, dev), to_dev(x, dev)
+    pick = np.sort(np.random.default_rng(953).choice(m, 24, replace=False))
+    for top_p in (None, 0.8):
+        say(f"moe prefill a3b m={m} top_p={top_p}")
+        idx, w = lib.moe_route_topk(xd, to_dev(wr, dev), k, True, top_p=top_p, workspace=True)
+        y = lib.q8_moe_grouped_linear(gud, dnd, e, f, h, xd, idx, w).cpu().numpy()
+        idx_h, w_h = idx.cpu().numpy(), w.cpu().numpy().astype(np.float64)
+        ref = oracle.moe_mixture_ref(gu, dn, e, f, h, x[pick], idx_h[pick], w_h[pick])
+        assert_close(y[pick], ref, f"a3b prefill top_p={top_p} (24 sampled tokens)", tol=MOE_PREFILL_TOL)
+        assert np.all(np.isfinite(y))
