@@ -369,6 +369,36 @@ def bench_moe(torch, dev, q8, layers, steps, warmup, top_p=None):
     return res
 
 
+def bench_moe_prefill(torch, dev, q8, tokens, reps):
+    """Qwen3-30B-A3B MoE layer at prefill size: device routing (two-pass) then the grouped
+    mixture, which runs on the expert-grouped bf16 matrix-core tiles at this size.  Reports
+    the mixture's time and the TFLOP/s of its expert products."""
+    import workloads as wl
+    cfg = wl.QWEN3_30B_A3B_MOE
+    e, f, hd, k = cfg.n_exp, cfg.ffn, cfg.hidden, cfg.k
+    distinct = 8
+    gu_h = np.concatenate([wl.q8_weight(cfg.seed * 100 + i, 2 * f, hd)[0] for i in range(distinct)])
+    dn_h = np.concatenate([wl.q8_weight(cfg.seed * 100 + 50 + i, hd, f)[0] for i in range(distinct)])
+    gu = torch.cat([torch.from_numpy(gu_h).to(dev)] * (e // distinct))
+    dn = torch.cat([torch.from_numpy(dn_h).to(dev)] * (e // distinct))
+    x = torch.from_numpy(wl.activations(cfg.seed + 11, tokens, hd)).to(dev)
+    wr = torch.from_numpy(wl.router_weight(cfg.seed + 12, e, hd, cfg.router_std)).to(dev)
+    idx, wts = q8.moe_route_topk(x, wr, k, True, workspace=True)
+    y = torch.empty((tokens, hd), device=dev)
+    ws = torch.empty(q8.q8_moe_workspace_bytes(tokens, k, e, f, hd), dtype=torch.uint8, device=dev)
+    ms = graph_launch_ms(torch, lambda: [q8.q8_moe_grouped_linear(gu, dn, e, f, hd, x, idx, wts, out=y, workspace=ws)
+                                         for _ in range(reps)], reps)
+    pairs = int((idx >= 0).sum())
+    flops = 2.0 * pairs * (2 * f * hd + hd * f)
+    res = {"workload": cfg.name + "-prefill", "tokens": tokens, "routed_pairs": pairs, "experts": e, "top_k": k,
+           "path": "expert-grouped bf16 MFMA tiles", "us_per_layer": round(ms * 1e3, 2),
+           "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+           "mfma_bf16_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+           "tok_s": round(tokens * 1000.0 / ms, 1)}
+    log(f"moe prefill: {res}")
+    return res
+
+
 PROFILE_LINEARS = {"qkv": (6144, 4096, False), "gate_up": (24576, 4096, True), "down": (4096, 12288, False)}
 
 
@@ -491,6 +521,7 @@ def main():
         extras["gemma-4-12b-ffn-down-q4_0-m1"] = bench_linear(torch, dev, q8, "gemma4 12b down q4_0 m1",
                                                               3840, 15360, 1, False, reps, fmt="q4_0")
         extras["qwen3-30b-a3b-moe-16tok"] = bench_moe(torch, dev, q8, 4, args.steps, args.warmup)
+        extras["qwen3-30b-a3b-moe-2048tok-prefill"] = bench_moe_prefill(torch, dev, q8, 2048, 5)
         extras["qwen3-30b-a3b-moe-16tok-expert-top-p-0.9"] = bench_moe(torch, dev, q8, 4, args.steps, args.warmup,
                                                                         top_p=0.9)
         line["configs"] = extras
