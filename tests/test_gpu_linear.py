@@ -336,3 +336,19 @@ def test_prefill_exact_arithmetic(q8, n, k, m):
     x = wl.activations_exact(97 + m, m, k)
     y = lib.q8_linear(to_dev(wb, dev), n, k, to_dev(x, dev)).cpu().numpy()
     assert np.array_equal(y.astype(np.float64), oracle.q8_linear_ref(wb, n, k, x))
+
+
+@pytest.mark.parametrize("n,k,m", [(64, 32768, 1), (33, 20480, 1), (64, 32768, 3), (130, 65536, 2)])
+def test_long_rows(q8, n, k, m):
+    """K beyond what the one-row kernel keeps in registers (more than 4 pair rounds per
+    lane): one row falls back to the rows kernel; long rows also in the fused form."""
+    lib, torch, dev = q8
+    wb, _, _ = wl.q8_weight(1900 + n + k, n, k)
+    x = wl.activations(1901 + m, m, k)
+    say(f"long rows n={n} k={k} m={m}")
+    y = lib.q8_linear(to_dev(wb, dev), n, k, to_dev(x, dev)).cpu().numpy()
+    assert_close(y, oracle.q8_linear_ref(wb, n, k, x), f"long rows n={n} k={k} m={m}")
+    f = n // 2
+    wf = row_slice(wb, k, np.arange(2 * f))
+    h = lib.q8_linear_fused_gate_up_silu(to_dev(wf, dev), f, k, to_dev(x, dev)).cpu().numpy()
+    assert_close(h, oracle.fused_gate_up_silu_ref(wf, f, k, x), f"long rows fused f={f} k={k} m={m}")

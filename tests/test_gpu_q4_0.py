@@ -115,3 +115,12 @@ def test_q4_0_batch_invariance(q8, n, k):
     assert np.array_equal(y20, lib.q4_0_linear(wd, n, k, xd).cpu().numpy())
     for r0, r1 in ((0, 1), (3, 4), (0, 5), (7, 19)):
         assert np.array_equal(lib.q4_0_linear(wd, n, k, xd[r0:r1].contiguous()).cpu().numpy(), y20[r0:r1]), (r0, r1)
+
+
+@pytest.mark.parametrize("n,k,m", [(64, 32768, 1), (70, 65536, 3)])
+def test_q4_0_long_rows(q8, n, k, m):
+    lib, torch, dev = q8
+    wb, _, _ = wl.q4_0_weight(2200 + k, n, k)
+    x = wl.activations(2201 + m, m, k)
+    y = lib.q4_0_linear(to_dev(wb, dev), n, k, to_dev(x, dev)).cpu().numpy()
+    assert_close(y, oracle.q4_0_linear_ref(wb, n, k, x), f"q4_0 long rows k={k} m={m}")

@@ -241,3 +241,15 @@ def test_q8act_graph_replay_matches_eager(q8):
                 assert torch.equal(got, want), (m, rep)
             step()
             torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("n,k,m", [(64, 32768, 1), (100, 65536, 5)])
+def test_q8act_long_rows(q8, n, k, m):
+    lib, torch, dev = q8
+    wb, _, _ = wl.q8_weight(2100 + k, n, k)
+    x = wl.activations(2101 + m, m, k)
+    xq, xd = lib.q8_quantize_act(to_dev(x, dev))
+    qx, dx = oracle.quantize_act_q8_ref(x)
+    assert np.array_equal(xq.cpu().numpy(), qx)
+    y = lib.q8_linear_q8act(to_dev(wb, dev), n, k, xq, xd).cpu().numpy()
+    assert_close(y, oracle.q8_linear_codes_ref(wb, n, k, qx, dx), f"q8act long rows k={k} m={m}")
