@@ -495,7 +495,7 @@ def main():
         "hbm_frac": r1["hbm_frac"],
         "decode_tok_s": r1["tok_s"],
         "execution": "HIP graph replay of the step (eager per-call timing in ms_per_step_eager)",
-        "roofline": {"bound": "hbm", "kernel": "fused gate_up + SiLU, one activation row (gemv_xreg_kernel)",
+        "roofline": {"bound": "hbm", "kernel": "fused gate_up + SiLU, one activation row (gemv_one_row_kernel)",
                      "achieved": r1["gate_up_gbps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(r1["gate_up_gbps"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE)",

@@ -1,4 +1,4 @@
-// Dense Q8_0 x float32 linears for 1..16 activation rows per launch (gfx950).
+// Dense Q8_0 x float32 linears for 1..8 activation rows per launch (gfx950).
 //
 // The packed-weight linear of "14. Model families and example applications" section
 // 14.1 (LinearWeight: quant forms run packed kernels, no global dequantization; q/k/v
@@ -6,11 +6,11 @@
 // Lockstep batch decode multiplies one pass over the weights by several activation
 // rows (section 14.2), so all rows of a launch share every weight load.
 //
-// Grid: persistent workgroups of 4 waves, as many as fit on the device at once (at
-// most one row group per wave); each wave walks row groups at a stride of the total
-// wave count.  Activation rows are staged in LDS once per workgroup when they fit in
-// 64 KB, else read from global memory (L2-resident).  See gemv_core.h for the lane
-// layout and the summation order.
+// Two kernels: gemv_one_row_kernel for one activation row (weights streamed through LDS
+// with coalesced direct copies, activations in registers) and gemv_rows_kernel for 2..8
+// rows per launch (weights in registers, activations through LDS).  Both run persistent
+// grids of the blocks that fit on the device at once, each walking its share of the rows.
+// See gemv_core.h for the pair layout and the one-row summation order.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -21,9 +21,6 @@
 #include "q8_internal.h"
 
 namespace q8k {
-
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
 
 // Calls f(std::integral_constant<int, 0>{}), ..., f(std::integral_constant<int, N-1>{}).
 template <class F, int... I>
@@ -41,123 +38,154 @@ struct XArr {
     __device__ __forceinline__ float4 get(int m, int, int c) const { return v[m][c]; }
 };
 
-template <int M, int R, int NR, int D, int WPE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, WPE))) void gemv_xreg_kernel(const uint8_t* __restrict__ w, int n_out, int P, int log2S,
-                                                             const float* __restrict__ x, int ldx,
-                                                             float* __restrict__ y, int ldy, int ipw) {
-    static_assert(D % NR == 0, "the ring depth must be a multiple of the rounds per row");
-    extern __shared__ float4 x_lds[];
+// One activation row (the decode class).  A wave works on "items": the pairs j + S*i
+// (slot j, round i) of one row group, i.e. one contiguous stretch of at most 4352 weight
+// bytes per row (64 pairs; with G > 1 rows per wave, G whole rows).  The wave copies an
+// item's bytes (and, fused, the matching up rows' bytes) straight into its own LDS slot
+// with five wave-wide loads per row, each lane reading consecutive bytes (1 KB per load
+// instruction), so every load is fully coalesced; each lane then reads its 68-byte pair
+// from LDS (a 17-dword stride: conflict-free) and multiplies it in registers.  Reading the
+// pairs directly (a 68-byte stride across lanes) made every load instruction touch every
+// cache line of the row and measured ~20% slower.  A slot is refilled with the item D
+// ahead as soon as its bytes are in registers, so D items per wave stay in flight while
+// one is multiplied.
+//
+// Activations: each block copies x into LDS with one 256-byte direct copy per pair, row p
+// at p * kXRow (kXRow = 272: the 16-byte pad makes the lanes' reads of their own pair's
+// 64 activations conflict-free); each lane then keeps the activations of its pairs in
+// registers.  The activation copies are issued before the first weight copies, so the
+// wait for them (then a barrier) leaves the weights in flight.
+//
+// Items of wave w: the row groups w, w + W, w + 2W, ... (W waves in the grid, `ipw`
+// items per wave, a multiple of NR), so the grid streams one window of the matrix at a
+// time; items past the end repeat the last row group (same bits to the same address).
+// Per-output order and arithmetic are those of gemv_core.h (mac_pair, then the xor
+// butterfly over the S slots).
+constexpr int kXRow = 272;
+
+template <int R, int NR, int D, int NW>
+__global__ __launch_bounds__(64 * NW) void gemv_one_row_kernel(const uint8_t* __restrict__ w, int n_out, int P,
+                                                              int log2S, const float* __restrict__ x,
+                                                              float* __restrict__ y, int ipw) {
+    static_assert((D - 1) * 5 * R < 64 && D * 5 * R < 64, "copies in flight must fit the vmcnt counter");
+    extern __shared__ float4 smem4[];
+    uint8_t* smem = reinterpret_cast<uint8_t*>(smem4);
     const int S = 1 << log2S;
     const int G = 64 >> log2S;
     const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int j = lane & (S - 1);
     const int g = lane >> log2S;
     const size_t row_bytes = (size_t)P * 68;
-
     const int total = ((n_out + G - 1) / G) * NR;  // items: (row group, round)
-    const int wid = blockIdx.x * kWaves + (threadIdx.x >> 6);
-    const int nw = gridDim.x * kWaves;
+    const int wid = blockIdx.x * NW + wv;
+    const int nw = gridDim.x * NW;
+    uint8_t* ring = smem + (size_t)P * kXRow + (size_t)wv * (D * R * kLdsItemBytes);
+    const uint32_t ring_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)ring);
+    const uint32_t x_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
 
-    // Wave w takes the row groups w, w + W, w + 2W, ... (W waves in the grid; `ipw` items
-    // per wave, a multiple of D and of NR), so at any time the grid streams one window of
-    // the matrix.  Every load and
-    // store below is unconditional so the compiler counts the outstanding memory
-    // operations exactly and keeps the ring's loads in flight while an item is
-    // multiplied (a load inside a branch makes it wait for all of them):
-    //  - a lane whose pair index is past the row (p >= P, only when S does not divide
-    //    P) loads pair p - P of the same row instead and skips the multiply;
-    //  - a lane whose row is past the matrix, and any item past the last one (only in
-    //    the grid's last wave), work on the last row group again and store the same
-    //    bits its owner stores.
-    // After the xor butterfly every lane of a row holds the same bits, so all of them
-    // store it.
-
-    // local item it -> row (clamped) of this lane; its round is it % NR
-    auto item_row = [&](int itl) __attribute__((always_inline)) {
+    // local item -> (row group, round), clamped to the last row group past the end
+    auto item_of = [&](int itl, int& rg, int& i) __attribute__((always_inline)) {
         const int it = (wid + (itl / NR) * nw) * NR + (itl % NR);
         const int itc = it < total ? it : total - NR + (it % NR);
-        const int n = (itc / NR) * G + g;
-        return n < n_out ? n : n_out - 1;
+        rg = itc / NR;
+        i = itc % NR;
     };
-    auto load_item = [&](int it, int i, uint32_t(&wr)[R][17]) __attribute__((always_inline)) {
-        const int n = item_row(it);
-        const int p = j + S * i;
-        const int pc = p < P ? p : p - P;
+    // copy item itl's bytes (R rows) into LDS slot `slot`: 5 * R vmcnt events
+    auto issue = [&](int itl, int slot) __attribute__((always_inline)) {
+        int rg, i;
+        item_of(itl, rg, i);
+        rg = __builtin_amdgcn_readfirstlane(rg);
+        i = __builtin_amdgcn_readfirstlane(i);
+        const int row0 = rg * G;
+        int len;
+        if (G > 1) {  // G whole rows (P <= S): the rows that exist
+            const int rows = (n_out - row0) < G ? (n_out - row0) : G;
+            len = rows * P * 68;
+        } else {  // pairs S*i .. of one row
+            const int pairs = (P - S * i) < S ? (P - S * i) : S;
+            len = pairs * 68;
+        }
 #pragma unroll
-        for (int r = 0; r < R; ++r) load_pair(w + (size_t)(n + r * n_out) * row_bytes + 68 * (size_t)pc, wr[r]);
+        for (int r = 0; r < R; ++r)
+            lds_copy_4352(w + (size_t)(row0 + r * n_out) * row_bytes + (size_t)68 * S * i, len,
+                          ring_lds + (slot * R + r) * kLdsItemBytes, lane);
     };
 
-    float acc[R][M];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
-
-    // The ring's first weight loads are issued before the activations are staged, so the
-    // weights' HBM latency runs under the staging instead of after it (with one round per
-    // row; with more, the extra live registers cost the ring its overlap).
-    uint32_t ring[D][R][17];
-    auto ring_prologue = [&]() __attribute__((always_inline)) {
-        static_for<D - 1>([&](auto sc) __attribute__((always_inline)) {
-            constexpr int s = decltype(sc)::value;
-            load_item(s, s % NR, ring[s]);
-        });
-    };
-    if constexpr (NR == 1) ring_prologue();
-    // Activations: one coalesced pass from global into the slot-major LDS layout per
-    // block, then each lane copies the values of its own pair slots into registers.
-    stage_x_lds(x_lds, M, P, [&](int m) { return x + (size_t)m * ldx; }, threadIdx.x, kThreads);
-    __syncthreads();
-    if (wid >= total / NR) return;
-    float4 xr[NR][M][16];
+    const bool active = wid < total / NR;
+    const int n_pro = active ? (ipw < D ? ipw : D) : 0;
+    for (int q = wv; q < P; q += NW)
+        lds_copy4(reinterpret_cast<const uint8_t*>(x) + 256 * q + 4 * lane, x_lds + kXRow * q);
+    static_for<D>([&](auto sc) __attribute__((always_inline)) {
+        constexpr int s = decltype(sc)::value;
+        if (s < n_pro) issue(s, s);
+    });
+    // the activation copies are the oldest: wait until at most the weight prologue is
+    // outstanding, then every wave's share of x is in LDS after the barrier
+    static_for<D + 1>([&](auto kc) __attribute__((always_inline)) {
+        constexpr int k = decltype(kc)::value;
+        if (n_pro == k) wait_vmcnt_mem<k * 5 * R>();
+    });
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (!active) return;
+    float4 xr[NR][1][16];
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
         const int p = j + S * i;
-        const int pc = p < P ? p : p - P;
+        const int pc = p < P ? p : p - P;  // a slot past the row: any pair (not multiplied)
 #pragma unroll
-        for (int m = 0; m < M; ++m)
-#pragma unroll
-            for (int c = 0; c < 16; ++c) xr[i][m][c] = x_lds[(m * 16 + c) * P + pc];
+        for (int c = 0; c < 16; ++c) xr[i][0][c] = *reinterpret_cast<const float4*>(smem + kXRow * pc + 16 * c);
     }
-    if constexpr (NR > 1) ring_prologue();
+    float acc[R][1];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r][0] = 0.0f;
 
-    // One ring step: prefetch item it+D-1 (when LOAD), multiply item it, and finish the
-    // row after its last round.
-    auto step = [&](int it0, auto sc, auto load_tag) __attribute__((always_inline)) {
-        constexpr int s = decltype(sc)::value;
-        constexpr int i = s % NR;
-        const int it = it0 + s;
-        if constexpr (decltype(load_tag)::value) load_item(it + D - 1, (s + D - 1) % NR, ring[(s + D - 1) % D]);
-        if (j + S * i < P) mac_pair<M, R>(ring[s], XArr<M>{xr[i]}, j + S * i, acc);
-        if constexpr (i == NR - 1) {
-            for (int off = S >> 1; off >= 1; off >>= 1) {
-#pragma unroll
-                for (int r = 0; r < R; ++r)
-#pragma unroll
-                    for (int m = 0; m < M; ++m) acc[r][m] += __shfl_xor(acc[r][m], off, 64);
+    for (int rgl = 0; rgl < ipw / NR; ++rgl) {
+        static_for<NR>([&](auto ic) __attribute__((always_inline)) {
+            constexpr int i = decltype(ic)::value;
+            const int itl = rgl * NR + i;
+            const int slot = itl % D;
+            // items itl .. min(itl + D - 1, ipw - 1) are in flight: wait for the oldest
+            const int rem = ipw - 1 - itl;
+            if (rem >= D - 1) {
+                wait_vmcnt_mem<(D - 1) * 5 * R>();
+            } else {
+                static_for<D - 1>([&](auto kc) __attribute__((always_inline)) {
+                    constexpr int k = decltype(kc)::value;
+                    if (rem == k) wait_vmcnt_mem<k * 5 * R>();
+                });
             }
-            const int n = item_row(it);
+            int rg, ii;
+            item_of(itl, rg, ii);
+            const int n = rg * G + g;
+            const int nc = n < n_out ? n : n_out - 1;  // a lane past the matrix: the last row
+            const int lds_off = (G > 1 ? (nc - rg * G) * P * 68 : 0) + 68 * j;
+            uint32_t wr[R][17];
 #pragma unroll
-            for (int m = 0; m < M; ++m) {
+            for (int r = 0; r < R; ++r) {
+                const uint32_t* src = reinterpret_cast<const uint32_t*>(ring + (slot * R + r) * kLdsItemBytes + lds_off);
+#pragma unroll
+                for (int q = 0; q < 17; ++q) wr[r][q] = src[q];
+            }
+            wait_lgkmcnt_mem<0>();
+            if (itl + D < ipw) issue(itl + D, slot);  // refill the slot just read
+            if (j + S * i < P) mac_pair<1, R>(wr, XArr<1>{xr[i]}, j + S * i, acc);
+            if constexpr (i == NR - 1) {
+                for (int off = S >> 1; off >= 1; off >>= 1) {
+#pragma unroll
+                    for (int r = 0; r < R; ++r) acc[r][0] += __shfl_xor(acc[r][0], off, 64);
+                }
+                // every lane of the row holds the same bits: all store
                 if constexpr (R == 2)
-                    y[(size_t)m * ldy + n] = silu_mul(acc[0][m], acc[1][m]);
+                    y[nc] = silu_mul(acc[0][0], acc[1][0]);
                 else
-                    y[(size_t)m * ldy + n] = acc[0][m];
+                    y[nc] = acc[0][0];
+#pragma unroll
+                for (int r = 0; r < R; ++r) acc[r][0] = 0.0f;
             }
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-#pragma unroll
-                for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
-        }
-    };
-    // Steady state: every step prefetches.  The last ring of the wave is straight-line
-    // code that only prefetches the wave's final item, so no load sits in a branch.
-    const int last = ipw - D;
-    for (int it0 = 0; it0 < last; it0 += D)
-        static_for<D>([&](auto sc) __attribute__((always_inline)) { step(it0, sc, std::true_type{}); });
-    static_for<D>([&](auto sc) __attribute__((always_inline)) {
-        step(last, sc, std::integral_constant<bool, decltype(sc)::value == 0>{});
-    });
+        });
+    }
 }
 
 // Block-pair formats of the rows kernel.  A "pair" is two consecutive blocks (64
@@ -426,67 +454,61 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(1,
 
 namespace {
 
-// Blocks resident per CU for a kernel, queried once per kernel and LDS size.
-template <class K>
-int resident_blocks(K kernel, size_t lds) {
+template <int R, int NR, int D, int NW>
+hipError_t launch_one_row(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, int log2S, const float* x,
+                          float* y, hipStream_t stream) {
+    auto kernel = gemv_one_row_kernel<R, NR, D, NW>;
+    const size_t lds = (size_t)P * kXRow + (size_t)NW * D * R * kLdsItemBytes;
+    // Once per device: allow the largest dynamic LDS this instance uses (rows of up to
+    // 64*NR pairs), above the default limit.  Resident blocks per CU depend on the LDS
+    // size: kept for the last few sizes seen (a model alternates a handful of shapes).
+    constexpr size_t kLdsMax = (size_t)64 * NR * kXRow + (size_t)NW * D * R * kLdsItemBytes;
+    struct Occ { int dev, lds, per_cu; };
+    static thread_local int attr_dev = -1;
+    static thread_local Occ occ[4] = {{-1, -1, 1}, {-1, -1, 1}, {-1, -1, 1}, {-1, -1, 1}};
+    static thread_local int occ_next = 0;
+    if (attr_dev != dev.device) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax);
+        if (e != hipSuccess) return e;
+        attr_dev = dev.device;
+    }
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, lds) != hipSuccess || per_cu < 1)
-        per_cu = 1;
-    return per_cu;
-}
-
-inline int grid_for(const DeviceInfo& dev, int per_cu, int row_groups) {
-    const int want = (row_groups + kWaves - 1) / kWaves;
-    int blocks = dev.cu_count * per_cu;
-    if (blocks > want) blocks = want;
-    return blocks < 1 ? 1 : blocks;
-}
-
-template <int M, int R, int NR, int D, int WPE>
-hipError_t launch_xreg(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, int log2S, const float* x, int ldx,
-                       float* y, int ldy, hipStream_t stream) {
-    const size_t lds = (size_t)M * P * 256;
-    static thread_local int cached_lds = -1, per_cu = 1;
-    if (cached_lds != (int)lds) {
-        per_cu = resident_blocks(gemv_xreg_kernel<M, R, NR, D, WPE>, lds);
-        cached_lds = (int)lds;
+    for (const Occ& o : occ)
+        if (o.dev == dev.device && o.lds == (int)lds) per_cu = o.per_cu;
+    if (per_cu == 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64 * NW, lds) != hipSuccess || per_cu < 1)
+            per_cu = 1;
+        occ[occ_next] = {dev.device, (int)lds, per_cu};
+        occ_next = (occ_next + 1) & 3;
     }
     const int G = 64 >> log2S;
     const int total = ((n_out + G - 1) / G) * NR;
-    // items per wave: enough to cover the work with the waves that fit at once, rounded
-    // up to a multiple of the ring depth (at least one ring)
-    const int resident = dev.cu_count * per_cu * kWaves;
+    // items per wave: enough to cover the work with the waves that fit at once, a
+    // multiple of the rounds per row group
+    const int resident = dev.cu_count * per_cu * NW;
     int ipw = (total + resident - 1) / resident;
-    ipw = ((ipw + D - 1) / D) * D;
+    ipw = ((ipw + NR - 1) / NR) * NR;
     const int waves = (total + ipw - 1) / ipw;
-    const int blocks = (waves + kWaves - 1) / kWaves;
-    hipLaunchKernelGGL((gemv_xreg_kernel<M, R, NR, D, WPE>), dim3(blocks), dim3(kThreads), lds, stream, w, n_out, P,
-                       log2S, x, ldx, y, ldy, ipw);
+    const int blocks = (waves + NW - 1) / NW;
+    hipLaunchKernelGGL(kernel, dim3(blocks), dim3(64 * NW), lds, stream, w, n_out, P, log2S, x, y, ipw);
     return hipGetLastError();
 }
 
-// Register-resident activations for one row and at most 4 pair rounds per lane
-// (K <= 16384); the ring depth is a multiple of the rounds.
-template <int M, int R>
-bool try_xreg_m(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, int log2S, const float* x, int ldx,
-              float* y, int ldy, hipStream_t stream, hipError_t* err) {
+// One activation row with K <= 16384 (at most 4 rounds of 64 pairs per row; activations
+// in registers).  Two slots per wave; 4 waves per block for the fused gate_up (two rows
+// per item), 8 for one row per item (the LDS then holds about the same bytes in flight).
+template <int R>
+bool try_one_row(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, int log2S, const float* x, float* y,
+                 hipStream_t stream, hipError_t* err) {
     const int S = 1 << log2S;
-    const int NR = (P + S - 1) / S;
-    // (ring depth, waves per SIMD) per shape: the ring and the activations stay in registers
-    switch (NR) {
-        case 1: {
-            // A matrix with few row groups would leave most SIMDs idle if every wave had to
-            // fill a whole ring: shallower rings give one wave per SIMD first.
-            const int items = (n_out + (64 >> log2S) - 1) / (64 >> log2S);
-            const int simds = dev.cu_count * kWaves;
-            if (items <= simds) *err = launch_xreg<M, R, 1, 1, 4>(dev, w, n_out, P, log2S, x, ldx, y, ldy, stream);
-            else if (items <= 2 * simds) *err = launch_xreg<M, R, 1, 2, 3>(dev, w, n_out, P, log2S, x, ldx, y, ldy, stream);
-            else *err = launch_xreg<M, R, 1, (R == 1 ? 4 : 3), (R == 1 ? 3 : 2)>(dev, w, n_out, P, log2S, x, ldx, y, ldy, stream);
-            return true;
-        }
-        case 2: *err = launch_xreg<M, R, 2, (R == 1 ? 4 : 2), 2>(dev, w, n_out, P, log2S, x, ldx, y, ldy, stream); return true;
-        case 3: *err = launch_xreg<M, R, 3, 3, 1>(dev, w, n_out, P, log2S, x, ldx, y, ldy, stream); return true;
-        case 4: *err = launch_xreg<M, R, 4, 4, 1>(dev, w, n_out, P, log2S, x, ldx, y, ldy, stream); return true;
+    constexpr int NW = R == 2 ? 4 : 8;
+    switch ((P + S - 1) / S) {
+        case 1: *err = launch_one_row<R, 1, 2, NW>(dev, w, n_out, P, log2S, x, y, stream); return true;
+        case 2: *err = launch_one_row<R, 2, 2, NW>(dev, w, n_out, P, log2S, x, y, stream); return true;
+        case 3: *err = launch_one_row<R, 3, 2, NW>(dev, w, n_out, P, log2S, x, y, stream); return true;
+        // 256 activations a lane: 4 waves a block, so a wave may use more registers
+        case 4: *err = launch_one_row<R, 4, 2, 4>(dev, w, n_out, P, log2S, x, y, stream); return true;
         default: return false;
     }
 }
@@ -594,10 +616,10 @@ hipError_t launch_gemv_q8(const DeviceInfo& dev, const uint8_t* w, int64_t n_out
                           const float* x, int64_t m, int64_t ldx, float* y, int64_t ldy, hipStream_t stream) {
     const int P = (int)(k / 64);
     const int log2S = slots_log2(P);
-    if (m == 1) {  // one row: the register-ring kernel when K fits it
+    if (m == 1) {  // one row: the LDS-streaming kernel when K fits it
         hipError_t e;
-        if (silu_pairs ? try_xreg_m<1, 2>(dev, w, (int)n_out, P, log2S, x, (int)ldx, y, (int)ldy, stream, &e)
-                       : try_xreg_m<1, 1>(dev, w, (int)n_out, P, log2S, x, (int)ldx, y, (int)ldy, stream, &e))
+        if (silu_pairs ? try_one_row<2>(dev, w, (int)n_out, P, log2S, x, y, stream, &e)
+                       : try_one_row<1>(dev, w, (int)n_out, P, log2S, x, y, stream, &e))
             return e;
     }
     // several rows (or one row with K beyond the register kernel): 8-row launches

@@ -33,4 +33,71 @@ __device__ __forceinline__ void lds_copy16(const void* src, void* lds) {
         : "v"(src), "s"(base));
 }
 
+// The same wait with a compiler memory barrier: nothing is moved across it, so LDS reads
+// after it see what direct-to-LDS copies older than the limit wrote.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_mem() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_lgkmcnt_mem() {
+    static_assert(N >= 0 && N < 16, "lgkmcnt range");
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// One wave-wide 256-byte direct-to-LDS copy: lane l copies 4 bytes from its src to
+// lds + 4*l (lds is the wave-uniform 32-bit LDS address).
+__device__ __forceinline__ void lds_copy4(const void* src, uint32_t lds) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(lds)
+        : "memory");
+}
+
+// 4352 contiguous bytes (4 x 1 KB with 16 bytes a lane, then 256 B with 4 bytes a lane)
+// from src to lds .. lds + 4351, as five direct-to-LDS loads (five vmcnt events).  Only
+// the first len bytes (len >= 16, a multiple of 4) are read: a lane whose bytes lie past
+// them reads the last 16 (or 4) bytes instead, and what it writes is never used.
+constexpr int kLdsItemBytes = 4352;
+__device__ __forceinline__ void lds_copy_4352(const uint8_t* src, int len, uint32_t lds, int lane) {
+    const uint8_t* p[5];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int off = 1024 * c + 16 * lane;
+        p[c] = src + (off <= len - 16 ? off : len - 16);
+    }
+    const int off4 = 4096 + 4 * lane;
+    p[4] = src + (off4 <= len - 4 ? off4 : len - 4);
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %6\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %7\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, off\n\t"
+        "s_mov_b32 m0, %8\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %3, off\n\t"
+        "s_mov_b32 m0, %9\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %4, off\n\t"
+        "s_mov_b32 m0, %10\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %5, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "s"(lds), "s"(lds + 1024), "s"(lds + 2048),
+          "s"(lds + 3072), "s"(lds + 4096)
+        : "memory");
+}
+
 }  // namespace q8k
