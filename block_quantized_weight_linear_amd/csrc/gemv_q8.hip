@@ -140,6 +140,20 @@ __global__ __launch_bounds__(64 * NW) void gemv_one_row_kernel(const uint8_t* __
     float acc[R][1];
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r][0] = 0.0f;
+    // Outputs wait in registers: the result of the wave's t-th row group stays in lanes
+    // j == t % S (one per output row of the group) and goes out in one store per S row
+    // groups.  A store between the weight copies would also be counted by the vmcnt waits
+    // above and make them wait for the newest copies.
+    float keep = 0.0f;
+    int kept_base = 0;  // local row group of lane j == 0's kept value
+    auto flush = [&](int count) __attribute__((always_inline)) {
+        if (j < count) {
+            int rg, ii;
+            item_of((kept_base + j) * NR, rg, ii);
+            const int n = rg * G + g;
+            y[n < n_out ? n : n_out - 1] = keep;  // a clamped duplicate stores the same bits
+        }
+    };
 
     for (int rgl = 0; rgl < ipw / NR; ++rgl) {
         static_for<NR>([&](auto ic) __attribute__((always_inline)) {
@@ -176,16 +190,20 @@ __global__ __launch_bounds__(64 * NW) void gemv_one_row_kernel(const uint8_t* __
 #pragma unroll
                     for (int r = 0; r < R; ++r) acc[r][0] += __shfl_xor(acc[r][0], off, 64);
                 }
-                // every lane of the row holds the same bits: all store
-                if constexpr (R == 2)
-                    y[nc] = silu_mul(acc[0][0], acc[1][0]);
-                else
-                    y[nc] = acc[0][0];
+                // every lane of the row holds the same bits
+                const float v = R == 2 ? silu_mul(acc[0][0], acc[R - 1][0]) : acc[0][0];
+                const int t = rgl - kept_base;
+                if (j == t) keep = v;
+                if (t == S - 1) {
+                    flush(S);
+                    kept_base = rgl + 1;
+                }
 #pragma unroll
                 for (int r = 0; r < R; ++r) acc[r][0] = 0.0f;
             }
         });
     }
+    flush(ipw / NR - kept_base);
 }
 
 // Block-pair formats of the rows kernel.  A "pair" is two consecutive blocks (64
@@ -496,18 +514,31 @@ hipError_t launch_one_row(const DeviceInfo& dev, const uint8_t* w, int n_out, in
 }
 
 // One activation row with K <= 16384 (at most 4 rounds of 64 pairs per row; activations
-// in registers).  Two slots per wave; 4 waves per block for the fused gate_up (two rows
-// per item), 8 for one row per item (the LDS then holds about the same bytes in flight).
+// in registers).  With at least two items per wave for 8-wave blocks (the 8B shapes):
+// 8 waves and one slot each (the slot is refilled as soon as it is read, so one item is in
+// flight per wave while another is multiplied).  Smaller matrices (or 4 rounds, where the
+// activations need more registers): 4-wave blocks, spread over more CUs, two slots each.
+// Measured on the Qwen3 shapes.
 template <int R>
 bool try_one_row(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, int log2S, const float* x, float* y,
                  hipStream_t stream, hipError_t* err) {
     const int S = 1 << log2S;
-    constexpr int NW = R == 2 ? 4 : 8;
-    switch ((P + S - 1) / S) {
-        case 1: *err = launch_one_row<R, 1, 2, NW>(dev, w, n_out, P, log2S, x, y, stream); return true;
-        case 2: *err = launch_one_row<R, 2, 2, NW>(dev, w, n_out, P, log2S, x, y, stream); return true;
-        case 3: *err = launch_one_row<R, 3, 2, NW>(dev, w, n_out, P, log2S, x, y, stream); return true;
-        // 256 activations a lane: 4 waves a block, so a wave may use more registers
+    const int NR = (P + S - 1) / S;
+    const int64_t items = (int64_t)((n_out + (64 >> log2S) - 1) / (64 >> log2S)) * NR;
+    const bool wide = items >= (int64_t)16 * dev.cu_count;
+    switch (NR) {
+        case 1:
+            *err = wide ? launch_one_row<R, 1, 1, 8>(dev, w, n_out, P, log2S, x, y, stream)
+                        : launch_one_row<R, 1, 2, 4>(dev, w, n_out, P, log2S, x, y, stream);
+            return true;
+        case 2:
+            *err = wide ? launch_one_row<R, 2, 1, 8>(dev, w, n_out, P, log2S, x, y, stream)
+                        : launch_one_row<R, 2, 2, 4>(dev, w, n_out, P, log2S, x, y, stream);
+            return true;
+        case 3:
+            *err = wide && R == 1 ? launch_one_row<R, 3, 1, 8>(dev, w, n_out, P, log2S, x, y, stream)
+                                  : launch_one_row<R, 3, 2, 4>(dev, w, n_out, P, log2S, x, y, stream);
+            return true;
         case 4: *err = launch_one_row<R, 4, 2, 4>(dev, w, n_out, P, log2S, x, y, stream); return true;
         default: return false;
     }
