@@ -7,14 +7,17 @@
 // HBM ("14. Model families and example applications", section 14.1: no global
 // dequantization); every block is dequantized once per tile into LDS.
 //
-// Tile: 128 activation rows x BN weight rows (BN = 128 or 64; fused gate_up: BN/2 gate +
-// BN/2 up rows, interleaved in groups of 16 so a lane holds gate and up of the same
-// output), K in steps of 64 (one Q8_0 block pair per weight row).  Per step the 256
-// threads dequantize the tile's Q8_0 blocks (d * q rounded to bf16, exactly: d*q needs at
-// most 19 significant bits, then one rounding) and convert 128 x 64 activations to bf16
-// (round to nearest even), both into LDS rows padded to 144 bytes; each of the 4 waves
-// then runs a 64 x BN/2 sub-tile as 16 x 16 MFMA tiles, two K=32 steps.
-//
+// Tile: 128 activation rows x BN weight rows (BN = 256 with 8 waves, or 128 / 64 with 4;
+// fused gate_up: BN/2 gate + BN/2 up rows, interleaved in groups of 16 so a lane holds gate
+// and up of the same output), K in steps of 64 (one Q8_0 block pair per weight row).  Per
+// step the threads dequantize the tile's Q8_0 blocks (d * q rounded to bf16, exactly: d*q
+// needs at most 19 significant bits, then one rounding) and convert 128 x 64 activations to
+// bf16 (round to nearest even), both into LDS rows padded to 144 bytes; each wave then runs
+// a 64 x BN/(waves/2) sub-tile as 16 x 16 MFMA tiles, two K=32 steps.  Every weight tile
+// re-reads (from L2) and re-converts the float32 activations, so wider tiles cut that
+// traffic per flop: 256-wide tiles measured 1.16x (M = 512) to 1.45x (M = 2048) faster than
+// 128-wide ones on the Qwen3-8B gate_up.
+
 // Latency: the Q8_0 bytes come from HBM, so each thread keeps a ring of the next
 // kRing steps' blocks in registers (9 dwords a step); activations are re-read by every
 // weight tile and mostly hit L2, so one step of look-ahead covers them.  LDS is double
@@ -85,20 +88,23 @@ struct GroupArgs {
     bool gather;
 };
 
-template <int BN, bool SILU, bool GROUPED>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_q8_mfma_kernel(const uint8_t* __restrict__ w, int n_out, int P,
+template <int BN, bool SILU, bool GROUPED, int NT = 256>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_q8_mfma_kernel(const uint8_t* __restrict__ w, int n_out, int P,
                                                            const float* __restrict__ x, int M, int ldx,
                                                            float* __restrict__ y, int ldy, int m_tiles,
                                                            GroupArgs g) {
-    constexpr int TJ = BN / 32;        // 16x16 tiles per wave along n
-    constexpr int SPLIT = 128 / BN;    // threads per Q8_0 block (1: whole block, 2: 16 quants each)
-    static_assert(SPLIT == 1 || SPLIT == 2, "2*BN blocks per step over 256 threads");
+    constexpr int WN = NT / 128;       // waves along n (two along m)
+    constexpr int TJ = BN / (16 * WN); // 16x16 tiles per wave along n
+    constexpr int SPLIT = NT / (2 * BN);  // threads per Q8_0 block (1: whole block, 2: 16 quants each)
+    static_assert(SPLIT == 1 || SPLIT == 2, "2*BN blocks per step over NT threads");
+    constexpr int XPT = kBM * kBK / NT;   // activations per thread per step (32 or 16)
+    constexpr int XPR = kBK / XPT;        // threads per activation row
     __shared__ __attribute__((aligned(16))) __bf16 xs[2][kBM * kLdsRow];
     __shared__ __attribute__((aligned(16))) __bf16 ws[2][BN * kLdsRow];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = tid >> 6;
-    const int wm = wv & 1, wn = wv >> 1;
+    const int wm = wv & 1, wn = wv >> 1;  // wn < WN
     int mt = blockIdx.x % m_tiles;  // m tiles of one n tile run side by side (shared weights)
     int nt = blockIdx.x / m_tiles;
     int mbase = 0;  // grouped: first position of the tile (its rows are positions mbase + r)
@@ -126,13 +132,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // block 1 at bytes 2..3 (scale) and 4..35 (quants).
     const int wc = (tid / (2 * SPLIT)), wb = (tid / SPLIT) & 1, hh = tid & (SPLIT - 1);
     const uint8_t* wrow = w + (size_t)tile_row<BN, SILU>(nt, wc, n_out) * row_bytes + 32 * wb;
-    // activation role: 32 inputs (half xh of the step) of tile row xr
-    const int xr = tid >> 1, xh = tid & 1;
+    // activation role: XPT inputs (part xh of the step) of tile row xr
+    const int xr = tid / XPR, xh = tid % XPR;
     int xm = mt * kBM + xr;
     xm = xm < M ? xm : M - 1;
     size_t xoff = (size_t)xm;
     if constexpr (GROUPED) xoff = g.gather ? (size_t)(g.sorted[mbase + xm] / g.k) : (size_t)(mbase + xm);
-    const float* xrow = x + xoff * ldx + 32 * xh;
+    const float* xrow = x + xoff * ldx + XPT * xh;
 
     f32x4 acc[4][TJ];
 #pragma unroll
@@ -141,7 +147,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     Q8Pair ring[kRing];
-    float4 rx[8];
+    float4 rx[XPT / 4];
     auto load_w = [&](Q8Pair& r, int s) __attribute__((always_inline)) {
         const uint8_t* src = wrow + (size_t)68 * s;
         const u32x4_a4m a = *reinterpret_cast<const u32x4_a4m*>(src);
@@ -153,7 +159,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     auto load_x = [&](int s) __attribute__((always_inline)) {
         const float4* src = reinterpret_cast<const float4*>(xrow + kBK * s);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) rx[i] = src[i];
+        for (int i = 0; i < XPT / 4; ++i) rx[i] = src[i];
     };
     auto store_w = [&](const Q8Pair& r, int buf) __attribute__((always_inline)) {
         const float d = wb == 0 ? mf_half_lo(r.dw[0]) : mf_half_hi(r.dw[0]);
@@ -177,17 +183,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int i = 0; i < NQ / 8; ++i) dst[i] = v[i];
     };
     auto store_x = [&](int buf) __attribute__((always_inline)) {
-        bf16x8 v[4];
+        bf16x8 v[XPT / 8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < XPT / 4; ++i) {
             v[i >> 1][4 * (i & 1) + 0] = (__bf16)rx[i].x;
             v[i >> 1][4 * (i & 1) + 1] = (__bf16)rx[i].y;
             v[i >> 1][4 * (i & 1) + 2] = (__bf16)rx[i].z;
             v[i >> 1][4 * (i & 1) + 3] = (__bf16)rx[i].w;
         }
-        bf16x8* dst = reinterpret_cast<bf16x8*>(&xs[buf][xr * kLdsRow + 32 * xh]);
+        bf16x8* dst = reinterpret_cast<bf16x8*>(&xs[buf][xr * kLdsRow + XPT * xh]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = v[i];
+        for (int i = 0; i < XPT / 8; ++i) dst[i] = v[i];
     };
     auto mma = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
@@ -199,7 +205,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 af[i] = *reinterpret_cast<const bf16x8*>(&xs[buf][(64 * wm + 16 * i + (lane & 15)) * kLdsRow + ko]);
 #pragma unroll
             for (int j = 0; j < TJ; ++j)
-                bfr[j] = *reinterpret_cast<const bf16x8*>(&ws[buf][((BN / 2) * wn + 16 * j + (lane & 15)) * kLdsRow + ko]);
+                bfr[j] = *reinterpret_cast<const bf16x8*>(&ws[buf][((BN / WN) * wn + 16 * j + (lane & 15)) * kLdsRow + ko]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -244,8 +250,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if constexpr (SILU) {
 #pragma unroll
                 for (int jp = 0; jp < TJ / 2; ++jp) {
-                    // wave columns (BN/2)*wn + 16*j: even j gate, odd j up of the same outputs
-                    const int f = nt * (BN / 2) + (BN / 4) * wn + 16 * jp + (lane & 15);
+                    // wave columns (BN/WN)*wn + 16*j: even j gate, odd j up of the same outputs
+                    const int f = nt * (BN / 2) + (BN / (2 * WN)) * wn + 16 * jp + (lane & 15);
                     if (f < n_out) {
                         const float g = acc[i][2 * jp][e];
                         const float u = acc[i][2 * jp + 1][e];
@@ -255,7 +261,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             } else {
 #pragma unroll
                 for (int j = 0; j < TJ; ++j) {
-                    const int n = nt * BN + (BN / 2) * wn + 16 * j + (lane & 15);
+                    const int n = nt * BN + (BN / WN) * wn + 16 * j + (lane & 15);
                     if (n < n_out) y[(size_t)m * ldy + n] = acc[i][j][e];
                 }
             }
@@ -263,7 +269,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 }
 
-template <int BN>
+template <int BN, int NT = 256>
 hipError_t launch_tiles(const uint8_t* w, int64_t n_out, int P, bool silu, const float* x, int64_t m, int64_t ldx,
                         float* y, int64_t ldy, hipStream_t stream) {
     const GroupArgs none{};
@@ -272,10 +278,10 @@ hipError_t launch_tiles(const uint8_t* w, int64_t n_out, int P, bool silu, const
     const int64_t blocks = (n_out + cols - 1) / cols * m_tiles;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     if (silu)
-        hipLaunchKernelGGL((gemm_q8_mfma_kernel<BN, true, false>), dim3((unsigned)blocks), dim3(256), 0, stream, w,
+        hipLaunchKernelGGL((gemm_q8_mfma_kernel<BN, true, false, NT>), dim3((unsigned)blocks), dim3(NT), 0, stream, w,
                            (int)n_out, P, x, (int)m, (int)ldx, y, (int)ldy, m_tiles, none);
     else
-        hipLaunchKernelGGL((gemm_q8_mfma_kernel<BN, false, false>), dim3((unsigned)blocks), dim3(256), 0, stream, w,
+        hipLaunchKernelGGL((gemm_q8_mfma_kernel<BN, false, false, NT>), dim3((unsigned)blocks), dim3(NT), 0, stream, w,
                            (int)n_out, P, x, (int)m, (int)ldx, y, (int)ldy, m_tiles, none);
     return hipGetLastError();
 }
@@ -285,16 +291,16 @@ hipError_t launch_gemm_q8_mfma_grouped(const uint8_t* w_stack, size_t expert_byt
                                        const int32_t* offsets, const int32_t* tile_start, const int32_t* sorted,
                                        int n_exp, int top_k, bool gather, int64_t max_tiles, hipStream_t stream) {
     const int P = (int)(k / kBK);
-    const int64_t cols = silu_pairs ? 64 : 128;  // outputs per 128 x 128 tile
+    const int64_t cols = silu_pairs ? 128 : 256;  // outputs per 128 x 256 tile
     const int n_tiles = (int)((n_out + cols - 1) / cols);
     const int64_t blocks = max_tiles * n_tiles;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     const GroupArgs g{offsets, tile_start, sorted, n_exp, top_k, n_tiles, expert_bytes, gather};
     if (silu_pairs)
-        hipLaunchKernelGGL((gemm_q8_mfma_kernel<128, true, true>), dim3((unsigned)blocks), dim3(256), 0, stream,
+        hipLaunchKernelGGL((gemm_q8_mfma_kernel<256, true, true, 512>), dim3((unsigned)blocks), dim3(512), 0, stream,
                            w_stack, (int)n_out, P, x, 0, (int)ldx, y, (int)ldy, 1, g);
     else
-        hipLaunchKernelGGL((gemm_q8_mfma_kernel<128, false, true>), dim3((unsigned)blocks), dim3(256), 0, stream,
+        hipLaunchKernelGGL((gemm_q8_mfma_kernel<256, false, true, 512>), dim3((unsigned)blocks), dim3(512), 0, stream,
                            w_stack, (int)n_out, P, x, 0, (int)ldx, y, (int)ldy, 1, g);
     return hipGetLastError();
 }
@@ -302,10 +308,13 @@ hipError_t launch_gemm_q8_mfma_grouped(const uint8_t* w_stack, size_t expert_byt
 hipError_t launch_gemm_q8_mfma(const DeviceInfo& dev, const uint8_t* w, int64_t n_out, int64_t k, bool silu_pairs,
                                const float* x, int64_t m, int64_t ldx, float* y, int64_t ldy, hipStream_t stream) {
     const int P = (int)(k / kBK);
-    // 128 x 128 tiles when they give at least one tile per CU, else 128 x 64 (small N
-    // stays spread over the chip at the cost of reading the activations twice as often).
+    // The widest tiles that still give at least one tile per CU: 128 x 256 (8 waves),
+    // 128 x 128, else 128 x 64 (small N stays spread over the chip at the cost of reading
+    // the activations more often).
     const int64_t cols128 = silu_pairs ? 64 : 128;
     const int64_t tiles128 = ((n_out + cols128 - 1) / cols128) * ((m + kBM - 1) / kBM);
+    const int64_t tiles256 = (tiles128 + 1) / 2;
+    if (tiles256 >= dev.cu_count) return launch_tiles<256, 512>(w, n_out, P, silu_pairs, x, m, ldx, y, ldy, stream);
     if (tiles128 >= dev.cu_count) return launch_tiles<128>(w, n_out, P, silu_pairs, x, m, ldx, y, ldy, stream);
     return launch_tiles<64>(w, n_out, P, silu_pairs, x, m, ldx, y, ldy, stream);
 }
