@@ -285,8 +285,11 @@ def test_graph_replay_matches_eager(q8):
 PREFILL_TOL = 2e-2   # bf16 operands, float32 accumulation
 
 
+# With at least as many 128 x 256 tiles as CUs (256 on the MI355X) the prefill runs 8-wave
+# 128 x 256 tiles: (32768, 256, 256) and the ragged (33000, 256, 300) take that path there;
+# the smaller shapes take the 4-wave 128 x 128 / 128 x 64 tiles.
 @pytest.mark.parametrize("n,k,m", [(300, 1024, 256), (129, 512, 300), (1024, 4096, 512), (77, 3072, 257),
-                                   (520, 256, 1000)])
+                                   (520, 256, 1000), (32768, 256, 256), (33000, 256, 300)])
 def test_prefill_vs_oracle(q8, n, k, m):
     lib, torch, dev = q8
     wb, _, _ = wl.q8_weight(91 + n, n, k)
@@ -299,7 +302,8 @@ def test_prefill_vs_oracle(q8, n, k, m):
     assert_close(y, diag, f"prefill vs bf16-operand oracle n={n} m={m}", tol=1e-4)
 
 
-@pytest.mark.parametrize("f,k,m", [(64, 1024, 256), (200, 512, 300), (1536, 2048, 512)])
+@pytest.mark.parametrize("f,k,m", [(64, 1024, 256), (200, 512, 300), (1536, 2048, 512), (16384, 256, 256),
+                                   (16500, 256, 260)])
 def test_prefill_fused_vs_oracle(q8, f, k, m):
     lib, torch, dev = q8
     wb, _, _ = wl.q8_weight(93 + f, 2 * f, k)
@@ -327,7 +331,7 @@ def test_prefill_qwen3_8b_gate_up_sampled(q8):
                  "8b gate_up m=512 vs bf16-operand oracle", tol=1e-4)
 
 
-@pytest.mark.parametrize("n,k,m", [(4096, 1024, 256), (1000, 4096, 512)])
+@pytest.mark.parametrize("n,k,m", [(4096, 1024, 256), (1000, 4096, 512), (32768, 256, 256)])
 def test_prefill_exact_arithmetic(q8, n, k, m):
     """Integer activations and scales 2^-7 / 2^-8: bf16 holds every operand exactly and every
     float32 partial sum is exact, so the matrix-core result equals the oracle bit for bit."""
