@@ -63,7 +63,7 @@ struct XArr {
 // butterfly over the S slots).
 constexpr int kXRow = 272;
 
-template <int R, int NR, int D, int NW>
+template <int R, int NR, int D, int NW, bool NT>
 __global__ __launch_bounds__(64 * NW) void gemv_one_row_kernel(const uint8_t* __restrict__ w, int n_out, int P,
                                                               int log2S, const float* __restrict__ x,
                                                               float* __restrict__ y, int ipw) {
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_one_row_kernel(const uint8_t* __
         }
 #pragma unroll
         for (int r = 0; r < R; ++r)
-            lds_copy_4352(w + (size_t)(row0 + r * n_out) * row_bytes + (size_t)68 * S * i, len,
+            lds_copy_4352<NT>(w + (size_t)(row0 + r * n_out) * row_bytes + (size_t)68 * S * i, len,
                           ring_lds + (slot * R + r) * kLdsItemBytes, lane);
     };
 
@@ -472,10 +472,10 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(1,
 
 namespace {
 
-template <int R, int NR, int D, int NW>
+template <int R, int NR, int D, int NW, bool NT = false>
 hipError_t launch_one_row(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, int log2S, const float* x,
                           float* y, hipStream_t stream) {
-    auto kernel = gemv_one_row_kernel<R, NR, D, NW>;
+    auto kernel = gemv_one_row_kernel<R, NR, D, NW, NT>;
     const size_t lds = (size_t)P * kXRow + (size_t)NW * D * R * kLdsItemBytes;
     // Once per device: allow the largest dynamic LDS this instance uses (rows of up to
     // 64*NR pairs), above the default limit.  Resident blocks per CU depend on the LDS
@@ -516,9 +516,10 @@ hipError_t launch_one_row(const DeviceInfo& dev, const uint8_t* w, int n_out, in
 // One activation row with K <= 16384 (at most 4 rounds of 64 pairs per row; activations
 // in registers).  With at least two items per wave for 8-wave blocks (the 8B shapes):
 // 8 waves and one slot each (the slot is refilled as soon as it is read, so one item is in
-// flight per wave while another is multiplied).  Smaller matrices (or 4 rounds, where the
-// activations need more registers): 4-wave blocks, spread over more CUs, two slots each.
-// Measured on the Qwen3 shapes.
+// flight per wave while another is multiplied), weight copies with the non-temporal hint
+// (2-6% faster there).  Smaller matrices (or 4 rounds, where the activations need more
+// registers): 4-wave blocks, spread over more CUs, two slots each, plain copies (the hint
+// measured slower on the Qwen3-0.6B shapes).  Measured on the Qwen3 shapes.
 template <int R>
 bool try_one_row(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, int log2S, const float* x, float* y,
                  hipStream_t stream, hipError_t* err) {
@@ -528,15 +529,15 @@ bool try_one_row(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, int 
     const bool wide = items >= (int64_t)16 * dev.cu_count;
     switch (NR) {
         case 1:
-            *err = wide ? launch_one_row<R, 1, 1, 8>(dev, w, n_out, P, log2S, x, y, stream)
+            *err = wide ? launch_one_row<R, 1, 1, 8, true>(dev, w, n_out, P, log2S, x, y, stream)
                         : launch_one_row<R, 1, 2, 4>(dev, w, n_out, P, log2S, x, y, stream);
             return true;
         case 2:
-            *err = wide ? launch_one_row<R, 2, 1, 8>(dev, w, n_out, P, log2S, x, y, stream)
+            *err = wide ? launch_one_row<R, 2, 1, 8, true>(dev, w, n_out, P, log2S, x, y, stream)
                         : launch_one_row<R, 2, 2, 4>(dev, w, n_out, P, log2S, x, y, stream);
             return true;
         case 3:
-            *err = wide && R == 1 ? launch_one_row<R, 3, 1, 8>(dev, w, n_out, P, log2S, x, y, stream)
+            *err = wide && R == 1 ? launch_one_row<R, 3, 1, 8, true>(dev, w, n_out, P, log2S, x, y, stream)
                                   : launch_one_row<R, 3, 2, 4>(dev, w, n_out, P, log2S, x, y, stream);
             return true;
         case 4: *err = launch_one_row<R, 4, 2, 4>(dev, w, n_out, P, log2S, x, y, stream); return true;

@@ -64,8 +64,10 @@ __device__ __forceinline__ void lds_copy4(const void* src, uint32_t lds) {
 // 4352 contiguous bytes (4 x 1 KB with 16 bytes a lane, then 256 B with 4 bytes a lane)
 // from src to lds .. lds + 4351, as five direct-to-LDS loads (five vmcnt events).  Only
 // the first len bytes (len >= 16, a multiple of 4) are read: a lane whose bytes lie past
-// them reads the last 16 (or 4) bytes instead, and what it writes is never used.
+// them reads the last 16 (or 4) bytes instead, and what it writes is never used.  NT: the
+// loads carry the non-temporal hint (streamed data that is read once).
 constexpr int kLdsItemBytes = 4352;
+template <bool NT = false>
 __device__ __forceinline__ void lds_copy_4352(const uint8_t* src, int len, uint32_t lds, int lane) {
     const uint8_t* p[5];
 #pragma unroll
@@ -76,28 +78,34 @@ __device__ __forceinline__ void lds_copy_4352(const uint8_t* src, int len, uint3
     const int off4 = 4096 + 4 * lane;
     p[4] = src + (off4 <= len - 4 ? off4 : len - 4);
     uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %6\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, off\n\t"
-        "s_mov_b32 m0, %7\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %2, off\n\t"
-        "s_mov_b32 m0, %8\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %3, off\n\t"
-        "s_mov_b32 m0, %9\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %4, off\n\t"
-        "s_mov_b32 m0, %10\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dword %5, off\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "s"(lds), "s"(lds + 1024), "s"(lds + 2048),
-          "s"(lds + 3072), "s"(lds + 4096)
-        : "memory");
+#define Q8K_LDS_COPY_4352(H)                                                                                 \
+    asm volatile(                                                                                              \
+        "s_mov_b32 %0, m0\n\t"                                                                                 \
+        "s_mov_b32 m0, %6\n\t"                                                                                 \
+        "s_nop 0\n\t"                                                                                          \
+        "global_load_lds_dwordx4 %1, off" H "\n\t"                                                             \
+        "s_mov_b32 m0, %7\n\t"                                                                                 \
+        "s_nop 0\n\t"                                                                                          \
+        "global_load_lds_dwordx4 %2, off" H "\n\t"                                                             \
+        "s_mov_b32 m0, %8\n\t"                                                                                 \
+        "s_nop 0\n\t"                                                                                          \
+        "global_load_lds_dwordx4 %3, off" H "\n\t"                                                             \
+        "s_mov_b32 m0, %9\n\t"                                                                                 \
+        "s_nop 0\n\t"                                                                                          \
+        "global_load_lds_dwordx4 %4, off" H "\n\t"                                                             \
+        "s_mov_b32 m0, %10\n\t"                                                                                \
+        "s_nop 0\n\t"                                                                                          \
+        "global_load_lds_dword %5, off" H "\n\t"                                                               \
+        "s_mov_b32 m0, %0"                                                                                     \
+        : "=&s"(saved)                                                                                         \
+        : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "s"(lds), "s"(lds + 1024), "s"(lds + 2048),    \
+          "s"(lds + 3072), "s"(lds + 4096)                                                                     \
+        : "memory")
+    if constexpr (NT)
+        Q8K_LDS_COPY_4352(" nt");
+    else
+        Q8K_LDS_COPY_4352("");
+#undef Q8K_LDS_COPY_4352
 }
 
 }  // namespace q8k
