@@ -52,6 +52,25 @@ def test_fused_small_vs_oracle(q8, f, k, m):
     assert_close(h, oracle.fused_gate_up_silu_ref(wb, f, k, x), f"fused f={f} k={k} m={m}")
 
 
+# One activation row on matrices with at least 16 row groups per CU: the one-row kernel's
+# 8-wave configuration (non-temporal weight copies), 1, 2 and 3 rounds of 64 pairs, ragged
+# pair counts (K = 4352: 68 pairs; K = 6144: 96), plain and fused; full oracle.
+@pytest.mark.parametrize("n,k,fused", [(6144, 4096, False), (4096, 12288, False), (2048, 8192, False),
+                                       (5000, 6144, False), (4096, 4096, True), (2048, 8192, True),
+                                       (2100, 4352, True)])
+def test_one_row_large_vs_oracle(q8, n, k, fused):
+    lib, torch, dev = q8
+    wb, _, _ = wl.q8_weight(5000 + n + k, 2 * n if fused else n, k)
+    x = wl.activations(6000 + k, 1, k)
+    say(f"one row n={n} k={k} fused={fused}")
+    if fused:
+        h = lib.q8_linear_fused_gate_up_silu(to_dev(wb, dev), n, k, to_dev(x, dev)).cpu().numpy()
+        assert_close(h, oracle.fused_gate_up_silu_ref(wb, n, k, x), f"one row fused f={n} k={k}")
+    else:
+        y = lib.q8_linear(to_dev(wb, dev), n, k, to_dev(x, dev)).cpu().numpy()
+        assert_close(y, oracle.q8_linear_ref(wb, n, k, x), f"one row n={n} k={k}")
+
+
 # ------------------------------------------------------------ real layer shapes
 
 LAYER_LINEARS = [
@@ -89,7 +108,7 @@ def test_layer_shapes_sampled(q8, name, n, k, fused, rows):
 
 
 @pytest.mark.parametrize("n,k,m", [(4096, 1024, 1), (6144, 4096, 8), (4096, 12288, 3), (24576, 4096, 16),
-                                   (1024, 3072, 1), (999, 256, 33)])
+                                   (1024, 3072, 1), (999, 256, 33), (6144, 4096, 1), (4096, 12288, 1)])
 def test_exact_arithmetic_bit_identical(q8, n, k, m):
     """Integer activations in [-2, 2], scales 2^-7 / 2^-8: every float32 partial sum is exact."""
     lib, torch, dev = q8
