@@ -39,6 +39,108 @@ struct XArr {
     __device__ __forceinline__ float4 get(int m, int, int c) const { return v[m][c]; }
 };
 
+// Block-pair formats.  A "pair" is two consecutive blocks (64 weights); rows are 16-byte
+// aligned, so pairs start on dword boundaries.  weights<HALF> (the rows kernel) gives the 4
+// weights, as exact float32, of inputs 4*cc .. 4*cc+3 of block HALF; mac_row (the one-row
+// kernel) adds one pair of R rows against the lane's 64 activations x (float4 c holds inputs
+// 4c .. 4c+3 of the pair) and their per-block sums sx.
+struct FmtQ8_0 {  // 68 bytes: [d0 | 32 q] [d1 | 32 q]
+    static constexpr int kPairBytes = 68, kDwords = 17, kLoads = 5;
+    static __device__ __forceinline__ void load(const uint8_t* p, uint32_t (&w)[kDwords]) { load_pair(p, w); }
+    template <int HALF>
+    static __device__ __forceinline__ void weights(const uint32_t (&w)[kDwords], int cc, float (&wf)[4]) {
+        if constexpr (HALF == 0) {  // block 0: scale in dword 0 (low half), quants at bytes 2..33
+            const float d = half_lo(w[0]);
+            wf[0] = sbyte<2>(w[cc]) * d;
+            wf[1] = sbyte<3>(w[cc]) * d;
+            wf[2] = sbyte<0>(w[cc + 1]) * d;
+            wf[3] = sbyte<1>(w[cc + 1]) * d;
+        } else {  // block 1: scale in dword 8 (high half), quants in dwords 9..16
+            const float d = half_hi(w[8]);
+            const uint32_t v = w[9 + cc];
+            wf[0] = sbyte<0>(v) * d;
+            wf[1] = sbyte<1>(v) * d;
+            wf[2] = sbyte<2>(v) * d;
+            wf[3] = sbyte<3>(v) * d;
+        }
+    }
+    // per block: t = sum q*x, then acc = fma(d, t, acc) (gemv_core.h mac_pair)
+    template <int R>
+    static __device__ __forceinline__ void mac_row(const uint32_t (&w)[R][kDwords], const float4 (&x)[1][16],
+                                                   const float (&)[2], float (&acc)[R][1]);
+};
+
+// GGUF Q4_0: 36 bytes a pair, [d0 | 16 bytes] [d1 | 16 bytes]; weight j < 16 of a block is
+// the low nibble of its byte j, weight j + 16 the high nibble; w = d * (nibble - 8), exact
+// in float32 (a 4-bit integer times an 11-bit scale).
+struct FmtQ4_0 {
+    static constexpr int kPairBytes = 36, kDwords = 9, kLoads = 3;
+    static __device__ __forceinline__ void load(const uint8_t* p, uint32_t (&w)[kDwords]) {
+        const u32x4_a4 a = *reinterpret_cast<const u32x4_a4*>(p);
+        const u32x4_a4 b = *reinterpret_cast<const u32x4_a4*>(p + 16);
+        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+        w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+        w[8] = *reinterpret_cast<const uint32_t*>(p + 32);
+    }
+    template <int HALF>
+    static __device__ __forceinline__ void weights(const uint32_t (&w)[kDwords], int cc, float (&wf)[4]) {
+        const int c4 = cc & 3;  // quant dword of the block: bytes 4*c4 .. 4*c4+3
+        float d;
+        uint32_t v;
+        if constexpr (HALF == 0) {  // scale = low half of dword 0, quant bytes at 2..17
+            d = half_lo(w[0]);
+            v = __builtin_amdgcn_alignbyte(w[c4 + 1], w[c4], 2);
+        } else {  // scale = high half of dword 4, quant bytes in dwords 5..8
+            d = half_hi(w[4]);
+            v = w[5 + c4];
+        }
+        const uint32_t nib = (cc < 4 ? v : v >> 4) & 0x0F0F0F0Fu;  // inputs 4cc..: low nibbles, then high
+        // q*d - 8d in one fma: the exact value (q - 8)*d has at most 15 significant bits
+        const float m8d = -8.0f * d;
+        wf[0] = __builtin_fmaf((float)(nib & 0xFFu), d, m8d);
+        wf[1] = __builtin_fmaf((float)((nib >> 8) & 0xFFu), d, m8d);
+        wf[2] = __builtin_fmaf((float)((nib >> 16) & 0xFFu), d, m8d);
+        wf[3] = __builtin_fmaf((float)(nib >> 24), d, m8d);
+    }
+    // per block: t = sum nibble*x (nibbles 0..15, exact), then acc = fma(d, t - 8*sx, acc):
+    // sum (nibble - 8)*d*x with the offset carried by the block's activation sum sx
+    template <int R>
+    static __device__ __forceinline__ void mac_row(const uint32_t (&w)[R][kDwords], const float4 (&x)[1][16],
+                                                   const float (&sx)[2], float (&acc)[R][1]) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const float d = half == 0 ? half_lo(w[r][0]) : half_hi(w[r][4]);
+                float t = 0.0f;
+#pragma unroll
+                for (int c4 = 0; c4 < 4; ++c4) {
+                    // quant bytes 4*c4 .. 4*c4+3 of the block: weights j = 4*c4 + i (low nibbles)
+                    // and 16 + j (high nibbles)
+                    const uint32_t v = half == 0 ? __builtin_amdgcn_alignbyte(w[r][c4 + 1], w[r][c4], 2) : w[r][5 + c4];
+                    const uint32_t lo = v & 0x0F0F0F0Fu, hi = (v >> 4) & 0x0F0F0F0Fu;
+                    const float4 xl = x[0][8 * half + c4], xh = x[0][8 * half + 4 + c4];
+                    t = __builtin_fmaf((float)(lo & 0xFFu), xl.x, t);
+                    t = __builtin_fmaf((float)((lo >> 8) & 0xFFu), xl.y, t);
+                    t = __builtin_fmaf((float)((lo >> 16) & 0xFFu), xl.z, t);
+                    t = __builtin_fmaf((float)(lo >> 24), xl.w, t);
+                    t = __builtin_fmaf((float)(hi & 0xFFu), xh.x, t);
+                    t = __builtin_fmaf((float)((hi >> 8) & 0xFFu), xh.y, t);
+                    t = __builtin_fmaf((float)((hi >> 16) & 0xFFu), xh.z, t);
+                    t = __builtin_fmaf((float)(hi >> 24), xh.w, t);
+                }
+                acc[r][0] = __builtin_fmaf(d, t - 8.0f * sx[half], acc[r][0]);
+            }
+        }
+    }
+};
+
+template <int R>
+__device__ __forceinline__ void FmtQ8_0::mac_row(const uint32_t (&w)[R][kDwords], const float4 (&x)[1][16],
+                                                 const float (&)[2], float (&acc)[R][1]) {
+    mac_pair<1, R>(w, XArr<1>{x}, 0, acc);
+}
+
 // One activation row (the decode class).  A wave works on "items": the pairs j + S*i
 // (slot j, round i) of one row group, i.e. one contiguous stretch of at most 4352 weight
 // bytes per row (64 pairs; with G > 1 rows per wave, G whole rows).  The wave copies an
@@ -64,7 +166,7 @@ struct XArr {
 // butterfly over the S slots).
 constexpr int kXRow = 272;
 
-template <int R, int NR, int D, int NW, bool NT>
+template <class Fmt, int R, int NR, int D, int NW, bool NT>
 __global__ __launch_bounds__(64 * NW) void gemv_one_row_kernel(const uint8_t* __restrict__ w, int n_out, int P,
                                                               int log2S, const float* __restrict__ x,
                                                               float* __restrict__ y, int ipw) {
@@ -77,7 +179,8 @@ __global__ __launch_bounds__(64 * NW) void gemv_one_row_kernel(const uint8_t* __
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int j = lane & (S - 1);
     const int g = lane >> log2S;
-    const size_t row_bytes = (size_t)P * 68;
+    constexpr int PB = Fmt::kPairBytes;
+    const size_t row_bytes = (size_t)P * PB;
     const int total = ((n_out + G - 1) / G) * NR;  // items: (row group, round)
     const int wid = blockIdx.x * NW + wv;
     const int nw = gridDim.x * NW;
@@ -102,14 +205,14 @@ __global__ __launch_bounds__(64 * NW) void gemv_one_row_kernel(const uint8_t* __
         int len;
         if (G > 1) {  // G whole rows (P <= S): the rows that exist
             const int rows = (n_out - row0) < G ? (n_out - row0) : G;
-            len = rows * P * 68;
+            len = rows * P * PB;
         } else {  // pairs S*i .. of one row
             const int pairs = (P - S * i) < S ? (P - S * i) : S;
-            len = pairs * 68;
+            len = pairs * PB;
         }
 #pragma unroll
         for (int r = 0; r < R; ++r)
-            lds_copy_4352<NT>(w + (size_t)(row0 + r * n_out) * row_bytes + (size_t)68 * S * i, len,
+            lds_copy_4352<NT>(w + (size_t)(row0 + r * n_out) * row_bytes + (size_t)PB * S * i, len,
                           ring_lds + (slot * R + r) * kLdsItemBytes, lane);
     };
 
@@ -138,6 +241,23 @@ __global__ __launch_bounds__(64 * NW) void gemv_one_row_kernel(const uint8_t* __
 #pragma unroll
         for (int c = 0; c < 16; ++c) xr[i][0][c] = *reinterpret_cast<const float4*>(smem + kXRow * pc + 16 * c);
     }
+    // per-block activation sums of the lane's pairs (used by formats with an offset)
+    float sx[NR][2];
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+            float a = 0.0f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const float4 v = xr[i][0][8 * hb + c];
+                a += v.x;
+                a += v.y;
+                a += v.z;
+                a += v.w;
+            }
+            sx[i][hb] = a;
+        }
     float acc[R][1];
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r][0] = 0.0f;
@@ -175,17 +295,17 @@ __global__ __launch_bounds__(64 * NW) void gemv_one_row_kernel(const uint8_t* __
             item_of(itl, rg, ii);
             const int n = rg * G + g;
             const int nc = n < n_out ? n : n_out - 1;  // a lane past the matrix: the last row
-            const int lds_off = (G > 1 ? (nc - rg * G) * P * 68 : 0) + 68 * j;
-            uint32_t wr[R][17];
+            const int lds_off = (G > 1 ? (nc - rg * G) * P * PB : 0) + PB * j;
+            uint32_t wr[R][Fmt::kDwords];
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const uint32_t* src = reinterpret_cast<const uint32_t*>(ring + (slot * R + r) * kLdsItemBytes + lds_off);
 #pragma unroll
-                for (int q = 0; q < 17; ++q) wr[r][q] = src[q];
+                for (int q = 0; q < Fmt::kDwords; ++q) wr[r][q] = src[q];
             }
             wait_lgkmcnt_mem<0>();
             if (itl + D < ipw) issue(itl + D, slot);  // refill the slot just read
-            if (j + S * i < P) mac_pair<1, R>(wr, XArr<1>{xr[i]}, j + S * i, acc);
+            if (j + S * i < P) Fmt::template mac_row<R>(wr, xr[i], sx[i], acc);
             if constexpr (i == NR - 1) {
                 for (int off = S >> 1; off >= 1; off >>= 1) {
 #pragma unroll
@@ -206,65 +326,6 @@ __global__ __launch_bounds__(64 * NW) void gemv_one_row_kernel(const uint8_t* __
     }
     flush(ipw / NR - kept_base);
 }
-
-// Block-pair formats of the rows kernel.  A "pair" is two consecutive blocks (64
-// weights); rows are 16-byte aligned, so pairs start on dword boundaries.  weights<HALF>
-// gives the 4 weights, as exact float32, of inputs 4*cc .. 4*cc+3 of block HALF.
-struct FmtQ8_0 {  // 68 bytes: [d0 | 32 q] [d1 | 32 q]
-    static constexpr int kPairBytes = 68, kDwords = 17, kLoads = 5;
-    static __device__ __forceinline__ void load(const uint8_t* p, uint32_t (&w)[kDwords]) { load_pair(p, w); }
-    template <int HALF>
-    static __device__ __forceinline__ void weights(const uint32_t (&w)[kDwords], int cc, float (&wf)[4]) {
-        if constexpr (HALF == 0) {  // block 0: scale in dword 0 (low half), quants at bytes 2..33
-            const float d = half_lo(w[0]);
-            wf[0] = sbyte<2>(w[cc]) * d;
-            wf[1] = sbyte<3>(w[cc]) * d;
-            wf[2] = sbyte<0>(w[cc + 1]) * d;
-            wf[3] = sbyte<1>(w[cc + 1]) * d;
-        } else {  // block 1: scale in dword 8 (high half), quants in dwords 9..16
-            const float d = half_hi(w[8]);
-            const uint32_t v = w[9 + cc];
-            wf[0] = sbyte<0>(v) * d;
-            wf[1] = sbyte<1>(v) * d;
-            wf[2] = sbyte<2>(v) * d;
-            wf[3] = sbyte<3>(v) * d;
-        }
-    }
-};
-
-// GGUF Q4_0: 36 bytes a pair, [d0 | 16 bytes] [d1 | 16 bytes]; weight j < 16 of a block is
-// the low nibble of its byte j, weight j + 16 the high nibble; w = d * (nibble - 8), exact
-// in float32 (a 4-bit integer times an 11-bit scale).
-struct FmtQ4_0 {
-    static constexpr int kPairBytes = 36, kDwords = 9, kLoads = 3;
-    static __device__ __forceinline__ void load(const uint8_t* p, uint32_t (&w)[kDwords]) {
-        const u32x4_a4 a = *reinterpret_cast<const u32x4_a4*>(p);
-        const u32x4_a4 b = *reinterpret_cast<const u32x4_a4*>(p + 16);
-        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-        w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
-        w[8] = *reinterpret_cast<const uint32_t*>(p + 32);
-    }
-    template <int HALF>
-    static __device__ __forceinline__ void weights(const uint32_t (&w)[kDwords], int cc, float (&wf)[4]) {
-        const int c4 = cc & 3;  // quant dword of the block: bytes 4*c4 .. 4*c4+3
-        float d;
-        uint32_t v;
-        if constexpr (HALF == 0) {  // scale = low half of dword 0, quant bytes at 2..17
-            d = half_lo(w[0]);
-            v = __builtin_amdgcn_alignbyte(w[c4 + 1], w[c4], 2);
-        } else {  // scale = high half of dword 4, quant bytes in dwords 5..8
-            d = half_hi(w[4]);
-            v = w[5 + c4];
-        }
-        const uint32_t nib = (cc < 4 ? v : v >> 4) & 0x0F0F0F0Fu;  // inputs 4cc..: low nibbles, then high
-        // q*d - 8d in one fma: the exact value (q - 8)*d has at most 15 significant bits
-        const float m8d = -8.0f * d;
-        wf[0] = __builtin_fmaf((float)(nib & 0xFFu), d, m8d);
-        wf[1] = __builtin_fmaf((float)((nib >> 8) & 0xFFu), d, m8d);
-        wf[2] = __builtin_fmaf((float)((nib >> 16) & 0xFFu), d, m8d);
-        wf[3] = __builtin_fmaf((float)(nib >> 24), d, m8d);
-    }
-};
 
 // Several activation rows (1 <= M <= 8 per launch; the class used for 2..255 rows).  A
 // block tile is 8*R rows (fused: R gate/up row pairs) over the whole K, worked on by two
@@ -473,10 +534,10 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(1,
 
 namespace {
 
-template <int R, int NR, int D, int NW, bool NT = false>
+template <class Fmt, int R, int NR, int D, int NW, bool NT = false>
 hipError_t launch_one_row(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, int log2S, const float* x,
                           float* y, hipStream_t stream) {
-    auto kernel = gemv_one_row_kernel<R, NR, D, NW, NT>;
+    auto kernel = gemv_one_row_kernel<Fmt, R, NR, D, NW, NT>;
     const size_t lds = (size_t)P * kXRow + (size_t)NW * D * R * kLdsItemBytes;
     // Once per device: allow the largest dynamic LDS this instance uses (rows of up to
     // 64*NR pairs), above the default limit.  Resident blocks per CU depend on the LDS
@@ -521,7 +582,7 @@ hipError_t launch_one_row(const DeviceInfo& dev, const uint8_t* w, int n_out, in
 // (2-6% faster there).  Smaller matrices (or 4 rounds, where the activations need more
 // registers): 4-wave blocks, spread over more CUs, two slots each, plain copies (the hint
 // measured slower on the Qwen3-0.6B shapes).  Measured on the Qwen3 shapes.
-template <int R>
+template <class Fmt, int R>
 bool try_one_row(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, int log2S, const float* x, float* y,
                  hipStream_t stream, hipError_t* err) {
     const int S = 1 << log2S;
@@ -530,18 +591,18 @@ bool try_one_row(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, int 
     const bool wide = items >= (int64_t)16 * dev.cu_count;
     switch (NR) {
         case 1:
-            *err = wide ? launch_one_row<R, 1, 1, 8, true>(dev, w, n_out, P, log2S, x, y, stream)
-                        : launch_one_row<R, 1, 2, 4>(dev, w, n_out, P, log2S, x, y, stream);
+            *err = wide ? launch_one_row<Fmt, R, 1, 1, 8, true>(dev, w, n_out, P, log2S, x, y, stream)
+                        : launch_one_row<Fmt, R, 1, 2, 4>(dev, w, n_out, P, log2S, x, y, stream);
             return true;
         case 2:
-            *err = wide ? launch_one_row<R, 2, 1, 8, true>(dev, w, n_out, P, log2S, x, y, stream)
-                        : launch_one_row<R, 2, 2, 4>(dev, w, n_out, P, log2S, x, y, stream);
+            *err = wide ? launch_one_row<Fmt, R, 2, 1, 8, true>(dev, w, n_out, P, log2S, x, y, stream)
+                        : launch_one_row<Fmt, R, 2, 2, 4>(dev, w, n_out, P, log2S, x, y, stream);
             return true;
         case 3:
-            *err = wide && R == 1 ? launch_one_row<R, 3, 1, 8, true>(dev, w, n_out, P, log2S, x, y, stream)
-                                  : launch_one_row<R, 3, 2, 4>(dev, w, n_out, P, log2S, x, y, stream);
+            *err = wide && R == 1 ? launch_one_row<Fmt, R, 3, 1, 8, true>(dev, w, n_out, P, log2S, x, y, stream)
+                                  : launch_one_row<Fmt, R, 3, 2, 4>(dev, w, n_out, P, log2S, x, y, stream);
             return true;
-        case 4: *err = launch_one_row<R, 4, 2, 4>(dev, w, n_out, P, log2S, x, y, stream); return true;
+        case 4: *err = launch_one_row<Fmt, R, 4, 2, 4>(dev, w, n_out, P, log2S, x, y, stream); return true;
         default: return false;
     }
 }
@@ -641,6 +702,17 @@ hipError_t launch_q4_0_m(const DeviceInfo& dev, const uint8_t* w, int n_out, int
 hipError_t launch_gemv_q4_0(const DeviceInfo& dev, const uint8_t* w, int64_t n_out, int64_t k, bool silu_pairs,
                             const float* x, int64_t m, int64_t ldx, float* y, int64_t ldy, hipStream_t stream) {
     const int P = (int)(k / 64);
+    // One row, K <= 4096 (one round of pairs) and at least 16 row groups per CU: the
+    // LDS-streaming one-row kernel (Gemma 4 12B gate_up 30720x3840: 23.3 -> 19.1 us).  With
+    // more rounds (the 3840x15360 down: 13.6 -> 17.1 us) and on small matrices the rows
+    // kernel stays faster for Q4_0, whose 36-byte pairs carry half the bytes per item.
+    if (m == 1 && P <= 64) {
+        const int log2S = slots_log2(P);
+        const int64_t groups = (n_out + (64 >> log2S) - 1) / (64 >> log2S);
+        if (groups >= (int64_t)16 * dev.cu_count)
+            return silu_pairs ? launch_one_row<FmtQ4_0, 2, 1, 1, 8, true>(dev, w, (int)n_out, P, log2S, x, y, stream)
+                              : launch_one_row<FmtQ4_0, 1, 1, 1, 8, true>(dev, w, (int)n_out, P, log2S, x, y, stream);
+    }
     for (int64_t m0 = 0; m0 < m; m0 += 8) {
         const int mm = (int)((m - m0) < 8 ? (m - m0) : 8);
         const float* xc = x + m0 * ldx;
@@ -658,8 +730,8 @@ hipError_t launch_gemv_q8(const DeviceInfo& dev, const uint8_t* w, int64_t n_out
     const int log2S = slots_log2(P);
     if (m == 1) {  // one row: the LDS-streaming kernel when K fits it
         hipError_t e;
-        if (silu_pairs ? try_one_row<2>(dev, w, (int)n_out, P, log2S, x, y, stream, &e)
-                       : try_one_row<1>(dev, w, (int)n_out, P, log2S, x, y, stream, &e))
+        if (silu_pairs ? try_one_row<FmtQ8_0, 2>(dev, w, (int)n_out, P, log2S, x, y, stream, &e)
+                       : try_one_row<FmtQ8_0, 1>(dev, w, (int)n_out, P, log2S, x, y, stream, &e))
             return e;
     }
     // several rows (or one row with K beyond the register kernel): 8-row launches

@@ -109,10 +109,13 @@ q8_status q8_linear_fused_gate_up_silu(const void* w_gate_up_q8, int64_t f, int6
  * block, rows of k/32 blocks back to back.
  *   q4_0_linear                     : y[m][n] = x . W^T,  W = Q4_0 [n][k]
  *   q4_0_linear_fused_gate_up_silu  : h = SiLU(x . W_gate^T) * (x . W_up^T), W = Q4_0 [2f][k]
- * Arguments, rules and errors as for q8_linear / q8_linear_fused_gate_up_silu.  Every m
- * runs on the float32 rows kernel in 8-row launches (weights w = d*(q-8) exact in
- * float32, one fma per weight and row, the per-output order depends only on k: every row
- * is bit-identical whatever m is).
+ * Arguments, rules and errors as for q8_linear / q8_linear_fused_gate_up_silu.  Two or
+ * more rows run the float32 rows kernel in 8-row launches (weights w = d*(q-8) exact in
+ * float32, one fma per weight and row, the per-output order depends only on k: those rows
+ * are bit-identical whatever m is).  One row with k <= 4096 on a matrix with at least 16
+ * row groups per CU runs the one-row kernel (per block t = sum nibble*x, then
+ * acc += d*(t - 8*sum x)), whose rows agree with the multi-row results to float32
+ * reassociation; other one-row calls run the rows kernel.
  */
 q8_status q4_0_linear(const void* w_q4_0, int64_t n, int64_t k,
                       const float* x, int64_t m, int64_t ldx,
