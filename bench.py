@@ -32,6 +32,9 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix cores
+# float32 VALU lane operations per second without packed instructions (the build disables
+# packed float32): 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+VALU_LANE_OPS_PER_S = 256 * 64 * 2.4e9
 METRIC = "effective weight GB/s & % of HBM peak for Q8_0 linear at M=1/8/16; decode tok/s"
 
 
@@ -201,6 +204,13 @@ def bench_block(args, torch, dev, q8, spec, m_values):
         avg_ms = float(np.mean(durs))
         res["gate_up_avg_us"] = round(avg_ms * 1e3, 3)
         res["gate_up_gbps"] = round(gate_up_bytes / (avg_ms * 1e-3) / 1e9, 2)
+        if m > 1:
+            # VALU roofline of the float32 rows kernel: per weight one int8 -> float32
+            # conversion and one scale multiply (shared by the rows) plus one fma per
+            # activation row, against the non-packed float32 lane rate of the chip
+            weights = gu.n * gu.k
+            lane_ops = weights * (2 + m)
+            res["gate_up_valu_frac"] = round(lane_ops / (avg_ms * 1e-3) / VALU_LANE_OPS_PER_S, 4)
         out[m] = res
         log(f"M={m}: {res}")
     return stack, out, gate_up_bytes
