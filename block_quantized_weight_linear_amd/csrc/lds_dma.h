@@ -46,21 +46,6 @@ __device__ __forceinline__ void wait_lgkmcnt_mem() {
     asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// One wave-wide 256-byte direct-to-LDS copy: lane l copies 4 bytes from its src to
-// lds + 4*l (lds is the wave-uniform 32-bit LDS address).
-__device__ __forceinline__ void lds_copy4(const void* src, uint32_t lds) {
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %2\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dword %1, off\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(src), "s"(lds)
-        : "memory");
-}
-
 // 4352 contiguous bytes (4 x 1 KB with 16 bytes a lane, then 256 B with 4 bytes a lane)
 // from src to lds .. lds + 4351, as five direct-to-LDS loads (five vmcnt events).  Only
 // the first len bytes (len >= 16, a multiple of 4) are read: a lane whose bytes lie past
