@@ -132,8 +132,28 @@ def time_steps(torch, fn, steps, warmup):
     return start.elapsed_time(stop) / steps  # ms per step
 
 
-def cpu_baseline_block(spec, seconds_hint=15.0):
-    """The oracle on one full layer of the stack (QKV, fused gate_up, down) at M = 1."""
+def host_cpu_info():
+    """Logical and physical core counts and the CPU model of the host running the bench."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        import psutil
+        physical = psutil.cpu_count(logical=False)
+    except Exception:  # pragma: no cover
+        physical = None
+    affinity = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None
+    return {"logical_cpus": os.cpu_count(), "physical_cores": physical, "usable_cpus": affinity, "model": model}
+
+
+def cpu_baseline_block(spec, reps=5):
+    """The oracle on one full layer of the stack (QKV, fused gate_up, down) at M = 1: one
+    warm-up pass, then the best of `reps` timed passes (each includes the dequantization)."""
     import oracle
     import workloads as wl
     try:
@@ -144,25 +164,27 @@ def cpu_baseline_block(spec, seconds_hint=15.0):
     hosts = [wl.q8_weight(900 + i, lin.n, lin.k)[0] for i, lin in enumerate(spec.linears)]
     xs = [wl.activations(950 + i, 1, lin.k) for i, lin in enumerate(spec.linears)]
     nbytes = sum(int(h.size) for h in hosts)
-    best = None
-    t_all = time.perf_counter()
-    reps = 0
-    while True:
-        t0 = time.perf_counter()
+
+    def one_layer():
         for lin, wb, x in zip(spec.linears, hosts, xs):
             if lin.fused_silu:
                 oracle.fused_gate_up_silu_ref(wb, lin.n // 2, lin.k, x)
             else:
                 oracle.q8_linear_ref(wb, lin.n, lin.k, x)
-        dt = time.perf_counter() - t0
-        reps += 1
-        best = dt if best is None else min(best, dt)
-        if reps >= 3 or time.perf_counter() - t_all > seconds_hint:
-            break
+
+    one_layer()  # warm-up
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        one_layer()
+        times.append(time.perf_counter() - t0)
+    best = min(times)
+    info = host_cpu_info()
     return {"value": round(nbytes / best / 1e9, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "sample": f"one full layer ({'+'.join(l.name for l in spec.linears)}, {nbytes} Q8_0 bytes) at M=1, "
-                      f"float64 dequantize-then-matmul, best of {reps}",
-            "tok_s_per_layer": round(1.0 / best, 3)}
+                      f"float64 dequantize-then-matmul, one warm-up then best of {reps}",
+            "tok_s_per_layer": round(1.0 / best, 3), "blas_threads": int(threads),
+            "median_s": round(float(np.median(times)), 4), **info}
 
 
 def bench_block(args, torch, dev, q8, spec, m_values):

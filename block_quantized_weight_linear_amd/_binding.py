@@ -82,20 +82,17 @@ def abi_version() -> int:
     return int(lib.q8_abi_version())
 
 
-def _torch():
-    return torch
-
-
 def _stream(t):
-    torch = _torch()
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
-def _dev(t, dtype, name):
-    if not t.is_cuda:
+def _dev(t, dtype, name, device=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
     if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
     return t
 
 
@@ -106,91 +103,110 @@ def _ld(x, width):
     return x.stride(0)
 
 
+def _rows_in(x, width, name):
+    """A 2-D [m][width] input with unit column stride and rows that do not overlap."""
+    if x.dim() != 2 or x.shape[1] != width:
+        raise ValueError(f"{name} must be [m][{width}], got {tuple(x.shape)}")
+    if x.numel() and (x.stride(1) != 1 or (x.shape[0] > 1 and x.stride(0) < width)):
+        raise ValueError(f"{name} must have contiguous, non-overlapping rows")
+    return x.shape[0]
+
+
+def _rows_out(out, m, width, name, dtype, device):
+    """A caller-supplied output: exactly [m][width], unit column stride, rows that do not
+    overlap (the kernels write m rows of width values at the tensor's row stride)."""
+    _dev(out, dtype, name, device)
+    if out.dim() != 2 or tuple(out.shape) != (m, width):
+        raise ValueError(f"{name} must be [{m}][{width}], got {tuple(out.shape)}")
+    if out.numel() and (out.stride(1) != 1 or (m > 1 and out.stride(0) < width)):
+        raise ValueError(f"{name} must have unit column stride and non-overlapping rows")
+    return out
+
+
+def _contig_out(t, shape, name, dtype, device):
+    _dev(t, dtype, name, device)
+    if tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {list(shape)} tensor, got {tuple(t.shape)}")
+    return t
+
+
+def _bytes(w, need, name, device):
+    """A byte tensor (uint8, contiguous) holding at least `need` bytes."""
+    _dev(w, torch.uint8, name, device)
+    if not w.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if w.numel() < need:
+        raise ValueError(f"{name} holds {w.numel()} bytes, the shape needs {need}")
+    return w
+
+
+def _quant_bytes(rows, k, block_bytes):
+    if k <= 0 or k % 256 or rows < 0:
+        return 0  # the library reports the shape error
+    return rows * (k // 32) * block_bytes
+
+
+def _call(device, fn, *args):
+    # the library launches on the current device: make it the tensors' device
+    with torch.cuda.device(device):
+        check(fn(*args))
+
+
+def _dense(fn, w, n_w, n_out, k, x, out, block_bytes):
+    """Shared marshalling of the dense linears: weight rows n_w, outputs n_out."""
+    _dev(x, torch.float32, "x")
+    dev = x.device
+    m = _rows_in(x, k, "x")
+    _bytes(w, _quant_bytes(n_w, k, block_bytes) if n_out and m else 0, "w", dev)
+    if out is None:
+        out = torch.empty((m, n_out), dtype=torch.float32, device=dev)
+    _rows_out(out, m, n_out, "out", torch.float32, dev)
+    _call(dev, fn, w.data_ptr(), n_out, k, x.data_ptr(), m, _ld(x, k), out.data_ptr(), _ld(out, n_out),
+          _stream(x))
+    return out
+
+
 def q8_linear(w, n: int, k: int, x, out=None):
     """y = x . W^T for a Q8_0 weight W [n][k] (uint8 bytes) and float32 x [m][k]."""
-    torch = _torch()
-    _dev(w, torch.uint8, "w")
-    _dev(x, torch.float32, "x")
-    if x.dim() != 2 or x.shape[1] != k or (x.numel() and x.stride(1) != 1):
-        raise ValueError(f"x must be [m][{k}] with contiguous rows")
-    m = x.shape[0]
-    if out is None:
-        out = torch.empty((m, n), dtype=torch.float32, device=x.device)
-    _dev(out, torch.float32, "out")
-    check(lib.q8_linear(w.data_ptr(), n, k, x.data_ptr(), m, _ld(x, k), out.data_ptr(), _ld(out, n), _stream(x)))
-    return out
+    return _dense(lib.q8_linear, w, n, n, k, x, out, 34)
 
 
 def q8_linear_fused_gate_up_silu(w, f: int, k: int, x, out=None):
     """h = SiLU(x . W_gate^T) * (x . W_up^T); W is Q8_0 [2f][k], gate rows first."""
-    torch = _torch()
-    _dev(w, torch.uint8, "w")
-    _dev(x, torch.float32, "x")
-    if x.dim() != 2 or x.shape[1] != k or (x.numel() and x.stride(1) != 1):
-        raise ValueError(f"x must be [m][{k}] with contiguous rows")
-    m = x.shape[0]
-    if out is None:
-        out = torch.empty((m, f), dtype=torch.float32, device=x.device)
-    _dev(out, torch.float32, "out")
-    check(lib.q8_linear_fused_gate_up_silu(w.data_ptr(), f, k, x.data_ptr(), m, _ld(x, k), out.data_ptr(),
-                                           _ld(out, f), _stream(x)))
-    return out
+    return _dense(lib.q8_linear_fused_gate_up_silu, w, 2 * f, f, k, x, out, 34)
 
 
 def q4_0_linear(w, n: int, k: int, x, out=None):
     """y = x . W^T for a GGUF Q4_0 weight W [n][k] (uint8 bytes) and float32 x [m][k]."""
-    torch = _torch()
-    _dev(w, torch.uint8, "w")
-    _dev(x, torch.float32, "x")
-    if x.dim() != 2 or x.shape[1] != k or (x.numel() and x.stride(1) != 1):
-        raise ValueError(f"x must be [m][{k}] with contiguous rows")
-    m = x.shape[0]
-    if out is None:
-        out = torch.empty((m, n), dtype=torch.float32, device=x.device)
-    _dev(out, torch.float32, "out")
-    check(lib.q4_0_linear(w.data_ptr(), n, k, x.data_ptr(), m, _ld(x, k), out.data_ptr(), _ld(out, n), _stream(x)))
-    return out
+    return _dense(lib.q4_0_linear, w, n, n, k, x, out, 18)
 
 
 def q4_0_linear_fused_gate_up_silu(w, f: int, k: int, x, out=None):
     """h = SiLU(x . W_gate^T) * (x . W_up^T); W is GGUF Q4_0 [2f][k], gate rows first."""
-    torch = _torch()
-    _dev(w, torch.uint8, "w")
-    _dev(x, torch.float32, "x")
-    if x.dim() != 2 or x.shape[1] != k or (x.numel() and x.stride(1) != 1):
-        raise ValueError(f"x must be [m][{k}] with contiguous rows")
-    m = x.shape[0]
-    if out is None:
-        out = torch.empty((m, f), dtype=torch.float32, device=x.device)
-    _dev(out, torch.float32, "out")
-    check(lib.q4_0_linear_fused_gate_up_silu(w.data_ptr(), f, k, x.data_ptr(), m, _ld(x, k), out.data_ptr(),
-                                             _ld(out, f), _stream(x)))
-    return out
+    return _dense(lib.q4_0_linear_fused_gate_up_silu, w, 2 * f, f, k, x, out, 18)
 
 
 def q8_quantize_act(x, xq=None, xd=None):
     """Int8 codes [m][k] and float32 scales [m][k/32] of float32 activation rows x [m][k]."""
-    torch = _torch()
     _dev(x, torch.float32, "x")
-    if x.dim() != 2 or (x.numel() and x.stride(1) != 1):
-        raise ValueError("x must be [m][k] with contiguous rows")
+    if x.dim() != 2:
+        raise ValueError("x must be [m][k]")
     m, k = x.shape
+    _rows_in(x, k, "x")
+    dev = x.device
     if xq is None:
-        xq = torch.empty((m, k), dtype=torch.int8, device=x.device)
+        xq = torch.empty((m, k), dtype=torch.int8, device=dev)
     if xd is None:
-        xd = torch.empty((m, k // 32), dtype=torch.float32, device=x.device)
-    _dev(xq, torch.int8, "xq")
-    _dev(xd, torch.float32, "xd")
-    if tuple(xq.shape) != (m, k) or tuple(xd.shape) != (m, k // 32) or not (xq.is_contiguous() and xd.is_contiguous()):
-        raise ValueError("xq must be a contiguous [m][k] tensor and xd a contiguous [m][k/32] tensor")
-    check(lib.q8_quantize_act(x.data_ptr(), m, k, _ld(x, k), xq.data_ptr(), xd.data_ptr(), _stream(x)))
+        xd = torch.empty((m, k // 32), dtype=torch.float32, device=dev)
+    _contig_out(xq, (m, k), "xq", torch.int8, dev)
+    _contig_out(xd, (m, k // 32), "xd", torch.float32, dev)
+    _call(dev, lib.q8_quantize_act, x.data_ptr(), m, k, _ld(x, k), xq.data_ptr(), xd.data_ptr(), _stream(x))
     return xq, xd
 
 
 def _codes(xq, xd, k):
-    torch = _torch()
     _dev(xq, torch.int8, "xq")
-    _dev(xd, torch.float32, "xd")
+    _dev(xd, torch.float32, "xd", xq.device)
     if xq.dim() != 2 or xq.shape[1] != k or not xq.is_contiguous():
         raise ValueError(f"xq must be a contiguous [m][{k}] tensor")
     m = xq.shape[0]
@@ -199,30 +215,26 @@ def _codes(xq, xd, k):
     return m
 
 
+def _dense_codes(fn, w, n_w, n_out, k, xq, xd, out):
+    m = _codes(xq, xd, k)
+    dev = xq.device
+    _bytes(w, _quant_bytes(n_w, k, 34) if n_out and m else 0, "w", dev)
+    if out is None:
+        out = torch.empty((m, n_out), dtype=torch.float32, device=dev)
+    _rows_out(out, m, n_out, "out", torch.float32, dev)
+    _call(dev, fn, w.data_ptr(), n_out, k, xq.data_ptr(), xd.data_ptr(), m, out.data_ptr(), _ld(out, n_out),
+          _stream(xq))
+    return out
+
+
 def q8_linear_q8act(w, n: int, k: int, xq, xd, out=None):
     """y = the Q8_0 weight W [n][k] against int8 activation codes xq [m][k] with scales xd."""
-    torch = _torch()
-    _dev(w, torch.uint8, "w")
-    m = _codes(xq, xd, k)
-    if out is None:
-        out = torch.empty((m, n), dtype=torch.float32, device=xq.device)
-    _dev(out, torch.float32, "out")
-    check(lib.q8_linear_q8act(w.data_ptr(), n, k, xq.data_ptr(), xd.data_ptr(), m, out.data_ptr(), _ld(out, n),
-                              _stream(xq)))
-    return out
+    return _dense_codes(lib.q8_linear_q8act, w, n, n, k, xq, xd, out)
 
 
 def q8_linear_fused_gate_up_silu_q8act(w, f: int, k: int, xq, xd, out=None):
     """h = SiLU(gate) * up from a fused Q8_0 gate_up matrix [2f][k] on int8 activation codes."""
-    torch = _torch()
-    _dev(w, torch.uint8, "w")
-    m = _codes(xq, xd, k)
-    if out is None:
-        out = torch.empty((m, f), dtype=torch.float32, device=xq.device)
-    _dev(out, torch.float32, "out")
-    check(lib.q8_linear_fused_gate_up_silu_q8act(w.data_ptr(), f, k, xq.data_ptr(), xd.data_ptr(), m,
-                                                 out.data_ptr(), _ld(out, f), _stream(xq)))
-    return out
+    return _dense_codes(lib.q8_linear_fused_gate_up_silu_q8act, w, 2 * f, f, k, xq, xd, out)
 
 
 def moe_route_topk(x, w_router, k: int, normalize: bool = True, idx_out=None, w_out=None, top_p=None,
@@ -233,39 +245,33 @@ def moe_route_topk(x, w_router, k: int, normalize: bool = True, idx_out=None, w_
     dropped slots hold expert -1 and weight 0.  With a workspace (uint8 device tensor of
     at least moe_route_workspace_bytes(m, n_exp) bytes; True allocates one) the two-pass
     form runs (moe_route_topk_ws), bit-identical to the one-pass calls."""
-    torch = _torch()
     _dev(x, torch.float32, "x")
-    _dev(w_router, torch.float32, "w_router")
+    dev = x.device
+    _dev(w_router, torch.float32, "w_router", dev)
     if not w_router.is_contiguous() or w_router.dim() != 2:
         raise ValueError("w_router must be a contiguous [n_exp][h] tensor")
     n_exp, h = w_router.shape
-    if x.dim() != 2 or x.shape[1] != h or (x.numel() and x.stride(1) != 1):
-        raise ValueError(f"x must be [m][{h}] with contiguous rows")
-    m = x.shape[0]
+    m = _rows_in(x, h, "x")
     if idx_out is None:
-        idx_out = torch.empty((m, k), dtype=torch.int32, device=x.device)
+        idx_out = torch.empty((m, k), dtype=torch.int32, device=dev)
     if w_out is None:
-        w_out = torch.empty((m, k), dtype=torch.float32, device=x.device)
-    _dev(idx_out, torch.int32, "idx_out")
-    _dev(w_out, torch.float32, "w_out")
-    if not (idx_out.is_contiguous() and w_out.is_contiguous()):
-        raise ValueError("idx_out and w_out must be contiguous")
+        w_out = torch.empty((m, k), dtype=torch.float32, device=dev)
+    _contig_out(idx_out, (m, k), "idx_out", torch.int32, dev)
+    _contig_out(w_out, (m, k), "w_out", torch.float32, dev)
+    norm = 1 if normalize else 0
     if workspace is not None:
         if workspace is True:
-            workspace = torch.empty(max(moe_route_workspace_bytes(m, n_exp), 1), dtype=torch.uint8,
-                                    device=x.device)
-        _dev(workspace, torch.uint8, "workspace")
-        check(lib.moe_route_topk_ws(x.data_ptr(), m, h, _ld(x, h), w_router.data_ptr(), n_exp, k,
-                                    1 if normalize else 0, 1.0 if top_p is None else float(top_p),
-                                    idx_out.data_ptr(), w_out.data_ptr(), workspace.data_ptr(), workspace.numel(),
-                                    _stream(x)))
+            workspace = torch.empty(max(moe_route_workspace_bytes(m, n_exp), 1), dtype=torch.uint8, device=dev)
+        _bytes(workspace, 0, "workspace", dev)
+        _call(dev, lib.moe_route_topk_ws, x.data_ptr(), m, h, _ld(x, h), w_router.data_ptr(), n_exp, k, norm,
+              1.0 if top_p is None else float(top_p), idx_out.data_ptr(), w_out.data_ptr(), workspace.data_ptr(),
+              workspace.numel(), _stream(x))
     elif top_p is None:
-        check(lib.moe_route_topk(x.data_ptr(), m, h, _ld(x, h), w_router.data_ptr(), n_exp, k,
-                                 1 if normalize else 0, idx_out.data_ptr(), w_out.data_ptr(), _stream(x)))
+        _call(dev, lib.moe_route_topk, x.data_ptr(), m, h, _ld(x, h), w_router.data_ptr(), n_exp, k, norm,
+              idx_out.data_ptr(), w_out.data_ptr(), _stream(x))
     else:
-        check(lib.moe_route_topk_top_p(x.data_ptr(), m, h, _ld(x, h), w_router.data_ptr(), n_exp, k,
-                                       1 if normalize else 0, float(top_p), idx_out.data_ptr(), w_out.data_ptr(),
-                                       _stream(x)))
+        _call(dev, lib.moe_route_topk_top_p, x.data_ptr(), m, h, _ld(x, h), w_router.data_ptr(), n_exp, k, norm,
+              float(top_p), idx_out.data_ptr(), w_out.data_ptr(), _stream(x))
     return idx_out, w_out
 
 
@@ -280,28 +286,25 @@ def q8_moe_workspace_bytes(m: int, k: int, n_exp: int, f: int, h: int) -> int:
 def q8_moe_grouped_linear(w_gate_up_exps, w_down_exps, n_exp: int, f: int, h: int, x, topk_idx, topk_w,
                           out=None, workspace=None):
     """Router-weighted SwiGLU expert mixture; returns y float32 [m][h]."""
-    torch = _torch()
-    _dev(w_gate_up_exps, torch.uint8, "w_gate_up_exps")
-    _dev(w_down_exps, torch.uint8, "w_down_exps")
     _dev(x, torch.float32, "x")
-    _dev(topk_idx, torch.int32, "topk_idx")
-    _dev(topk_w, torch.float32, "topk_w")
-    if x.dim() != 2 or x.shape[1] != h or (x.numel() and x.stride(1) != 1):
-        raise ValueError(f"x must be [m][{h}] with contiguous rows")
-    m = x.shape[0]
+    dev = x.device
+    m = _rows_in(x, h, "x")
+    _dev(topk_idx, torch.int32, "topk_idx", dev)
+    _dev(topk_w, torch.float32, "topk_w", dev)
     if topk_idx.dim() != 2 or topk_idx.shape[0] != m or not topk_idx.is_contiguous():
         raise ValueError("topk_idx must be a contiguous [m][k] tensor")
     k = topk_idx.shape[1]
-    if tuple(topk_w.shape) != (m, k) or not topk_w.is_contiguous():
-        raise ValueError("topk_w must be a contiguous [m][k] tensor")
+    _contig_out(topk_w, (m, k), "topk_w", torch.float32, dev)
+    _bytes(w_gate_up_exps, _quant_bytes(n_exp * 2 * f, h, 34) if m else 0, "w_gate_up_exps", dev)
+    _bytes(w_down_exps, _quant_bytes(n_exp * h, f, 34) if m else 0, "w_down_exps", dev)
     if out is None:
-        out = torch.empty((m, h), dtype=torch.float32, device=x.device)
-    _dev(out, torch.float32, "out")
+        out = torch.empty((m, h), dtype=torch.float32, device=dev)
+    _rows_out(out, m, h, "out", torch.float32, dev)
     need = q8_moe_workspace_bytes(m, k, n_exp, f, h) if m else 0
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
-    _dev(workspace, torch.uint8, "workspace")
-    check(lib.q8_moe_grouped_linear(w_gate_up_exps.data_ptr(), w_down_exps.data_ptr(), n_exp, f, h, x.data_ptr(), m,
-                                    _ld(x, h), topk_idx.data_ptr(), topk_w.data_ptr(), k, out.data_ptr(),
-                                    _ld(out, h), workspace.data_ptr(), workspace.numel(), _stream(x)))
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _bytes(workspace, 0, "workspace", dev)
+    _call(dev, lib.q8_moe_grouped_linear, w_gate_up_exps.data_ptr(), w_down_exps.data_ptr(), n_exp, f, h,
+          x.data_ptr(), m, _ld(x, h), topk_idx.data_ptr(), topk_w.data_ptr(), k, out.data_ptr(), _ld(out, h),
+          workspace.data_ptr(), workspace.numel(), _stream(x))
     return out

@@ -18,10 +18,13 @@
 //       t = q_0*x_0;  t = fma(q_i, x_i, t) for i = 1..31;   acc = fma(d, t, acc)
 //   then the butterfly over the S slots (xor S/2, ..., 1).
 //
-// Memory: a lane loads its 68-byte pair with four 16-byte loads and one dword; whole
-// rows coalesce across the S lanes.  The next pair is prefetched into registers while
-// the current one is multiplied.  The int8 -> float32 conversion (one v_cvt with a
-// byte select) is done once per weight and shared by all activation rows.
+// Memory: wave_rows below (the MoE expert passes) has each lane load its 68-byte pair
+// with four 16-byte loads and one dword, prefetching the next pair into registers while
+// the current one is multiplied.  The dense one-row kernel (gemv_q8.hip) instead copies
+// whole row stretches into LDS with coalesced direct copies and reads each lane's pair
+// from there; both run mac_pair on the same pairs in the same order.  The int8 ->
+// float32 conversion (one v_cvt with a byte select) is done once per weight and shared
+// by all activation rows.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -1,10 +1,10 @@
 // Grouped Q8_0 SwiGLU expert mixture (gfx950).
 //
-// "14. Model families and example applications" section 14.2: the MoE FFN runs the
-// router-weighted SwiGLU mixture (moeSwiGluFfnSeq); with several tokens it groups them
-// by expert so each expert's weights are read once per batch.  Section 14.4 ("MoE
-// expert kernels"): a counting-sort route plan scatters (token, slot) pairs
-// expert-major, and each token's sum runs in a fixed order.
+// "14. Model families and example applications" section 14.2: the MoE FFN is the
+// router-weighted SwiGLU mixture (moeSwiGluFfnSeq), and with several tokens the work is
+// grouped per expert so that one pass over an expert's weights serves all the tokens
+// routed to it.  Section 14.4 ("MoE expert kernels"): a counting-sort route plan orders
+// the (token, slot) pairs by expert, and each token's sum keeps a fixed order.
 //
 // Four launches on one stream, no host synchronization:
 //   1. plan      one workgroup: counting sort of the m*k (token, slot) pairs by

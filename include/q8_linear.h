@@ -11,7 +11,7 @@
  *     decode runs the trunk as one m = n pass that reads the weights once for all
  *     streams; the MoE FFN routes with softmax top-k (routerTopK, normalize_selected =
  *     norm_topk_prob) and runs the router-weighted SwiGLU mixture (moeSwiGluFfnSeq),
- *     whose prefill groups tokens by expert so each expert's weights are read once.
+ *     grouped per expert, so that one pass over an expert's weights serves its tokens.
  *   - Same page, section 14.4 (Gemma 4 - text + MoE, "MoE expert kernels"): a
  *     counting-sort route plan and a per-token summation order kept fixed.
  *
@@ -230,7 +230,10 @@ size_t q8_moe_workspace_bytes(int64_t m, int32_t k, int64_t n_exp, int64_t f, in
  *   topk_w   : float32 [m][k]
  *   workspace: device memory of at least q8_moe_workspace_bytes(m, k, n_exp, f, h)
  *              bytes, 256-byte aligned; its contents on entry do not matter.
- * Each expert's weights are read once per call for all tokens routed to it.
+ * Weight traffic: on the float32 decode path one pass over an expert's weights serves up
+ * to 4 of its routed tokens (an expert with more tokens is streamed again for each further
+ * group of 4, mostly from cache); from 64 routed pairs per expert on average (prefill)
+ * the bf16 matrix-core tiles run, one pass per 128 of an expert's tokens.
  */
 q8_status q8_moe_grouped_linear(const void* w_gate_up_exps, const void* w_down_exps,
                                 int64_t n_exp, int64_t f, int64_t h,

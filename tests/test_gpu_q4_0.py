@@ -1,6 +1,6 @@
 """GPU parity of q4_0_linear and q4_0_linear_fused_gate_up_silu (GGUF Q4_0 weights)
 against the CPU oracle: small shapes element by element (tiles, ragged chunks, row
-counts that are not a launch size), the Gemma 4 12B FFN shape on sampled outputs, hand
+counts that are not a launch size), the Gemma 4 12B FFN shape at its real size (every output), hand
 blocks, exact-arithmetic inputs bit for bit, batch invariance (one-row calls are their own
 kernel class, as for Q8_0)."""
 
@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 import workloads as wl
-from gpu_util import assert_close, say, sample_rows, to_dev, torch_dev
+from gpu_util import assert_close, fused_ref_full, linear_ref_full, say, to_dev, torch_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -101,25 +101,24 @@ def test_q4_0_exact_arithmetic_bit_identical(q8, n, k, m):
     assert np.array_equal(y.astype(np.float64), oracle.q4_0_linear_ref(wb, n, k, x))
 
 
-def test_q4_0_gemma4_12b_ffn_sampled(q8):
+def test_q4_0_gemma4_12b_ffn_full(q8):
     """Gemma 4 12B FFN (hidden 3840, intermediate 15360): fused gate_up 30720 x 3840 and
-    down 3840 x 15360 at m = 1 and 8, sampled outputs against the oracle."""
+    down 3840 x 15360 at m = 1 and 8, every output against the oracle."""
     lib, torch, dev = q8
     hid, ff = 3840, 15360
     wg, _, _ = wl.q4_0_weight(1700, 2 * ff, hid)
     wd, _, _ = wl.q4_0_weight(1701, hid, ff)
     wgd, wdd = to_dev(wg, dev), to_dev(wd, dev)
-    pick_g = sample_rows(ff, 96, seed=5)
-    pick_d = sample_rows(hid, 96, seed=6)
     for m in (1, 8):
         x = wl.activations(1702 + m, m, hid)
         say(f"gemma-4-12b q4_0 gate_up m={m}")
         h = lib.q4_0_linear_fused_gate_up_silu(wgd, ff, hid, to_dev(x, dev)).cpu().numpy()
-        sub = np.concatenate([q4_rows(wg, hid, pick_g), q4_rows(wg, hid, pick_g + ff)])
-        assert_close(h[:, pick_g], oracle.fused_gate_up_silu_q4_0_ref(sub, len(pick_g), hid, x), f"gate_up m={m}")
+        ref = fused_ref_full(wg, ff, hid, x, ref=oracle.fused_gate_up_silu_q4_0_ref, block_bytes=Q4_BLOCK)
+        assert_close(h, ref, f"gate_up m={m}")
         xh = wl.activations(1704 + m, m, ff)
         y = lib.q4_0_linear(wdd, hid, ff, to_dev(xh, dev)).cpu().numpy()
-        assert_close(y[:, pick_d], oracle.q4_0_linear_ref(q4_rows(wd, ff, pick_d), len(pick_d), ff, xh), f"down m={m}")
+        ref = linear_ref_full(wd, hid, ff, xh, ref=oracle.q4_0_linear_ref, block_bytes=Q4_BLOCK)
+        assert_close(y, ref, f"down m={m}")
 
 
 @pytest.mark.parametrize("n,k", [(4096, 1024), (777, 3840), (15360, 3840)])

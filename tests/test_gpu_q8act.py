@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 import workloads as wl
-from gpu_util import assert_close, row_slice, sample_rows, say, to_dev, torch_dev
+from gpu_util import assert_close, codes_ref, fused_ref_full, linear_ref_full, say, to_dev, torch_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -121,7 +121,7 @@ def test_full_int8_range_codes(q8):
 
 
 @pytest.mark.parametrize("n,k,m", [(4096, 1024, 1), (6144, 4096, 8), (4096, 12288, 3), (24576, 4096, 16),
-                                   (999, 256, 33)])
+                                   (999, 256, 33), (24576, 4096, 1), (24576, 4096, 8), (4096, 12288, 16)])
 def test_exact_arithmetic_bit_identical(q8, n, k, m):
     """Codes in [-2, 2], scales 2^-3, weight scales 2^-7 / 2^-8: every float32 partial sum
     is a multiple of 2^-11 below 2^13, so exact in any order."""
@@ -131,14 +131,8 @@ def test_exact_arithmetic_bit_identical(q8, n, k, m):
     dx = np.full((m, k // 32), 2.0 ** -3, np.float32)
     say(f"q8act exact n={n} k={k} m={m}")
     y = lib.q8_linear_q8act(to_dev(wb, dev), n, k, to_dev(qx, dev), to_dev(dx, dev)).cpu().numpy()
-    if n * k > 30_000_000:
-        pick = sample_rows(n, 256, seed=4)
-        ref = oracle.q8_linear_codes_ref(row_slice(wb, k, pick), len(pick), k, qx, dx)
-        got = y[:, pick]
-    else:
-        ref = oracle.q8_linear_codes_ref(wb, n, k, qx, dx)
-        got = y
-    assert np.array_equal(got.astype(np.float64), ref), np.max(np.abs(got - ref))
+    ref = linear_ref_full(wb, n, k, (qx, dx), ref=codes_ref(oracle.q8_linear_codes_ref))
+    assert np.array_equal(y.astype(np.float64), ref), np.max(np.abs(y - ref))
 
 
 LAYER_LINEARS = [
@@ -150,25 +144,25 @@ LAYER_LINEARS = [
 
 
 @pytest.mark.parametrize("name,n,k,fused,rows", LAYER_LINEARS, ids=[c[0] for c in LAYER_LINEARS])
-def test_layer_shapes_sampled_end_to_end(q8, name, n, k, fused, rows):
-    """Quantize on the device, then the linear, against the oracle from float32 inputs."""
+def test_layer_shapes_full_end_to_end(q8, name, n, k, fused, rows):
+    """Quantize on the device (codes bit-exact), then the linear: every output against the
+    oracle from the float32 inputs."""
     lib, torch, dev = q8
     wb, _, _ = wl.q8_weight(41, 2 * n if fused else n, k)
     wd = to_dev(wb, dev)
-    pick = sample_rows(n, 96, seed=n + 1)
     for m in rows:
         x = wl.activations(42 + m, m, k)
         say(f"{name} q8act m={m}")
         xq, xd = lib.q8_quantize_act(to_dev(x, dev))
+        qx, dx = oracle.quantize_act_q8_ref(x)
+        assert np.array_equal(xq.cpu().numpy(), qx) and np.array_equal(xd.cpu().numpy(), dx)
         if fused:
             y = lib.q8_linear_fused_gate_up_silu_q8act(wd, n, k, xq, xd).cpu().numpy()
-            sub = np.concatenate([row_slice(wb, k, pick), row_slice(wb, k, pick + n)])
-            ref = oracle.fused_gate_up_silu_q8act_ref(sub, len(pick), k, x)
+            ref = fused_ref_full(wb, n, k, (qx, dx), ref=codes_ref(oracle.fused_gate_up_silu_codes_ref))
         else:
             y = lib.q8_linear_q8act(wd, n, k, xq, xd).cpu().numpy()
-            ref = oracle.q8_linear_q8act_ref(row_slice(wb, k, pick), len(pick), k, x)
-        assert_close(y[:, pick], ref, f"{name} q8act m={m} ({len(pick)} sampled outputs)")
-        assert np.all(np.isfinite(y))
+            ref = linear_ref_full(wb, n, k, (qx, dx), ref=codes_ref(oracle.q8_linear_codes_ref))
+        assert_close(y, ref, f"{name} q8act m={m} (all {y.size} outputs)")
 
 
 @pytest.mark.parametrize("n,k", [(4096, 1024), (1024, 3072), (6144, 4096), (777, 12288)])
