@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     q8_linear_fused_gate_up_silu_q8act,
     q8_linear_q8act,
     q8_moe_grouped_linear,
+    q8_moe_grouped_linear_noalloc,
     q8_moe_workspace_bytes,
     q8_quantize_act,
 )

@@ -64,6 +64,10 @@ lib.q8_moe_grouped_linear.restype = ctypes.c_int
 lib.q8_moe_grouped_linear.argtypes = [_vp, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _i32, _vp, _i64,
                                       _vp, _sz, _vp]
 
+lib.q8_moe_grouped_linear_noalloc.restype = ctypes.c_int
+lib.q8_moe_grouped_linear_noalloc.argtypes = [_vp, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _i32, _vp,
+                                              _i64, _vp]
+
 Q8_OK, Q8_ERR_NULL, Q8_ERR_SHAPE, Q8_ERR_ALIGN, Q8_ERR_WORKSPACE, Q8_ERR_DEVICE = range(6)
 
 
@@ -283,9 +287,7 @@ def q8_moe_workspace_bytes(m: int, k: int, n_exp: int, f: int, h: int) -> int:
     return int(lib.q8_moe_workspace_bytes(m, k, n_exp, f, h))
 
 
-def q8_moe_grouped_linear(w_gate_up_exps, w_down_exps, n_exp: int, f: int, h: int, x, topk_idx, topk_w,
-                          out=None, workspace=None):
-    """Router-weighted SwiGLU expert mixture; returns y float32 [m][h]."""
+def _moe_args(w_gate_up_exps, w_down_exps, n_exp, f, h, x, topk_idx, topk_w, out):
     _dev(x, torch.float32, "x")
     dev = x.device
     m = _rows_in(x, h, "x")
@@ -300,6 +302,13 @@ def q8_moe_grouped_linear(w_gate_up_exps, w_down_exps, n_exp: int, f: int, h: in
     if out is None:
         out = torch.empty((m, h), dtype=torch.float32, device=dev)
     _rows_out(out, m, h, "out", torch.float32, dev)
+    return dev, m, k, out
+
+
+def q8_moe_grouped_linear(w_gate_up_exps, w_down_exps, n_exp: int, f: int, h: int, x, topk_idx, topk_w,
+                          out=None, workspace=None):
+    """Router-weighted SwiGLU expert mixture; returns y float32 [m][h]."""
+    dev, m, k, out = _moe_args(w_gate_up_exps, w_down_exps, n_exp, f, h, x, topk_idx, topk_w, out)
     need = q8_moe_workspace_bytes(m, k, n_exp, f, h) if m else 0
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -307,4 +316,16 @@ def q8_moe_grouped_linear(w_gate_up_exps, w_down_exps, n_exp: int, f: int, h: in
     _call(dev, lib.q8_moe_grouped_linear, w_gate_up_exps.data_ptr(), w_down_exps.data_ptr(), n_exp, f, h,
           x.data_ptr(), m, _ld(x, h), topk_idx.data_ptr(), topk_w.data_ptr(), k, out.data_ptr(), _ld(out, h),
           workspace.data_ptr(), workspace.numel(), _stream(x))
+    return out
+
+
+def q8_moe_grouped_linear_noalloc(w_gate_up_exps, w_down_exps, n_exp: int, f: int, h: int, x, topk_idx, topk_w,
+                                  out=None):
+    """The same mixture with the library's fixed per-device scratch instead of a workspace
+    (the C entry point allocates nothing; pass `out` to keep this wrapper allocation-free
+    too).  Sizes whose workspace exceeds the scratch raise Q8Error."""
+    dev, m, k, out = _moe_args(w_gate_up_exps, w_down_exps, n_exp, f, h, x, topk_idx, topk_w, out)
+    _call(dev, lib.q8_moe_grouped_linear_noalloc, w_gate_up_exps.data_ptr(), w_down_exps.data_ptr(), n_exp, f, h,
+          x.data_ptr(), m, _ld(x, h), topk_idx.data_ptr(), topk_w.data_ptr(), k, out.data_ptr(), _ld(out, h),
+          _stream(x))
     return out

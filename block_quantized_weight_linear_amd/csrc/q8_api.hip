@@ -32,6 +32,37 @@ q8k::DeviceInfo g_dev[kMaxDevices];
 
 }  // namespace
 
+// Fixed device scratch of q8_moe_grouped_linear_noalloc (Q8_MOE_NOALLOC_SCRATCH_BYTES).
+// Each device holds its own copy for the life of the process.  Host code never passes
+// the name itself to a kernel (on the host it is only a stand-in for the symbol): the
+// device address comes from hipGetSymbolAddress, looked up once per device.
+static __device__ __align__(256) unsigned char scratch[Q8_MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on first use there).
+hipError_t scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
 namespace q8k {
 
 hipError_t current_device_info(DeviceInfo* out) {
@@ -261,6 +292,40 @@ q8_status q8_moe_grouped_linear(const void* w_gate_up_exps, const void* w_down_e
                                 static_cast<const uint8_t*>(w_down_exps), n_exp, f, h, x, m, ldx, topk_idx, topk_w, k,
                                 y, ldy, workspace, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return device_fail("q8_moe_grouped_linear", e);
+    return Q8_OK;
+}
+
+q8_status q8_moe_grouped_linear_noalloc(const void* w_gate_up_exps, const void* w_down_exps, int64_t n_exp,
+                                         int64_t f, int64_t h, const float* x, int64_t m, int64_t ldx,
+                                         const int32_t* topk_idx, const float* topk_w, int32_t k, float* y,
+                                         int64_t ldy, void* stream) {
+    g_err[0] = 0;
+    char msg[256];
+    q8_status s = q8v::check_moe_args(w_gate_up_exps, w_down_exps, n_exp, f, h, x, m, ldx, topk_idx, topk_w, k, y,
+                                      ldy, msg, sizeof msg);
+    if (s == Q8_OK && m > 0) {
+        const size_t need = q8v::moe_workspace_layout(m, k, n_exp, f, h).total;
+        if (need > (size_t)Q8_MOE_NOALLOC_SCRATCH_BYTES) {
+            snprintf(msg, sizeof msg, "these sizes need %lld bytes of scratch; the fixed scratch holds %lld",
+                     (long long)need, (long long)Q8_MOE_NOALLOC_SCRATCH_BYTES);
+            s = Q8_ERR_WORKSPACE;
+        }
+    }
+    if (s != Q8_OK) {
+        set_err("q8_moe_grouped_linear_noalloc: %s", msg);
+        return s;
+    }
+    if (m == 0) return Q8_OK;
+    q8k::DeviceInfo dev;
+    hipError_t e = q8k::current_device_info(&dev);
+    if (e != hipSuccess) return device_fail("q8_moe_grouped_linear_noalloc", e);
+    void* ws = nullptr;
+    e = scratch_address(&ws);
+    if (e != hipSuccess) return device_fail("q8_moe_grouped_linear_noalloc: scratch address", e);
+    e = q8k::launch_moe_grouped(dev, static_cast<const uint8_t*>(w_gate_up_exps),
+                                static_cast<const uint8_t*>(w_down_exps), n_exp, f, h, x, m, ldx, topk_idx, topk_w, k,
+                                y, ldy, ws, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_fail("q8_moe_grouped_linear_noalloc", e);
     return Q8_OK;
 }
 

@@ -158,9 +158,10 @@ inline MoeWorkspace moe_workspace_layout(int64_t m, int32_t k, int64_t n_exp, in
     return w;
 }
 
-inline q8_status check_moe(const void* wgu, const void* wdn, int64_t n_exp, int64_t f, int64_t h, const float* x,
-                           int64_t m, int64_t ldx, const int32_t* idx, const float* wts, int32_t k, const float* y,
-                           int64_t ldy, const void* ws, size_t ws_bytes, char* msg, size_t cap) {
+// Arguments of the grouped MoE call other than its workspace.
+inline q8_status check_moe_args(const void* wgu, const void* wdn, int64_t n_exp, int64_t f, int64_t h, const float* x,
+                                int64_t m, int64_t ldx, const int32_t* idx, const float* wts, int32_t k,
+                                const float* y, int64_t ldy, char* msg, size_t cap) {
     q8_status s;
     if ((s = check_dim("m", m, msg, cap)) != Q8_OK) return s;
     if ((s = check_k("h", h, msg, cap)) != Q8_OK) return s;
@@ -173,14 +174,22 @@ inline q8_status check_moe(const void* wgu, const void* wdn, int64_t n_exp, int6
     if (m * int64_t(k) > (int64_t(1) << 24)) return fail(msg, cap, Q8_ERR_SHAPE, "m*k=%lld above 2^24", m * int64_t(k));
     if (m == 0) return Q8_OK;
     if (!wgu || !wdn || !x || !idx || !wts || !y) return fail(msg, cap, Q8_ERR_NULL, "null pointer among the tensor arguments");
-    if (!ws) return fail(msg, cap, Q8_ERR_WORKSPACE, "workspace is NULL");
-    const size_t need = moe_workspace_layout(m, k, n_exp, f, h).total;
-    if (ws_bytes < need) return fail(msg, cap, Q8_ERR_WORKSPACE, "workspace %lld bytes < required %lld", (long long)ws_bytes, (long long)need);
-    if (!aligned(ws, 256)) return fail(msg, cap, Q8_ERR_ALIGN, "workspace not 256-byte aligned");
     if (!aligned(wgu, 16) || !aligned(wdn, 16)) return fail(msg, cap, Q8_ERR_ALIGN, "expert stacks not 16-byte aligned");
     if (!aligned(x, 16)) return fail(msg, cap, Q8_ERR_ALIGN, "x not 16-byte aligned");
     if (ldx % 4 != 0) return fail(msg, cap, Q8_ERR_ALIGN, "ldx=%lld not a multiple of 4", ldx);
     if (!aligned(idx, 4) || !aligned(wts, 4) || !aligned(y, 4)) return fail(msg, cap, Q8_ERR_ALIGN, "topk or y not 4-byte aligned");
+    return Q8_OK;
+}
+
+inline q8_status check_moe(const void* wgu, const void* wdn, int64_t n_exp, int64_t f, int64_t h, const float* x,
+                           int64_t m, int64_t ldx, const int32_t* idx, const float* wts, int32_t k, const float* y,
+                           int64_t ldy, const void* ws, size_t ws_bytes, char* msg, size_t cap) {
+    q8_status s = check_moe_args(wgu, wdn, n_exp, f, h, x, m, ldx, idx, wts, k, y, ldy, msg, cap);
+    if (s != Q8_OK || m == 0) return s;
+    if (!ws) return fail(msg, cap, Q8_ERR_WORKSPACE, "workspace is NULL");
+    const size_t need = moe_workspace_layout(m, k, n_exp, f, h).total;
+    if (ws_bytes < need) return fail(msg, cap, Q8_ERR_WORKSPACE, "workspace %lld bytes < required %lld", (long long)ws_bytes, (long long)need);
+    if (!aligned(ws, 256)) return fail(msg, cap, Q8_ERR_ALIGN, "workspace not 256-byte aligned");
     return Q8_OK;
 }
 

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define Q8_ABI_VERSION 5
+#define Q8_ABI_VERSION 6
 
 typedef enum q8_status {
     Q8_OK = 0,
@@ -241,6 +241,28 @@ q8_status q8_moe_grouped_linear(const void* w_gate_up_exps, const void* w_down_e
                                 const int32_t* topk_idx, const float* topk_w, int32_t k,
                                 float* y, int64_t ldy,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * q8_moe_grouped_linear without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  The route plan and hidden
+ * activations live in a fixed scratch array in device memory that the library holds
+ * per device for the life of the process (Q8_MOE_NOALLOC_SCRATCH_BYTES, 16 MiB; about
+ * 1170 routed (token, slot) pairs at the Qwen3-30B-A3B sizes f = 768, h = 2048).
+ *   Arguments, arithmetic and results as q8_moe_grouped_linear (bit-identical outputs).
+ *   Sizes whose workspace (q8_moe_workspace_bytes) exceeds the scratch are refused with
+ *   Q8_ERR_WORKSPACE before anything is enqueued.  The first call on a device looks up
+ *   the scratch's device address (a runtime query, no allocation).
+ *   Every call on one device shares that device's scratch: calls that can overlap on one
+ *   device (different streams, different host threads) race and must be serialized by
+ *   the caller.  Nothing in the scratch needs to start at any value.
+ */
+#define Q8_MOE_NOALLOC_SCRATCH_BYTES (16u << 20)
+q8_status q8_moe_grouped_linear_noalloc(const void* w_gate_up_exps, const void* w_down_exps,
+                                        int64_t n_exp, int64_t f, int64_t h,
+                                        const float* x, int64_t m, int64_t ldx,
+                                        const int32_t* topk_idx, const float* topk_w, int32_t k,
+                                        float* y, int64_t ldy, void* stream);
 
 #ifdef __cplusplus
 }

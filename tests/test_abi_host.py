@@ -35,14 +35,14 @@ def test_header_declares_the_four_calls():
               "q8_moe_workspace_bytes", "q8_status_string", "q8_last_error", "q8_abi_version",
               "q8_quantize_act", "q8_linear_q8act", "q8_linear_fused_gate_up_silu_q8act",
               "moe_route_topk_top_p", "moe_route_topk_ws", "moe_route_workspace_bytes",
-              "q4_0_linear", "q4_0_linear_fused_gate_up_silu"):
+              "q4_0_linear", "q4_0_linear_fused_gate_up_silu", "q8_moe_grouped_linear_noalloc"):
         assert n in names, names
 
 
 def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert q8.abi_version() == 5
+    assert q8.abi_version() == 6
 
 
 def test_status_strings():
@@ -228,3 +228,24 @@ def test_one_hip_runtime_in_process():
     maps = open("/proc/self/maps").read()
     paths = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
     assert len(paths) == 1, paths
+
+
+def test_moe_noalloc_refuses_sizes_beyond_its_scratch():
+    """The no-allocation mixture refuses, on the host, sizes whose workspace exceeds its
+    fixed 16 MiB scratch (nothing is enqueued); argument errors are reported as for the
+    workspace form; zero rows is a valid no-op."""
+    scratch = 16 << 20
+    # A3B sizes: 146 tokens x 8 slots fit, 147 do not
+    assert lib.q8_moe_workspace_bytes(146, 8, 128, 768, 2048) <= scratch
+    assert lib.q8_moe_workspace_bytes(147, 8, 128, 768, 2048) > scratch
+
+    def call(m, k=8, e=128, f=768, h=2048, idx=FAKE):
+        return lib.q8_moe_grouped_linear_noalloc(FAKE, FAKE, e, f, h, FAKE, m, h, idx, FAKE, k, FAKE, h, None)
+
+    assert call(147) == ERR_WORKSPACE
+    assert "scratch" in lib.q8_last_error().decode()
+    assert call(2048) == ERR_WORKSPACE
+    assert call(4, k=129) == ERR_SHAPE
+    assert call(4, f=700) == ERR_SHAPE
+    assert call(4, idx=None) == ERR_NULL
+    assert call(0, idx=None) == OK
