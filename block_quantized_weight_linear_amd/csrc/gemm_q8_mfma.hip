@@ -5,26 +5,39 @@
 // kernel-class boundary of the fucina DGX Spark README, Performance): each weight is
 // used M times, so the matrix cores, not memory, bound it.  The weights stay Q8_0 in
 // HBM ("14. Model families and example applications", section 14.1: no global
-// dequantization); every block is dequantized once per tile into LDS.
+// dequantization); each tile dequantizes the blocks it needs.
 //
-// Tile: 128 activation rows x BN weight rows (BN = 256 with 8 waves, or 128 / 64 with 4;
-// fused gate_up: BN/2 gate + BN/2 up rows, interleaved in groups of 16 so a lane holds gate
-// and up of the same output), K in steps of 64 (one Q8_0 block pair per weight row).  Per
-// step the threads dequantize the tile's Q8_0 blocks (d * q rounded to bf16, exactly: d*q
-// needs at most 19 significant bits, then one rounding) and convert 128 x 64 activations to
-// bf16 (round to nearest even), both into LDS rows padded to 144 bytes; each wave then runs
-// a 64 x BN/(waves/2) sub-tile as 16 x 16 MFMA tiles, two K=32 steps.  Every weight tile
-// re-reads (from L2) and re-converts the float32 activations, so wider tiles cut that
-// traffic per flop: 256-wide tiles measured 1.16x (M = 512) to 1.45x (M = 2048) faster than
-// 128-wide ones on the Qwen3-8B gate_up.
-
-// Latency: the Q8_0 bytes come from HBM, so each thread keeps a ring of the next
-// kRing steps' blocks in registers (9 dwords a step); activations are re-read by every
-// weight tile and mostly hit L2, so one step of look-ahead covers them.  LDS is double
-// buffered: one barrier per step.
+// Tile: 128 activation rows x BN = 4*WN weight rows, four waves, one block per CU.  Each
+// wave owns WN weight rows (fused gate_up: WN/2 outputs; in each 32-row fragment rows 0..15
+// are gate rows and rows 16..31 the up rows of the same 16 outputs) for all 128 activation
+// rows, so a weight is dequantized by exactly one wave: its Q8_0 bytes reach the wave's
+// own LDS ring by direct-to-LDS 16-byte copies (a lane's 32-bit offset into the matrix is
+// fixed for the whole K loop, the step is a scalar base), and the wave turns them into
+// MFMA B operands in registers (bf16(fp32(d) * q), one rounding; d*q needs at most 19
+// significant bits).  The activations of a K step (128 x 64 float32) reach LDS by direct
+// 16-byte copies and are rounded to bf16 (nearest even) once per block into the tile the
+// four waves share.  Per wave a K step is 4 x 4 x WN/32 v_mfma_f32_32x32x16_bf16 on a 128 x
+// WN accumulator tile (on gfx950 this shape keeps the matrix cores busy from one wave per
+// SIMD; 16x16x32 with as many accumulators does not).
 //
-// MFMA lane layout (checked on the device): lane l supplies A[l%16][8*(l/16) + i] and
-// B[8*(l/16) + i][l%16], i = 0..7, and receives D[4*(l/16) + i][l%16], i = 0..3.
+// Inputs of a Q8_0 block are multiplied in a permuted order: the four groups of 8 inputs
+// run as groups 0, 2, 1, 3 (both operands alike, so the products and sums are those of
+// the block): then the 16 quants a lane needs are contiguous in the block, and the lane
+// reads them as whole 16-byte LDS chunks (conflict-free across the 32 rows of a fragment).
+//
+// Pipeline: weight bytes are copied two steps ahead into a ring of three stages per wave,
+// float32 activations one step ahead into one stage; every vector-memory load of the loop
+// is such a copy, so the waits are explicit counts of them.  Per K step: wait, barrier,
+// round the activations, barrier, issue the next copies, then the MFMAs of block 0 of the
+// pair while block 1 is dequantized and the MFMAs of block 1 while the next step's block 0
+// is (the dequantization runs under the matrix cores).  The step loop is unrolled by four,
+// the period of a pair's position inside its 16-byte chunks.
+//
+// Dense grids map tiles to blocks so that the 128-row tiles sharing a weight tile land
+// on the same XCD (blocks are handed to the 8 XCDs in turn), where they share its L2.
+//
+// MFMA lane layout (checked on the device): lane l supplies A[l%32][8*(l/32) + i] and
+// B[8*(l/32) + i][l%32], i = 0..7, and register j of D holds D[8*(j/4) + 4*(l/32) + j%4][l%32].
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -35,18 +48,34 @@
 namespace q8k {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_a4m __attribute__((ext_vector_type(4), aligned(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 128;           // activation rows per tile
-constexpr int kBK = 64;            // inputs per K step (one Q8_0 block pair per weight row)
-constexpr int kLdsRow = kBK + 8;   // bf16 per LDS row (144 bytes: 16-byte steps between rows)
-constexpr int kRing = 4;           // K steps of Q8_0 bytes in flight per thread (K/64 is a multiple of 4)
+constexpr int kBM = 128;          // activation rows per tile
+constexpr int kBK = 64;           // inputs per K step (one Q8_0 block pair per weight row)
+constexpr int kXStride = 72;      // bf16 per LDS row of the activation tile (144 bytes)
+constexpr int kMfWaves = 4;
+constexpr int kMfThreads = 64 * kMfWaves;
+constexpr int kWRing = 3;         // weight stages per wave
+constexpr int kXcds = 8;          // dense grids: tiles sharing weights go to one XCD
 
-// Calls f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>) in order.
-template <typename F, int... I>
-__device__ __forceinline__ void mf_static_for(F&& f, std::integer_sequence<int, I...>) {
-    (f(std::integral_constant<int, I>{}), ...);
+// Per-wave weight stage for WN weight rows.  A row's pair for K step s is bytes 68s ..
+// 68s+67 of the row; the stage holds the five aligned 16-byte chunks that contain it (80
+// bytes from 68s - 4*(s%4): rows are 16-byte aligned and hold a multiple of four pairs, so
+// the chunks never pass the row's end), copied as 64 chunks per instruction, padded to
+// whole copies.  The pair starts at dword s%4 of its 20-dword stage row.
+template <int WN>
+struct WStage {
+    static constexpr int kChunks = 5;
+    static constexpr int kRowDwords = 4 * kChunks;
+    static constexpr int kCopies = (WN * kChunks + 63) / 64;
+    static constexpr int kDwords = kCopies * 256;
+};
+
+constexpr size_t kXf32Bytes = (size_t)kBM * kBK * 4;      // float32 activation stage
+constexpr size_t kXbfBytes = (size_t)kBM * kXStride * 2;   // bf16 activation tile
+template <int WN>
+constexpr size_t mfma_lds_bytes() {
+    return kXf32Bytes + kXbfBytes + (size_t)kMfWaves * kWRing * WStage<WN>::kDwords * 4;
 }
 
 __device__ __forceinline__ float mf_half_lo(uint32_t v) {
@@ -55,24 +84,44 @@ __device__ __forceinline__ float mf_half_lo(uint32_t v) {
 __device__ __forceinline__ float mf_half_hi(uint32_t v) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
 }
+__device__ __forceinline__ float mf_sbyte(uint32_t v, int b) { return (float)(int)(int8_t)(v >> (8 * b)); }
 
-// Weight row of tile column c for output tile nt (BN columns; fused: BN/2 outputs with
-// gate and up columns interleaved in groups of 16).
-template <int BN, bool SILU>
-__device__ __forceinline__ int tile_row(int nt, int c, int n_out) {
-    if constexpr (SILU) {
-        int f = nt * (BN / 2) + 16 * (c >> 5) + (c & 15);
-        f = f < n_out ? f : n_out - 1;
-        return ((c >> 4) & 1) ? f + n_out : f;
-    } else {
-        const int n = nt * BN + c;
-        return n < n_out ? n : n_out - 1;
-    }
+// One wave-wide direct-to-LDS 16-byte copy with a scalar base: lane l copies the 16 bytes
+// at base + off to lds + 16*l.  base and lds are wave-uniform (an SGPR pair and M0); M0 is
+// saved and restored, and a write of M0 needs one wait state before the copy reads it.
+__device__ __forceinline__ void lds_copy16_sbase(const uint8_t* base, uint32_t off, uint32_t lds) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(off), "s"(base), "s"(lds)
+        : "memory");
 }
 
-struct Q8Pair {  // 9 dwords of one Q8_0 block as it sits in its pair (see the loader)
-    uint32_t dw[9];
-};
+// One wave-wide direct-to-LDS 16-byte copy: lane l copies 16 bytes from src to
+// lds + 16*l (lds wave-uniform, through M0 as above).
+__device__ __forceinline__ void lds_copy16_mf(const void* src, uint32_t lds) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(lds)
+        : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void mf_wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // Expert-grouped tiles (the MoE prefill form): tile t of the grid's tile list belongs to
 // the expert e with tile_start[e] <= t < tile_start[e + 1]; its activation rows are the
@@ -83,36 +132,40 @@ struct GroupArgs {
     const int32_t* offsets;     // [n_exp + 1] pair positions per expert
     const int32_t* tile_start;  // [n_exp + 1] first 128-row tile of each expert
     const int32_t* sorted;      // [pairs] pair index (token * k + slot) at each position
-    int n_exp, k, n_tiles;      // n_tiles: output tiles per expert (grid = tiles x n_tiles)
+    int n_exp, k;
     size_t expert_bytes;        // bytes of one expert's Q8_0 matrix
     bool gather;
 };
 
-template <int BN, bool SILU, bool GROUPED, int NT = 256>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_q8_mfma_kernel(const uint8_t* __restrict__ w, int n_out, int P,
-                                                           const float* __restrict__ x, int M, int ldx,
-                                                           float* __restrict__ y, int ldy, int m_tiles,
-                                                           GroupArgs g) {
-    constexpr int WN = NT / 128;       // waves along n (two along m)
-    constexpr int TJ = BN / (16 * WN); // 16x16 tiles per wave along n
-    constexpr int SPLIT = NT / (2 * BN);  // threads per Q8_0 block (1: whole block, 2: 16 quants each)
-    static_assert(SPLIT == 1 || SPLIT == 2, "2*BN blocks per step over NT threads");
-    constexpr int XPT = kBM * kBK / NT;   // activations per thread per step (32 or 16)
-    constexpr int XPR = kBK / XPT;        // threads per activation row
-    __shared__ __attribute__((aligned(16))) __bf16 xs[2][kBM * kLdsRow];
-    __shared__ __attribute__((aligned(16))) __bf16 ws[2][BN * kLdsRow];
+// Four bf16 weights d*q from the quant bytes of dword v (byte b: weight b).
+__device__ __forceinline__ void dq4(uint32_t v, float d, bf16x8& o, int at) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) o[at + b] = (__bf16)(mf_sbyte(v, b) * d);
+}
+
+template <int WN, bool SILU, bool GROUPED>
+__global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_q8_mfma_kernel(
+    const uint8_t* __restrict__ w, int n_out, int P, const float* __restrict__ x, int M, int ldx,
+    float* __restrict__ y, int ldy, int m_tiles, int n_tiles, int tiles, GroupArgs g) {
+    constexpr int BN = kMfWaves * WN;
+    constexpr int NF = WN / 32;  // 32-column fragments per wave
+    constexpr int L = WStage<WN>::kCopies;
+    static_assert(WN % 32 == 0, "whole 32-column fragments per wave");
+    static_assert(L < 64, "copies of a stage must fit the vmcnt counter");
+    extern __shared__ __attribute__((aligned(16))) uint8_t mf_smem[];
+    float* xf = reinterpret_cast<float*>(mf_smem);                          // [kBM][kBK] float32
+    __bf16* xs = reinterpret_cast<__bf16*>(mf_smem + kXf32Bytes);           // [kBM][kXStride] bf16
+    uint32_t* wr = reinterpret_cast<uint32_t*>(mf_smem + kXf32Bytes + kXbfBytes);  // [waves][ring][stage]
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wv = tid >> 6;
-    const int wm = wv & 1, wn = wv >> 1;  // wn < WN
-    int mt = blockIdx.x % m_tiles;  // m tiles of one n tile run side by side (shared weights)
-    int nt = blockIdx.x / m_tiles;
-    int mbase = 0;  // grouped: first position of the tile (its rows are positions mbase + r)
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    int mt, nt, mbase = 0;
     if constexpr (GROUPED) {
-        const int t = blockIdx.x / g.n_tiles;
-        nt = blockIdx.x - t * g.n_tiles;
-        if (t >= g.tile_start[g.n_exp]) return;  // past the tile list (block-uniform, no barrier yet)
-        int lo = 0, hi = g.n_exp;  // tile_start[lo] <= t < tile_start[hi]: the expert is the largest such lo
+        const int t = blockIdx.x / n_tiles;
+        nt = blockIdx.x - t * n_tiles;
+        if (t >= g.tile_start[g.n_exp]) return;  // past the tile list (block-uniform, before any barrier)
+        int lo = 0, hi = g.n_exp;                 // largest lo with tile_start[lo] <= t
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
             if (g.tile_start[mid] <= t) lo = mid;
@@ -122,201 +175,300 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         const int rows = g.offsets[lo + 1] - mbase;
         M = rows < kBM ? rows : kBM;
         mt = 0;
-        w += (size_t)lo * g.expert_bytes;
+        w += (size_t)__builtin_amdgcn_readfirstlane(lo) * g.expert_bytes;
+    } else {
+        const int per_xcd = (tiles + kXcds - 1) / kXcds;
+        const int t = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+        if (t >= tiles) return;  // block-uniform, before any barrier
+        mt = t % m_tiles;
+        nt = t / m_tiles;
     }
-    const size_t row_bytes = (size_t)P * 68;
+    const uint32_t row_bytes = (uint32_t)P * 68u;
 
-    // weight role: block wb of the pair of tile column wc (part hh of it when SPLIT = 2).
-    // In a pair (68 bytes) block 0 is bytes [0, 34) and block 1 bytes [34, 68); the 9
-    // dwords loaded from byte 32*wb hold block 0 at byte 0 (scale) and 2..33 (quants), or
-    // block 1 at bytes 2..3 (scale) and 4..35 (quants).
-    const int wc = (tid / (2 * SPLIT)), wb = (tid / SPLIT) & 1, hh = tid & (SPLIT - 1);
-    const uint8_t* wrow = w + (size_t)tile_row<BN, SILU>(nt, wc, n_out) * row_bytes + 32 * wb;
-    // activation role: XPT inputs (part xh of the step) of tile row xr
-    const int xr = tid / XPR, xh = tid % XPR;
-    int xm = mt * kBM + xr;
-    xm = xm < M ? xm : M - 1;
-    size_t xoff = (size_t)xm;
-    if constexpr (GROUPED) xoff = g.gather ? (size_t)(g.sorted[mbase + xm] / g.k) : (size_t)(mbase + xm);
-    const float* xrow = x + xoff * ldx + XPT * xh;
+    // Weight row of the wave's column c (0 <= c < WN); past the matrix: the last row.
+    auto w_row = [&](int c) __attribute__((always_inline)) {
+        if constexpr (SILU) {
+            const int f = c >> 5, w32 = c & 31;
+            int o = nt * (BN / 2) + wave * (WN / 2) + 16 * f + (w32 & 15);
+            o = o < n_out ? o : n_out - 1;
+            return (w32 >= 16) ? o + n_out : o;
+        } else {
+            const int n = nt * BN + wave * WN + c;
+            return n < n_out ? n : n_out - 1;
+        }
+    };
+    // Copy j of a stage moves stage chunks 64j .. 64j+63: chunk i is chunk i % 5 of column
+    // i / 5 (the padding past WN*5 re-reads the last column's chunks).
+    uint32_t woff[L];
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+        const int i = 64 * j + lane;
+        int r = i / WStage<WN>::kChunks;
+        const int c = i - WStage<WN>::kChunks * r;
+        r = r < WN ? r : WN - 1;
+        woff[j] = (uint32_t)w_row(r) * row_bytes + 16u * (uint32_t)c;
+    }
+    const uint32_t wr_lds = (uint32_t)(uintptr_t)wr + (uint32_t)(wave * kWRing * WStage<WN>::kDwords * 4);
+    auto issue_w = [&](int s, int slot) __attribute__((always_inline)) {
+        const uint8_t* base = w + (size_t)s * 68 - 4 * (s & 3);  // 16-byte aligned within the row
+        const uint32_t lds = __builtin_amdgcn_readfirstlane(wr_lds + (uint32_t)(slot * WStage<WN>::kDwords * 4));
+#pragma unroll
+        for (int j = 0; j < L; ++j) lds_copy16_sbase(base, woff[j], lds + 1024u * j);
+    };
 
-    f32x4 acc[4][TJ];
+    // Activation copies: copy j of wave w moves tile rows 32w + 4j .. 32w + 4j + 3 of a
+    // step (256 bytes each, lane l: row 32w + 4j + l/16, bytes 16*(l%16) ..); past the
+    // call's rows a lane re-reads the last row.
+    const float* xsrc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        int r = mt * kBM + 32 * wave + 4 * j + (lane >> 4);
+        r = r < M ? r : M - 1;
+        size_t ri = (size_t)r;
+        if constexpr (GROUPED) ri = g.gather ? (size_t)(g.sorted[mbase + r] / g.k) : (size_t)(mbase + r);
+        xsrc[j] = x + ri * (size_t)ldx + 4 * (lane & 15);
+    }
+    const uint32_t xf_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)xf + (uint32_t)(wave * 32 * kBK * 4));
+    auto issue_x = [&](int s) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) lds_copy16_mf(xsrc[j] + (size_t)kBK * s, xf_lds + 1024u * j);
+    };
+    // float32 stage -> bf16 tile: thread t rounds chunk t%16 (4 inputs) of rows t/16 + 16q.
+    // Within each 32-input block the groups of 8 inputs are stored in the order 0, 2, 1, 3.
+    const int xc = tid & 15;                       // chunk: inputs 4xc .. 4xc + 3 of the step
+    const int xgrp = (xc >> 1) & 3;                // its group of 8 within the block
+    const int xpos = 32 * (xc >> 3) + 8 * ((xgrp == 1) ? 2 : (xgrp == 2) ? 1 : xgrp) + 4 * (xc & 1);
+    auto round_x = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int r = (tid >> 4) + 16 * q;
+            const float4 v = *reinterpret_cast<const float4*>(xf + r * kBK + 4 * xc);
+            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+            bf16x4 o;
+            o[0] = (__bf16)v.x; o[1] = (__bf16)v.y; o[2] = (__bf16)v.z; o[3] = (__bf16)v.w;
+            *reinterpret_cast<bf16x4*>(xs + r * kXStride + xpos) = o;
+        }
+    };
+
+    const int h = lane >> 5, c32 = lane & 31;
+    f32x16 acc[4][NF];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][f][e] = 0.f;
 
-    Q8Pair ring[kRing];
-    float4 rx[XPT / 4];
-    auto load_w = [&](Q8Pair& r, int s) __attribute__((always_inline)) {
-        const uint8_t* src = wrow + (size_t)68 * s;
-        const u32x4_a4m a = *reinterpret_cast<const u32x4_a4m*>(src);
-        const u32x4_a4m b = *reinterpret_cast<const u32x4_a4m*>(src + 16);
-        r.dw[0] = a.x; r.dw[1] = a.y; r.dw[2] = a.z; r.dw[3] = a.w;
-        r.dw[4] = b.x; r.dw[5] = b.y; r.dw[6] = b.z; r.dw[7] = b.w;
-        r.dw[8] = *reinterpret_cast<const uint32_t*>(src + 32);
-    };
-    auto load_x = [&](int s) __attribute__((always_inline)) {
-        const float4* src = reinterpret_cast<const float4*>(xrow + kBK * s);
+    // B operands of block hb of a step whose stage is `stage` and whose pair starts at dword
+    // U of its 20-dword stage row: bq[sub][f] holds quants 16h + 8sub .. +7 of the block.
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    auto dequant_block = [&](auto uc, auto hbc, const uint32_t* stage, bf16x8 (&bq)[2][NF])
+                             __attribute__((always_inline)) {
+        constexpr int U = decltype(uc)::value, HB = decltype(hbc)::value;
 #pragma unroll
-        for (int i = 0; i < XPT / 4; ++i) rx[i] = src[i];
-    };
-    auto store_w = [&](const Q8Pair& r, int buf) __attribute__((always_inline)) {
-        const float d = wb == 0 ? mf_half_lo(r.dw[0]) : mf_half_hi(r.dw[0]);
-        constexpr int NQ = 32 / SPLIT;  // quants this thread converts
-        bf16x8 v[NQ / 8];
+        for (int f = 0; f < NF; ++f) {
+            const u32x4* row = reinterpret_cast<const u32x4*>(stage + (32 * f + c32) * WStage<WN>::kRowDwords);
+            if constexpr (HB == 0) {
+                // scale: dword U (low half); quants 16h.. at bytes 2 + 16h .. 17 + 16h of the
+                // pair = dwords U + 4h .. U + 4h + 4, i.e. in chunks h and h + 1
+                const u32x4 sc = row[0], x = row[h], y = row[h + 1];
+                const float d = mf_half_lo(sc[U]);
+                uint32_t q[5];
 #pragma unroll
-        for (int g = 0; g < NQ / 4; ++g) {
-            // quant dword g + hh*NQ/4 of the block (selects, not a dynamic register index)
-            uint32_t lo = r.dw[g], hi = r.dw[g + 1];
-            if constexpr (SPLIT == 2) {
-                lo = hh ? r.dw[g + 4] : lo;
-                hi = hh ? r.dw[g + 5] : hi;
+                for (int k = 0; k < 5; ++k) q[k] = (U + k < 4) ? x[U + k] : y[U + k - 4];
+#pragma unroll
+                for (int sub = 0; sub < 2; ++sub) {
+                    dq4(__builtin_amdgcn_alignbyte(q[2 * sub + 1], q[2 * sub], 2), d, bq[sub][f], 0);
+                    dq4(__builtin_amdgcn_alignbyte(q[2 * sub + 2], q[2 * sub + 1], 2), d, bq[sub][f], 4);
+                }
+            } else {
+                // scale: dword U + 8 (high half, chunk 2); quants 16h.. at dwords U + 9 + 4h ..
+                // U + 12 + 4h, i.e. in chunks 2 + h and 3 + h
+                const u32x4 sc = row[2], x = row[2 + h], y = row[3 + h];
+                const float d = mf_half_hi(sc[U]);
+                uint32_t q[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) q[k] = (U + 1 + k < 4) ? x[U + 1 + k] : y[U + 1 + k - 4];
+#pragma unroll
+                for (int sub = 0; sub < 2; ++sub) {
+                    dq4(q[2 * sub], d, bq[sub][f], 0);
+                    dq4(q[2 * sub + 1], d, bq[sub][f], 4);
+                }
             }
-            const uint32_t q4 = wb == 0 ? __builtin_amdgcn_alignbit(hi, lo, 16) : hi;
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-                v[g >> 1][4 * (g & 1) + b] = (__bf16)((float)(int)(int8_t)(q4 >> (8 * b)) * d);
         }
-        bf16x8* dst = reinterpret_cast<bf16x8*>(&ws[buf][wc * kLdsRow + 32 * wb + NQ * hh]);
-#pragma unroll
-        for (int i = 0; i < NQ / 8; ++i) dst[i] = v[i];
     };
-    auto store_x = [&](int buf) __attribute__((always_inline)) {
-        bf16x8 v[XPT / 8];
+    // MFMAs of block hb (LDS positions 32hb .. 32hb + 31 of the tile rows)
+    auto mma_block = [&](int hb, const bf16x8 (&bq)[2][NF]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < XPT / 4; ++i) {
-            v[i >> 1][4 * (i & 1) + 0] = (__bf16)rx[i].x;
-            v[i >> 1][4 * (i & 1) + 1] = (__bf16)rx[i].y;
-            v[i >> 1][4 * (i & 1) + 2] = (__bf16)rx[i].z;
-            v[i >> 1][4 * (i & 1) + 3] = (__bf16)rx[i].w;
-        }
-        bf16x8* dst = reinterpret_cast<bf16x8*>(&xs[buf][xr * kLdsRow + XPT * xh]);
-#pragma unroll
-        for (int i = 0; i < XPT / 8; ++i) dst[i] = v[i];
-    };
-    auto mma = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-        for (int kk = 0; kk < kBK; kk += 32) {
-            bf16x8 af[4], bfr[TJ];
-            const int ko = kk + 8 * (lane >> 4);
+        for (int sub = 0; sub < 2; ++sub) {
+            bf16x8 af[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                af[i] = *reinterpret_cast<const bf16x8*>(&xs[buf][(64 * wm + 16 * i + (lane & 15)) * kLdsRow + ko]);
-#pragma unroll
-            for (int j = 0; j < TJ; ++j)
-                bfr[j] = *reinterpret_cast<const bf16x8*>(&ws[buf][((BN / WN) * wn + 16 * j + (lane & 15)) * kLdsRow + ko]);
+                af[i] = *reinterpret_cast<const bf16x8*>(xs + (32 * i + c32) * kXStride + 32 * hb + 16 * sub + 8 * h);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < TJ; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+                for (int f = 0; f < NF; ++f)
+                    acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bq[sub][f], acc[i][f], 0, 0, 0);
         }
+    };
+    auto stage_of = [&](int t) __attribute__((always_inline)) {
+        return wr + (size_t)(wave * kWRing + t % kWRing) * WStage<WN>::kDwords;
     };
 
-    // prologue: K steps 0..kRing-1 of Q8_0 bytes, step 0 of the activations (P >= kRing)
-    // Issue order matters: the wait counter retires loads in order, so the activations a
-    // step needs next are issued before the weight loads it needs kRing steps later.
-    load_w(ring[0], 0);
-    load_x(0);
-    __builtin_amdgcn_sched_barrier(0);
-    mf_static_for([&](auto j) __attribute__((always_inline)) {
-        if constexpr (j.value > 0) load_w(ring[j.value], j.value);
-    }, std::make_integer_sequence<int, kRing>{});
-    for (int s0 = 0; s0 < P; s0 += kRing) {
-        mf_static_for([&](auto j) __attribute__((always_inline)) {
-            const int s = s0 + j.value;
-            const int buf = j.value & 1;  // kRing is even, so buf == s & 1
-            store_x(buf);
-            store_w(ring[j.value], buf);
-            load_x(s + 1 < P ? s + 1 : s);
-            __builtin_amdgcn_sched_barrier(0);
-            load_w(ring[j.value], s + kRing < P ? s + kRing : s);
-            __syncthreads();
-            mma(buf);
-            // keep the next step's conversions (which wait for its loads) below this step's MFMAs
-            __builtin_amdgcn_sched_barrier(0);
-        }, std::make_integer_sequence<int, kRing>{});
+    // prologue: X(0), W(0), W(1) in flight, in that order; block 0 of step 0 dequantized
+    bf16x8 b0[2][NF], b1[2][NF];
+    issue_x(0);
+    issue_w(0, 0);
+    issue_w(1, 1);  // P >= 4
+    mf_wait_vmcnt<L>();  // X(0), W(0)
+    dequant_block(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, stage_of(0), b0);
+    auto step = [&](int s, auto uc) __attribute__((always_inline)) {
+        constexpr int U = decltype(uc)::value;  // s % 4
+        // X(s) and W(s) have arrived: only W(s+1), the newest L copies, may be in flight
+        if (s + 1 < P)
+            mf_wait_vmcnt<L>();
+        else
+            mf_wait_vmcnt<0>();
+        __syncthreads();  // every wave's copies of X(s) are in; all waves are done with step s-1
+        round_x();
+        __syncthreads();  // the bf16 tile is complete; the float32 stage is free
+        const bool more = s + 1 < P;
+        if (more) issue_x(s + 1);
+        if (s + 2 < P) issue_w(s + 2, (s + 2) % kWRing);
+        dequant_block(uc, std::integral_constant<int, 1>{}, stage_of(s), b1);
+        mma_block(0, b0);
+        if (more) {
+            // W(s+1) is older than the 8 + L copies just issued
+            if (s + 2 < P) mf_wait_vmcnt<8 + L>(); else mf_wait_vmcnt<8>();
+            dequant_block(std::integral_constant<int, (U + 1) & 3>{}, std::integral_constant<int, 0>{}, stage_of(s + 1), b0);
+        }
+        mma_block(1, b1);
+    };
+    for (int s = 0; s < P; s += 4) {  // P is a multiple of 4
+        step(s, std::integral_constant<int, 0>{});
+        step(s + 1, std::integral_constant<int, 1>{});
+        step(s + 2, std::integral_constant<int, 2>{});
+        step(s + 3, std::integral_constant<int, 3>{});
     }
 
-    // ---- epilogue: lane holds D[m = 4*(lane/16) + e][n = lane%16] of each 16 x 16 tile
+    // epilogue: register e of fragment (i, f) holds row 32i + 8(e/4) + 4h + e%4, column
+    // 32f + c32 of the wave's tile
     if constexpr (GROUPED) y += (size_t)mbase * ldy;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int m = mt * kBM + 64 * wm + 16 * i + 4 * (lane >> 4) + e;
-            if (m >= M) continue;
-            if constexpr (SILU) {
+        for (int e = 0; e < 16; ++e) {
+            const int m = mt * kBM + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
 #pragma unroll
-                for (int jp = 0; jp < TJ / 2; ++jp) {
-                    // wave columns (BN/WN)*wn + 16*j: even j gate, odd j up of the same outputs
-                    const int f = nt * (BN / 2) + (BN / (2 * WN)) * wn + 16 * jp + (lane & 15);
-                    if (f < n_out) {
-                        const float g = acc[i][2 * jp][e];
-                        const float u = acc[i][2 * jp + 1][e];
-                        y[(size_t)m * ldy + f] = g / (1.0f + __expf(-g)) * u;
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < TJ; ++j) {
-                    const int n = nt * BN + (BN / WN) * wn + 16 * j + (lane & 15);
-                    if (n < n_out) y[(size_t)m * ldy + n] = acc[i][j][e];
+            for (int f = 0; f < NF; ++f) {
+                if constexpr (SILU) {
+                    // columns 0..15 of a fragment are gate rows, 16..31 the up rows of the same
+                    // outputs: the up value comes from lane ^ 16
+                    const float v = acc[i][f][e];
+                    const float other = __shfl_xor(v, 16, 64);
+                    const int o = nt * (BN / 2) + wave * (WN / 2) + 16 * f + c32;
+                    if (c32 < 16 && m < M && o < n_out) y[(size_t)m * ldy + o] = v / (1.0f + __expf(-v)) * other;
+                } else {
+                    const int n = nt * BN + wave * WN + 32 * f + c32;
+                    if (m < M && n < n_out) y[(size_t)m * ldy + n] = acc[i][f][e];
                 }
             }
         }
     }
 }
 
-template <int BN, int NT = 256>
-hipError_t launch_tiles(const uint8_t* w, int64_t n_out, int P, bool silu, const float* x, int64_t m, int64_t ldx,
-                        float* y, int64_t ldy, hipStream_t stream) {
-    const GroupArgs none{};
-    const int m_tiles = (int)((m + kBM - 1) / kBM);
-    const int64_t cols = silu ? BN / 2 : BN;  // outputs per tile
-    const int64_t blocks = (n_out + cols - 1) / cols * m_tiles;
-    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    if (silu)
-        hipLaunchKernelGGL((gemm_q8_mfma_kernel<BN, true, false, NT>), dim3((unsigned)blocks), dim3(NT), 0, stream, w,
-                           (int)n_out, P, x, (int)m, (int)ldx, y, (int)ldy, m_tiles, none);
-    else
-        hipLaunchKernelGGL((gemm_q8_mfma_kernel<BN, false, false, NT>), dim3((unsigned)blocks), dim3(NT), 0, stream, w,
-                           (int)n_out, P, x, (int)m, (int)ldx, y, (int)ldy, m_tiles, none);
+namespace {
+
+// The widest per-wave tile (96, 64 or 32 weight rows) that wastes at most a tenth of
+// its columns on the output edge and, for dense grids, still gives every CU a tile;
+// otherwise the one with the least waste.
+int pick_wn(int64_t n_out, bool silu, int64_t row_tiles, int cu_count) {
+    const int cand[3] = {96, 64, 32};
+    int best = 32;
+    double best_fill = -1.0;
+    for (int wn : cand) {
+        const int64_t cols = silu ? 2 * wn : 4 * wn;
+        const int64_t nt = (n_out + cols - 1) / cols;
+        const double fill = (double)n_out / (double)(nt * cols);
+        if (fill >= 0.9 && nt * row_tiles >= cu_count) return wn;
+        if (fill > best_fill + 1e-9) {
+            best_fill = fill;
+            best = wn;
+        }
+    }
+    return best;
+}
+
+template <int WN, bool SILU, bool GROUPED>
+hipError_t launch_wn(unsigned blocks, const uint8_t* w, int n_out, int P, const float* x, int m, int ldx, float* y,
+                     int ldy, int m_tiles, int n_tiles, int tiles, const GroupArgs& g, hipStream_t stream) {
+    auto kernel = gemm_q8_mfma_kernel<WN, SILU, GROUPED>;
+    const size_t lds = mfma_lds_bytes<WN>();
+    // once per device and kernel: raise the dynamic LDS limit above the default
+    static thread_local uint64_t allowed = 0;  // bit d: done on device d
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 64 || !((allowed >> dev) & 1)) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)lds);
+        if (e != hipSuccess) return e;
+        if (dev < 64) allowed |= uint64_t(1) << dev;
+    }
+    hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kMfThreads), lds, stream, w, n_out, P, x, m, ldx, y, ldy, m_tiles,
+                       n_tiles, tiles, g);
     return hipGetLastError();
 }
+
+template <bool SILU, bool GROUPED>
+hipError_t launch_any(int wn, unsigned blocks, const uint8_t* w, int n_out, int P, const float* x, int m, int ldx,
+                      float* y, int ldy, int m_tiles, int n_tiles, int tiles, const GroupArgs& g,
+                      hipStream_t stream) {
+    switch (wn) {
+        case 96: return launch_wn<96, SILU, GROUPED>(blocks, w, n_out, P, x, m, ldx, y, ldy, m_tiles, n_tiles, tiles, g, stream);
+        case 64: return launch_wn<64, SILU, GROUPED>(blocks, w, n_out, P, x, m, ldx, y, ldy, m_tiles, n_tiles, tiles, g, stream);
+        default: return launch_wn<32, SILU, GROUPED>(blocks, w, n_out, P, x, m, ldx, y, ldy, m_tiles, n_tiles, tiles, g, stream);
+    }
+}
+
+}  // namespace
 
 hipError_t launch_gemm_q8_mfma_grouped(const uint8_t* w_stack, size_t expert_bytes, int64_t n_out, int64_t k,
                                        bool silu_pairs, const float* x, int64_t ldx, float* y, int64_t ldy,
                                        const int32_t* offsets, const int32_t* tile_start, const int32_t* sorted,
                                        int n_exp, int top_k, bool gather, int64_t max_tiles, hipStream_t stream) {
     const int P = (int)(k / kBK);
-    const int64_t cols = silu_pairs ? 128 : 256;  // outputs per 128 x 256 tile
+    const int wn = pick_wn(n_out, silu_pairs, 1, 0);
+    const int64_t cols = silu_pairs ? 2 * wn : 4 * wn;
     const int n_tiles = (int)((n_out + cols - 1) / cols);
     const int64_t blocks = max_tiles * n_tiles;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    const GroupArgs g{offsets, tile_start, sorted, n_exp, top_k, n_tiles, expert_bytes, gather};
-    if (silu_pairs)
-        hipLaunchKernelGGL((gemm_q8_mfma_kernel<256, true, true, 512>), dim3((unsigned)blocks), dim3(512), 0, stream,
-                           w_stack, (int)n_out, P, x, 0, (int)ldx, y, (int)ldy, 1, g);
-    else
-        hipLaunchKernelGGL((gemm_q8_mfma_kernel<256, false, true, 512>), dim3((unsigned)blocks), dim3(512), 0, stream,
-                           w_stack, (int)n_out, P, x, 0, (int)ldx, y, (int)ldy, 1, g);
-    return hipGetLastError();
+    const GroupArgs g{offsets, tile_start, sorted, n_exp, top_k, expert_bytes, gather};
+    return silu_pairs ? launch_any<true, true>(wn, (unsigned)blocks, w_stack, (int)n_out, P, x, 0, (int)ldx, y,
+                                               (int)ldy, 1, n_tiles, 0, g, stream)
+                      : launch_any<false, true>(wn, (unsigned)blocks, w_stack, (int)n_out, P, x, 0, (int)ldx, y,
+                                                (int)ldy, 1, n_tiles, 0, g, stream);
 }
 
 hipError_t launch_gemm_q8_mfma(const DeviceInfo& dev, const uint8_t* w, int64_t n_out, int64_t k, bool silu_pairs,
                                const float* x, int64_t m, int64_t ldx, float* y, int64_t ldy, hipStream_t stream) {
     const int P = (int)(k / kBK);
-    // The widest tiles that still give at least one tile per CU: 128 x 256 (8 waves),
-    // 128 x 128, else 128 x 64 (small N stays spread over the chip at the cost of reading
-    // the activations more often).
-    const int64_t cols128 = silu_pairs ? 64 : 128;
-    const int64_t tiles128 = ((n_out + cols128 - 1) / cols128) * ((m + kBM - 1) / kBM);
-    const int64_t tiles256 = (tiles128 + 1) / 2;
-    if (tiles256 >= dev.cu_count) return launch_tiles<256, 512>(w, n_out, P, silu_pairs, x, m, ldx, y, ldy, stream);
-    if (tiles128 >= dev.cu_count) return launch_tiles<128>(w, n_out, P, silu_pairs, x, m, ldx, y, ldy, stream);
-    return launch_tiles<64>(w, n_out, P, silu_pairs, x, m, ldx, y, ldy, stream);
+    // Weight offsets are 32-bit within the matrix: larger matrices run the float32 path.
+    const uint64_t matrix_bytes = (uint64_t)(silu_pairs ? 2 * n_out : n_out) * (uint64_t)P * 68u;
+    if (matrix_bytes >= (uint64_t(1) << 32)) return launch_gemv_q8(dev, w, n_out, k, silu_pairs, x, m, ldx, y, ldy, stream);
+    const int m_tiles = (int)((m + kBM - 1) / kBM);
+    const int wn = pick_wn(n_out, silu_pairs, m_tiles, dev.cu_count);
+    const int64_t cols = silu_pairs ? 2 * wn : 4 * wn;
+    const int64_t n_tiles = (n_out + cols - 1) / cols;
+    const int64_t tiles = n_tiles * m_tiles;
+    const int64_t blocks = (tiles + kXcds - 1) / kXcds * kXcds;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    const GroupArgs none{};
+    return silu_pairs ? launch_any<true, false>(wn, (unsigned)blocks, w, (int)n_out, P, x, (int)m, (int)ldx, y,
+                                                (int)ldy, m_tiles, (int)n_tiles, (int)tiles, none, stream)
+                      : launch_any<false, false>(wn, (unsigned)blocks, w, (int)n_out, P, x, (int)m, (int)ldx, y,
+                                                 (int)ldy, m_tiles, (int)n_tiles, (int)tiles, none, stream);
 }
 
 }  // namespace q8k
