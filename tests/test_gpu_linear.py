@@ -31,7 +31,7 @@ SMALL = [(1, 256), (3, 256), (37, 512), (257, 768), (1000, 1024), (4099, 1024), 
 
 
 @pytest.mark.parametrize("n,k", SMALL)
-@pytest.mark.parametrize("m", [1, 2, 3, 5, 8, 16, 17, 33])
+@pytest.mark.parametrize("m", [1, 2, 3, 5, 8, 9, 12, 13, 16, 17, 33])
 def test_linear_small_vs_oracle(q8, n, k, m):
     lib, torch, dev = q8
     wb, _, _ = wl.q8_weight(1000 + n + k, n, k)
@@ -42,7 +42,7 @@ def test_linear_small_vs_oracle(q8, n, k, m):
 
 
 @pytest.mark.parametrize("f,k", [(1, 256), (5, 512), (300, 1024), (1536, 1024), (129, 4096), (64, 768)])
-@pytest.mark.parametrize("m", [1, 4, 8, 16, 19])
+@pytest.mark.parametrize("m", [1, 4, 8, 11, 16, 19])
 def test_fused_small_vs_oracle(q8, f, k, m):
     lib, torch, dev = q8
     wb, _, _ = wl.q8_weight(3000 + f + k, 2 * f, k)
@@ -167,7 +167,7 @@ def test_batch_invariance_and_determinism(q8, n, k):
     y40 = lib.q8_linear(wd, n, k, xd).cpu().numpy()
     y40b = lib.q8_linear(wd, n, k, xd).cpu().numpy()
     assert np.array_equal(y40, y40b)  # run to run
-    for m in (2, 5, 8, 16):
+    for m in (2, 5, 8, 10, 13, 16):
         ym = lib.q8_linear(wd, n, k, xd[:m].contiguous()).cpu().numpy()
         assert np.array_equal(ym, y40[:m]), m
     for r in (3, 17, 38):
@@ -183,7 +183,7 @@ def test_batch_invariance_and_determinism(q8, n, k):
     # fused: same properties
     f = n // 2
     h40 = lib.q8_linear_fused_gate_up_silu(wd, f, k, xd).cpu().numpy()
-    for m in (2, 9):
+    for m in (2, 9, 12, 15):
         hm = lib.q8_linear_fused_gate_up_silu(wd, f, k, xd[:m].contiguous()).cpu().numpy()
         assert np.array_equal(hm, h40[:m]), m
     h1 = lib.q8_linear_fused_gate_up_silu(wd, f, k, xd[5:6].contiguous()).cpu().numpy()

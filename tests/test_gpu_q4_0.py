@@ -34,7 +34,7 @@ SMALL = [(1, 256), (3, 256), (37, 512), (257, 768), (1000, 1024), (513, 3072), (
 
 
 @pytest.mark.parametrize("n,k", SMALL)
-@pytest.mark.parametrize("m", [1, 2, 3, 8, 9, 17])
+@pytest.mark.parametrize("m", [1, 2, 3, 8, 9, 13, 16, 17])
 def test_q4_0_linear_small_vs_oracle(q8, n, k, m):
     lib, torch, dev = q8
     wb, _, _ = wl.q4_0_weight(1100 + n + k, n, k)
