@@ -143,6 +143,119 @@ def fused_gate_up_silu_q4_0_ref(w_gate_up_q4, f: int, k: int, x) -> np.ndarray:
     return silu_ref(y[:, :f]) * y[:, f:]
 
 
+# ------------------------------------------------------------- Q4_K and Q6_K
+#
+# "14. Model families and example applications" section 14.1 says the ggml quant forms
+# Q4_K, Q5_K and Q6_K run their own packed kernels, and the DGX Spark README (Features)
+# lists Q4_K and Q6_K among the formats its GEMV reads directly; neither page spells the
+# layouts out.  Reading: the GGUF k-quant super-blocks of 256 weights.
+#
+# Q4_K, 144 bytes: binary16 d, binary16 dmin, 12 bytes of packed 6-bit sub-block scales
+# and mins, 128 bytes of 4-bit quants.  Sub-block j (weights 32j .. 32j+31) has scale
+# sc[j] and min m[j]: for j < 4, sc = byte[j] & 63 and m = byte[j+4] & 63; for j >= 4 the
+# low four bits come from byte[j+4] (low nibble for sc, high nibble for m) and the top two
+# bits from bits 6-7 of byte[j-4] (sc) or byte[j] (m).  Weight 64c + i (i < 32) is the low
+# nibble of quant byte 32c + i, weight 64c + 32 + i its high nibble;
+# w = d * sc[j] * q - dmin * m[j].
+#
+# Q6_K, 210 bytes: 128 bytes ql, 64 bytes qh, 16 int8 scales, binary16 d.  Weights run in
+# two halves of 128; in half t, weight 128t + 32k + l (k < 4, l < 32) has the 6-bit quant
+# whose low four bits are the low (k < 2) or high (k >= 2) nibble of ql[64t + l + 32*(k%2)]
+# and whose top two bits are bits 2k, 2k+1 of qh[32t + l]; weight i uses scale i // 16;
+# w = d * scale * (q - 32).
+
+QK_K = 256
+Q4_K_BLOCK_BYTES = 144
+Q6_K_BLOCK_BYTES = 210
+_Q4_K_RECORD = np.dtype([("d", "<f2"), ("dmin", "<f2"), ("scales", "u1", (12,)), ("qs", "u1", (QK_K // 2,))])
+_Q6_K_RECORD = np.dtype([("ql", "u1", (QK_K // 2,)), ("qh", "u1", (QK_K // 4,)), ("scales", "i1", (QK_K // 16,)),
+                         ("d", "<f2")])
+assert _Q4_K_RECORD.itemsize == Q4_K_BLOCK_BYTES and _Q6_K_RECORD.itemsize == Q6_K_BLOCK_BYTES
+
+
+def _k_records(buf, n_rows: int, k: int, record, block_bytes: int):
+    if k % QK_K:
+        raise ValueError(f"K={k} is not a multiple of {QK_K}")
+    raw = np.frombuffer(memoryview(buf).cast("B"), dtype=np.uint8)
+    need = n_rows * (k // QK_K) * block_bytes
+    if raw.size != need:
+        raise ValueError(f"buffer has {raw.size} bytes, expected {need}")
+    return raw.view(record).reshape(n_rows, k // QK_K)
+
+
+def q4_k_scale_min(scales):
+    """The eight 6-bit (scale, min) pairs of Q4_K super-blocks: scales [..., 12] bytes ->
+    (sc [..., 8], m [..., 8]) as integers 0..63."""
+    b = np.asarray(scales, dtype=np.int64)
+    sc = np.empty(b.shape[:-1] + (8,), dtype=np.int64)
+    m = np.empty_like(sc)
+    for j in range(4):
+        sc[..., j] = b[..., j] & 63
+        m[..., j] = b[..., j + 4] & 63
+    for j in range(4, 8):
+        sc[..., j] = (b[..., j + 4] & 0x0F) | ((b[..., j - 4] >> 6) << 4)
+        m[..., j] = (b[..., j + 4] >> 4) | ((b[..., j] >> 6) << 4)
+    return sc, m
+
+
+def dequantize_q4_k(buf, n_rows: int, k: int) -> np.ndarray:
+    """W[n, 256b + i] of a GGUF Q4_K matrix in float64 (exact: each weight is a difference of
+    two products of at most 21 significant bits)."""
+    rec = _k_records(buf, n_rows, k, _Q4_K_RECORD, Q4_K_BLOCK_BYTES)
+    d = rec["d"].astype(np.float64)
+    dmin = rec["dmin"].astype(np.float64)
+    sc, m = q4_k_scale_min(rec["scales"])                       # [n][nb][8]
+    qs = rec["qs"].astype(np.int64).reshape(n_rows, k // QK_K, 4, 32)
+    q = np.empty((n_rows, k // QK_K, 4, 2, 32), dtype=np.int64)  # chunk c, sub-block 2c + s
+    q[:, :, :, 0, :] = qs & 0x0F
+    q[:, :, :, 1, :] = qs >> 4
+    q = q.reshape(n_rows, k // QK_K, 8, 32)                    # sub-block j = 2c + s
+    w = (d[:, :, None, None] * sc[:, :, :, None]) * q - (dmin[:, :, None, None] * m[:, :, :, None])
+    return w.reshape(n_rows, -1)
+
+
+def dequantize_q6_k(buf, n_rows: int, k: int) -> np.ndarray:
+    """W[n, 256b + i] of a GGUF Q6_K matrix in float64 (exact)."""
+    rec = _k_records(buf, n_rows, k, _Q6_K_RECORD, Q6_K_BLOCK_BYTES)
+    nb = k // QK_K
+    d = rec["d"].astype(np.float64)                             # [n][nb]
+    scales = rec["scales"].astype(np.float64)                   # [n][nb][16]
+    ql = rec["ql"].astype(np.int64).reshape(n_rows, nb, 2, 64)  # half t
+    qh = rec["qh"].astype(np.int64).reshape(n_rows, nb, 2, 32)
+    q = np.empty((n_rows, nb, 2, 4, 32), dtype=np.int64)        # half t, k, l
+    for kk in range(4):
+        nib = ql[..., 32 * (kk % 2):32 * (kk % 2) + 32]
+        low = (nib & 0x0F) if kk < 2 else (nib >> 4)
+        high = (qh >> (2 * kk)) & 3
+        q[:, :, :, kk, :] = low | (high << 4)
+    q = q.reshape(n_rows, nb, QK_K)                             # weight 128t + 32k + l
+    s = np.repeat(scales, 16, axis=2)                           # scale of weight i: i // 16
+    w = d[:, :, None] * s * (q - 32)
+    return w.reshape(n_rows, -1)
+
+
+def q4_k_linear_ref(w_q4k, n: int, k: int, x) -> np.ndarray:
+    """y = x . W^T for a GGUF Q4_K weight W [n][k] (float64)."""
+    return np.asarray(x, dtype=np.float64) @ dequantize_q4_k(w_q4k, n, k).T
+
+
+def q6_k_linear_ref(w_q6k, n: int, k: int, x) -> np.ndarray:
+    """y = x . W^T for a GGUF Q6_K weight W [n][k] (float64)."""
+    return np.asarray(x, dtype=np.float64) @ dequantize_q6_k(w_q6k, n, k).T
+
+
+def fused_gate_up_silu_q4_k_ref(w, f: int, k: int, x) -> np.ndarray:
+    """SiLU(x . W_gate^T) * (x . W_up^T) from one Q4_K [2f][k] matrix, gate rows first."""
+    y = q4_k_linear_ref(w, 2 * f, k, x)
+    return silu_ref(y[:, :f]) * y[:, f:]
+
+
+def fused_gate_up_silu_q6_k_ref(w, f: int, k: int, x) -> np.ndarray:
+    """SiLU(x . W_gate^T) * (x . W_up^T) from one Q6_K [2f][k] matrix, gate rows first."""
+    y = q6_k_linear_ref(w, 2 * f, k, x)
+    return silu_ref(y[:, :f]) * y[:, f:]
+
+
 # ------------------------------------------------------------------------- linear
 
 

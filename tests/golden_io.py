@@ -167,3 +167,34 @@ def load_q4_0_cases(path=None):
         elif head == "w":
             cur["w"] = [float(v) for v in rest]
     return cases
+
+
+def _rle(tokens, conv):
+    out = []
+    for t in tokens:
+        if "x" in t:
+            v, n = t.rsplit("x", 1)
+            out.extend([conv(v)] * int(n))
+        else:
+            out.append(conv(t))
+    return out
+
+
+def load_k_quant_cases(path=None):
+    """Cases of tests/golden/k_quants_hand.txt: dicts with name, format ('q4_k' or 'q6_k'),
+    bytes (144 or 210), w (256 floats)."""
+    path = path or os.path.join(GOLDEN, "k_quants_hand.txt")
+    cases, cur = [], None
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        head, *rest = line.split()
+        if head == "case":
+            cur = {"name": rest[0], "format": rest[1]}
+            cases.append(cur)
+        elif head == "bytes":
+            cur["bytes"] = bytes(_rle(rest, lambda v: int(v, 16)))
+        elif head == "w":
+            cur["w"] = _rle(rest, float)
+    return cases

@@ -49,6 +49,23 @@ MUTANTS = {
     "act_amax_signed": ("amax = np.max(np.abs(blocks), axis=2)", "amax = np.max(blocks, axis=2)"),
     "q8act_drops_dx": ("(dw * dx[mi][None, :] * isum)", "(dw * isum)"),
     "act_zero_only_exact_zero": ("nz = amax >= ACT_ZERO_BELOW", "nz = amax > 0"),
+    "q4_k_scale_min_swapped": ("sc[..., j] = b[..., j] & 63\n        m[..., j] = b[..., j + 4] & 63",
+                               "sc[..., j] = b[..., j + 4] & 63\n        m[..., j] = b[..., j] & 63"),
+    "q4_k_top_bits_from_scale_byte": ("m[..., j] = (b[..., j + 4] >> 4) | ((b[..., j] >> 6) << 4)",
+                                      "m[..., j] = (b[..., j + 4] >> 4) | ((b[..., j - 4] >> 6) << 4)"),
+    "q4_k_high_bits_unshifted": ("sc[..., j] = (b[..., j + 4] & 0x0F) | ((b[..., j - 4] >> 6) << 4)",
+                                 "sc[..., j] = (b[..., j + 4] & 0x0F) | (b[..., j - 4] >> 6)"),
+    "q4_k_nibbles_swapped": ("q[:, :, :, 0, :] = qs & 0x0F\n    q[:, :, :, 1, :] = qs >> 4",
+                             "q[:, :, :, 0, :] = qs >> 4\n    q[:, :, :, 1, :] = qs & 0x0F"),
+    "q4_k_min_added": ("* q - (dmin[:, :, None, None]", "* q + (dmin[:, :, None, None]"),
+    "q4_k_d_dmin_swapped": ('_Q4_K_RECORD = np.dtype([("d", "<f2"), ("dmin", "<f2")',
+                            '_Q4_K_RECORD = np.dtype([("dmin", "<f2"), ("d", "<f2")'),
+    "q6_k_qh_shift": ("high = (qh >> (2 * kk)) & 3", "high = (qh >> kk) & 3"),
+    "q6_k_no_offset": ("w = d[:, :, None] * s * (q - 32)", "w = d[:, :, None] * s * q"),
+    "q6_k_scale_per_32": ("s = np.repeat(scales, 16, axis=2)", "s = np.repeat(scales[:, :, :8], 32, axis=2)"),
+    "q6_k_ql_half_offset": ("nib = ql[..., 32 * (kk % 2):32 * (kk % 2) + 32]", "nib = ql[..., 32 * (kk // 2):32 * (kk // 2) + 32]"),
+    "q6_k_nibble_choice": ("low = (nib & 0x0F) if kk < 2 else (nib >> 4)", "low = (nib & 0x0F) if kk % 2 == 0 else (nib >> 4)"),
+    "q6_k_scales_unsigned": ('("scales", "i1", (QK_K // 16,))', '("scales", "u1", (QK_K // 16,))'),
     "q8act_wrong_block": ('isum = np.einsum("nbi,bi->nb", qw, qx[mi])', 'isum = np.einsum("nbi,bi->nb", qw, qx[mi][::-1])'),
 }
 

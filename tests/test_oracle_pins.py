@@ -26,13 +26,14 @@ import scipy.special
 
 import oracle as O
 import workloads as wl
-from golden_io import (half_bits_to_fraction, load_act_quant_cases, load_linear_cases, load_q4_0_cases,
-                       load_swiglu_router_cases)
+from golden_io import (half_bits_to_fraction, load_act_quant_cases, load_k_quant_cases, load_linear_cases,
+                       load_q4_0_cases, load_swiglu_router_cases)
 
 LINEAR_CASES = load_linear_cases()
 FUSED_CASES, ROUTE_CASES = load_swiglu_router_cases()
 ACT_CASES = load_act_quant_cases()
 Q4_CASES = load_q4_0_cases()
+KQ_CASES = load_k_quant_cases()
 
 
 # ------------------------------------------------------------------ checks
@@ -467,13 +468,74 @@ def check_q4_0_properties(o):
     np.testing.assert_allclose(h, scipy.special.expit(yy[:, :f]) * yy[:, :f] * yy[:, f:], rtol=1e-12, atol=1e-15)
 
 
+# ------------------------------------------------------------------- Q4_K, Q6_K
+
+
+def check_k_quant_hand(o):
+    """Hand-derived super-blocks (tests/golden/k_quants_hand.txt): the packing of the 6-bit
+    scales and mins, nibble order, the Q6_K bit-pair and index map, the -32 offset, scale
+    groups; and a linear over the Q4_K blocks and one over the Q6_K blocks against the hand
+    weights."""
+    for fmt, deq, lin in (("q4_k", o.dequantize_q4_k, o.q4_k_linear_ref), ("q6_k", o.dequantize_q6_k,
+                                                                          o.q6_k_linear_ref)):
+        cases = [c for c in KQ_CASES if c["format"] == fmt]
+        for c in cases:
+            w = deq(c["bytes"], 1, 256)
+            assert w[0].tolist() == c["w"], c["name"]
+        raw = b"".join(c["bytes"] for c in cases)
+        x = wl.activations(97, 2, 256)
+        wh = np.array([c["w"] for c in cases])
+        np.testing.assert_allclose(lin(raw, len(cases), 256, x), x.astype(np.float64) @ wh.T, rtol=1e-13)
+
+
+def check_k_quant_properties(o):
+    """Fields drawn by the generator, combined by the format's formula in rationals (one
+    super-block row, brute force), agree with the oracle's parse of the packed bytes;
+    linearity in d (and dmin); zero quants; the fused split."""
+    n, k = 3, 512
+    wb, q, sc, mn, d, dmin = wl.q4_k_weight(98, n, k)
+    x = wl.activations(99, 2, k)
+    y = o.q4_k_linear_ref(wb, n, k, x)
+    row, xr = 1, x[1]
+    exact = Fraction(0)
+    for i in range(k):
+        b, j = i // 256, (i % 256) // 32
+        dd = half_bits_to_fraction(int(d.view(np.uint16)[row, b]))
+        dm = half_bits_to_fraction(int(dmin.view(np.uint16)[row, b]))
+        exact += (dd * int(sc[row, b, j]) * int(q[row, i]) - dm * int(mn[row, b, j])) * Fraction(float(xr[i]))
+    assert abs(y[1, row] - float(exact)) <= 1e-12 * max(1.0, abs(float(exact)))
+    two = lambda a: (a.astype(np.float32) * 2).astype(np.float16)
+    np.testing.assert_allclose(o.q4_k_linear_ref(wl.pack_q4_k(q, sc, mn, two(d), two(dmin)), n, k, x), 2 * y,
+                               rtol=1e-13)
+    z = o.q4_k_linear_ref(wl.pack_q4_k(np.zeros_like(q), sc, mn, d, np.zeros_like(dmin)), n, k, x)
+    assert np.all(z == 0)
+    wb6, q6, s6, d6 = wl.q6_k_weight(100, n, k)
+    y6 = o.q6_k_linear_ref(wb6, n, k, x)
+    exact = Fraction(0)
+    for i in range(k):
+        b = i // 256
+        dd = half_bits_to_fraction(int(d6.view(np.uint16)[row, b]))
+        exact += dd * int(s6[row, b, (i % 256) // 16]) * (int(q6[row, i]) - 32) * Fraction(float(xr[i]))
+    assert abs(y6[1, row] - float(exact)) <= 1e-12 * max(1.0, abs(float(exact)))
+    np.testing.assert_allclose(o.q6_k_linear_ref(wl.pack_q6_k(q6, s6, two(d6)), n, k, x), 2 * y6, rtol=1e-13)
+    assert np.all(o.q6_k_linear_ref(wl.pack_q6_k(np.full_like(q6, 32), s6, d6), n, k, x) == 0)
+    f = 3
+    for lin, fused, gen in ((o.q4_k_linear_ref, o.fused_gate_up_silu_q4_k_ref, wl.q4_k_weight),
+                            (o.q6_k_linear_ref, o.fused_gate_up_silu_q6_k_ref, wl.q6_k_weight)):
+        wg = gen(101, 2 * f, k)[0]
+        h = fused(wg, f, k, x)
+        yy = lin(wg, 2 * f, k, x)
+        np.testing.assert_allclose(h, scipy.special.expit(yy[:, :f]) * yy[:, :f] * yy[:, f:], rtol=1e-12,
+                                   atol=1e-15)
+
+
 ALL_CHECKS = [
     check_hand_linear, check_hand_fused, check_hand_route, check_bruteforce_linear,
     check_dequant_exact, check_linearity, check_zero_scale, check_one_hot, check_silu,
     check_fused_split, check_route_invariants, check_moe, check_moe_bruteforce,
     check_act_quant_hand, check_act_quant_props, check_q8act_linear, check_q8act_fused,
     check_top_p_exact_boundaries, check_top_p_hand_and_identity, check_top_p_properties,
-    check_q4_0_hand, check_q4_0_properties,
+    check_q4_0_hand, check_q4_0_properties, check_k_quant_hand, check_k_quant_properties,
 ]
 
 

@@ -58,3 +58,12 @@ def test_workload_sizes():
     assert wl.QWEN3_06B_BLOCK.layer_weight_bytes * 28 == 405_536_768
     assert wl.QWEN3_8B_BLOCK.layer_weight_bytes == 187_170_816
     assert wl.QWEN3_8B_GATE_UP.weight_bytes == 106_954_752
+
+
+def test_k_quant_generators_sizes_and_ranges():
+    wb, q, sc, mn, d, dmin = wl.q4_k_weight(1, 3, 512)
+    assert wb.size == 3 * 2 * 144 and q.max() <= 15 and sc.max() <= 63 and mn.max() <= 63
+    wb6, q6, s6, d6 = wl.q6_k_weight(2, 3, 512)
+    assert wb6.size == 3 * 2 * 210 and q6.max() <= 63 and s6.dtype == np.int8
+    we, _, sce, _, de, dme = wl.q4_k_weight(3, 2, 256, exact=True)
+    assert sce.max() <= 15 and set(np.unique(de.astype(np.float64))) <= {2.0 ** -7, 2.0 ** -8}

@@ -73,6 +73,69 @@ def pack_q4_0(q: np.ndarray, d_f16: np.ndarray) -> np.ndarray:
     return out.reshape(-1)
 
 
+Q4_K_BLOCK_BYTES = 144
+Q6_K_BLOCK_BYTES = 210
+QK_K = 256
+
+
+def pack_q4_k(q, sc, m, d_f16, dmin_f16) -> np.ndarray:
+    """Lay GGUF Q4_K super-blocks out as bytes: nibbles q [N][K] (0..15), 6-bit sub-block
+    scales sc and mins m [N][K/256][8] (0..63), binary16 d and dmin [N][K/256].
+
+    Per 144-byte super-block: d, dmin, then 12 bytes -- bytes 0..3 hold sc[0..3] in bits
+    0-5 and the top two bits of sc[4..7] in bits 6-7, bytes 4..7 the same for m, bytes
+    8..11 the low four bits of sc[4..7] (low nibble) and m[4..7] (high nibble) -- then 128
+    bytes: byte 32c + i = q[64c + i] | q[64c + 32 + i] << 4.
+    """
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    n, k = q.shape
+    nb = k // QK_K
+    sc = np.asarray(sc, dtype=np.uint8).reshape(n, nb, 8)
+    m = np.asarray(m, dtype=np.uint8).reshape(n, nb, 8)
+    if k % QK_K or q.max(initial=0) > 15 or sc.max(initial=0) > 63 or m.max(initial=0) > 63:
+        raise ValueError("bad Q4_K fields")
+    out = np.zeros((n, nb, Q4_K_BLOCK_BYTES), dtype=np.uint8)
+    out[:, :, 0:2] = np.asarray(d_f16, dtype="<f2").reshape(n, nb).view(np.uint8).reshape(n, nb, 2)
+    out[:, :, 2:4] = np.asarray(dmin_f16, dtype="<f2").reshape(n, nb).view(np.uint8).reshape(n, nb, 2)
+    for j in range(4):
+        out[:, :, 4 + j] = (sc[:, :, j] & 63) | ((sc[:, :, j + 4] >> 4) << 6)
+        out[:, :, 8 + j] = (m[:, :, j] & 63) | ((m[:, :, j + 4] >> 4) << 6)
+        out[:, :, 12 + j] = (sc[:, :, j + 4] & 15) | ((m[:, :, j + 4] & 15) << 4)
+    qb = q.reshape(n, nb, 4, 2, 32)
+    out[:, :, 16:] = (qb[:, :, :, 0, :] | (qb[:, :, :, 1, :] << 4)).reshape(n, nb, 128)
+    return out.reshape(-1)
+
+
+def pack_q6_k(q, scales, d_f16) -> np.ndarray:
+    """Lay GGUF Q6_K super-blocks out as bytes: 6-bit quants q [N][K] (0..63), int8 scales
+    [N][K/256][16], binary16 d [N][K/256].
+
+    Per 210-byte super-block: 128 bytes ql, 64 bytes qh, 16 scales, d.  Weight
+    128t + 32k + l (t < 2, k < 4, l < 32) keeps its low four bits in the low (k < 2) or
+    high (k >= 2) nibble of ql[64t + l + 32*(k%2)] and its top two bits in bits 2k, 2k+1 of
+    qh[32t + l].
+    """
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    n, k = q.shape
+    nb = k // QK_K
+    if k % QK_K or q.max(initial=0) > 63:
+        raise ValueError("bad Q6_K fields")
+    qb = q.reshape(n, nb, 2, 4, 32)                          # t, k, l
+    ql = np.zeros((n, nb, 2, 64), dtype=np.uint8)
+    qh = np.zeros((n, nb, 2, 32), dtype=np.uint8)
+    for kk in range(4):
+        low = qb[:, :, :, kk, :] & 15
+        seg = slice(32 * (kk % 2), 32 * (kk % 2) + 32)
+        ql[..., seg] |= low if kk < 2 else (low << 4)
+        qh |= (qb[:, :, :, kk, :] >> 4) << (2 * kk)
+    out = np.zeros((n, nb, Q6_K_BLOCK_BYTES), dtype=np.uint8)
+    out[:, :, 0:128] = ql.reshape(n, nb, 128)
+    out[:, :, 128:192] = qh.reshape(n, nb, 64)
+    out[:, :, 192:208] = np.asarray(scales, dtype=np.int8).reshape(n, nb, 16).view(np.uint8)
+    out[:, :, 208:210] = np.asarray(d_f16, dtype="<f2").reshape(n, nb).view(np.uint8).reshape(n, nb, 2)
+    return out.reshape(-1)
+
+
 # ------------------------------------------------------------------ generators
 
 
@@ -114,6 +177,42 @@ def q4_0_weight_exact(seed: int, n: int, k: int):
     q = rq.integers(0, 16, size=(n, k), dtype=np.uint8)
     d = np.where(rd.integers(0, 2, size=(n, k // QK)) == 0, 2.0 ** -7, 2.0 ** -8).astype(np.float16)
     return pack_q4_0(q, d), q, d
+
+
+def q4_k_weight(seed: int, n: int, k: int, exact: bool = False):
+    """Random GGUF Q4_K matrix [n][k]: returns (bytes, q, sc, m, d, dmin).  Nibbles
+    uniform 0..15, scales and mins uniform 0..63, d and dmin uniform in [2e-5, 2e-4]
+    (binary16, some subnormal).  exact: d, dmin in {2^-7, 2^-8} and scales, mins 0..15, so
+    with small-integer activations every float32 partial sum is exact."""
+    rq, rs, rm, rd, re = _rngs(seed, 5)
+    nb = k // QK_K
+    q = rq.integers(0, 16, size=(n, k), dtype=np.uint8)
+    top = 16 if exact else 64
+    sc = rs.integers(0, top, size=(n, nb, 8), dtype=np.uint8)
+    mn = rm.integers(0, top, size=(n, nb, 8), dtype=np.uint8)
+    if exact:
+        d = np.where(rd.integers(0, 2, size=(n, nb)) == 0, 2.0 ** -7, 2.0 ** -8).astype(np.float16)
+        dmin = np.where(re.integers(0, 2, size=(n, nb)) == 0, 2.0 ** -7, 2.0 ** -8).astype(np.float16)
+    else:
+        d = rd.uniform(2e-5, 2e-4, size=(n, nb)).astype(np.float16)
+        dmin = re.uniform(2e-5, 2e-4, size=(n, nb)).astype(np.float16)
+    return pack_q4_k(q, sc, mn, d, dmin), q, sc, mn, d, dmin
+
+
+def q6_k_weight(seed: int, n: int, k: int, exact: bool = False):
+    """Random GGUF Q6_K matrix [n][k]: returns (bytes, q, scales, d).  Quants uniform
+    0..63, scales uniform in [-128, 127], d uniform in [2e-5, 2e-4] (binary16).  exact: d
+    in {2^-7, 2^-8}, scales in [-15, 15]."""
+    rq, rs, rd = _rngs(seed, 3)
+    nb = k // QK_K
+    q = rq.integers(0, 64, size=(n, k), dtype=np.uint8)
+    if exact:
+        scales = rs.integers(-15, 16, size=(n, nb, 16)).astype(np.int8)
+        d = np.where(rd.integers(0, 2, size=(n, nb)) == 0, 2.0 ** -7, 2.0 ** -8).astype(np.float16)
+    else:
+        scales = rs.integers(-128, 128, size=(n, nb, 16)).astype(np.int8)
+        d = rd.uniform(2e-5, 2e-4, size=(n, nb)).astype(np.float16)
+    return pack_q6_k(q, scales, d), q, scales, d
 
 
 def activations(seed: int, m: int, k: int) -> np.ndarray:
