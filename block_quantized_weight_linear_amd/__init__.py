@@ -13,6 +13,10 @@ from ._binding import (  # noqa: F401
     moe_route_topk,
     q4_0_linear,
     q4_0_linear_fused_gate_up_silu,
+    q4_k_linear,
+    q4_k_linear_fused_gate_up_silu,
+    q6_k_linear,
+    q6_k_linear_fused_gate_up_silu,
     moe_route_workspace_bytes,
     q8_linear,
     q8_linear_fused_gate_up_silu,

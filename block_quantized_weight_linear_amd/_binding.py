@@ -43,6 +43,9 @@ lib.q4_0_linear.restype = ctypes.c_int
 lib.q4_0_linear.argtypes = [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp]
 lib.q4_0_linear_fused_gate_up_silu.restype = ctypes.c_int
 lib.q4_0_linear_fused_gate_up_silu.argtypes = [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp]
+for _name in ("q4_k_linear", "q4_k_linear_fused_gate_up_silu", "q6_k_linear", "q6_k_linear_fused_gate_up_silu"):
+    getattr(lib, _name).restype = ctypes.c_int
+    getattr(lib, _name).argtypes = [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp]
 lib.q8_quantize_act.restype = ctypes.c_int
 lib.q8_quantize_act.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp]
 lib.q8_linear_q8act.restype = ctypes.c_int
@@ -144,10 +147,14 @@ def _bytes(w, need, name, device):
     return w
 
 
-def _quant_bytes(rows, k, block_bytes):
+# bytes per 256 weights of each packed format
+Q8_0_BYTES, Q4_0_BYTES, Q4_K_BYTES, Q6_K_BYTES = 272, 144, 144, 210
+
+
+def _quant_bytes(rows, k, bytes_256):
     if k <= 0 or k % 256 or rows < 0:
         return 0  # the library reports the shape error
-    return rows * (k // 32) * block_bytes
+    return rows * (k // 256) * bytes_256
 
 
 def _call(device, fn, *args):
@@ -156,12 +163,12 @@ def _call(device, fn, *args):
         check(fn(*args))
 
 
-def _dense(fn, w, n_w, n_out, k, x, out, block_bytes):
+def _dense(fn, w, n_w, n_out, k, x, out, bytes_256):
     """Shared marshalling of the dense linears: weight rows n_w, outputs n_out."""
     _dev(x, torch.float32, "x")
     dev = x.device
     m = _rows_in(x, k, "x")
-    _bytes(w, _quant_bytes(n_w, k, block_bytes) if n_out and m else 0, "w", dev)
+    _bytes(w, _quant_bytes(n_w, k, bytes_256) if n_out and m else 0, "w", dev)
     if out is None:
         out = torch.empty((m, n_out), dtype=torch.float32, device=dev)
     _rows_out(out, m, n_out, "out", torch.float32, dev)
@@ -172,22 +179,42 @@ def _dense(fn, w, n_w, n_out, k, x, out, block_bytes):
 
 def q8_linear(w, n: int, k: int, x, out=None):
     """y = x . W^T for a Q8_0 weight W [n][k] (uint8 bytes) and float32 x [m][k]."""
-    return _dense(lib.q8_linear, w, n, n, k, x, out, 34)
+    return _dense(lib.q8_linear, w, n, n, k, x, out, Q8_0_BYTES)
 
 
 def q8_linear_fused_gate_up_silu(w, f: int, k: int, x, out=None):
     """h = SiLU(x . W_gate^T) * (x . W_up^T); W is Q8_0 [2f][k], gate rows first."""
-    return _dense(lib.q8_linear_fused_gate_up_silu, w, 2 * f, f, k, x, out, 34)
+    return _dense(lib.q8_linear_fused_gate_up_silu, w, 2 * f, f, k, x, out, Q8_0_BYTES)
 
 
 def q4_0_linear(w, n: int, k: int, x, out=None):
     """y = x . W^T for a GGUF Q4_0 weight W [n][k] (uint8 bytes) and float32 x [m][k]."""
-    return _dense(lib.q4_0_linear, w, n, n, k, x, out, 18)
+    return _dense(lib.q4_0_linear, w, n, n, k, x, out, Q4_0_BYTES)
 
 
 def q4_0_linear_fused_gate_up_silu(w, f: int, k: int, x, out=None):
     """h = SiLU(x . W_gate^T) * (x . W_up^T); W is GGUF Q4_0 [2f][k], gate rows first."""
-    return _dense(lib.q4_0_linear_fused_gate_up_silu, w, 2 * f, f, k, x, out, 18)
+    return _dense(lib.q4_0_linear_fused_gate_up_silu, w, 2 * f, f, k, x, out, Q4_0_BYTES)
+
+
+def q4_k_linear(w, n: int, k: int, x, out=None):
+    """y = x . W^T for a GGUF Q4_K weight W [n][k] (uint8 bytes) and float32 x [m][k]."""
+    return _dense(lib.q4_k_linear, w, n, n, k, x, out, Q4_K_BYTES)
+
+
+def q4_k_linear_fused_gate_up_silu(w, f: int, k: int, x, out=None):
+    """h = SiLU(x . W_gate^T) * (x . W_up^T); W is GGUF Q4_K [2f][k], gate rows first."""
+    return _dense(lib.q4_k_linear_fused_gate_up_silu, w, 2 * f, f, k, x, out, Q4_K_BYTES)
+
+
+def q6_k_linear(w, n: int, k: int, x, out=None):
+    """y = x . W^T for a GGUF Q6_K weight W [n][k] (uint8 bytes) and float32 x [m][k]."""
+    return _dense(lib.q6_k_linear, w, n, n, k, x, out, Q6_K_BYTES)
+
+
+def q6_k_linear_fused_gate_up_silu(w, f: int, k: int, x, out=None):
+    """h = SiLU(x . W_gate^T) * (x . W_up^T); W is GGUF Q6_K [2f][k], gate rows first."""
+    return _dense(lib.q6_k_linear_fused_gate_up_silu, w, 2 * f, f, k, x, out, Q6_K_BYTES)
 
 
 def q8_quantize_act(x, xq=None, xd=None):
@@ -222,7 +249,7 @@ def _codes(xq, xd, k):
 def _dense_codes(fn, w, n_w, n_out, k, xq, xd, out):
     m = _codes(xq, xd, k)
     dev = xq.device
-    _bytes(w, _quant_bytes(n_w, k, 34) if n_out and m else 0, "w", dev)
+    _bytes(w, _quant_bytes(n_w, k, Q8_0_BYTES) if n_out and m else 0, "w", dev)
     if out is None:
         out = torch.empty((m, n_out), dtype=torch.float32, device=dev)
     _rows_out(out, m, n_out, "out", torch.float32, dev)
@@ -297,8 +324,8 @@ def _moe_args(w_gate_up_exps, w_down_exps, n_exp, f, h, x, topk_idx, topk_w, out
         raise ValueError("topk_idx must be a contiguous [m][k] tensor")
     k = topk_idx.shape[1]
     _contig_out(topk_w, (m, k), "topk_w", torch.float32, dev)
-    _bytes(w_gate_up_exps, _quant_bytes(n_exp * 2 * f, h, 34) if m else 0, "w_gate_up_exps", dev)
-    _bytes(w_down_exps, _quant_bytes(n_exp * h, f, 34) if m else 0, "w_down_exps", dev)
+    _bytes(w_gate_up_exps, _quant_bytes(n_exp * 2 * f, h, Q8_0_BYTES) if m else 0, "w_gate_up_exps", dev)
+    _bytes(w_down_exps, _quant_bytes(n_exp * h, f, Q8_0_BYTES) if m else 0, "w_down_exps", dev)
     if out is None:
         out = torch.empty((m, h), dtype=torch.float32, device=dev)
     _rows_out(out, m, h, "out", torch.float32, dev)

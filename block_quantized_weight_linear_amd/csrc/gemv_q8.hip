@@ -45,10 +45,14 @@ struct XArr {
 // kernel) adds one pair of R rows against the lane's 64 activations x (float4 c holds inputs
 // 4c .. 4c+3 of the pair) and their per-block sums sx.
 struct FmtQ8_0 {  // 68 bytes: [d0 | 32 q] [d1 | 32 q]
-    static constexpr int kPairBytes = 68, kDwords = 17, kLoads = 5;
+    static constexpr int kPairBytes = 68, kDwords = 17, kLoads = 5, kMaxR = 4;
+    static __host__ __device__ size_t row_bytes(int P) { return (size_t)P * kPairBytes; }
     static __device__ __forceinline__ void load(const uint8_t* p, uint32_t (&w)[kDwords]) { load_pair(p, w); }
+    static __device__ __forceinline__ void load(const uint8_t* row, int pc, uint32_t (&w)[kDwords]) {
+        load_pair(row + (size_t)kPairBytes * pc, w);
+    }
     template <int HALF>
-    static __device__ __forceinline__ void weights(const uint32_t (&w)[kDwords], int cc, float (&wf)[4]) {
+    static __device__ __forceinline__ void weights(const uint32_t (&w)[kDwords], int cc, float (&wf)[4], int = 0) {
         if constexpr (HALF == 0) {  // block 0: scale in dword 0 (low half), quants at bytes 2..33
             const float d = half_lo(w[0]);
             wf[0] = sbyte<2>(w[cc]) * d;
@@ -74,7 +78,11 @@ struct FmtQ8_0 {  // 68 bytes: [d0 | 32 q] [d1 | 32 q]
 // the low nibble of its byte j, weight j + 16 the high nibble; w = d * (nibble - 8), exact
 // in float32 (a 4-bit integer times an 11-bit scale).
 struct FmtQ4_0 {
-    static constexpr int kPairBytes = 36, kDwords = 9, kLoads = 3;
+    static constexpr int kPairBytes = 36, kDwords = 9, kLoads = 3, kMaxR = 4;
+    static __host__ __device__ size_t row_bytes(int P) { return (size_t)P * kPairBytes; }
+    static __device__ __forceinline__ void load(const uint8_t* row, int pc, uint32_t (&w)[kDwords]) {
+        load(row + (size_t)kPairBytes * pc, w);
+    }
     static __device__ __forceinline__ void load(const uint8_t* p, uint32_t (&w)[kDwords]) {
         const u32x4_a4 a = *reinterpret_cast<const u32x4_a4*>(p);
         const u32x4_a4 b = *reinterpret_cast<const u32x4_a4*>(p + 16);
@@ -83,7 +91,7 @@ struct FmtQ4_0 {
         w[8] = *reinterpret_cast<const uint32_t*>(p + 32);
     }
     template <int HALF>
-    static __device__ __forceinline__ void weights(const uint32_t (&w)[kDwords], int cc, float (&wf)[4]) {
+    static __device__ __forceinline__ void weights(const uint32_t (&w)[kDwords], int cc, float (&wf)[4], int = 0) {
         const int c4 = cc & 3;  // quant dword of the block: bytes 4*c4 .. 4*c4+3
         float d;
         uint32_t v;
@@ -132,6 +140,102 @@ struct FmtQ4_0 {
                 acc[r][0] = __builtin_fmaf(d, t - 8.0f * sx[half], acc[r][0]);
             }
         }
+    }
+};
+
+// GGUF Q4_K: 144-byte super-blocks of 256 weights (four pairs each): d and dmin
+// (binary16), 12 bytes of packed 6-bit sub-block scales and mins, 128 bytes of nibbles.
+// Pair c of a super-block (inputs 64c .. 64c+63) is sub-block 2c (the low nibbles of quant
+// bytes 32c .. 32c+31) then sub-block 2c+1 (their high nibbles); w = d*sc*q - dmin*m,
+// computed as fma(q, d*sc, -dmin*m) (the two products are exact in float32).
+struct FmtQ4_K {
+    // w[0]: d | dmin, w[1..3]: the scale bytes, w[4..11]: the pair's 32 quant bytes
+    static constexpr int kDwords = 12, kLoads = 3, kMaxR = 2;
+    static __host__ __device__ size_t row_bytes(int P) { return (size_t)(P / 4) * 144; }
+    static __device__ __forceinline__ void load(const uint8_t* row, int pc, uint32_t (&w)[kDwords]) {
+        const uint8_t* sb = row + (size_t)(pc >> 2) * 144;
+        const u32x4_a4 h = *reinterpret_cast<const u32x4_a4*>(sb);
+        const u32x4_a4 a = *reinterpret_cast<const u32x4_a4*>(sb + 16 + 32 * (pc & 3));
+        const u32x4_a4 b = *reinterpret_cast<const u32x4_a4*>(sb + 32 + 32 * (pc & 3));
+        w[0] = h.x; w[1] = h.y; w[2] = h.z; w[3] = h.w;
+        w[4] = a.x; w[5] = a.y; w[6] = a.z; w[7] = a.w;
+        w[8] = b.x; w[9] = b.y; w[10] = b.z; w[11] = b.w;
+    }
+    template <int HALF>
+    static __device__ __forceinline__ void weights(const uint32_t (&w)[kDwords], int cc, float (&wf)[4], int pc) {
+        // sub-block j = 2c + HALF; its scale-byte position within dwords 1, 2, 3 is j % 4
+        const int c = pc & 3;
+        const uint32_t sh = 8u * (uint32_t)(2 * (c & 1) + HALF);
+        const uint32_t b1 = (w[1] >> sh) & 0xFFu, b2 = (w[2] >> sh) & 0xFFu, b3 = (w[3] >> sh) & 0xFFu;
+        // sub-blocks 0..3: the low six bits of bytes j and j + 4; sub-blocks 4..7: a nibble
+        // of byte j + 4 below the top two bits of byte j - 4 (scale) or j (min).  Lanes of
+        // a wave hold different pairs, so the choice is a bit select, not a branch.
+        const uint32_t hi = 0u - (uint32_t)(c >> 1);  // all ones for sub-blocks 4..7
+        const uint32_t sc = ((b1 & 63u) & ~hi) | (((b3 & 15u) | ((b1 >> 2) & 0x30u)) & hi);
+        const uint32_t mn = ((b2 & 63u) & ~hi) | (((b3 >> 4) | ((b2 >> 2) & 0x30u)) & hi);
+        const float ds = half_lo(w[0]) * (float)sc, dm = half_hi(w[0]) * (float)mn;
+        const uint32_t v = (w[4 + cc] >> (4 * HALF)) & 0x0F0F0F0Fu;  // inputs 4cc .. 4cc+3 of the half
+        wf[0] = __builtin_fmaf((float)(v & 0xFFu), ds, -dm);
+        wf[1] = __builtin_fmaf((float)((v >> 8) & 0xFFu), ds, -dm);
+        wf[2] = __builtin_fmaf((float)((v >> 16) & 0xFFu), ds, -dm);
+        wf[3] = __builtin_fmaf((float)(v >> 24), ds, -dm);
+    }
+};
+
+// GGUF Q6_K: 210-byte super-blocks of 256 weights (four pairs each): ql[128], qh[64],
+// int8 scales[16], d (binary16).  Pair c of a super-block lies in half t = c/2; its block
+// HALF holds the weights 128t + 32k + l (l < 32) with k = 2(c%2) + HALF: their low four
+// bits are the low (c%2 == 0) or high nibble of ql[64t + 32 HALF + l], their top two bits
+// bits 2k, 2k+1 of qh[32t + l], their scale scales[8t + 2k + l/16];
+// w = fma(q, d*scale, -32 d*scale), exact in float32 (at most 23 significant bits).
+// Super-blocks start on 2-byte boundaries: the loads read whole dwords from the dword
+// boundary at or below each field (never past the super-block: d is a 16-bit load) and
+// the weights realign them with v_alignbyte by 0 or 2 bytes.
+struct FmtQ6_K {
+    // w[0..16]: ql of half t, w[17..25]: qh of half t, w[26..27]: the pair's four scale
+    // bytes, w[28]: d, w[29]: the realignment (0 or 2 bytes)
+    static constexpr int kDwords = 30, kLoads = 11, kMaxR = 2;
+    static __host__ __device__ size_t row_bytes(int P) { return (size_t)(P / 4) * 210; }
+    static __device__ __forceinline__ void load(const uint8_t* row, int pc, uint32_t (&w)[kDwords]) {
+        const uint8_t* sb = row + (size_t)(pc >> 2) * 210;
+        const uint32_t shift = (uint32_t)(uintptr_t)sb & 3u;  // 0 or 2
+        const int t = (pc >> 1) & 1;
+        const uint8_t* ql = sb + 64 * t - shift;
+        const uint8_t* qh = sb + 128 + 32 * t - shift;
+        const uint8_t* scl = sb + 192 + 8 * t + 4 * (pc & 1) - shift;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const u32x4_a4 v = *reinterpret_cast<const u32x4_a4*>(ql + 16 * i);
+            w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+        }
+        w[16] = *reinterpret_cast<const uint32_t*>(ql + 64);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const u32x4_a4 v = *reinterpret_cast<const u32x4_a4*>(qh + 16 * i);
+            w[17 + 4 * i] = v.x; w[18 + 4 * i] = v.y; w[19 + 4 * i] = v.z; w[20 + 4 * i] = v.w;
+        }
+        w[25] = *reinterpret_cast<const uint32_t*>(qh + 32);
+        w[26] = *reinterpret_cast<const uint32_t*>(scl);
+        w[27] = *reinterpret_cast<const uint32_t*>(scl + (shift ? 4 : 0));  // only read when realigning
+        w[28] = *reinterpret_cast<const uint16_t*>(sb + 208);
+        w[29] = shift;
+    }
+    template <int HALF>
+    static __device__ __forceinline__ void weights(const uint32_t (&w)[kDwords], int cc, float (&wf)[4], int pc) {
+        const uint32_t shift = w[29];
+        const int hi_nib = pc & 1;             // c % 2
+        const int k = 2 * hi_nib + HALF;
+        const uint32_t qlw = __builtin_amdgcn_alignbyte(w[8 * HALF + cc + 1], w[8 * HALF + cc], shift);
+        const uint32_t qhw = __builtin_amdgcn_alignbyte(w[17 + cc + 1], w[17 + cc], shift);
+        const uint32_t scw = __builtin_amdgcn_alignbyte(w[27], w[26], shift);
+        const uint32_t q6 = ((qlw >> (4 * hi_nib)) & 0x0F0F0F0Fu) | (((qhw >> (2 * k)) & 0x03030303u) << 4);
+        const float sc = (float)(int)(int8_t)(scw >> (8 * (2 * HALF + (cc >> 2))));
+        const float ds = half_lo(w[28]) * sc;
+        const float m32 = -32.0f * ds;
+        wf[0] = __builtin_fmaf((float)(q6 & 0xFFu), ds, m32);
+        wf[1] = __builtin_fmaf((float)((q6 >> 8) & 0xFFu), ds, m32);
+        wf[2] = __builtin_fmaf((float)((q6 >> 16) & 0xFFu), ds, m32);
+        wf[3] = __builtin_fmaf((float)(q6 >> 24), ds, m32);
     }
 };
 
@@ -371,7 +475,7 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(1,
     const int lane = tid & 63;
     const int j = lane & 15;
     const int slot = (wv & 1) * 4 + (lane >> 4);  // row slot within the group, 0..7
-    const size_t row_bytes = (size_t)P * Fmt::kPairBytes;
+    const size_t row_bytes = Fmt::row_bytes(P);
     const int nch = (P + 15) >> 4;
     const int steps = (nch + 1) >> 1;
     const int tiles = (n_out + 8 * R - 1) / (8 * R);
@@ -398,8 +502,8 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(1,
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int n = out_row(i, r);
-            Fmt::load(w + (size_t)n * row_bytes + Fmt::kPairBytes * (size_t)pc, wr[r]);
-            if constexpr (SILU) Fmt::load(w + (size_t)(n + n_out) * row_bytes + Fmt::kPairBytes * (size_t)pc, wr[R + r]);
+            Fmt::load(w + (size_t)n * row_bytes, pc, wr[r]);
+            if constexpr (SILU) Fmt::load(w + (size_t)(n + n_out) * row_bytes, pc, wr[R + r]);
         }
     };
     // Half `half` of the group's activation chunk for step st: 2*M wave-wide copies of 64
@@ -437,7 +541,7 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(1,
             for (int cc = 0; cc < 8; ++cc) {
                 float wf[RR][4];
 #pragma unroll
-                for (int r = 0; r < RR; ++r) Fmt::template weights<HALF>(wc[r], cc, wf[r]);
+                for (int r = 0; r < RR; ++r) Fmt::template weights<HALF>(wc[r], cc, wf[r], 16 * ch + j);
 #pragma unroll
                 for (int m = 0; m < M; ++m) {
                     const float4 xv = xs[(m * 8 + cc) * 16 + j];
@@ -659,18 +763,24 @@ hipError_t launch_rows(const DeviceInfo& dev, const uint8_t* w, int n_out, int P
     // kernel as much as the fmas: measured on the Qwen3-8B and Gemma 4 12B shapes (fused
     // gate_up 24576x4096, M = 8: 52.2 -> 47.3 us; down 4096x12288, M = 8: 32.9 -> 30.6 us;
     // plain rows with fewer activation rows, and Q4_0 down, stay faster with R = 1).
+    // A format's kMaxR bounds the weight rows a lane holds (fused: 2R), so that its
+    // register ring fits two waves per SIMD.
+    constexpr int kRows = SILU ? 2 : 1;
+    constexpr bool kTwo = 2 * kRows <= Fmt::kMaxR, kFour = !SILU && 4 <= Fmt::kMaxR;
     const int64_t cus = dev.cu_count;
     const double f1 = round_fill((n_out + 7) / 8, cus * rows_per_cu<Fmt, M, 1, SILU>());
-    const double f2 = round_fill((n_out + 15) / 16, cus * rows_per_cu<Fmt, M, 2, SILU>());
-    double f4 = 0.0;
-    if constexpr (!SILU) f4 = round_fill((n_out + 31) / 32, cus * rows_per_cu<Fmt, M, 4, SILU>());
+    double f2 = 0.0, f4 = 0.0;
+    if constexpr (kTwo) f2 = round_fill((n_out + 15) / 16, cus * rows_per_cu<Fmt, M, 2, SILU>());
+    if constexpr (kFour) f4 = round_fill((n_out + 31) / 32, cus * rows_per_cu<Fmt, M, 4, SILU>());
     const double best = f1 > f2 ? (f1 > f4 ? f1 : f4) : (f2 > f4 ? f2 : f4);
-    if constexpr (!SILU) {
+    if constexpr (kFour) {
         if (f4 >= 0.95 * best) return launch_rows_r<Fmt, M, 4, SILU>(dev, n_out, P, w, x, ldx, y, ldy, stream);
     }
-    constexpr bool kPreferTwo = SILU || (std::is_same<Fmt, FmtQ8_0>::value && M >= 8);
-    if (f2 >= (kPreferTwo ? 0.5 : 0.95) * best)
-        return launch_rows_r<Fmt, M, 2, SILU>(dev, n_out, P, w, x, ldx, y, ldy, stream);
+    if constexpr (kTwo) {
+        constexpr bool kPreferTwo = SILU || (std::is_same<Fmt, FmtQ8_0>::value && M >= 8);
+        if (f2 >= (kPreferTwo ? 0.5 : 0.95) * best)
+            return launch_rows_r<Fmt, M, 2, SILU>(dev, n_out, P, w, x, ldx, y, ldy, stream);
+    }
     return launch_rows_r<Fmt, M, 1, SILU>(dev, n_out, P, w, x, ldx, y, ldy, stream);
 }
 
@@ -729,6 +839,45 @@ hipError_t launch_gemv_q4_0(const DeviceInfo& dev, const uint8_t* w, int64_t n_o
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+template <class Fmt, bool SILU>
+hipError_t launch_kq_m(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, const float* x, int ldx, int m,
+                       float* y, int ldy, hipStream_t stream) {
+    switch (m) {
+#define KQ_CASE(MM) \
+    case MM: return launch_rows<Fmt, MM, SILU>(dev, w, n_out, P, x, ldx, y, ldy, stream);
+        KQ_CASE(1) KQ_CASE(2) KQ_CASE(3) KQ_CASE(4) KQ_CASE(5) KQ_CASE(6) KQ_CASE(7) KQ_CASE(8)
+#undef KQ_CASE
+        default: return hipErrorInvalidValue;
+    }
+}
+
+// GGUF k-quant weights (Q4_K, Q6_K): every row count on the float32 rows kernel in
+// 8-row launches.
+template <class Fmt>
+hipError_t launch_gemv_kq(const DeviceInfo& dev, const uint8_t* w, int64_t n_out, int64_t k, bool silu_pairs,
+                          const float* x, int64_t m, int64_t ldx, float* y, int64_t ldy, hipStream_t stream) {
+    const int P = (int)(k / 64);
+    for (int64_t m0 = 0; m0 < m; m0 += 8) {
+        const int mm = (int)((m - m0) < 8 ? (m - m0) : 8);
+        const float* xc = x + m0 * ldx;
+        float* yc = y + m0 * ldy;
+        hipError_t e = silu_pairs ? launch_kq_m<Fmt, true>(dev, w, (int)n_out, P, xc, (int)ldx, mm, yc, (int)ldy, stream)
+                                  : launch_kq_m<Fmt, false>(dev, w, (int)n_out, P, xc, (int)ldx, mm, yc, (int)ldy, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_gemv_q4_k(const DeviceInfo& dev, const uint8_t* w, int64_t n_out, int64_t k, bool silu_pairs,
+                            const float* x, int64_t m, int64_t ldx, float* y, int64_t ldy, hipStream_t stream) {
+    return launch_gemv_kq<FmtQ4_K>(dev, w, n_out, k, silu_pairs, x, m, ldx, y, ldy, stream);
+}
+
+hipError_t launch_gemv_q6_k(const DeviceInfo& dev, const uint8_t* w, int64_t n_out, int64_t k, bool silu_pairs,
+                            const float* x, int64_t m, int64_t ldx, float* y, int64_t ldy, hipStream_t stream) {
+    return launch_gemv_kq<FmtQ6_K>(dev, w, n_out, k, silu_pairs, x, m, ldx, y, ldy, stream);
 }
 
 hipError_t launch_gemv_q8(const DeviceInfo& dev, const uint8_t* w, int64_t n_out, int64_t k, bool silu_pairs,

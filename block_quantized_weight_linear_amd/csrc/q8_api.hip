@@ -167,6 +167,49 @@ q8_status q4_0_linear_fused_gate_up_silu(const void* w_gate_up_q4_0, int64_t f, 
     return q4_0_common("q4_0_linear_fused_gate_up_silu", w_gate_up_q4_0, f, k, true, x, m, ldx, h, ldh, stream);
 }
 
+using kq_launcher = hipError_t (*)(const q8k::DeviceInfo&, const uint8_t*, int64_t, int64_t, bool, const float*, int64_t,
+                                   int64_t, float*, int64_t, hipStream_t);
+
+static q8_status kq_common(const char* name, kq_launcher launch, const void* w, int64_t n_out, int64_t k, bool silu,
+                           const float* x, int64_t m, int64_t ldx, float* y, int64_t ldy, void* stream) {
+    g_err[0] = 0;
+    char msg[256];
+    q8_status s = q8v::check_linear(w, n_out, k, x, m, ldx, y, ldy, msg, sizeof msg);
+    if (s != Q8_OK) {
+        set_err("%s: %s", name, msg);
+        return s;
+    }
+    if (m == 0 || n_out == 0) return Q8_OK;
+    q8k::DeviceInfo dev;
+    hipError_t e = q8k::current_device_info(&dev);
+    if (e != hipSuccess) return device_fail(name, e);
+    e = launch(dev, static_cast<const uint8_t*>(w), n_out, k, silu, x, m, ldx, y, ldy, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_fail(name, e);
+    return Q8_OK;
+}
+
+q8_status q4_k_linear(const void* w_q4_k, int64_t n, int64_t k, const float* x, int64_t m, int64_t ldx, float* y,
+                      int64_t ldy, void* stream) {
+    return kq_common("q4_k_linear", q8k::launch_gemv_q4_k, w_q4_k, n, k, false, x, m, ldx, y, ldy, stream);
+}
+
+q8_status q4_k_linear_fused_gate_up_silu(const void* w_gate_up_q4_k, int64_t f, int64_t k, const float* x, int64_t m,
+                                         int64_t ldx, float* h, int64_t ldh, void* stream) {
+    return kq_common("q4_k_linear_fused_gate_up_silu", q8k::launch_gemv_q4_k, w_gate_up_q4_k, f, k, true, x, m, ldx, h,
+                     ldh, stream);
+}
+
+q8_status q6_k_linear(const void* w_q6_k, int64_t n, int64_t k, const float* x, int64_t m, int64_t ldx, float* y,
+                      int64_t ldy, void* stream) {
+    return kq_common("q6_k_linear", q8k::launch_gemv_q6_k, w_q6_k, n, k, false, x, m, ldx, y, ldy, stream);
+}
+
+q8_status q6_k_linear_fused_gate_up_silu(const void* w_gate_up_q6_k, int64_t f, int64_t k, const float* x, int64_t m,
+                                         int64_t ldx, float* h, int64_t ldh, void* stream) {
+    return kq_common("q6_k_linear_fused_gate_up_silu", q8k::launch_gemv_q6_k, w_gate_up_q6_k, f, k, true, x, m, ldx, h,
+                     ldh, stream);
+}
+
 q8_status q8_quantize_act(const float* x, int64_t m, int64_t k, int64_t ldx, int8_t* xq, float* xd, void* stream) {
     g_err[0] = 0;
     char msg[256];

@@ -57,8 +57,12 @@ def _n_rows(x) -> int:
     return (x[0] if isinstance(x, tuple) else np.asarray(x)).shape[0]
 
 
-def _row_range(wbytes: np.ndarray, k: int, r0: int, r1: int, block_bytes: int = Q8_BLOCK) -> np.ndarray:
-    rb = (k // 32) * block_bytes
+def _row_range(wbytes: np.ndarray, k: int, r0: int, r1: int, block_bytes: float = Q8_BLOCK) -> np.ndarray:
+    """Rows r0 .. r1-1 of a packed matrix; block_bytes is the bytes per 32 weights (210/8
+    for Q6_K, whose 256-weight super-blocks are 210 bytes)."""
+    rb = k * block_bytes / 32
+    assert rb == int(rb), (k, block_bytes)
+    rb = int(rb)
     return wbytes[r0 * rb:r1 * rb]
 
 

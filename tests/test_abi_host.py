@@ -35,14 +35,15 @@ def test_header_declares_the_four_calls():
               "q8_moe_workspace_bytes", "q8_status_string", "q8_last_error", "q8_abi_version",
               "q8_quantize_act", "q8_linear_q8act", "q8_linear_fused_gate_up_silu_q8act",
               "moe_route_topk_top_p", "moe_route_topk_ws", "moe_route_workspace_bytes",
-              "q4_0_linear", "q4_0_linear_fused_gate_up_silu", "q8_moe_grouped_linear_noalloc"):
+              "q4_0_linear", "q4_0_linear_fused_gate_up_silu", "q8_moe_grouped_linear_noalloc",
+              "q4_k_linear", "q4_k_linear_fused_gate_up_silu", "q6_k_linear", "q6_k_linear_fused_gate_up_silu"):
         assert n in names, names
 
 
 def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert q8.abi_version() == 6
+    assert q8.abi_version() == 7
 
 
 def test_status_strings():
@@ -51,15 +52,18 @@ def test_status_strings():
     assert lib.q8_status_string(99) == b"unknown status"
 
 
-def _lin_base(w=FAKE, n=64, k=256, x=FAKE, m=1, ldx=256, y=FAKE, ldy=64, fused=False, q4=False):
-    if q4:
-        fn = lib.q4_0_linear_fused_gate_up_silu if fused else lib.q4_0_linear
-    else:
-        fn = lib.q8_linear_fused_gate_up_silu if fused else lib.q8_linear
+LINEAR_FORMATS = {"q8_0": ("q8_linear", "q8_linear_fused_gate_up_silu"),
+                  "q4_0": ("q4_0_linear", "q4_0_linear_fused_gate_up_silu"),
+                  "q4_k": ("q4_k_linear", "q4_k_linear_fused_gate_up_silu"),
+                  "q6_k": ("q6_k_linear", "q6_k_linear_fused_gate_up_silu")}
+
+
+def _lin_base(w=FAKE, n=64, k=256, x=FAKE, m=1, ldx=256, y=FAKE, ldy=64, fused=False, q4="q8_0"):
+    fn = getattr(lib, LINEAR_FORMATS[q4][1 if fused else 0])
     return fn(w, n, k, x, m, ldx, y, ldy, None)
 
 
-@pytest.mark.parametrize("q4", [False, True])
+@pytest.mark.parametrize("q4", sorted(LINEAR_FORMATS))
 @pytest.mark.parametrize("fused", [False, True])
 def test_linear_argument_errors(fused, q4):
     def _lin(**kw):
