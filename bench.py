@@ -306,9 +306,13 @@ def graph_launch_ms(torch, seq, launches, replays=5):
 
 def bench_linear(torch, dev, q8, name, n, k, m, fused, reps, min_bytes=600e6, fmt="q8_0"):
     """One linear launched back to back over distinct resident weight copies (enough of
-    them to exceed the 256 MB Infinity Cache twice).  fmt: "q8_0" or "q4_0" weights."""
+    them to exceed the 256 MB Infinity Cache twice).  fmt: "q8_0", "q4_0", "q4_k" or
+    "q6_k" weights."""
     import workloads as wl
-    wb, _, _ = (wl.q4_0_weight if fmt == "q4_0" else wl.q8_weight)(31, n, k)
+    gen = {"q8_0": wl.q8_weight, "q4_0": wl.q4_0_weight, "q4_k": wl.q4_k_weight, "q6_k": wl.q6_k_weight}[fmt]
+    wb = gen(31, n, k)[0]
+    plain = getattr(q8, "q8_linear" if fmt == "q8_0" else f"{fmt}_linear")
+    fused_fn = getattr(q8, "q8_linear_fused_gate_up_silu" if fmt == "q8_0" else f"{fmt}_linear_fused_gate_up_silu")
     base = torch.from_numpy(wb).to(dev)
     copies = [base] + [base.clone() for _ in range(max(1, int(min_bytes // wb.size)))]
     x = torch.from_numpy(wl.activations(37, m, k)).to(dev)
@@ -319,15 +323,10 @@ def bench_linear(torch, dev, q8, name, n, k, m, fused, reps, min_bytes=600e6, fm
     def seq():
         for i in range(launches):
             w = copies[i % len(copies)]
-            if fmt == "q4_0":
-                if fused:
-                    q8.q4_0_linear_fused_gate_up_silu(w, nout, k, x, out=y)
-                else:
-                    q8.q4_0_linear(w, n, k, x, out=y)
-            elif fused:
-                q8.q8_linear_fused_gate_up_silu(w, nout, k, x, out=y)
+            if fused:
+                fused_fn(w, nout, k, x, out=y)
             else:
-                q8.q8_linear(w, n, k, x, out=y)
+                plain(w, n, k, x, out=y)
 
     ms = graph_launch_ms(torch, seq, launches)
     flops = 2.0 * m * n * k
@@ -438,7 +437,7 @@ def kernel_driver(which, m, q8act):
     """Short launch sequence for rocprofv3 counter and trace runs: a plain 256 MiB
     device-to-device copy (the calibration dispatch for FETCH_SIZE / WRITE_SIZE), then one
     Qwen3-8B linear at m rows on 12 distinct resident weight copies (each launch streams
-    its weights from HBM)."""
+    its weights from HBM), or with which = "moe" the Qwen3-30B-A3B MoE layer at m tokens."""
     import torch
 
     import block_quantized_weight_linear_amd as q8
@@ -451,6 +450,23 @@ def kernel_driver(which, m, q8act):
         dst.copy_(src)
     torch.cuda.synchronize()
     del src, dst
+    if which == "moe":
+        # the Qwen3-30B-A3B MoE layer at m tokens: two-pass routing, then the grouped
+        # mixture, four times over the same resident experts
+        cfg = wl.QWEN3_30B_A3B_MOE
+        e, f, hd, kk = cfg.n_exp, cfg.ffn, cfg.hidden, cfg.k
+        gu_h = np.concatenate([wl.q8_weight(cfg.seed * 100 + i, 2 * f, hd)[0] for i in range(8)])
+        dn_h = np.concatenate([wl.q8_weight(cfg.seed * 100 + 50 + i, hd, f)[0] for i in range(8)])
+        gu = torch.cat([torch.from_numpy(gu_h).to(dev)] * (e // 8))
+        dn = torch.cat([torch.from_numpy(dn_h).to(dev)] * (e // 8))
+        x = torch.from_numpy(wl.activations(cfg.seed + 11, m, hd)).to(dev)
+        wr = torch.from_numpy(wl.router_weight(cfg.seed + 12, e, hd, cfg.router_std)).to(dev)
+        for _ in range(4):
+            idx, wts = q8.moe_route_topk(x, wr, kk, True, workspace=True)
+            q8.q8_moe_grouped_linear(gu, dn, e, f, hd, x, idx, wts)
+        torch.cuda.synchronize()
+        log(f"kernel driver: moe tokens={m} done")
+        return
     n, k, fused = PROFILE_LINEARS[which]
     wb, _, _ = wl.q8_weight(1, n, k)
     base = torch.from_numpy(wb).to(dev)

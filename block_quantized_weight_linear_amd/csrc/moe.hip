@@ -7,9 +7,9 @@
 // the (token, slot) pairs by expert, and each token's sum keeps a fixed order.
 //
 // Four launches on one stream, no host synchronization:
-//   1. plan      one workgroup: counting sort of the m*k (token, slot) pairs by
-//                expert, stable in pair order; offsets[e], sorted pair list, and the
-//                inverse map pair -> position.
+//   1. plan      one workgroup of 16 waves: counting sort of the m*k (token, slot)
+//                pairs by expert, stable in pair order; offsets[e], sorted pair list,
+//                and the inverse map pair -> position.
 //   2. gate_up   grid (expert, row tile): an expert with no pairs exits at once;
 //                otherwise its tokens' activation rows are staged in LDS (up to 4 at a
 //                time) and one pass over the tile's rows serves all of them (same
@@ -39,9 +39,25 @@ constexpr int kMoeWaves = kMoeThreads / 64;
 template <bool GATE_UP>
 constexpr int moe_groups_per_wave() { return GATE_UP ? 8 : 4; }
 constexpr int kMoeMaxRows = 4;        // activation rows staged per pass
-constexpr int kPlanThreads = 256;
+constexpr int kPlanThreads = 1024;
 
 // ---------------------------------------------------------------- 1. route plan
+
+// Sixteen waves; wave w owns the contiguous pair segment [w*seg, (w+1)*seg) (seg a
+// multiple of 64), so a stable order needs no block barrier inside the scatter:
+//   a. each wave counts its segment's pairs per expert into its own LDS histogram row;
+//   b. thread e sums expert e's row entries (the count) and turns them into exclusive
+//      prefixes over the waves;
+//   c. scans over the experts give offsets, the active-expert list and the first
+//      matrix-core tile of each expert; every wave's running position for expert e
+//      becomes offsets[e] + the count of e in the segments before it;
+//   d. each wave walks its segment 64 pairs at a time (ids loaded 16 steps ahead in one
+//      batch, as in a.): a pair's place is its wave's
+//      running position for its expert plus the number of earlier lanes of the step
+//      with the same expert (found with eight ballots, one per bit of the id, ids < 256);
+//      the highest such lane advances the running position.
+constexpr int kPlanWaves = kPlanThreads / 64;
+constexpr int kPlanBatch = 16;  // pair ids a lane loads at once
 
 __global__ __launch_bounds__(kPlanThreads) void moe_plan_kernel(const int32_t* __restrict__ idx, int n_pairs,
                                                                 int n_exp, int32_t* __restrict__ offsets,
@@ -49,111 +65,112 @@ __global__ __launch_bounds__(kPlanThreads) void moe_plan_kernel(const int32_t* _
                                                                 int32_t* __restrict__ inv,
                                                                 int32_t* __restrict__ active,
                                                                 int32_t* __restrict__ tile_start) {
-    __shared__ int counts[q8v::kMaxExperts + 1];
-    __shared__ int running[q8v::kMaxExperts + 1];
+    __shared__ int run[kPlanWaves][q8v::kMaxExperts];  // per-wave counts, then running positions
+    __shared__ int base_of[q8v::kMaxExperts];
+    __shared__ int wave_total[kPlanWaves], wave_active[kPlanWaves], wave_tiles[kPlanWaves];
     const int tid = threadIdx.x;
-    for (int e = tid; e <= n_exp; e += kPlanThreads) counts[e] = 0;
-    __syncthreads();
-    for (int i = tid; i < n_pairs; i += kPlanThreads) {
-        const int e = idx[i];
-        if (e >= 0 && e < n_exp) atomicAdd(&counts[e], 1);
-    }
-    __syncthreads();
-    {
-        // exclusive scan of the counts (thread e takes expert e; n_exp <= kPlanThreads):
-        // a shuffle scan per wave, then the totals of the waves before it
-        __shared__ int wave_total[kPlanThreads / 64];
-        const int lane = tid & 63;
-        const int c = tid < n_exp ? counts[tid] : 0;
-        int incl = c;
-        for (int off = 1; off < 64; off <<= 1) {
-            const int v = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += v;
-        }
-        if (lane == 63) wave_total[tid >> 6] = incl;
-        __syncthreads();
-        int base = 0;
-        for (int w = 0; w < (tid >> 6); ++w) base += wave_total[w];
-        const int excl = base + incl - c;
-        if (tid < n_exp) {
-            running[tid] = excl;
-            offsets[tid] = excl;
-        }
-        if (tid == n_exp - 1) offsets[n_exp] = excl + c;
-        // the experts with pairs, in expert order, and their number at active[n_exp]
-        const int has = c > 0 ? 1 : 0;
-        int aincl = has;
-        for (int off = 1; off < 64; off <<= 1) {
-            const int v = __shfl_up(aincl, off, 64);
-            if (lane >= off) aincl += v;
-        }
-        __shared__ int wave_active[kPlanThreads / 64];
-        if (lane == 63) wave_active[tid >> 6] = aincl;
-        __syncthreads();
-        int abase = 0;
-        for (int w = 0; w < (tid >> 6); ++w) abase += wave_active[w];
-        if (has) active[abase + aincl - 1] = tid;
-        if (tid == kPlanThreads - 1) active[n_exp] = abase + aincl;
-        // the first 128-row tile of each expert in the grouped matrix-core form
-        const int nt = (c + 127) / 128;
-        int tincl = nt;
-        for (int off = 1; off < 64; off <<= 1) {
-            const int v = __shfl_up(tincl, off, 64);
-            if (lane >= off) tincl += v;
-        }
-        __shared__ int wave_tiles[kPlanThreads / 64];
-        if (lane == 63) wave_tiles[tid >> 6] = tincl;
-        __syncthreads();
-        int tbase = 0;
-        for (int w = 0; w < (tid >> 6); ++w) tbase += wave_tiles[w];
-        if (tid < n_exp) tile_start[tid] = tbase + tincl - nt;
-        if (tid == n_exp - 1) tile_start[n_exp] = tbase + tincl;
-    }
-    __syncthreads();
-    // Stable scatter, one chunk of kPlanThreads pairs at a time: a pair's place is the
-    // running count of its expert plus the number of earlier pairs of the chunk with
-    // the same expert.  Within a wave the lanes holding the same expert are found with
-    // eight ballots (one per bit of the id, ids < 256); earlier waves' counts come
-    // through LDS.
-    __shared__ int wave_cnt[kPlanThreads / 64][q8v::kMaxExperts];
     const int lane = tid & 63;
     const int wv = tid >> 6;
-    for (int base = 0; base < n_pairs; base += kPlanThreads) {
-        const int i = base + tid;
-        int e = -1;
-        if (i < n_pairs) {
-            e = idx[i];
-            if (e < 0 || e >= n_exp) e = -1;
-        }
-        uint64_t same = __ballot(e >= 0);
+    for (int x = tid; x < kPlanWaves * q8v::kMaxExperts; x += kPlanThreads) (&run[0][0])[x] = 0;
+    __syncthreads();
+    const int seg = (n_pairs + 64 * kPlanWaves - 1) / (64 * kPlanWaves) * 64;
+    const int s0 = wv * seg;
+    const int s1 = s0 + seg < n_pairs ? s0 + seg : n_pairs;
+    // the segment's expert ids, kPlanBatch per lane at a time (all loads issued together):
+    // id j of batch bb is pair bb + 64 j + lane; -1 past the segment or out of range
+    auto load_batch = [&](int bb, int (&ids)[kPlanBatch]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            const uint64_t set = __ballot(e >= 0 && ((e >> b) & 1));
-            same &= ((e >> b) & 1) ? set : ~set;
+        for (int j = 0; j < kPlanBatch; ++j) {
+            const int i = bb + 64 * j + lane;
+            const int e = i < s1 ? idx[i] : -1;
+            ids[j] = (e >= 0 && e < n_exp) ? e : -1;
         }
-        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-        const int rank_in_wave = __popcll(same & below);
-        // the highest lane of each group publishes the wave's count for that expert
-        for (int x = tid; x < (kPlanThreads / 64) * q8v::kMaxExperts; x += kPlanThreads) (&wave_cnt[0][0])[x] = 0;
-        __syncthreads();
-        if (e >= 0 && (same >> lane) == 1ull) wave_cnt[wv][e] = __popcll(same);
-        __syncthreads();
-        int rank = rank_in_wave;
-        if (e >= 0)
-            for (int w = 0; w < wv; ++w) rank += wave_cnt[w][e];
-        const int pos = (e >= 0) ? running[e] + rank : -1;
-        if (i < n_pairs) {
-            inv[i] = pos;
-            if (pos >= 0) sorted[pos] = i;
+    };
+    // a. per-wave histogram (LDS atomics on the wave's own row)
+    for (int bb = s0; bb < s1; bb += 64 * kPlanBatch) {
+        int ids[kPlanBatch];
+        load_batch(bb, ids);
+#pragma unroll
+        for (int j = 0; j < kPlanBatch; ++j)
+            if (ids[j] >= 0) atomicAdd(&run[wv][ids[j]], 1);
+    }
+    __syncthreads();
+    // b. thread e: count of expert e, per-wave exclusive prefixes
+    int c = 0;
+    if (tid < n_exp) {
+        for (int w = 0; w < kPlanWaves; ++w) {
+            const int v = run[w][tid];
+            run[w][tid] = c;
+            c += v;
         }
-        __syncthreads();
-        // the chunk's last pair of each expert advances its running count
-        if (e >= 0) {
-            int later = 0;
-            for (int w = wv + 1; w < kPlanThreads / 64; ++w) later += wave_cnt[w][e];
-            if (later == 0 && (same >> lane) == 1ull) running[e] = pos + 1;
+    }
+    // c. exclusive scans over the experts (thread e holds expert e; n_exp <= 256 <= threads):
+    // a shuffle scan per wave, then the totals of the waves before it
+    auto wave_incl = [&](int v) {
+        for (int off = 1; off < 64; off <<= 1) {
+            const int u = __shfl_up(v, off, 64);
+            if (lane >= off) v += u;
         }
-        __syncthreads();
+        return v;
+    };
+    const int incl = wave_incl(c);
+    const int has = c > 0 ? 1 : 0;
+    const int aincl = wave_incl(has);
+    const int nt = (c + 127) / 128;  // 128-row matrix-core tiles of the expert
+    const int tincl = wave_incl(nt);
+    if (lane == 63) {
+        wave_total[wv] = incl;
+        wave_active[wv] = aincl;
+        wave_tiles[wv] = tincl;
+    }
+    __syncthreads();
+    int base = 0, abase = 0, tbase = 0;
+    for (int w = 0; w < wv; ++w) {
+        base += wave_total[w];
+        abase += wave_active[w];
+        tbase += wave_tiles[w];
+    }
+    const int excl = base + incl - c;
+    if (tid < n_exp) {
+        base_of[tid] = excl;
+        offsets[tid] = excl;
+        tile_start[tid] = tbase + tincl - nt;
+    }
+    if (tid == n_exp - 1) {
+        offsets[n_exp] = excl + c;
+        tile_start[n_exp] = tbase + tincl;
+    }
+    // the experts with pairs, in expert order, and their number at active[n_exp]
+    if (has) active[abase + aincl - 1] = tid;
+    if (tid == kPlanThreads - 1) active[n_exp] = abase + aincl;
+    __syncthreads();
+    for (int x = tid; x < kPlanWaves * n_exp; x += kPlanThreads) {
+        const int w = x / n_exp, e = x - w * n_exp;
+        run[w][e] += base_of[e];
+    }
+    __syncthreads();
+    // d. stable scatter of the wave's segment
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int bb = s0; bb < s1; bb += 64 * kPlanBatch) {
+        int ids[kPlanBatch];
+        load_batch(bb, ids);
+#pragma unroll
+        for (int j = 0; j < kPlanBatch; ++j) {
+            const int i = bb + 64 * j + lane;
+            const int e = ids[j];
+            uint64_t same = __ballot(e >= 0);
+#pragma unroll
+            for (int bit = 0; bit < 8; ++bit) {
+                const uint64_t set = __ballot(e >= 0 && ((e >> bit) & 1));
+                same &= ((e >> bit) & 1) ? set : ~set;
+            }
+            const int pos = e >= 0 ? run[wv][e] + __popcll(same & below) : -1;
+            if (i < s1) {
+                inv[i] = pos;
+                if (pos >= 0) sorted[pos] = i;
+            }
+            if (e >= 0 && (same >> lane) == 1ull) run[wv][e] = pos + 1;  // the group's highest lane
+        }
     }
 }
 

@@ -25,6 +25,7 @@
 
 #include <type_traits>
 
+#include "lds_dma.h"
 #include "q8_internal.h"
 
 namespace q8k {
@@ -302,6 +303,106 @@ __global__ __launch_bounds__(kLogitThreads) void route_logits_kernel(const float
     }
 }
 
+// Pass 1 for many tokens: block (token group, expert group) multiplies kTileTokens
+// tokens by 32 experts (8 per wave), so each router row read from L2 serves 16 tokens and
+// each staged activation value 8 experts (the 4-token form re-reads the router matrix
+// once per 4 tokens).  Every logit keeps the lane slices and fma order of
+// route_topk_kernel; its 64 lane partials are then summed by a transpose-reduce that
+// pairs lanes exactly as the xor butterfly does (lane l with l ^ 32, then ^ 16, ..., ^ 1)
+// while halving the values each lane carries at every step: a lane keeps the half whose
+// index bit matches its own lane bit and trades the other half with its partner, so the
+// 128 logits of a wave need 126 shuffles instead of 768 and come out as values 2l and
+// 2l + 1 on lane l, bit-identical to the butterfly's sums.
+constexpr int kTileTokens = 16;
+// measured on the Qwen3-30B-A3B router (128 x 2048): the 4-token form takes 9.9 us at 192
+// tokens and grows linearly; the tiles take 18.6 us at 256 tokens and 19.0 at 512
+constexpr int kTiledLogitsMinTokens = 384;
+constexpr int kTileExperts = 8;  // per wave
+constexpr int kTileChunk = 1024;
+
+__global__ __launch_bounds__(256) void route_logits_tiled_kernel(const float* __restrict__ x, int m, int h, int ldx,
+                                                                 const float* __restrict__ wr, int n_exp,
+                                                                 float* __restrict__ logits) {
+    constexpr int T = kTileTokens, E = kTileExperts, NV = T * E;  // NV = 128 = 2 * 64
+    __shared__ float4 xs[T][kTileChunk / 4];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int t0 = blockIdx.x * T;
+    const int e0 = (blockIdx.y * 4 + wave) * E;
+    const float* we[E];
+#pragma unroll
+    for (int b = 0; b < E; ++b) {
+        const int e = e0 + b;
+        we[b] = wr + (size_t)(e < n_exp ? e : n_exp - 1) * h;  // past n_exp: not stored
+    }
+    float acc[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) acc[j] = 0.0f;
+    for (int c0 = 0; c0 < h; c0 += kTileChunk) {
+        const int len = h - c0 < kTileChunk ? h - c0 : kTileChunk;  // a multiple of 256
+        const int steps = len / 256;
+        __syncthreads();  // every wave is done with the previous chunk
+        // the chunk's activations: T * steps wave-wide direct-to-LDS copies of 1 KB
+        // (copy q = token t, 256 inputs c), taken by the four waves in turn
+        for (int q = wave; q < T * steps; q += 4) {
+            const int t = q / steps, c = q - t * steps;
+            const int tc = t0 + t < m ? t0 + t : m - 1;  // past m: the last token, not stored
+            lds_copy16(x + (size_t)tc * ldx + c0 + 256 * c + 4 * lane, &xs[t][64 * c]);
+        }
+        float4 v[E];
+#pragma unroll
+        for (int b = 0; b < E; ++b) v[b] = *reinterpret_cast<const float4*>(we[b] + c0 + 4 * lane);
+        wait_vmcnt_mem<0>();
+        __syncthreads();
+        for (int i = 0; i < steps; ++i) {
+            // the router slices of the next step load while this one is multiplied
+            float4 vn[E];
+            const int ni = i + 1 < steps ? i + 1 : i;
+#pragma unroll
+            for (int b = 0; b < E; ++b) vn[b] = *reinterpret_cast<const float4*>(we[b] + c0 + 4 * lane + 256 * ni);
+            float4 a = xs[0][lane + 64 * i];
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const float4 an = xs[t + 1 < T ? t + 1 : t][lane + 64 * i];  // read ahead
+#pragma unroll
+                for (int b = 0; b < E; ++b) {
+                    float& r = acc[t * E + b];
+                    r = __builtin_fmaf(a.x, v[b].x, r);
+                    r = __builtin_fmaf(a.y, v[b].y, r);
+                    r = __builtin_fmaf(a.z, v[b].z, r);
+                    r = __builtin_fmaf(a.w, v[b].w, r);
+                }
+                a = an;
+            }
+#pragma unroll
+            for (int b = 0; b < E; ++b) v[b] = vn[b];
+        }
+    }
+    // transpose-reduce: at the step with offset `off` a lane holds n values; it keeps the
+    // upper half if its lane bit `off` is set, else the lower half, and adds the
+    // partner's copy of the half it keeps
+#pragma unroll
+    for (int st = 0; st < 6; ++st) {
+        const int off = 32 >> st;
+        const int n = NV >> st;
+        const bool up = (lane & off) != 0;
+#pragma unroll
+        for (int r = 0; r < n / 2; ++r) {
+            const float keep = up ? acc[n / 2 + r] : acc[r];
+            const float send = up ? acc[r] : acc[n / 2 + r];
+            acc[r] = keep + __shfl_xor(send, off, 64);
+        }
+    }
+    // lane l holds values j = 2l and 2l + 1, j = t * E + b
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int j = 2 * lane + r;
+        const int t = t0 + j / E;
+        const int e = e0 + j % E;
+        if (t < m && e < n_exp) logits[(size_t)t * n_exp + e] = acc[r];
+    }
+}
+
 // Pass 2: one wave per token.
 __global__ __launch_bounds__(256) void route_select_kernel(const float* __restrict__ logits, int m, int n_exp, int k,
                                                            int normalize, float top_p,
@@ -317,9 +418,16 @@ hipError_t launch_route_topk(const DeviceInfo&, const float* x, int64_t m, int64
                              const float* w_router, int64_t n_exp, int k, bool normalize, float top_p, int32_t* idx,
                              float* wts, float* logits, hipStream_t stream) {
     if (logits) {
-        const dim3 grid((unsigned)((m + kLogitTokens - 1) / kLogitTokens), (unsigned)((n_exp + 3) / 4));
-        hipLaunchKernelGGL(route_logits_kernel, grid, dim3(kLogitThreads), 0, stream, x, (int)m, (int)h, (int)ldx,
-                           w_router, (int)n_exp, logits);
+        if (m >= kTiledLogitsMinTokens) {
+            const dim3 grid((unsigned)((m + kTileTokens - 1) / kTileTokens),
+                            (unsigned)((n_exp + 4 * kTileExperts - 1) / (4 * kTileExperts)));
+            hipLaunchKernelGGL(route_logits_tiled_kernel, grid, dim3(256), 0, stream, x, (int)m, (int)h, (int)ldx,
+                               w_router, (int)n_exp, logits);
+        } else {
+            const dim3 grid((unsigned)((m + kLogitTokens - 1) / kLogitTokens), (unsigned)((n_exp + 3) / 4));
+            hipLaunchKernelGGL(route_logits_kernel, grid, dim3(kLogitThreads), 0, stream, x, (int)m, (int)h, (int)ldx,
+                               w_router, (int)n_exp, logits);
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(route_select_kernel, dim3((unsigned)((m + 3) / 4)), dim3(256), 0, stream, logits, (int)m,

@@ -266,10 +266,12 @@ size_t q8_moe_workspace_bytes(int64_t m, int32_t k, int64_t n_exp, int64_t f, in
  *   topk_w   : float32 [m][k]
  *   workspace: device memory of at least q8_moe_workspace_bytes(m, k, n_exp, f, h)
  *              bytes, 256-byte aligned; its contents on entry do not matter.
- * Weight traffic: on the float32 decode path one pass over an expert's weights serves up
- * to 4 of its routed tokens (an expert with more tokens is streamed again for each further
- * group of 4, mostly from cache); from 64 routed pairs per expert on average (prefill)
- * the bf16 matrix-core tiles run, one pass per 128 of an expert's tokens.
+ * Paths: below 8 routed pairs per expert on average (decode) the float32 GEMV passes run,
+ * one pass over an expert's weights serving up to 4 of its routed tokens (an expert with
+ * more tokens is streamed again for each further group of 4); from 8 pairs per expert on
+ * average the bf16 matrix-core tiles run (activations, d*q and the hidden SiLU*up rounded
+ * to bf16 once, float32 accumulation), one pass per 128 of an expert's tokens.  The
+ * switch point is the measured crossover on the Qwen3-30B-A3B layer.
  */
 q8_status q8_moe_grouped_linear(const void* w_gate_up_exps, const void* w_down_exps,
                                 int64_t n_exp, int64_t f, int64_t h,
