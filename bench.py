@@ -63,6 +63,24 @@ def measured_traffic():
         return None
 
 
+def measured_mfma():
+    """Counter-based matrix-core utilisation of the prefill tiles from the committed
+    rocprofv3 summary (SQ_VALU_MFMA_BUSY_CYCLES over the SIMDs' cycles), or {} once
+    gemm_q8_mfma.hip differs from the source the counters were taken with."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "mfma_prefill_qwen3_8b_gate_up_and_a3b_moe.md")
+    src = os.path.join(ROOT, "block_quantized_weight_linear_amd", "csrc", "gemm_q8_mfma.hip")
+    try:
+        text = open(path).read()
+        with open(src, "rb") as f:
+            h = hashlib.sha256(f.read()).hexdigest()
+        if re.search(r"sources_sha256: ([0-9a-f]{64})", text).group(1) != h:
+            return {}
+        return {k: float(v) for k, v in re.findall(r"(\w+_mfma_busy_frac): ([0-9.]+)", text)}
+    except (OSError, AttributeError):
+        return {}
+
+
 # --------------------------------------------------------------------- workloads
 
 
@@ -563,6 +581,15 @@ def main():
         extras["qwen3-8b-gate-up-m16"] = bench_linear(torch, dev, q8, "8b gate_up m16", 24576, 4096, 16, True, reps)
         extras["qwen3-8b-gate-up-m512-prefill"] = bench_linear(torch, dev, q8, "8b gate_up m512", 24576, 4096, 512,
                                                                True, reps)
+        mfma = measured_mfma()
+        if "gate_up_m512_mfma_busy_frac" in mfma:
+            extras["qwen3-8b-gate-up-m512-prefill"]["mfma_busy_frac_counters"] = mfma["gate_up_m512_mfma_busy_frac"]
+        # GGUF Q4_K_M mix on the Qwen3-8B FFN: gate_up in Q4_K, down in Q6_K
+        for m in (1, 8):
+            extras[f"qwen3-8b-ffn-gate-up-q4_k-m{m}"] = bench_linear(torch, dev, q8, f"8b gate_up q4_k m{m}", 24576,
+                                                                     4096, m, True, reps, fmt="q4_k")
+            extras[f"qwen3-8b-ffn-down-q6_k-m{m}"] = bench_linear(torch, dev, q8, f"8b down q6_k m{m}", 4096, 12288,
+                                                                  m, False, reps, fmt="q6_k")
         # GGUF Q4_0 weights: the Gemma 4 12B FFN (hidden 3840, intermediate 15360), one token
         extras["gemma-4-12b-ffn-gate-up-q4_0-m1"] = bench_linear(torch, dev, q8, "gemma4 12b gate_up q4_0 m1",
                                                                  30720, 3840, 1, True, reps, fmt="q4_0")
@@ -570,6 +597,10 @@ def main():
                                                               3840, 15360, 1, False, reps, fmt="q4_0")
         extras["qwen3-30b-a3b-moe-16tok"] = bench_moe(torch, dev, q8, 4, args.steps, args.warmup)
         extras["qwen3-30b-a3b-moe-2048tok-prefill"] = bench_moe_prefill(torch, dev, q8, 2048, 5)
+        if "a3b_moe_2048_gate_up_mfma_busy_frac" in mfma:
+            extras["qwen3-30b-a3b-moe-2048tok-prefill"]["mfma_busy_frac_counters"] = {
+                "gate_up": mfma["a3b_moe_2048_gate_up_mfma_busy_frac"], "down": mfma["a3b_moe_2048_down_mfma_busy_frac"]}
+        extras["qwen3-30b-a3b-moe-512tok"] = bench_moe_prefill(torch, dev, q8, 512, 5)
         extras["qwen3-30b-a3b-moe-16tok-expert-top-p-0.9"] = bench_moe(torch, dev, q8, 4, args.steps, args.warmup,
                                                                         top_p=0.9)
         line["configs"] = extras
