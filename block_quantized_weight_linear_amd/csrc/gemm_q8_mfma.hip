@@ -1,5 +1,5 @@
 // Prefill (M >= 256 activation rows): Q8_0 weights x float32 activations on the bf16
-// matrix cores of gfx950 (v_mfma_f32_16x16x32_bf16), float32 accumulation and output.
+// matrix cores of gfx950 (v_mfma_f32_32x32x16_bf16), float32 accumulation and output.
 //
 // With hundreds of rows the linear is a dense contraction (the tensor-core vs GEMV
 // kernel-class boundary of the fucina DGX Spark README, Performance): each weight is
