@@ -143,7 +143,7 @@ def fused_gate_up_silu_q4_0_ref(w_gate_up_q4, f: int, k: int, x) -> np.ndarray:
     return silu_ref(y[:, :f]) * y[:, f:]
 
 
-# ------------------------------------------------------------- Q4_K and Q6_K
+# ----------------------------------------------------------- Q4_K, Q5_K, Q6_K
 #
 # "14. Model families and example applications" section 14.1 says the ggml quant forms
 # Q4_K, Q5_K and Q6_K run their own packed kernels, and the DGX Spark README (Features)
@@ -158,6 +158,13 @@ def fused_gate_up_silu_q4_0_ref(w_gate_up_q4, f: int, k: int, x) -> np.ndarray:
 # nibble of quant byte 32c + i, weight 64c + 32 + i its high nibble;
 # w = d * sc[j] * q - dmin * m[j].
 #
+# Q5_K, 176 bytes: binary16 d, binary16 dmin, the 12 scale/min bytes of Q4_K (same
+# packing), 32 bytes qh, 128 bytes of 4-bit quants.  Weight 64c + 32s + l (c < 4, s < 2,
+# l < 32) has the 5-bit quant whose low four bits are nibble s (low for s = 0) of quant
+# byte 32c + l and whose top bit is bit 2c + s of qh[l]; it is in sub-block j = 2c + s;
+# w = d * sc[j] * q - dmin * m[j].  (Section 14.1 names Q5_K with Q4_K and Q6_K; the same
+# reading of the GGUF layout.)
+#
 # Q6_K, 210 bytes: 128 bytes ql, 64 bytes qh, 16 int8 scales, binary16 d.  Weights run in
 # two halves of 128; in half t, weight 128t + 32k + l (k < 4, l < 32) has the 6-bit quant
 # whose low four bits are the low (k < 2) or high (k >= 2) nibble of ql[64t + l + 32*(k%2)]
@@ -166,11 +173,15 @@ def fused_gate_up_silu_q4_0_ref(w_gate_up_q4, f: int, k: int, x) -> np.ndarray:
 
 QK_K = 256
 Q4_K_BLOCK_BYTES = 144
+Q5_K_BLOCK_BYTES = 176
 Q6_K_BLOCK_BYTES = 210
 _Q4_K_RECORD = np.dtype([("d", "<f2"), ("dmin", "<f2"), ("scales", "u1", (12,)), ("qs", "u1", (QK_K // 2,))])
 _Q6_K_RECORD = np.dtype([("ql", "u1", (QK_K // 2,)), ("qh", "u1", (QK_K // 4,)), ("scales", "i1", (QK_K // 16,)),
                          ("d", "<f2")])
+_Q5_K_RECORD = np.dtype([("d", "<f2"), ("dmin", "<f2"), ("scales", "u1", (12,)), ("qh", "u1", (QK_K // 8,)),
+                         ("qs", "u1", (QK_K // 2,))])
 assert _Q4_K_RECORD.itemsize == Q4_K_BLOCK_BYTES and _Q6_K_RECORD.itemsize == Q6_K_BLOCK_BYTES
+assert _Q5_K_RECORD.itemsize == Q5_K_BLOCK_BYTES
 
 
 def _k_records(buf, n_rows: int, k: int, record, block_bytes: int):
@@ -214,6 +225,27 @@ def dequantize_q4_k(buf, n_rows: int, k: int) -> np.ndarray:
     return w.reshape(n_rows, -1)
 
 
+def dequantize_q5_k(buf, n_rows: int, k: int) -> np.ndarray:
+    """W[n, 256b + i] of a GGUF Q5_K matrix in float64 (exact: products of at most 22
+    significant bits)."""
+    rec = _k_records(buf, n_rows, k, _Q5_K_RECORD, Q5_K_BLOCK_BYTES)
+    nb = k // QK_K
+    d = rec["d"].astype(np.float64)
+    dmin = rec["dmin"].astype(np.float64)
+    sc, m = q4_k_scale_min(rec["scales"])                       # [n][nb][8]
+    qs = rec["qs"].astype(np.int64).reshape(n_rows, nb, 4, 32)  # chunk c, byte l
+    qh = rec["qh"].astype(np.int64)                             # [n][nb][32], byte l
+    q5 = np.empty((n_rows, nb, 4, 2, 32), dtype=np.int64)        # chunk c, half s, l
+    for c in range(4):
+        for half in range(2):
+            low4 = (qs[:, :, c, :] >> (4 * half)) & 0x0F
+            top = (qh >> (2 * c + half)) & 1
+            q5[:, :, c, half, :] = low4 + 16 * top
+    q5 = q5.reshape(n_rows, nb, 8, 32)                          # sub-block j = 2c + s
+    w = (d[:, :, None, None] * sc[:, :, :, None]) * q5 - (dmin[:, :, None, None] * m[:, :, :, None])
+    return w.reshape(n_rows, -1)
+
+
 def dequantize_q6_k(buf, n_rows: int, k: int) -> np.ndarray:
     """W[n, 256b + i] of a GGUF Q6_K matrix in float64 (exact)."""
     rec = _k_records(buf, n_rows, k, _Q6_K_RECORD, Q6_K_BLOCK_BYTES)
@@ -239,6 +271,11 @@ def q4_k_linear_ref(w_q4k, n: int, k: int, x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64) @ dequantize_q4_k(w_q4k, n, k).T
 
 
+def q5_k_linear_ref(w_q5k, n: int, k: int, x) -> np.ndarray:
+    """y = x . W^T for a GGUF Q5_K weight W [n][k] (float64)."""
+    return np.asarray(x, dtype=np.float64) @ dequantize_q5_k(w_q5k, n, k).T
+
+
 def q6_k_linear_ref(w_q6k, n: int, k: int, x) -> np.ndarray:
     """y = x . W^T for a GGUF Q6_K weight W [n][k] (float64)."""
     return np.asarray(x, dtype=np.float64) @ dequantize_q6_k(w_q6k, n, k).T
@@ -248,6 +285,12 @@ def fused_gate_up_silu_q4_k_ref(w, f: int, k: int, x) -> np.ndarray:
     """SiLU(x . W_gate^T) * (x . W_up^T) from one Q4_K [2f][k] matrix, gate rows first."""
     y = q4_k_linear_ref(w, 2 * f, k, x)
     return silu_ref(y[:, :f]) * y[:, f:]
+
+
+def fused_gate_up_silu_q5_k_ref(w, f: int, k: int, x) -> np.ndarray:
+    """SiLU(x . W_gate^T) * (x . W_up^T) from one Q5_K [2f][k] matrix, gate rows first."""
+    yy = q5_k_linear_ref(w, 2 * f, k, x)
+    return silu_ref(yy[:, :f]) * yy[:, f:]
 
 
 def fused_gate_up_silu_q6_k_ref(w, f: int, k: int, x) -> np.ndarray:

@@ -66,6 +66,12 @@ MUTANTS = {
     "q6_k_ql_half_offset": ("nib = ql[..., 32 * (kk % 2):32 * (kk % 2) + 32]", "nib = ql[..., 32 * (kk // 2):32 * (kk // 2) + 32]"),
     "q6_k_nibble_choice": ("low = (nib & 0x0F) if kk < 2 else (nib >> 4)", "low = (nib & 0x0F) if kk % 2 == 0 else (nib >> 4)"),
     "q6_k_scales_unsigned": ('("scales", "i1", (QK_K // 16,))', '("scales", "u1", (QK_K // 16,))'),
+    "q5_k_top_bit_index": ("top = (qh >> (2 * c + half)) & 1", "top = (qh >> (c + half)) & 1"),
+    "q5_k_top_bit_weight": ("q5[:, :, c, half, :] = low4 + 16 * top", "q5[:, :, c, half, :] = low4 + 32 * top"),
+    "q5_k_nibble_order": ("low4 = (qs[:, :, c, :] >> (4 * half)) & 0x0F", "low4 = (qs[:, :, c, :] >> (4 - 4 * half)) & 0x0F"),
+    "q5_k_qh_after_quants": ('("scales", "u1", (12,)), ("qh", "u1", (QK_K // 8,)),\n                         ("qs", "u1", (QK_K // 2,))',
+                             '("scales", "u1", (12,)), ("qs", "u1", (QK_K // 2,)),\n                         ("qh", "u1", (QK_K // 8,))'),
+    "q5_k_min_added": ("* q5 - (dmin[:, :, None, None]", "* q5 + (dmin[:, :, None, None]"),
     "q8act_wrong_block": ('isum = np.einsum("nbi,bi->nb", qw, qx[mi])', 'isum = np.einsum("nbi,bi->nb", qw, qx[mi][::-1])'),
 }
 

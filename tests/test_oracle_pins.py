@@ -477,7 +477,8 @@ def check_k_quant_hand(o):
     groups; and a linear over the Q4_K blocks and one over the Q6_K blocks against the hand
     weights."""
     for fmt, deq, lin in (("q4_k", o.dequantize_q4_k, o.q4_k_linear_ref), ("q6_k", o.dequantize_q6_k,
-                                                                          o.q6_k_linear_ref)):
+                                                                          o.q6_k_linear_ref),
+                          ("q5_k", o.dequantize_q5_k, o.q5_k_linear_ref)):
         cases = [c for c in KQ_CASES if c["format"] == fmt]
         for c in cases:
             w = deq(c["bytes"], 1, 256)
@@ -519,8 +520,29 @@ def check_k_quant_properties(o):
     assert abs(y6[1, row] - float(exact)) <= 1e-12 * max(1.0, abs(float(exact)))
     np.testing.assert_allclose(o.q6_k_linear_ref(wl.pack_q6_k(q6, s6, two(d6)), n, k, x), 2 * y6, rtol=1e-13)
     assert np.all(o.q6_k_linear_ref(wl.pack_q6_k(np.full_like(q6, 32), s6, d6), n, k, x) == 0)
+    # Q5_K: rational brute force from the generator's fields; linearity in d and dmin
+    wb5, q5, sc5, mn5, d5, dmin5 = wl.q5_k_weight(102, n, k)
+    y5 = o.q5_k_linear_ref(wb5, n, k, x)
+    exact = Fraction(0)
+    for i in range(k):
+        b, j = i // 256, (i % 256) // 32
+        dd = half_bits_to_fraction(int(d5.view(np.uint16)[row, b]))
+        dm = half_bits_to_fraction(int(dmin5.view(np.uint16)[row, b]))
+        exact += (dd * int(sc5[row, b, j]) * int(q5[row, i]) - dm * int(mn5[row, b, j])) * Fraction(float(xr[i]))
+    assert abs(y5[1, row] - float(exact)) <= 1e-12 * max(1.0, abs(float(exact)))
+    np.testing.assert_allclose(o.q5_k_linear_ref(wl.pack_q5_k(q5, sc5, mn5, two(d5), two(dmin5)), n, k, x), 2 * y5,
+                               rtol=1e-13)
+    # Q5_K against Q4_K (pinned on its own above): with every top bit clear a Q5_K
+    # super-block is the Q4_K one with the same fields; with every top bit set each weight
+    # gains 16 * d * sc of its sub-block
+    low = q5 & 15
+    w4 = o.dequantize_q4_k(wl.pack_q4_k(low, sc5, mn5, d5, dmin5), n, k)
+    assert np.array_equal(o.dequantize_q5_k(wl.pack_q5_k(low, sc5, mn5, d5, dmin5), n, k), w4)
+    gain = 16 * np.repeat(d5.astype(np.float64)[:, :, None] * sc5.astype(np.float64), 32, axis=2).reshape(n, k)
+    assert np.array_equal(o.dequantize_q5_k(wl.pack_q5_k(low | 16, sc5, mn5, d5, dmin5), n, k), w4 + gain)
     f = 3
     for lin, fused, gen in ((o.q4_k_linear_ref, o.fused_gate_up_silu_q4_k_ref, wl.q4_k_weight),
+                            (o.q5_k_linear_ref, o.fused_gate_up_silu_q5_k_ref, wl.q5_k_weight),
                             (o.q6_k_linear_ref, o.fused_gate_up_silu_q6_k_ref, wl.q6_k_weight)):
         wg = gen(101, 2 * f, k)[0]
         h = fused(wg, f, k, x)

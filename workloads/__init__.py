@@ -74,6 +74,7 @@ def pack_q4_0(q: np.ndarray, d_f16: np.ndarray) -> np.ndarray:
 
 
 Q4_K_BLOCK_BYTES = 144
+Q5_K_BLOCK_BYTES = 176
 Q6_K_BLOCK_BYTES = 210
 QK_K = 256
 
@@ -103,6 +104,32 @@ def pack_q4_k(q, sc, m, d_f16, dmin_f16) -> np.ndarray:
         out[:, :, 12 + j] = (sc[:, :, j + 4] & 15) | ((m[:, :, j + 4] & 15) << 4)
     qb = q.reshape(n, nb, 4, 2, 32)
     out[:, :, 16:] = (qb[:, :, :, 0, :] | (qb[:, :, :, 1, :] << 4)).reshape(n, nb, 128)
+    return out.reshape(-1)
+
+
+def pack_q5_k(q, sc, m, d_f16, dmin_f16) -> np.ndarray:
+    """Lay GGUF Q5_K super-blocks out as bytes: 5-bit quants q [N][K] (0..31), sub-block
+    scales and mins as for Q4_K, binary16 d and dmin [N][K/256].
+
+    Per 176-byte super-block: d, dmin, the 12 scale bytes of Q4_K, 32 bytes qh (bit 2c + s
+    of byte l is the top bit of quant 64c + 32s + l), then 128 bytes with the low four bits
+    as in Q4_K (byte 32c + l = low(q[64c + l]) | low(q[64c + 32 + l]) << 4).
+    """
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    n, k = q.shape
+    nb = k // QK_K
+    if k % QK_K or q.max(initial=0) > 31:
+        raise ValueError("bad Q5_K fields")
+    q4 = pack_q4_k(q & 15, sc, m, d_f16, dmin_f16).reshape(n, nb, Q4_K_BLOCK_BYTES)
+    top = (q >> 4).reshape(n, nb, 4, 2, 32).astype(np.uint16)
+    qh = np.zeros((n, nb, 32), dtype=np.uint16)
+    for c in range(4):
+        for half in range(2):
+            qh |= top[:, :, c, half, :] << (2 * c + half)
+    out = np.zeros((n, nb, Q5_K_BLOCK_BYTES), dtype=np.uint8)
+    out[:, :, 0:16] = q4[:, :, 0:16]
+    out[:, :, 16:48] = qh.astype(np.uint8)
+    out[:, :, 48:] = q4[:, :, 16:]
     return out.reshape(-1)
 
 
@@ -197,6 +224,25 @@ def q4_k_weight(seed: int, n: int, k: int, exact: bool = False):
         d = rd.uniform(2e-5, 2e-4, size=(n, nb)).astype(np.float16)
         dmin = re.uniform(2e-5, 2e-4, size=(n, nb)).astype(np.float16)
     return pack_q4_k(q, sc, mn, d, dmin), q, sc, mn, d, dmin
+
+
+def q5_k_weight(seed: int, n: int, k: int, exact: bool = False):
+    """Random GGUF Q5_K matrix [n][k]: returns (bytes, q, sc, m, d, dmin).  Quants uniform
+    0..31, scales and mins uniform 0..63, d and dmin uniform in [2e-5, 2e-4] (binary16).
+    exact: d, dmin in {2^-7, 2^-8} and scales, mins 0..15."""
+    rq, rs, rm, rd, re = _rngs(seed, 5)
+    nb = k // QK_K
+    q = rq.integers(0, 32, size=(n, k), dtype=np.uint8)
+    top = 16 if exact else 64
+    sc = rs.integers(0, top, size=(n, nb, 8), dtype=np.uint8)
+    mn = rm.integers(0, top, size=(n, nb, 8), dtype=np.uint8)
+    if exact:
+        d = np.where(rd.integers(0, 2, size=(n, nb)) == 0, 2.0 ** -7, 2.0 ** -8).astype(np.float16)
+        dmin = np.where(re.integers(0, 2, size=(n, nb)) == 0, 2.0 ** -7, 2.0 ** -8).astype(np.float16)
+    else:
+        d = rd.uniform(2e-5, 2e-4, size=(n, nb)).astype(np.float16)
+        dmin = re.uniform(2e-5, 2e-4, size=(n, nb)).astype(np.float16)
+    return pack_q5_k(q, sc, mn, d, dmin), q, sc, mn, d, dmin
 
 
 def q6_k_weight(seed: int, n: int, k: int, exact: bool = False):
