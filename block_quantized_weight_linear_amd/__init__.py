@@ -15,6 +15,8 @@ from ._binding import (  # noqa: F401
     q4_0_linear_fused_gate_up_silu,
     q4_k_linear,
     q4_k_linear_fused_gate_up_silu,
+    q5_k_linear,
+    q5_k_linear_fused_gate_up_silu,
     q6_k_linear,
     q6_k_linear_fused_gate_up_silu,
     moe_route_workspace_bytes,

@@ -43,7 +43,8 @@ lib.q4_0_linear.restype = ctypes.c_int
 lib.q4_0_linear.argtypes = [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp]
 lib.q4_0_linear_fused_gate_up_silu.restype = ctypes.c_int
 lib.q4_0_linear_fused_gate_up_silu.argtypes = [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp]
-for _name in ("q4_k_linear", "q4_k_linear_fused_gate_up_silu", "q6_k_linear", "q6_k_linear_fused_gate_up_silu"):
+for _name in ("q4_k_linear", "q4_k_linear_fused_gate_up_silu", "q5_k_linear", "q5_k_linear_fused_gate_up_silu",
+              "q6_k_linear", "q6_k_linear_fused_gate_up_silu"):
     getattr(lib, _name).restype = ctypes.c_int
     getattr(lib, _name).argtypes = [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp]
 lib.q8_quantize_act.restype = ctypes.c_int
@@ -148,7 +149,7 @@ def _bytes(w, need, name, device):
 
 
 # bytes per 256 weights of each packed format
-Q8_0_BYTES, Q4_0_BYTES, Q4_K_BYTES, Q6_K_BYTES = 272, 144, 144, 210
+Q8_0_BYTES, Q4_0_BYTES, Q4_K_BYTES, Q5_K_BYTES, Q6_K_BYTES = 272, 144, 144, 176, 210
 
 
 def _quant_bytes(rows, k, bytes_256):
@@ -205,6 +206,16 @@ def q4_k_linear(w, n: int, k: int, x, out=None):
 def q4_k_linear_fused_gate_up_silu(w, f: int, k: int, x, out=None):
     """h = SiLU(x . W_gate^T) * (x . W_up^T); W is GGUF Q4_K [2f][k], gate rows first."""
     return _dense(lib.q4_k_linear_fused_gate_up_silu, w, 2 * f, f, k, x, out, Q4_K_BYTES)
+
+
+def q5_k_linear(w, n: int, k: int, x, out=None):
+    """y = x . W^T for a GGUF Q5_K weight W [n][k] (uint8 bytes) and float32 x [m][k]."""
+    return _dense(lib.q5_k_linear, w, n, n, k, x, out, Q5_K_BYTES)
+
+
+def q5_k_linear_fused_gate_up_silu(w, f: int, k: int, x, out=None):
+    """h = SiLU(x . W_gate^T) * (x . W_up^T); W is GGUF Q5_K [2f][k], gate rows first."""
+    return _dense(lib.q5_k_linear_fused_gate_up_silu, w, 2 * f, f, k, x, out, Q5_K_BYTES)
 
 
 def q6_k_linear(w, n: int, k: int, x, out=None):

@@ -182,6 +182,42 @@ struct FmtQ4_K {
     }
 };
 
+// GGUF Q5_K: 176-byte super-blocks of 256 weights (four pairs each): the Q4_K header (d,
+// dmin, 12 bytes of 6-bit scales and mins), 32 bytes qh, 128 bytes of nibbles.  Pair c is
+// sub-block 2c (low nibbles of quant bytes 32c .. 32c+31) then 2c+1 (high nibbles); the
+// quant of input l of sub-block 2c + HALF gains 16 when bit 2c + HALF of qh[l] is set;
+// w = fma(q, d*sc, -dmin*m) as for Q4_K.
+struct FmtQ5_K {
+    // w[0..3]: the header, w[4..11]: qh, w[12..19]: the pair's 32 quant bytes
+    static constexpr int kDwords = 20, kLoads = 5, kMaxR = 2;
+    static __host__ __device__ size_t row_bytes(int P) { return (size_t)(P / 4) * 176; }
+    static __device__ __forceinline__ void load(const uint8_t* row, int pc, uint32_t (&w)[kDwords]) {
+        const uint8_t* sb = row + (size_t)(pc >> 2) * 176;
+        const uint8_t* src[5] = {sb, sb + 16, sb + 32, sb + 48 + 32 * (pc & 3), sb + 64 + 32 * (pc & 3)};
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+            const u32x4_a4 v = *reinterpret_cast<const u32x4_a4*>(src[i]);
+            w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+        }
+    }
+    template <int HALF>
+    static __device__ __forceinline__ void weights(const uint32_t (&w)[kDwords], int cc, float (&wf)[4], int pc) {
+        const int c = pc & 3;
+        const uint32_t sh = 8u * (uint32_t)(2 * (c & 1) + HALF);
+        const uint32_t b1 = (w[1] >> sh) & 0xFFu, b2 = (w[2] >> sh) & 0xFFu, b3 = (w[3] >> sh) & 0xFFu;
+        const uint32_t hi = 0u - (uint32_t)(c >> 1);  // sub-blocks 4..7: bit select, not a branch
+        const uint32_t sc = ((b1 & 63u) & ~hi) | (((b3 & 15u) | ((b1 >> 2) & 0x30u)) & hi);
+        const uint32_t mn = ((b2 & 63u) & ~hi) | (((b3 >> 4) | ((b2 >> 2) & 0x30u)) & hi);
+        const float ds = half_lo(w[0]) * (float)sc, dm = half_hi(w[0]) * (float)mn;
+        const uint32_t top = (w[4 + cc] >> (uint32_t)(2 * c + HALF)) & 0x01010101u;
+        const uint32_t v = ((w[12 + cc] >> (4 * HALF)) & 0x0F0F0F0Fu) | (top << 4);
+        wf[0] = __builtin_fmaf((float)(v & 0xFFu), ds, -dm);
+        wf[1] = __builtin_fmaf((float)((v >> 8) & 0xFFu), ds, -dm);
+        wf[2] = __builtin_fmaf((float)((v >> 16) & 0xFFu), ds, -dm);
+        wf[3] = __builtin_fmaf((float)(v >> 24), ds, -dm);
+    }
+};
+
 // GGUF Q6_K: 210-byte super-blocks of 256 weights (four pairs each): ql[128], qh[64],
 // int8 scales[16], d (binary16).  Pair c of a super-block lies in half t = c/2; its block
 // HALF holds the weights 128t + 32k + l (l < 32) with k = 2(c%2) + HALF: their low four
@@ -878,6 +914,11 @@ hipError_t launch_gemv_q4_k(const DeviceInfo& dev, const uint8_t* w, int64_t n_o
 hipError_t launch_gemv_q6_k(const DeviceInfo& dev, const uint8_t* w, int64_t n_out, int64_t k, bool silu_pairs,
                             const float* x, int64_t m, int64_t ldx, float* y, int64_t ldy, hipStream_t stream) {
     return launch_gemv_kq<FmtQ6_K>(dev, w, n_out, k, silu_pairs, x, m, ldx, y, ldy, stream);
+}
+
+hipError_t launch_gemv_q5_k(const DeviceInfo& dev, const uint8_t* w, int64_t n_out, int64_t k, bool silu_pairs,
+                            const float* x, int64_t m, int64_t ldx, float* y, int64_t ldy, hipStream_t stream) {
+    return launch_gemv_kq<FmtQ5_K>(dev, w, n_out, k, silu_pairs, x, m, ldx, y, ldy, stream);
 }
 
 hipError_t launch_gemv_q8(const DeviceInfo& dev, const uint8_t* w, int64_t n_out, int64_t k, bool silu_pairs,

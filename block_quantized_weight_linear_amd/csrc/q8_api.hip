@@ -199,6 +199,17 @@ q8_status q4_k_linear_fused_gate_up_silu(const void* w_gate_up_q4_k, int64_t f, 
                      ldh, stream);
 }
 
+q8_status q5_k_linear(const void* w_q5_k, int64_t n, int64_t k, const float* x, int64_t m, int64_t ldx, float* y,
+                      int64_t ldy, void* stream) {
+    return kq_common("q5_k_linear", q8k::launch_gemv_q5_k, w_q5_k, n, k, false, x, m, ldx, y, ldy, stream);
+}
+
+q8_status q5_k_linear_fused_gate_up_silu(const void* w_gate_up_q5_k, int64_t f, int64_t k, const float* x, int64_t m,
+                                         int64_t ldx, float* h, int64_t ldh, void* stream) {
+    return kq_common("q5_k_linear_fused_gate_up_silu", q8k::launch_gemv_q5_k, w_gate_up_q5_k, f, k, true, x, m, ldx, h,
+                     ldh, stream);
+}
+
 q8_status q6_k_linear(const void* w_q6_k, int64_t n, int64_t k, const float* x, int64_t m, int64_t ldx, float* y,
                       int64_t ldy, void* stream) {
     return kq_common("q6_k_linear", q8k::launch_gemv_q6_k, w_q6_k, n, k, false, x, m, ldx, y, ldy, stream);

@@ -26,9 +26,11 @@ hipError_t launch_gemv_q8(const DeviceInfo& dev, const uint8_t* w, int64_t n_out
 hipError_t launch_gemv_q4_0(const DeviceInfo& dev, const uint8_t* w, int64_t n_out, int64_t k, bool silu_pairs,
                             const float* x, int64_t m, int64_t ldx, float* y, int64_t ldy, hipStream_t stream);
 
-// GGUF Q4_K / Q6_K weights (144 / 210-byte super-blocks of 256), every m in 8-row
+// GGUF Q4_K / Q5_K / Q6_K weights (144 / 176 / 210-byte super-blocks of 256), every m in 8-row
 // launches of the float32 rows kernel.
 hipError_t launch_gemv_q4_k(const DeviceInfo& dev, const uint8_t* w, int64_t n_out, int64_t k, bool silu_pairs,
+                            const float* x, int64_t m, int64_t ldx, float* y, int64_t ldy, hipStream_t stream);
+hipError_t launch_gemv_q5_k(const DeviceInfo& dev, const uint8_t* w, int64_t n_out, int64_t k, bool silu_pairs,
                             const float* x, int64_t m, int64_t ldx, float* y, int64_t ldy, hipStream_t stream);
 hipError_t launch_gemv_q6_k(const DeviceInfo& dev, const uint8_t* w, int64_t n_out, int64_t k, bool silu_pairs,
                             const float* x, int64_t m, int64_t ldx, float* y, int64_t ldy, hipStream_t stream);

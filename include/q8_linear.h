@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define Q8_ABI_VERSION 7
+#define Q8_ABI_VERSION 8
 
 typedef enum q8_status {
     Q8_OK = 0,
@@ -125,22 +125,26 @@ q8_status q4_0_linear_fused_gate_up_silu(const void* w_gate_up_q4_0, int64_t f, 
                                          float* h, int64_t ldh, void* stream);
 
 /*
- * GGUF k-quant weights, Q4_K and Q6_K ("14. Model families and example applications",
- * section 14.1, and the DGX Spark README, Features: the engine reads Q4_K and Q6_K blocks
- * directly in its quantized GEMV, without dequantizing the model at load).  The pages name
- * the formats only; the layouts are the ggml ones, super-blocks of 256 weights along k,
- * rows of k/256 super-blocks back to back:
+ * GGUF k-quant weights, Q4_K, Q5_K and Q6_K ("14. Model families and example
+ * applications", section 14.1: Q4_K, Q5_K and Q6_K run their own packed kernels; the DGX
+ * Spark README, Features: the engine reads Q4_K and Q6_K blocks directly in its quantized
+ * GEMV, without dequantizing the model at load).  The pages name the formats only; the
+ * layouts are the ggml ones, super-blocks of 256 weights along k, rows of k/256
+ * super-blocks back to back:
  *   Q4_K, 144 bytes: binary16 d, binary16 dmin, 12 bytes holding eight 6-bit (scale, min)
  *     pairs (sub-block j < 4: bits 0..5 of bytes j and j+4; j >= 4: the low / high
  *     nibble of byte j+4 below bits 6..7 of byte j-4 / j), 128 bytes of nibbles (weight
  *     64c+i is the low nibble of byte 32c+i, weight 64c+32+i its high nibble);
  *     w = d*sc*q - dmin*m for the weight's 32-wide sub-block.
+ *   Q5_K, 176 bytes: the Q4_K header (d, dmin, 12 scale/min bytes), qh[32], then the
+ *     Q4_K nibbles; weight 64c+32s+l (s < 2) gains 16 when bit 2c+s of qh[l] is set;
+ *     w = d*sc*q - dmin*m with q in 0..31.
  *   Q6_K, 210 bytes: ql[128], qh[64], int8 scales[16], binary16 d; weight 128t+32u+l
  *     (t < 2, u < 4, l < 32) takes its low four bits from the low (u < 2) or high nibble
  *     of ql[64t + 32(u%2) + l] and its top two bits from bits 2u, 2u+1 of qh[32t + l];
  *     w = d * scales[weight/16] * (q - 32).
- *   q4_k_linear / q6_k_linear       : y[m][n] = x . W^T, W [n][k]
- *   q4_k_/q6_k_linear_fused_gate_up_silu : h = SiLU(x . W_gate^T) * (x . W_up^T), W [2f][k]
+ *   q4_k_linear / q5_k_linear / q6_k_linear : y[m][n] = x . W^T, W [n][k]
+ *   q4_k_/q5_k_/q6_k_linear_fused_gate_up_silu : h = SiLU(x . W_gate^T) * (x . W_up^T), W [2f][k]
  * Arguments, rules and errors as for q8_linear / q8_linear_fused_gate_up_silu (k a
  * positive multiple of 256, the weight base 16-byte aligned).  Every m runs the float32
  * rows kernel in 8-row launches: weights are dequantized exactly in float32 (one fma per
@@ -151,6 +155,12 @@ q8_status q4_k_linear(const void* w_q4_k, int64_t n, int64_t k,
                       const float* x, int64_t m, int64_t ldx,
                       float* y, int64_t ldy, void* stream);
 q8_status q4_k_linear_fused_gate_up_silu(const void* w_gate_up_q4_k, int64_t f, int64_t k,
+                                         const float* x, int64_t m, int64_t ldx,
+                                         float* h, int64_t ldh, void* stream);
+q8_status q5_k_linear(const void* w_q5_k, int64_t n, int64_t k,
+                      const float* x, int64_t m, int64_t ldx,
+                      float* y, int64_t ldy, void* stream);
+q8_status q5_k_linear_fused_gate_up_silu(const void* w_gate_up_q5_k, int64_t f, int64_t k,
                                          const float* x, int64_t m, int64_t ldx,
                                          float* h, int64_t ldh, void* stream);
 q8_status q6_k_linear(const void* w_q6_k, int64_t n, int64_t k,

@@ -36,14 +36,15 @@ def test_header_declares_the_four_calls():
               "q8_quantize_act", "q8_linear_q8act", "q8_linear_fused_gate_up_silu_q8act",
               "moe_route_topk_top_p", "moe_route_topk_ws", "moe_route_workspace_bytes",
               "q4_0_linear", "q4_0_linear_fused_gate_up_silu", "q8_moe_grouped_linear_noalloc",
-              "q4_k_linear", "q4_k_linear_fused_gate_up_silu", "q6_k_linear", "q6_k_linear_fused_gate_up_silu"):
+              "q4_k_linear", "q4_k_linear_fused_gate_up_silu", "q6_k_linear", "q6_k_linear_fused_gate_up_silu",
+              "q5_k_linear", "q5_k_linear_fused_gate_up_silu"):
         assert n in names, names
 
 
 def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert q8.abi_version() == 7
+    assert q8.abi_version() == 8
 
 
 def test_status_strings():
@@ -55,6 +56,7 @@ def test_status_strings():
 LINEAR_FORMATS = {"q8_0": ("q8_linear", "q8_linear_fused_gate_up_silu"),
                   "q4_0": ("q4_0_linear", "q4_0_linear_fused_gate_up_silu"),
                   "q4_k": ("q4_k_linear", "q4_k_linear_fused_gate_up_silu"),
+                  "q5_k": ("q5_k_linear", "q5_k_linear_fused_gate_up_silu"),
                   "q6_k": ("q6_k_linear", "q6_k_linear_fused_gate_up_silu")}
 
 

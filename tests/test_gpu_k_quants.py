@@ -1,8 +1,9 @@
-"""GPU parity of the GGUF k-quant linears (q4_k_linear, q6_k_linear and their fused
+"""GPU parity of the GGUF k-quant linears (q4_k_linear, q5_k_linear, q6_k_linear and their fused
 gate_up + SiLU forms) against the CPU oracle: small shapes element by element (several
 tiles, ragged tiles, row counts that are not a launch size), the hand-derived
 super-blocks, exact-arithmetic inputs bit for bit, a Qwen3-8B FFN in the Q4_K_M mix
-(gate_up Q4_K, down Q6_K) at its real size with every output checked, long rows, and
+(gate_up Q4_K, down Q6_K) and its gate_up in Q5_K at their real sizes with every output
+checked, long rows, and
 batch invariance (every row count runs the same kernel class, so a row is bit-identical
 whatever m is)."""
 
@@ -18,8 +19,9 @@ from gpu_util import assert_close, fused_ref_full, linear_ref_full, say, to_dev,
 pytestmark = pytest.mark.gpu
 
 # bytes per 32 weights (the chunked oracle helpers slice rows with it)
-PER32 = {"q4_k": 144 / 8, "q6_k": 210 / 8}
-SB = {"q4_k": 144, "q6_k": 210}
+PER32 = {"q4_k": 144 / 8, "q5_k": 176 / 8, "q6_k": 210 / 8}
+SB = {"q4_k": 144, "q5_k": 176, "q6_k": 210}
+FORMATS = ["q4_k", "q5_k", "q6_k"]
 
 
 @pytest.fixture(scope="module")
@@ -30,7 +32,7 @@ def q8():
 
 
 def weight(fmt, seed, n, k, exact=False):
-    gen = wl.q4_k_weight if fmt == "q4_k" else wl.q6_k_weight
+    gen = {"q4_k": wl.q4_k_weight, "q5_k": wl.q5_k_weight, "q6_k": wl.q6_k_weight}[fmt]
     return gen(seed, n, k, exact=exact)[0]
 
 
@@ -45,7 +47,7 @@ def refs(fmt):
 SMALL = [(1, 256), (3, 256), (37, 512), (257, 768), (1000, 1024), (513, 3072), (129, 3840), (77, 12288), (64, 2048)]
 
 
-@pytest.mark.parametrize("fmt", ["q4_k", "q6_k"])
+@pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("n,k", SMALL)
 @pytest.mark.parametrize("m", [1, 2, 3, 8, 9, 13, 16, 17])
 def test_k_quant_linear_small_vs_oracle(q8, fmt, n, k, m):
@@ -59,7 +61,7 @@ def test_k_quant_linear_small_vs_oracle(q8, fmt, n, k, m):
     assert_close(y, ref(wb, n, k, x), f"{fmt} n={n} k={k} m={m}")
 
 
-@pytest.mark.parametrize("fmt", ["q4_k", "q6_k"])
+@pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("f,k", [(1, 256), (5, 512), (300, 1024), (129, 3840), (64, 768)])
 @pytest.mark.parametrize("m", [1, 4, 8, 11])
 def test_k_quant_fused_small_vs_oracle(q8, fmt, f, k, m):
@@ -79,7 +81,7 @@ def test_k_quant_hand_super_blocks(q8):
     from golden_io import load_k_quant_cases
     lib, torch, dev = q8
     cases = load_k_quant_cases()
-    for fmt in ("q4_k", "q6_k"):
+    for fmt in FORMATS:
         mine = [c for c in cases if c["format"] == fmt]
         assert mine
         raw = np.frombuffer(b"".join(c["bytes"] for c in mine), dtype=np.uint8)
@@ -93,7 +95,7 @@ def test_k_quant_hand_super_blocks(q8):
         assert np.array_equal(y.astype(np.float64), x.astype(np.float64) @ wh.T), fmt
 
 
-@pytest.mark.parametrize("fmt", ["q4_k", "q6_k"])
+@pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("n,k,m", [(4096, 1024, 1), (6144, 3840, 8), (999, 256, 33), (2048, 4096, 3),
                                    (16384, 1024, 1)])
 def test_k_quant_exact_arithmetic_bit_identical(q8, fmt, n, k, m):
@@ -110,7 +112,7 @@ def test_k_quant_exact_arithmetic_bit_identical(q8, fmt, n, k, m):
     assert np.array_equal(y.astype(np.float64), ref(wb, n, k, x))
 
 
-@pytest.mark.parametrize("fmt", ["q4_k", "q6_k"])
+@pytest.mark.parametrize("fmt", FORMATS)
 def test_k_quant_fused_exact_gate_up(q8, fmt):
     """Exact inputs through the fused form: the gate and up sums are exact, so the output
     is SiLU(g) * u of exact g, u, within the float32 epilogue's rounding."""
@@ -133,12 +135,18 @@ def test_k_quant_qwen3_8b_ffn_full(q8):
     wg = weight("q4_k", 3800, 2 * ff, hid)
     wgd = to_dev(wg, dev)
     downs = {fmt: weight(fmt, 3801, hid, ff) for fmt in ("q6_k", "q4_k")}
+    wg5 = weight("q5_k", 3806, 2 * ff, hid)
+    wg5d = to_dev(wg5, dev)
     for m in (1, 8):
         x = wl.activations(3802 + m, m, hid)
         say(f"qwen3-8b q4_k gate_up m={m}")
         h = lib.q4_k_linear_fused_gate_up_silu(wgd, ff, hid, to_dev(x, dev)).cpu().numpy()
         ref = fused_ref_full(wg, ff, hid, x, ref=oracle.fused_gate_up_silu_q4_k_ref, block_bytes=PER32["q4_k"])
         assert_close(h, ref, f"gate_up m={m}")
+        say(f"qwen3-8b q5_k gate_up m={m}")
+        h5 = lib.q5_k_linear_fused_gate_up_silu(wg5d, ff, hid, to_dev(x, dev)).cpu().numpy()
+        ref = fused_ref_full(wg5, ff, hid, x, ref=oracle.fused_gate_up_silu_q5_k_ref, block_bytes=PER32["q5_k"])
+        assert_close(h5, ref, f"q5_k gate_up m={m}")
         xh = wl.activations(3804 + m, m, ff)
         for fmt, wd in downs.items():
             say(f"qwen3-8b {fmt} down m={m}")
@@ -149,7 +157,7 @@ def test_k_quant_qwen3_8b_ffn_full(q8):
             assert_close(y, ref, f"{fmt} down m={m}")
 
 
-@pytest.mark.parametrize("fmt", ["q4_k", "q6_k"])
+@pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("n,k", [(4096, 1024), (777, 3840), (12288, 4096)])
 def test_k_quant_batch_invariance(q8, fmt, n, k):
     """Run to run identical, and every row of any call (one row included) bit-identical
@@ -171,7 +179,7 @@ def test_k_quant_batch_invariance(q8, fmt, n, k):
         assert np.array_equal(fused(wd, f, k, xd[r0:r1].contiguous()).cpu().numpy(), h20[r0:r1]), (r0, r1)
 
 
-@pytest.mark.parametrize("fmt", ["q4_k", "q6_k"])
+@pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("n,k,m", [(64, 32768, 1), (70, 65536, 3)])
 def test_k_quant_long_rows(q8, fmt, n, k, m):
     lib, torch, dev = q8
@@ -184,7 +192,7 @@ def test_k_quant_long_rows(q8, fmt, n, k, m):
     assert_close(y, ref(wb, n, k, x), f"{fmt} long rows k={k} m={m}")
 
 
-@pytest.mark.parametrize("fmt", ["q4_k", "q6_k"])
+@pytest.mark.parametrize("fmt", FORMATS)
 def test_k_quant_binding_rejects_short_weight(q8, fmt):
     lib, torch, dev = q8
     lin, _ = fns(lib, fmt)
