@@ -327,7 +327,8 @@ def bench_linear(torch, dev, q8, name, n, k, m, fused, reps, min_bytes=600e6, fm
     them to exceed the 256 MB Infinity Cache twice).  fmt: "q8_0", "q4_0", "q4_k" or
     "q6_k" weights."""
     import workloads as wl
-    gen = {"q8_0": wl.q8_weight, "q4_0": wl.q4_0_weight, "q4_k": wl.q4_k_weight, "q6_k": wl.q6_k_weight}[fmt]
+    gen = {"q8_0": wl.q8_weight, "q4_0": wl.q4_0_weight, "q4_k": wl.q4_k_weight, "q5_k": wl.q5_k_weight,
+           "q6_k": wl.q6_k_weight}[fmt]
     wb = gen(31, n, k)[0]
     plain = getattr(q8, "q8_linear" if fmt == "q8_0" else f"{fmt}_linear")
     fused_fn = getattr(q8, "q8_linear_fused_gate_up_silu" if fmt == "q8_0" else f"{fmt}_linear_fused_gate_up_silu")

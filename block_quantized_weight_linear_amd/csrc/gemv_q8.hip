@@ -45,8 +45,14 @@ struct XArr {
 // kernel) adds one pair of R rows against the lane's 64 activations x (float4 c holds inputs
 // 4c .. 4c+3 of the pair) and their per-block sums sx.
 struct FmtQ8_0 {  // 68 bytes: [d0 | 32 q] [d1 | 32 q]
-    static constexpr int kPairBytes = 68, kDwords = 17, kLoads = 5, kMaxR = 4;
+    static constexpr int kPairBytes = 68, kDwords = 17, kLoads = 5, kMaxR = 4, kSums = 2;
     static __host__ __device__ size_t row_bytes(int P) { return (size_t)P * kPairBytes; }
+    // pair j of a row's bytes in LDS (the one-row kernel)
+    static __device__ __forceinline__ void lds_load(const uint8_t* item_row, int j, uint32_t (&w)[kDwords]) {
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(item_row + kPairBytes * j);
+#pragma unroll
+        for (int q = 0; q < kDwords; ++q) w[q] = src[q];
+    }
     static __device__ __forceinline__ void load(const uint8_t* p, uint32_t (&w)[kDwords]) { load_pair(p, w); }
     static __device__ __forceinline__ void load(const uint8_t* row, int pc, uint32_t (&w)[kDwords]) {
         load_pair(row + (size_t)kPairBytes * pc, w);
@@ -71,15 +77,20 @@ struct FmtQ8_0 {  // 68 bytes: [d0 | 32 q] [d1 | 32 q]
     // per block: t = sum q*x, then acc = fma(d, t, acc) (gemv_core.h mac_pair)
     template <int R>
     static __device__ __forceinline__ void mac_row(const uint32_t (&w)[R][kDwords], const float4 (&x)[1][16],
-                                                   const float (&)[2], float (&acc)[R][1]);
+                                                   const float (&)[2], float (&acc)[R][1], int);
 };
 
 // GGUF Q4_0: 36 bytes a pair, [d0 | 16 bytes] [d1 | 16 bytes]; weight j < 16 of a block is
 // the low nibble of its byte j, weight j + 16 the high nibble; w = d * (nibble - 8), exact
 // in float32 (a 4-bit integer times an 11-bit scale).
 struct FmtQ4_0 {
-    static constexpr int kPairBytes = 36, kDwords = 9, kLoads = 3, kMaxR = 4;
+    static constexpr int kPairBytes = 36, kDwords = 9, kLoads = 3, kMaxR = 4, kSums = 2;
     static __host__ __device__ size_t row_bytes(int P) { return (size_t)P * kPairBytes; }
+    static __device__ __forceinline__ void lds_load(const uint8_t* item_row, int j, uint32_t (&w)[kDwords]) {
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(item_row + kPairBytes * j);
+#pragma unroll
+        for (int q = 0; q < kDwords; ++q) w[q] = src[q];
+    }
     static __device__ __forceinline__ void load(const uint8_t* row, int pc, uint32_t (&w)[kDwords]) {
         load(row + (size_t)kPairBytes * pc, w);
     }
@@ -114,7 +125,7 @@ struct FmtQ4_0 {
     // sum (nibble - 8)*d*x with the offset carried by the block's activation sum sx
     template <int R>
     static __device__ __forceinline__ void mac_row(const uint32_t (&w)[R][kDwords], const float4 (&x)[1][16],
-                                                   const float (&sx)[2], float (&acc)[R][1]) {
+                                                   const float (&sx)[2], float (&acc)[R][1], int) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
 #pragma unroll
@@ -143,6 +154,31 @@ struct FmtQ4_0 {
     }
 };
 
+// d*sc and dmin*m of sub-block 2c + HALF from a Q4_K / Q5_K header (w0: d | dmin, w1..w3: the
+// 12 scale bytes).  Sub-blocks 0..3: the low six bits of bytes j and j + 4; 4..7: a nibble of
+// byte j + 4 below the top two bits of byte j - 4 (scale) or j (min).  Lanes of a wave hold
+// different pairs, so the choice is a bit select, not a branch.
+template <int HALF>
+__device__ __forceinline__ void kq_scale_min(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, int c, float& ds,
+                                             float& dm) {
+    const uint32_t sh = 8u * (uint32_t)(2 * (c & 1) + HALF);
+    const uint32_t b1 = (w1 >> sh) & 0xFFu, b2 = (w2 >> sh) & 0xFFu, b3 = (w3 >> sh) & 0xFFu;
+    const uint32_t hi = 0u - (uint32_t)(c >> 1);  // all ones for sub-blocks 4..7
+    const uint32_t sc = ((b1 & 63u) & ~hi) | (((b3 & 15u) | ((b1 >> 2) & 0x30u)) & hi);
+    const uint32_t mn = ((b2 & 63u) & ~hi) | (((b3 >> 4) | ((b2 >> 2) & 0x30u)) & hi);
+    ds = half_lo(w0) * (float)sc;
+    dm = half_hi(w0) * (float)mn;
+}
+
+// acc += d*sc * sum(q*x) - dmin*m * sum(x) over the 32 inputs of one sub-block: t is a chain
+// of fmas over the quants (integers 0..31, exact), sx the sub-block's activation sum
+__device__ __forceinline__ float kq_chain4(uint32_t v, float4 xv, float t) {
+    t = __builtin_fmaf((float)(v & 0xFFu), xv.x, t);
+    t = __builtin_fmaf((float)((v >> 8) & 0xFFu), xv.y, t);
+    t = __builtin_fmaf((float)((v >> 16) & 0xFFu), xv.z, t);
+    return __builtin_fmaf((float)(v >> 24), xv.w, t);
+}
+
 // GGUF Q4_K: 144-byte super-blocks of 256 weights (four pairs each): d and dmin
 // (binary16), 12 bytes of packed 6-bit sub-block scales and mins, 128 bytes of nibbles.
 // Pair c of a super-block (inputs 64c .. 64c+63) is sub-block 2c (the low nibbles of quant
@@ -150,8 +186,38 @@ struct FmtQ4_0 {
 // computed as fma(q, d*sc, -dmin*m) (the two products are exact in float32).
 struct FmtQ4_K {
     // w[0]: d | dmin, w[1..3]: the scale bytes, w[4..11]: the pair's 32 quant bytes
-    static constexpr int kDwords = 12, kLoads = 3, kMaxR = 2;
+    static constexpr int kDwords = 12, kLoads = 3, kMaxR = 2, kSums = 2;
     static __host__ __device__ size_t row_bytes(int P) { return (size_t)(P / 4) * 144; }
+    // pair j of a row's bytes in LDS (the one-row kernel; rows start on 16-byte boundaries)
+    static __device__ __forceinline__ void lds_load(const uint8_t* item_row, int j, uint32_t (&w)[kDwords]) {
+        const uint8_t* sb = item_row + 144 * (j >> 2);
+        const uint32_t* h = reinterpret_cast<const uint32_t*>(sb);
+        const uint32_t* q = reinterpret_cast<const uint32_t*>(sb + 16 + 32 * (j & 3));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = h[i];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[4 + i] = q[i];
+    }
+    // per sub-block: t = sum nibble*x, acc = fma(d*sc, t, acc), acc = fma(-dmin*m, sx, acc)
+    template <int R>
+    static __device__ __forceinline__ void mac_row(const uint32_t (&w)[R][kDwords], const float4 (&x)[1][16],
+                                                   const float (&sx)[2], float (&acc)[R][1], int p) {
+        const int c = p & 3;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float ds[2], dm[2];
+            kq_scale_min<0>(w[r][0], w[r][1], w[r][2], w[r][3], c, ds[0], dm[0]);
+            kq_scale_min<1>(w[r][0], w[r][1], w[r][2], w[r][3], c, ds[1], dm[1]);
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+                float t = 0.0f;
+#pragma unroll
+                for (int cc = 0; cc < 8; ++cc) t = kq_chain4((w[r][4 + cc] >> (4 * hb)) & 0x0F0F0F0Fu, x[0][8 * hb + cc], t);
+                acc[r][0] = __builtin_fmaf(ds[hb], t, acc[r][0]);
+                acc[r][0] = __builtin_fmaf(-dm[hb], sx[hb], acc[r][0]);
+            }
+        }
+    }
     static __device__ __forceinline__ void load(const uint8_t* row, int pc, uint32_t (&w)[kDwords]) {
         const uint8_t* sb = row + (size_t)(pc >> 2) * 144;
         const u32x4_a4 h = *reinterpret_cast<const u32x4_a4*>(sb);
@@ -189,8 +255,40 @@ struct FmtQ4_K {
 // w = fma(q, d*sc, -dmin*m) as for Q4_K.
 struct FmtQ5_K {
     // w[0..3]: the header, w[4..11]: qh, w[12..19]: the pair's 32 quant bytes
-    static constexpr int kDwords = 20, kLoads = 5, kMaxR = 2;
+    static constexpr int kDwords = 20, kLoads = 5, kMaxR = 2, kSums = 2;
     static __host__ __device__ size_t row_bytes(int P) { return (size_t)(P / 4) * 176; }
+    static __device__ __forceinline__ void lds_load(const uint8_t* item_row, int j, uint32_t (&w)[kDwords]) {
+        const uint8_t* sb = item_row + 176 * (j >> 2);
+        const uint32_t* h = reinterpret_cast<const uint32_t*>(sb);  // header and qh: dwords 0..11
+        const uint32_t* q = reinterpret_cast<const uint32_t*>(sb + 48 + 32 * (j & 3));
+#pragma unroll
+        for (int i = 0; i < 12; ++i) w[i] = h[i];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[12 + i] = q[i];
+    }
+    template <int R>
+    static __device__ __forceinline__ void mac_row(const uint32_t (&w)[R][kDwords], const float4 (&x)[1][16],
+                                                   const float (&sx)[2], float (&acc)[R][1], int p) {
+        const int c = p & 3;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float ds[2], dm[2];
+            kq_scale_min<0>(w[r][0], w[r][1], w[r][2], w[r][3], c, ds[0], dm[0]);
+            kq_scale_min<1>(w[r][0], w[r][1], w[r][2], w[r][3], c, ds[1], dm[1]);
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+                float t = 0.0f;
+#pragma unroll
+                for (int cc = 0; cc < 8; ++cc) {
+                    const uint32_t top = (w[r][4 + cc] >> (uint32_t)(2 * c + hb)) & 0x01010101u;
+                    const uint32_t v = ((w[r][12 + cc] >> (4 * hb)) & 0x0F0F0F0Fu) | (top << 4);
+                    t = kq_chain4(v, x[0][8 * hb + cc], t);
+                }
+                acc[r][0] = __builtin_fmaf(ds[hb], t, acc[r][0]);
+                acc[r][0] = __builtin_fmaf(-dm[hb], sx[hb], acc[r][0]);
+            }
+        }
+    }
     static __device__ __forceinline__ void load(const uint8_t* row, int pc, uint32_t (&w)[kDwords]) {
         const uint8_t* sb = row + (size_t)(pc >> 2) * 176;
         const uint8_t* src[5] = {sb, sb + 16, sb + 32, sb + 48 + 32 * (pc & 3), sb + 64 + 32 * (pc & 3)};
@@ -230,8 +328,57 @@ struct FmtQ5_K {
 struct FmtQ6_K {
     // w[0..16]: ql of half t, w[17..25]: qh of half t, w[26..27]: the pair's four scale
     // bytes, w[28]: d, w[29]: the realignment (0 or 2 bytes)
-    static constexpr int kDwords = 30, kLoads = 11, kMaxR = 2;
+    static constexpr int kDwords = 30, kLoads = 11, kMaxR = 2, kSums = 4;
     static __host__ __device__ size_t row_bytes(int P) { return (size_t)(P / 4) * 210; }
+    // pair j of a row's bytes in LDS, realigned as in load (rows start on 16-byte boundaries;
+    // the one-row kernel takes Q6_K rows of a multiple of 8 super-blocks)
+    static __device__ __forceinline__ void lds_load(const uint8_t* item_row, int j, uint32_t (&w)[kDwords]) {
+        const uint8_t* sb = item_row + 210 * (j >> 2);
+        const uint32_t shift = (uint32_t)(uintptr_t)sb & 3u;  // 0 or 2
+        const int t = (j >> 1) & 1;
+        const uint32_t* ql = reinterpret_cast<const uint32_t*>(sb + 64 * t - shift);
+        const uint32_t* qh = reinterpret_cast<const uint32_t*>(sb + 128 + 32 * t - shift);
+        const uint32_t* scl = reinterpret_cast<const uint32_t*>(sb + 192 + 8 * t + 4 * (j & 1) - shift);
+#pragma unroll
+        for (int i = 0; i < 17; ++i) w[i] = ql[i];
+#pragma unroll
+        for (int i = 0; i < 9; ++i) w[17 + i] = qh[i];
+        w[26] = scl[0];
+        w[27] = scl[1];  // used only when realigning (then it ends at byte 209); else it may reach
+                         // 2 bytes into the next super-block of the LDS slot, unused
+        w[28] = *reinterpret_cast<const uint16_t*>(sb + 208);
+        w[29] = shift;
+    }
+    // per group of 16 weights (scale s): t = sum q*x, then acc = fma(d*s, t - 32*sx, acc)
+    template <int R>
+    static __device__ __forceinline__ void mac_row(const uint32_t (&w)[R][kDwords], const float4 (&x)[1][16],
+                                                   const float (&sx)[4], float (&acc)[R][1], int p) {
+        const int hi_nib = p & 1;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint32_t shift = w[r][29];
+            const float d = half_lo(w[r][28]);
+            const uint32_t scw = __builtin_amdgcn_alignbyte(w[r][27], w[r][26], shift);
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+                const int k = 2 * hi_nib + hb;
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    float t = 0.0f;
+#pragma unroll
+                    for (int cc = 4 * g; cc < 4 * g + 4; ++cc) {
+                        const uint32_t qlw = __builtin_amdgcn_alignbyte(w[r][8 * hb + cc + 1], w[r][8 * hb + cc], shift);
+                        const uint32_t qhw = __builtin_amdgcn_alignbyte(w[r][17 + cc + 1], w[r][17 + cc], shift);
+                        const uint32_t q6 =
+                            ((qlw >> (4 * hi_nib)) & 0x0F0F0F0Fu) | (((qhw >> (2 * k)) & 0x03030303u) << 4);
+                        t = kq_chain4(q6, x[0][8 * hb + cc], t);
+                    }
+                    const float ds = d * (float)(int)(int8_t)(scw >> (8 * (2 * hb + g)));
+                    acc[r][0] = __builtin_fmaf(ds, t - 32.0f * sx[2 * hb + g], acc[r][0]);
+                }
+            }
+        }
+    }
     static __device__ __forceinline__ void load(const uint8_t* row, int pc, uint32_t (&w)[kDwords]) {
         const uint8_t* sb = row + (size_t)(pc >> 2) * 210;
         const uint32_t shift = (uint32_t)(uintptr_t)sb & 3u;  // 0 or 2
@@ -277,7 +424,7 @@ struct FmtQ6_K {
 
 template <int R>
 __device__ __forceinline__ void FmtQ8_0::mac_row(const uint32_t (&w)[R][kDwords], const float4 (&x)[1][16],
-                                                 const float (&)[2], float (&acc)[R][1]) {
+                                                 const float (&)[2], float (&acc)[R][1], int) {
     mac_pair<1, R>(w, XArr<1>{x}, 0, acc);
 }
 
@@ -321,8 +468,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_one_row_kernel(const uint8_t* __
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int j = lane & (S - 1);
     const int g = lane >> log2S;
-    constexpr int PB = Fmt::kPairBytes;
-    const size_t row_bytes = (size_t)P * PB;
+    const size_t row_bytes = Fmt::row_bytes(P);
     const int total = ((n_out + G - 1) / G) * NR;  // items: (row group, round)
     const int wid = blockIdx.x * NW + wv;
     const int nw = gridDim.x * NW;
@@ -347,14 +493,14 @@ __global__ __launch_bounds__(64 * NW) void gemv_one_row_kernel(const uint8_t* __
         int len;
         if (G > 1) {  // G whole rows (P <= S): the rows that exist
             const int rows = (n_out - row0) < G ? (n_out - row0) : G;
-            len = rows * P * PB;
+            len = rows * (int)row_bytes;
         } else {  // pairs S*i .. of one row
             const int pairs = (P - S * i) < S ? (P - S * i) : S;
-            len = pairs * PB;
+            len = (int)Fmt::row_bytes(pairs);
         }
 #pragma unroll
         for (int r = 0; r < R; ++r)
-            lds_copy_4352<NT>(w + (size_t)(row0 + r * n_out) * row_bytes + (size_t)PB * S * i, len,
+            lds_copy_4352<NT>(w + (size_t)(row0 + r * n_out) * row_bytes + Fmt::row_bytes(S * i), len,
                           ring_lds + (slot * R + r) * kLdsItemBytes, lane);
     };
 
@@ -389,15 +535,17 @@ __global__ __launch_bounds__(64 * NW) void gemv_one_row_kernel(const uint8_t* __
             xr[i][0][c] = *reinterpret_cast<const float4*>(smem + kXRow * pc + 16 * ((c + pc) & 15));
     }
     // per-block activation sums of the lane's pairs (used by formats with an offset)
-    float sx[NR][2];
+    // (per group of 64 / kSums inputs: 2 groups of 32, or 4 of 16 for Q6_K's scale groups)
+    constexpr int kS = Fmt::kSums, kGroupF4 = 16 / kS;
+    float sx[NR][kS];
 #pragma unroll
     for (int i = 0; i < NR; ++i)
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
+        for (int hb = 0; hb < kS; ++hb) {
             float a = 0.0f;
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const float4 v = xr[i][0][8 * hb + c];
+            for (int c = 0; c < kGroupF4; ++c) {
+                const float4 v = xr[i][0][kGroupF4 * hb + c];
                 a += v.x;
                 a += v.y;
                 a += v.z;
@@ -442,17 +590,13 @@ __global__ __launch_bounds__(64 * NW) void gemv_one_row_kernel(const uint8_t* __
             item_of(itl, rg, ii);
             const int n = rg * G + g;
             const int nc = n < n_out ? n : n_out - 1;  // a lane past the matrix: the last row
-            const int lds_off = (G > 1 ? (nc - rg * G) * P * PB : 0) + PB * j;
+            const int lds_off = G > 1 ? (nc - rg * G) * (int)row_bytes : 0;  // the lane's row in the item
             uint32_t wr[R][Fmt::kDwords];
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const uint32_t* src = reinterpret_cast<const uint32_t*>(ring + (slot * R + r) * kLdsItemBytes + lds_off);
-#pragma unroll
-                for (int q = 0; q < Fmt::kDwords; ++q) wr[r][q] = src[q];
-            }
+            for (int r = 0; r < R; ++r) Fmt::lds_load(ring + (slot * R + r) * kLdsItemBytes + lds_off, j, wr[r]);
             wait_lgkmcnt_mem<0>();
             if (itl + D < ipw) issue(itl + D, slot);  // refill the slot just read
-            if (j + S * i < P) Fmt::template mac_row<R>(wr, xr[i], sx[i], acc);
+            if (j + S * i < P) Fmt::template mac_row<R>(wr, xr[i], sx[i], acc, j + S * i);
             if constexpr (i == NR - 1) {
                 for (int off = S >> 1; off >= 1; off >>= 1) {
 #pragma unroll
@@ -889,12 +1033,33 @@ hipError_t launch_kq_m(const DeviceInfo& dev, const uint8_t* w, int n_out, int P
     }
 }
 
-// GGUF k-quant weights (Q4_K, Q6_K): every row count on the float32 rows kernel in
-// 8-row launches.
+// One activation row of a k-quant matrix runs the one-row kernel for rows of at most three
+// rounds of 64 pairs (K <= 12288; fused gate_up: two, K <= 8192, as three spill registers),
+// Q6_K for at most two rounds of rows of a multiple of 8 super-blocks (16-byte aligned rows
+// for the direct copies).  Its items carry half the bytes of Q8_0's for more VALU work per
+// weight (nibble extraction, scale decode), so it is bound by the arithmetic, not by HBM:
+// measured on the Qwen3-8B shapes, 8B gate_up 24576x4096 at M = 1: Q4_K 21.1 -> 19.4 us, Q6_K
+// 31.5 -> 23.6 us against the rows kernel; down 4096x12288: Q4_K 12.4 -> 11.9 us, Q6_K 15.7 ->
+// 17.0 us (so three-round Q6_K rows stay on the rows kernel).
+template <class Fmt>
+bool kq_one_row(int64_t k, bool silu_pairs) {
+    if constexpr (std::is_same<Fmt, FmtQ6_K>::value) return k <= 8192 && k % 2048 == 0;
+    return k <= (silu_pairs ? 8192 : 12288);  // three rounds of the fused form spill
+}
+
+// GGUF k-quant weights (Q4_K, Q5_K, Q6_K): one row as above, every other row count on the
+// float32 rows kernel in 8-row launches.
 template <class Fmt>
 hipError_t launch_gemv_kq(const DeviceInfo& dev, const uint8_t* w, int64_t n_out, int64_t k, bool silu_pairs,
                           const float* x, int64_t m, int64_t ldx, float* y, int64_t ldy, hipStream_t stream) {
     const int P = (int)(k / 64);
+    if (m == 1 && kq_one_row<Fmt>(k, silu_pairs)) {
+        hipError_t e = hipSuccess;
+        const bool done = silu_pairs
+                              ? try_one_row<Fmt, 2>(dev, w, (int)n_out, P, slots_log2(P), x, y, stream, &e)
+                              : try_one_row<Fmt, 1>(dev, w, (int)n_out, P, slots_log2(P), x, y, stream, &e);
+        if (done) return e;
+    }
     for (int64_t m0 = 0; m0 < m; m0 += 8) {
         const int mm = (int)((m - m0) < 8 ? (m - m0) : 8);
         const float* xc = x + m0 * ldx;

@@ -146,10 +146,14 @@ q8_status q4_0_linear_fused_gate_up_silu(const void* w_gate_up_q4_0, int64_t f, 
  *   q4_k_linear / q5_k_linear / q6_k_linear : y[m][n] = x . W^T, W [n][k]
  *   q4_k_/q5_k_/q6_k_linear_fused_gate_up_silu : h = SiLU(x . W_gate^T) * (x . W_up^T), W [2f][k]
  * Arguments, rules and errors as for q8_linear / q8_linear_fused_gate_up_silu (k a
- * positive multiple of 256, the weight base 16-byte aligned).  Every m runs the float32
- * rows kernel in 8-row launches: weights are dequantized exactly in float32 (one fma per
- * weight), one fma per weight and row, and the per-output summation order depends only
- * on k, so a row's result is bit-identical whatever m is.
+ * positive multiple of 256, the weight base 16-byte aligned).  Two or more rows run the
+ * float32 rows kernel in 8-row launches: weights are dequantized exactly in float32 (one
+ * fma per weight), one fma per weight and row, and the per-output summation order depends
+ * only on k, so those rows are bit-identical whatever m is.  One row runs the one-row
+ * kernel when k <= 12288 (fused: k <= 8192; Q6_K: k <= 8192 and a multiple of 2048):
+ * per 32-wide sub-block (Q6_K: 16-wide group) t = sum q*x, then acc += d*sc*t - dmin*m*sum x
+ * (Q6_K: acc += d*s*(t - 32*sum x)), which agrees with the multi-row results to float32
+ * reassociation; other one-row calls run the rows kernel.
  */
 q8_status q4_k_linear(const void* w_q4_k, int64_t n, int64_t k,
                       const float* x, int64_t m, int64_t ldx,

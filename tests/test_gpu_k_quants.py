@@ -4,8 +4,8 @@ tiles, ragged tiles, row counts that are not a launch size), the hand-derived
 super-blocks, exact-arithmetic inputs bit for bit, a Qwen3-8B FFN in the Q4_K_M mix
 (gate_up Q4_K, down Q6_K) and its gate_up in Q5_K at their real sizes with every output
 checked, long rows, and
-batch invariance (every row count runs the same kernel class, so a row is bit-identical
-whatever m is)."""
+batch invariance (rows of calls with two or more activation rows are bit-identical; one
+row runs the one-row kernel where it applies and agrees to float32 reassociation)."""
 
 from __future__ import annotations
 
@@ -158,25 +158,37 @@ def test_k_quant_qwen3_8b_ffn_full(q8):
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
-@pytest.mark.parametrize("n,k", [(4096, 1024), (777, 3840), (12288, 4096)])
+@pytest.mark.parametrize("n,k", [(4096, 1024), (777, 3840), (12288, 4096), (4096, 12288)])
 def test_k_quant_batch_invariance(q8, fmt, n, k):
-    """Run to run identical, and every row of any call (one row included) bit-identical
-    to the same row of any other call: all row counts run the rows kernel, whose
-    per-output summation order depends only on K."""
+    """Run to run identical, and every row of a call with two or more activation rows
+    bit-identical to the same row of any other such call (the rows kernel's per-output
+    order depends only on K).  A one-row call runs the one-row kernel (per-sub-block chains,
+    the min / offset terms carried by the activation sums) where it applies, so there rows
+    agree to float32 reassociation; fused: the same."""
     lib, torch, dev = q8
     lin, fused = fns(lib, fmt)
+    ref_fn, fref = refs(fmt)
     wb = weight(fmt, 3900, n, k)
     wd = to_dev(wb, dev)
     x = wl.activations(3901, 20, k)
     xd = to_dev(x, dev)
     y20 = lin(wd, n, k, xd).cpu().numpy()
     assert np.array_equal(y20, lin(wd, n, k, xd).cpu().numpy())
-    for r0, r1 in ((3, 5), (0, 5), (7, 19), (4, 5), (19, 20)):
+    for r0, r1 in ((3, 5), (0, 5), (7, 19), (18, 20)):
         assert np.array_equal(lin(wd, n, k, xd[r0:r1].contiguous()).cpu().numpy(), y20[r0:r1]), (r0, r1)
+    ref = ref_fn(wb, n, k, x[:3])
+    for r in (0, 1, 2):
+        y1 = lin(wd, n, k, xd[r:r + 1].contiguous()).cpu().numpy()
+        assert np.array_equal(y1, lin(wd, n, k, xd[r:r + 1].contiguous()).cpu().numpy())
+        drift = np.max(np.abs(y1[0] - y20[r])) / np.max(np.abs(ref[r]))
+        assert drift <= 1e-5, drift
     f = n // 2
     h20 = fused(wd, f, k, xd).cpu().numpy()
-    for r0, r1 in ((0, 4), (5, 6), (9, 17)):
+    for r0, r1 in ((0, 4), (9, 17)):
         assert np.array_equal(fused(wd, f, k, xd[r0:r1].contiguous()).cpu().numpy(), h20[r0:r1]), (r0, r1)
+    h1 = fused(wd, f, k, xd[5:6].contiguous()).cpu().numpy()
+    href = fref(wb[:2 * f * (k // 256) * SB[fmt]], f, k, x[5:6])  # the 2f rows the fused call reads
+    assert np.max(np.abs(h1[0] - h20[5])) / np.max(np.abs(href)) <= 1e-5
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
