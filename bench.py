@@ -452,11 +452,12 @@ def bench_moe_prefill(torch, dev, q8, tokens, reps):
 PROFILE_LINEARS = {"qkv": (6144, 4096, False), "gate_up": (24576, 4096, True), "down": (4096, 12288, False)}
 
 
-def kernel_driver(which, m, q8act):
+def kernel_driver(which, m, q8act, fmt="q8_0"):
     """Short launch sequence for rocprofv3 counter and trace runs: a plain 256 MiB
     device-to-device copy (the calibration dispatch for FETCH_SIZE / WRITE_SIZE), then one
-    Qwen3-8B linear at m rows on 12 distinct resident weight copies (each launch streams
-    its weights from HBM), or with which = "moe" the Qwen3-30B-A3B MoE layer at m tokens."""
+    Qwen3-8B linear at m rows with fmt weights ("q8_0", "q4_0", "q4_k", "q5_k", "q6_k") on
+    12 distinct resident weight copies (each launch streams its weights from HBM), or with
+    which = "moe" the Qwen3-30B-A3B MoE layer at m tokens."""
     import torch
 
     import block_quantized_weight_linear_amd as q8
@@ -487,8 +488,11 @@ def kernel_driver(which, m, q8act):
         log(f"kernel driver: moe tokens={m} done")
         return
     n, k, fused = PROFILE_LINEARS[which]
-    wb, _, _ = wl.q8_weight(1, n, k)
-    base = torch.from_numpy(wb).to(dev)
+    gen = {"q8_0": wl.q8_weight, "q4_0": wl.q4_0_weight, "q4_k": wl.q4_k_weight, "q5_k": wl.q5_k_weight,
+           "q6_k": wl.q6_k_weight}[fmt]
+    if q8act and fmt != "q8_0":
+        raise SystemExit("bench.py: --q8act takes Q8_0 weights")
+    base = torch.from_numpy(gen(1, n, k)[0]).to(dev)
     ws = [base] + [base.clone() for _ in range(11)]
     x = torch.from_numpy(wl.activations(2, m, k)).to(dev)
     nout = n // 2 if fused else n
@@ -499,10 +503,11 @@ def kernel_driver(which, m, q8act):
             fn = q8.q8_linear_fused_gate_up_silu_q8act if fused else q8.q8_linear_q8act
             fn(w, nout, k, xq, xd)
         else:
-            fn = q8.q8_linear_fused_gate_up_silu if fused else q8.q8_linear
+            pre = "q8" if fmt == "q8_0" else fmt
+            fn = getattr(q8, f"{pre}_linear_fused_gate_up_silu" if fused else f"{pre}_linear")
             fn(w, nout, k, x)
     torch.cuda.synchronize()
-    log(f"kernel driver: {which} m={m} q8act={q8act} done")
+    log(f"kernel driver: {which} m={m} fmt={fmt} q8act={q8act} done")
 
 
 def main():
@@ -520,9 +525,11 @@ def main():
                     help="profiling driver only: a 256 MiB copy, then the Qwen3-8B LINEAR "
                          "(qkv | gate_up | down) at M rows on 12 distinct weight copies")
     ap.add_argument("--q8act", action="store_true", help="with --kernel-driver: the q8 x q8 path")
+    ap.add_argument("--fmt", default="q8_0", choices=["q8_0", "q4_0", "q4_k", "q5_k", "q6_k"],
+                    help="with --kernel-driver: the weight format")
     args = ap.parse_args()
     if args.kernel_driver:
-        kernel_driver(args.kernel_driver[0], int(args.kernel_driver[1]), args.q8act)
+        kernel_driver(args.kernel_driver[0], int(args.kernel_driver[1]), args.q8act, args.fmt)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
