@@ -452,6 +452,64 @@ def bench_moe_prefill(torch, dev, q8, tokens, reps):
 PROFILE_LINEARS = {"qkv": (6144, 4096, False), "gate_up": (24576, 4096, True), "down": (4096, 12288, False)}
 
 
+def read_ceiling_us(torch, dev, q8, nbytes, min_bytes=600e6):
+    """The time one launch of a plain streaming read of nbytes takes (best launch shape of
+    the library's read probe), over distinct resident buffers back to back like
+    bench_linear, so that every launch reads from HBM.  Returns (us, shape)."""
+    nb = nbytes - nbytes % 4096
+    copies = max(2, int(min_bytes // nb) + 1)
+    pool = torch.randint(0, 256, (copies * nb,), dtype=torch.uint8, device=dev)
+    views = [pool[i * nb:(i + 1) * nb] for i in range(copies)]
+    best = None
+    for shape in range(q8.probe_shape_count()):
+        sink = q8.probe_stream_read(views[0], nb, shape)
+
+        def seq():
+            for v in views:
+                q8.probe_stream_read(v, nb, shape, sink=sink)
+
+        ms = graph_launch_ms(torch, seq, copies)
+        if best is None or ms < best[0]:
+            best = (ms, shape)
+    del pool, views
+    return best[0] * 1e3 * nbytes / nb, best[1]
+
+
+def launch_floor_us(torch, dev, q8, blocks, launches=200):
+    """Average time per launch of a kernel of `blocks` workgroups that does nothing,
+    replayed back to back in a graph."""
+    return graph_launch_ms(torch, lambda: [q8.probe_empty(blocks, dev) for _ in range(launches)], launches) * 1e3
+
+
+def bench_bounds(torch, dev, q8, reps, known):
+    """Each one-row linear against the two bounds of its launch on this GPU: a plain
+    streaming read of its weight bytes in one launch, and an empty launch.  `known` maps
+    names to bench_linear results already measured."""
+    cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    floor = {"1_block": round(launch_floor_us(torch, dev, q8, 1), 3),
+             f"{8 * cu}_blocks": round(launch_floor_us(torch, dev, q8, 8 * cu), 3)}
+    log(f"launch floor: {floor}")
+    linears = [("qwen3-8b-qkv-m1", 6144, 4096, False, "q8_0"), ("qwen3-8b-gate-up-m1", 24576, 4096, True, "q8_0"),
+               ("qwen3-8b-down-m1", 4096, 12288, False, "q8_0"), ("qwen3-0.6b-qkv-m1", 4096, 1024, False, "q8_0"),
+               ("qwen3-0.6b-gate-up-m1", 6144, 1024, True, "q8_0"), ("qwen3-0.6b-down-m1", 1024, 3072, False, "q8_0"),
+               ("qwen3-8b-ffn-gate-up-q4_k-m1", 24576, 4096, True, "q4_k"),
+               ("qwen3-8b-ffn-down-q6_k-m1", 4096, 12288, False, "q6_k")]
+    out = {}
+    for name, n, k, fused, fmt in linears:
+        r = known.get(name) or bench_linear(torch, dev, q8, name, n, k, 1, fused, reps, fmt=fmt)
+        read_us, shape = read_ceiling_us(torch, dev, q8, r["weight_bytes"])
+        out[name] = {"weights": fmt.upper(), "bytes": r["weight_bytes"], "kernel_us": r["us_per_launch"],
+                     "read_us": round(read_us, 3), "read_gbps": round(r["weight_bytes"] / read_us / 1e3, 1),
+                     "kernel_over_read": round(read_us / r["us_per_launch"], 4),
+                     "hbm_frac": round(r["weight_bytes"] / r["us_per_launch"] / 1e3 / HBM_PEAK_GBS, 4),
+                     "read_hbm_frac": round(r["weight_bytes"] / read_us / 1e3 / HBM_PEAK_GBS, 4),
+                     "read_probe_shape": shape}
+        log(f"bounds {name}: {out[name]}")
+    return {"launch_floor_us": floor, "one_row_linears": out,
+            "note": "read_us: best of the library's plain streaming-read probe shapes over the same byte count in "
+                    "one launch; kernel_over_read = read_us / kernel_us"}
+
+
 def kernel_driver(which, m, q8act, fmt="q8_0"):
     """Short launch sequence for rocprofv3 counter and trace runs: a plain 256 MiB
     device-to-device copy (the calibration dispatch for FETCH_SIZE / WRITE_SIZE), then one
@@ -612,6 +670,10 @@ def main():
         extras["qwen3-30b-a3b-moe-16tok-expert-top-p-0.9"] = bench_moe(torch, dev, q8, 4, args.steps, args.warmup,
                                                                         top_p=0.9)
         line["configs"] = extras
+        line["bounds"] = bench_bounds(torch, dev, q8, reps, {
+            "qwen3-0.6b-qkv-m1": extras["qwen3-0.6b-qkv-m1"],
+            "qwen3-8b-ffn-gate-up-q4_k-m1": extras["qwen3-8b-ffn-gate-up-q4_k-m1"],
+            "qwen3-8b-ffn-down-q6_k-m1": extras["qwen3-8b-ffn-down-q6_k-m1"]})
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on one layer")
         line["cpu_baseline"] = cpu_baseline_block(spec)

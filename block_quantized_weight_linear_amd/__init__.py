@@ -1,6 +1,7 @@
 """MI355X (gfx950) Q8_0 block-quantized weight linear.
 
-Python binding of the C ABI in include/q8_linear.h (libq8linear.so, built in-tree by
+Python binding of the C ABI in include/q8_linear.h (and the measurement aids of
+include/q8_probe.h) (libq8linear.so, built in-tree by
 ``python -m block_quantized_weight_linear_amd.build``).  PyTorch provides device
 memory and streams; all computation runs in the library's HIP kernels.
 """
@@ -11,6 +12,9 @@ from ._binding import (  # noqa: F401
     abi_version,
     lib,
     moe_route_topk,
+    probe_empty,
+    probe_shape_count,
+    probe_stream_read,
     q4_0_linear,
     q4_0_linear_fused_gate_up_silu,
     q4_k_linear,

@@ -72,6 +72,16 @@ lib.q8_moe_grouped_linear_noalloc.restype = ctypes.c_int
 lib.q8_moe_grouped_linear_noalloc.argtypes = [_vp, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _i32, _vp,
                                               _i64, _vp]
 
+# measurement aids (include/q8_probe.h)
+lib.q8_probe_shape_count.restype = _i32
+lib.q8_probe_shape_count.argtypes = []
+lib.q8_probe_sink_words.restype = _i64
+lib.q8_probe_sink_words.argtypes = [_i32]
+lib.q8_probe_stream_read.restype = ctypes.c_int
+lib.q8_probe_stream_read.argtypes = [_vp, _i64, _i32, _vp, _i64, _vp]
+lib.q8_probe_empty.restype = ctypes.c_int
+lib.q8_probe_empty.argtypes = [_i64, _vp]
+
 Q8_OK, Q8_ERR_NULL, Q8_ERR_SHAPE, Q8_ERR_ALIGN, Q8_ERR_WORKSPACE, Q8_ERR_DEVICE = range(6)
 
 
@@ -367,3 +377,34 @@ def q8_moe_grouped_linear_noalloc(w_gate_up_exps, w_down_exps, n_exp: int, f: in
           x.data_ptr(), m, _ld(x, h), topk_idx.data_ptr(), topk_w.data_ptr(), k, out.data_ptr(), _ld(out, h),
           _stream(x))
     return out
+
+
+# ------------------------------------------------------------ measurement aids
+
+
+def probe_shape_count() -> int:
+    """Launch shapes of probe_stream_read (0 .. count-1)."""
+    return int(lib.q8_probe_shape_count())
+
+
+def probe_stream_read(buf, nbytes: int, shape: int, sink=None):
+    """Plain streaming read of the first nbytes bytes of a device byte tensor in one
+    launch (launch shape `shape`), for a benchmark's read ceiling; returns the sink
+    tensor of per-lane xor words."""
+    _bytes(buf, nbytes, "buf", None)
+    with torch.cuda.device(buf.device):
+        words = int(lib.q8_probe_sink_words(shape))
+    if words < 0:
+        raise ValueError(f"probe shape {shape} is out of range [0, {probe_shape_count()})")
+    if sink is None:
+        sink = torch.empty(words, dtype=torch.int32, device=buf.device)
+    _contig_out(sink, (words,), "sink", torch.int32, buf.device)
+    _call(buf.device, lib.q8_probe_stream_read, buf.data_ptr(), nbytes, shape, sink.data_ptr(), words, _stream(buf))
+    return sink
+
+
+def probe_empty(blocks: int, device=None):
+    """One launch of `blocks` workgroups that do nothing, on the current stream."""
+    device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    with torch.cuda.device(device):
+        check(lib.q8_probe_empty(blocks, ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)))

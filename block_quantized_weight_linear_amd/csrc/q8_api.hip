@@ -6,6 +6,7 @@
 
 #include <mutex>
 
+#include "../../include/q8_probe.h"
 #include "q8_internal.h"
 #include "q8_validate.h"
 
@@ -380,6 +381,57 @@ q8_status q8_moe_grouped_linear_noalloc(const void* w_gate_up_exps, const void* 
                                 static_cast<const uint8_t*>(w_down_exps), n_exp, f, h, x, m, ldx, topk_idx, topk_w, k,
                                 y, ldy, ws, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return device_fail("q8_moe_grouped_linear_noalloc", e);
+    return Q8_OK;
+}
+
+int32_t q8_probe_shape_count(void) { return q8k::probe_shape_count(); }
+
+int64_t q8_probe_sink_words(int32_t shape) {
+    if (shape < 0 || shape >= q8k::probe_shape_count()) return -1;
+    q8k::DeviceInfo dev;
+    if (q8k::current_device_info(&dev) != hipSuccess) return -1;
+    return q8k::probe_sink_words(shape, dev.cu_count);
+}
+
+q8_status q8_probe_stream_read(const void* src, int64_t bytes, int32_t shape, uint32_t* sink, int64_t sink_words,
+                               void* stream) {
+    g_err[0] = 0;
+    if (!src || !sink) {
+        set_err("q8_probe_stream_read: src and sink must not be NULL");
+        return Q8_ERR_NULL;
+    }
+    if (bytes <= 0 || bytes % 4096 != 0 || shape < 0 || shape >= q8k::probe_shape_count()) {
+        set_err("q8_probe_stream_read: bytes must be a positive multiple of 4096 (got %lld) and shape in [0, %d) "
+                "(got %d)",
+                (long long)bytes, q8k::probe_shape_count(), (int)shape);
+        return Q8_ERR_SHAPE;
+    }
+    if ((uintptr_t)src % 16 != 0 || (uintptr_t)sink % 4 != 0) {
+        set_err("q8_probe_stream_read: src must be 16-byte and sink 4-byte aligned");
+        return Q8_ERR_ALIGN;
+    }
+    q8k::DeviceInfo dev;
+    hipError_t e = q8k::current_device_info(&dev);
+    if (e != hipSuccess) return device_fail("q8_probe_stream_read", e);
+    const int64_t need = q8k::probe_sink_words(shape, dev.cu_count);
+    if (sink_words < need) {
+        set_err("q8_probe_stream_read: shape %d needs %lld sink words, got %lld", (int)shape, (long long)need,
+                (long long)sink_words);
+        return Q8_ERR_WORKSPACE;
+    }
+    e = q8k::launch_probe_read(dev, src, bytes, shape, sink, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_fail("q8_probe_stream_read", e);
+    return Q8_OK;
+}
+
+q8_status q8_probe_empty(int64_t blocks, void* stream) {
+    g_err[0] = 0;
+    if (blocks < 1 || blocks > INT32_MAX) {
+        set_err("q8_probe_empty: blocks must be in [1, 2^31 - 1] (got %lld)", (long long)blocks);
+        return Q8_ERR_SHAPE;
+    }
+    hipError_t e = q8k::launch_probe_empty(blocks, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_fail("q8_probe_empty", e);
     return Q8_OK;
 }
 

@@ -69,4 +69,12 @@ hipError_t launch_moe_grouped(const DeviceInfo& dev, const uint8_t* wgu, const u
                               int64_t h, const float* x, int64_t m, int64_t ldx, const int32_t* idx, const float* wts,
                               int k, float* y, int64_t ldy, void* workspace, hipStream_t stream);
 
+// Measurement aids (include/q8_probe.h): a plain streaming read of `bytes` (a multiple
+// of 4096) in launch shape `shape`, one xor word per lane into sink; an empty launch.
+int probe_shape_count();
+int64_t probe_sink_words(int shape, int cu_count);
+hipError_t launch_probe_read(const DeviceInfo& dev, const void* src, int64_t bytes, int shape, uint32_t* sink,
+                             hipStream_t stream);
+hipError_t launch_probe_empty(int64_t blocks, hipStream_t stream);
+
 }  // namespace q8k

@@ -8,13 +8,14 @@ and zero-size calls return before any HIP call.
 from __future__ import annotations
 
 import ctypes
+import glob
 import os
 import re
 
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "q8_linear.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 q8 = pytest.importorskip("block_quantized_weight_linear_amd")
 lib = q8.lib
@@ -24,7 +25,7 @@ FAKE = 0x10000  # 64 KiB: a 256-byte aligned, non-null address that is never der
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "\n".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
 
@@ -37,7 +38,8 @@ def test_header_declares_the_four_calls():
               "moe_route_topk_top_p", "moe_route_topk_ws", "moe_route_workspace_bytes",
               "q4_0_linear", "q4_0_linear_fused_gate_up_silu", "q8_moe_grouped_linear_noalloc",
               "q4_k_linear", "q4_k_linear_fused_gate_up_silu", "q6_k_linear", "q6_k_linear_fused_gate_up_silu",
-              "q5_k_linear", "q5_k_linear_fused_gate_up_silu"):
+              "q5_k_linear", "q5_k_linear_fused_gate_up_silu", "q8_probe_stream_read", "q8_probe_empty",
+              "q8_probe_shape_count", "q8_probe_sink_words"):
         assert n in names, names
 
 
@@ -255,3 +257,22 @@ def test_moe_noalloc_refuses_sizes_beyond_its_scratch():
     assert call(4, f=700) == ERR_SHAPE
     assert call(4, idx=None) == ERR_NULL
     assert call(0, idx=None) == OK
+
+
+def test_probe_argument_errors():
+    """The measurement aids reject bad arguments on the host (no launch)."""
+    f = lib.q8_probe_stream_read
+    assert lib.q8_probe_shape_count() >= 1
+    assert lib.q8_probe_sink_words(-1) == -1
+    assert lib.q8_probe_sink_words(lib.q8_probe_shape_count()) == -1
+    assert f(None, 4096, 0, FAKE, 1 << 20, None) == ERR_NULL
+    assert f(FAKE, 4096, 0, None, 1 << 20, None) == ERR_NULL
+    assert f(FAKE, 0, 0, FAKE, 1 << 20, None) == ERR_SHAPE
+    assert f(FAKE, 4000, 0, FAKE, 1 << 20, None) == ERR_SHAPE
+    assert f(FAKE, 4096, -1, FAKE, 1 << 20, None) == ERR_SHAPE
+    assert f(FAKE, 4096, lib.q8_probe_shape_count(), FAKE, 1 << 20, None) == ERR_SHAPE
+    assert f(FAKE + 8, 4096, 0, FAKE, 1 << 20, None) == ERR_ALIGN
+    assert f(FAKE, 4096, 0, FAKE + 2, 1 << 20, None) == ERR_ALIGN
+    assert b"probe" in lib.q8_last_error()
+    assert lib.q8_probe_empty(0, None) == ERR_SHAPE
+    assert lib.q8_probe_empty(1 << 31, None) == ERR_SHAPE
