@@ -823,6 +823,240 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(1,
     }
 }
 
+// The rows kernel's arithmetic on the matrix cores.  v_mfma_f32_4x4x1_16b_f32 computes,
+// in each of its 16 blocks, a 4 x 4 outer product added to a 4 x 4 accumulator with one
+// rounding per element (a fused multiply-add, checked against fmaf on the device), and it
+// runs at twice the non-packed float32 VALU rate.  Block b stands for lane j = b of the
+// float32 rows kernel: its four A values are the weights of four row slots, its four B
+// values one input of four activation rows, so that one instruction performs, for 16
+// pairs at once, the fma that 16 rows kernel lanes would do for 4 rows x 4 activation
+// rows.  The instruction stream follows the rows kernel's order exactly (per chain:
+// chunks of the group in increasing order, the pair's inputs in increasing order; then the
+// xor butterfly over the 16 blocks and group 0 + group 1), so every output is
+// bit-identical to the rows kernel's.  A block whose pair lies past the row multiplies
+// zero by zero: its accumulator, which can never hold -0 (it starts at +0 and every
+// fma in round-to-nearest keeps +0 + -0 = +0), is unchanged.
+//
+// Lane layout: lane l is (b = l / 4, t = l % 4): it supplies the weight of row slot t
+// and the input of activation row 4q + t; register i of accumulator (g, q) then holds
+// row slot i of weight row group g against activation row 4q + t.  Tiles, groups, the
+// activation staging (MT rows, rows past m_rows copy the last one and are not stored) and
+// the weight ring are those of gemv_rows_kernel.  Up to 16 activation rows per launch.
+template <class Fmt, int MT, int R, bool SILU>
+__global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(MT <= 8 ? 2 : 1, 2))) void gemv_rows_mfma_kernel(
+    const uint8_t* __restrict__ w, int n_out, int P, const float* __restrict__ x, int ldx, int m_rows,
+    float* __restrict__ y, int ldy) {
+    static_assert(MT % 4 == 0 && MT <= 16, "activation rows in groups of four, at most 16");
+    constexpr int RR = SILU ? 2 * R : R;  // weight row groups per wave (fused: R gate, R up)
+    constexpr int QG = MT / 4;            // activation row groups
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    // activation rows at a stride of 132 float4 (128 + 4 of padding): the four row slots
+    // t of a read then fall in different LDS banks
+    constexpr int kXm = 132;
+    __shared__ float4 xa[2][MT * kXm];
+    __shared__ float4 xb[2][MT * kXm];
+    __shared__ float part[8 * RR * MT];   // group 1's row sums: [slot][g][m]
+    const int tid = threadIdx.x;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = wv >> 1;                // group
+    const int lane = tid & 63;
+    const int b = lane >> 2;              // pair within the chunk (the rows kernel's lane j)
+    const int t = lane & 3;               // row slot within the wave / activation row in a group
+    const int slot = (wv & 1) * 4 + t;    // the lane's weight row slot within the group, 0..7
+    const size_t row_bytes = Fmt::row_bytes(P);
+    const int nch = (P + 15) >> 4;
+    const int steps = (nch + 1) >> 1;
+    const int tiles = (n_out + 8 * R - 1) / (8 * R);
+    const int my_tiles = (tiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int items = my_tiles * steps;
+    __builtin_assume(steps >= 1);
+    __builtin_assume(items >= 1);
+
+    // weight row of slot s, row r of the tile's slots in tile i (clamped past the end)
+    auto out_row = [&](int i, int s, int r) __attribute__((always_inline)) {
+        const int n = ((int)blockIdx.x + i * (int)gridDim.x) * (8 * R) + s * R + r;
+        return n < n_out ? n : n_out - 1;
+    };
+    auto chunk_of = [&](int st) __attribute__((always_inline)) {
+        const int ch = h + 2 * st;
+        return ch < nch ? ch : nch - 1;
+    };
+    auto load_w = [&](int i, int st, uint32_t(&wr)[RR][Fmt::kDwords]) __attribute__((always_inline)) {
+        const int p = 16 * chunk_of(st) + b;
+        const int pc = p < P ? p : P - 1;  // past the row: a pair of the same row (multiplied as zero)
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int n = out_row(i, slot, r);
+            Fmt::load(w + (size_t)n * row_bytes, pc, wr[r]);
+            if constexpr (SILU) Fmt::load(w + (size_t)(n + n_out) * row_bytes, pc, wr[R + r]);
+        }
+    };
+    // as in gemv_rows_kernel: 2*MT wave-wide copies of 64 float4 per half chunk, layout
+    // [m][c][j] (rows kXm float4 apart); activation rows past m_rows repeat the last row
+    auto stage_x = [&](int st, int half, float4* buf) __attribute__((always_inline)) {
+        const int c_lo = lane >> 4;
+        int pc = 16 * chunk_of(st) + (lane & 15);
+        pc = pc < P ? pc : P - 1;
+#pragma unroll
+        for (int qq = 0; qq < MT; ++qq) {
+            const int q = 2 * qq + (wv & 1);
+            int m = q >> 1;
+            m = m < m_rows ? m : m_rows - 1;
+            const int c = 4 * (q & 1) + c_lo;
+            const float* src = x + (size_t)m * ldx + 64 * (size_t)pc + 32 * half + 4 * c;
+            lds_copy16(src, buf + (q >> 1) * kXm + 64 * (q & 1));
+        }
+    };
+    constexpr int kWLoads = Fmt::kLoads * RR;
+
+    f32x4 acc[RR][QG];
+#pragma unroll
+    for (int g = 0; g < RR; ++g)
+#pragma unroll
+        for (int q = 0; q < QG; ++q) acc[g][q] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+
+    auto compute = [&](auto half, int st, const uint32_t(&wc)[RR][Fmt::kDwords], const float4* xs)
+                       __attribute__((always_inline)) {
+        constexpr int HALF = decltype(half)::value;
+        const int ch = h + 2 * st;
+        // a chunk past the row's end (partial: some pairs missing) masks its dead pairs.
+        // Per quant dword: the activations of the 4 inputs, then row group by row group
+        // its 4 weights and the MFMAs that use them (short register lives; every
+        // accumulator still sees its inputs in increasing order).
+        auto body = [&](auto partial) __attribute__((always_inline)) {
+            constexpr bool PARTIAL = decltype(partial)::value;
+            const bool live = 16 * ch + b < P;
+#pragma unroll
+            for (int cc = 0; cc < 8; ++cc) {
+                float4 xv[QG];
+#pragma unroll
+                for (int q = 0; q < QG; ++q) {
+                    xv[q] = xs[(4 * q + t) * kXm + cc * 16 + b];
+                    if constexpr (PARTIAL) {
+                        if (!live) xv[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                    }
+                }
+#pragma unroll
+                for (int g = 0; g < RR; ++g) {
+                    float wf[4];
+                    Fmt::template weights<HALF>(wc[g], cc, wf, 16 * ch + b);
+                    if constexpr (PARTIAL) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) wf[e] = live ? wf[e] : 0.0f;
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+#pragma unroll
+                        for (int q = 0; q < QG; ++q) {
+                            const float xe = e == 0 ? xv[q].x : e == 1 ? xv[q].y : e == 2 ? xv[q].z : xv[q].w;
+                            acc[g][q] = __builtin_amdgcn_mfma_f32_4x4x1f32(wf[e], xe, acc[g][q], 0, 0, 0);
+                        }
+                }
+            }
+        };
+        if (ch < nch) {  // wave-uniform
+            if (16 * ch + 16 <= P)
+                body(std::false_type{});
+            else
+                body(std::true_type{});
+        }
+    };
+    // Tile i done: butterfly over the 16 blocks (lane offsets 32, 16, 8, 4 for the rows
+    // kernel's 8, 4, 2, 1), group 1's sums to group 0 through LDS, group 0 adds and stores
+    // (lane (b, t) with b < 4 stores slot b of activation row 4q + t).
+    auto finish_tile = [&](int i) __attribute__((always_inline)) {
+#pragma unroll
+        for (int off = 32; off >= 4; off >>= 1) {
+#pragma unroll
+            for (int g = 0; g < RR; ++g)
+#pragma unroll
+                for (int q = 0; q < QG; ++q)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[g][q][e] += __shfl_xor(acc[g][q][e], off, 64);
+        }
+        if (h == 1 && b == 0) {
+#pragma unroll
+            for (int g = 0; g < RR; ++g)
+#pragma unroll
+                for (int q = 0; q < QG; ++q)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) part[(((wv & 1) * 4 + e) * RR + g) * MT + 4 * q + t] = acc[g][q][e];
+        }
+        __syncthreads();
+        if (h == 0 && b < 4) {
+#pragma unroll
+            for (int g = 0; g < RR; ++g)
+#pragma unroll
+                for (int q = 0; q < QG; ++q)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[g][q][e] += part[(((wv & 1) * 4 + e) * RR + g) * MT + 4 * q + t];
+            const int s = (wv & 1) * 4 + b;  // the slot this lane stores
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int n = out_row(i, s, r);
+#pragma unroll
+                for (int q = 0; q < QG; ++q) {
+                    const int m = 4 * q + t;
+                    float v = acc[r][q][0];
+#pragma unroll
+                    for (int e = 1; e < 4; ++e) v = b == e ? acc[r][q][e] : v;
+                    if constexpr (SILU) {
+                        float u = acc[R + r][q][0];
+#pragma unroll
+                        for (int e = 1; e < 4; ++e) u = b == e ? acc[R + r][q][e] : u;
+                        v = silu_mul(v, u);
+                    }
+                    if (m < m_rows) y[(size_t)m * ldy + n] = v;
+                }
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < RR; ++g)
+#pragma unroll
+            for (int q = 0; q < QG; ++q) acc[g][q] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    };
+
+    uint32_t wc[RR][Fmt::kDwords], wn[RR][Fmt::kDwords];
+    stage_x(0, 0, xa[h]);
+    load_w(0, 0, wc);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<0>();
+    __syncthreads();
+    int i = 0, st = 0;
+    for (int it = 0; it < items; ++it) {
+        const bool more = it + 1 < items;
+        const bool last_step = st + 1 == steps;
+        const int ni = last_step ? i + 1 : i;
+        const int nst = last_step ? 0 : st + 1;
+        stage_x(st, 1, xb[h]);
+        if (more) load_w(ni, nst, wn);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(std::integral_constant<int, 0>{}, st, wc, xa[h]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) {
+            wait_vmcnt<kWLoads>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        __syncthreads();
+        if (more) stage_x(nst, 0, xa[h]);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(std::integral_constant<int, 1>{}, st, wc, xb[h]);
+        if (last_step) finish_tile(i);
+        if (more) {
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vmcnt<0>();
+#pragma unroll
+            for (int g = 0; g < RR; ++g)
+#pragma unroll
+                for (int q = 0; q < Fmt::kDwords; ++q) wc[g][q] = wn[g][q];
+            __syncthreads();
+        }
+        i = ni;
+        st = nst;
+    }
+}
+
 namespace {
 
 template <class Fmt, int R, int NR, int D, int NW, bool NT = false>
@@ -964,6 +1198,54 @@ hipError_t launch_rows(const DeviceInfo& dev, const uint8_t* w, int n_out, int P
     return launch_rows_r<Fmt, M, 1, SILU>(dev, n_out, P, w, x, ldx, y, ldy, stream);
 }
 
+// Blocks of gemv_rows_mfma_kernel<Fmt, MT, R, SILU> resident per CU (queried once per kernel).
+template <class Fmt, int MT, int R, bool SILU>
+int rows_mfma_per_cu() {
+    static const int per_cu = [] {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemv_rows_mfma_kernel<Fmt, MT, R, SILU>, kRowsThreads,
+                                                         0) != hipSuccess ||
+            n < 1)
+            n = 1;
+        return n;
+    }();
+    return per_cu;
+}
+
+template <class Fmt, int MT, int R, bool SILU>
+hipError_t launch_rows_mfma_r(const DeviceInfo& dev, int n_out, int P, const uint8_t* w, const float* x, int ldx,
+                              int m_rows, float* y, int ldy, hipStream_t stream) {
+    const int tiles = (n_out + 8 * R - 1) / (8 * R);
+    const int64_t slots = (int64_t)dev.cu_count * rows_mfma_per_cu<Fmt, MT, R, SILU>();
+    const int blocks = (int)(tiles < slots ? tiles : slots);
+    hipLaunchKernelGGL((gemv_rows_mfma_kernel<Fmt, MT, R, SILU>), dim3(blocks), dim3(kRowsThreads), 0, stream, w,
+                       n_out, P, x, ldx, m_rows, y, ldy);
+    return hipGetLastError();
+}
+
+// Rows per lane: one gate/up pair for the fused form, up to two plain rows (the largest
+// within 5% of the best fill), so that the kernel keeps two waves per SIMD without spills.
+template <class Fmt, int MT, bool SILU>
+hipError_t launch_rows_mfma(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, const float* x, int ldx,
+                            int m_rows, float* y, int ldy, hipStream_t stream) {
+    if constexpr (!SILU) {
+        const int64_t cus = dev.cu_count;
+        const double f1 = round_fill((n_out + 7) / 8, cus * rows_mfma_per_cu<Fmt, MT, 1, SILU>());
+        const double f2 = round_fill((n_out + 15) / 16, cus * rows_mfma_per_cu<Fmt, MT, 2, SILU>());
+        if (f2 >= 0.95 * f1)
+            return launch_rows_mfma_r<Fmt, MT, 2, SILU>(dev, n_out, P, w, x, ldx, m_rows, y, ldy, stream);
+    }
+    return launch_rows_mfma_r<Fmt, MT, 1, SILU>(dev, n_out, P, w, x, ldx, m_rows, y, ldy, stream);
+}
+
+// 9..16 activation rows on the matrix-core form, padded to 12 or 16.
+template <class Fmt, bool SILU>
+hipError_t launch_rows_mfma_m(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, const float* x, int ldx,
+                              int m, float* y, int ldy, hipStream_t stream) {
+    if (m <= 12) return launch_rows_mfma<Fmt, 12, SILU>(dev, w, n_out, P, x, ldx, m, y, ldy, stream);
+    return launch_rows_mfma<Fmt, 16, SILU>(dev, w, n_out, P, x, ldx, m, y, ldy, stream);
+}
+
 template <int M, int R>
 hipError_t launch_m(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, int log2S, const float* x, int ldx,
                     float* y, int ldy, hipStream_t stream) {
@@ -1096,13 +1378,26 @@ hipError_t launch_gemv_q8(const DeviceInfo& dev, const uint8_t* w, int64_t n_out
                        : try_one_row<FmtQ8_0, 1>(dev, w, (int)n_out, P, log2S, x, y, stream, &e))
             return e;
     }
-    // several rows (or one row with K beyond the register kernel): 8-row launches
-    for (int64_t m0 = 0; m0 < m; m0 += 8) {
-        const int mm = (int)((m - m0) < 8 ? (m - m0) : 8);
+    if (m == 1)  // one row with K beyond the one-row kernel: the float32 rows kernel
+        return silu_pairs ? launch_r<2>(dev, w, (int)n_out, P, log2S, x, (int)ldx, 1, y, (int)ldy, stream)
+                          : launch_r<1>(dev, w, (int)n_out, P, log2S, x, (int)ldx, 1, y, (int)ldy, stream);
+    // Several rows, in launches of up to 16: 9..16 rows on the matrix-core form (one pass
+    // over the weights), up to 8 on the float32 rows kernel, which is faster there; both
+    // give the same bits.  Measured on the Qwen3-8B linears at 16 rows (one matrix-core
+    // launch against two 8-row launches): QKV 33.3 / 36 us, down 45.9 / 61 us, fused gate_up
+    // 90.9 / 89.6 us; at 8 rows the float32 kernel wins (fused gate_up 44.8 / 52.6 us).
+    for (int64_t m0 = 0; m0 < m; m0 += 16) {
+        const int mm = (int)((m - m0) < 16 ? (m - m0) : 16);
         const float* xc = x + m0 * ldx;
         float* yc = y + m0 * ldy;
-        hipError_t e = silu_pairs ? launch_r<2>(dev, w, (int)n_out, P, log2S, xc, (int)ldx, mm, yc, (int)ldy, stream)
-                                  : launch_r<1>(dev, w, (int)n_out, P, log2S, xc, (int)ldx, mm, yc, (int)ldy, stream);
+        hipError_t e;
+        if (mm > 8)
+            e = silu_pairs
+                    ? launch_rows_mfma_m<FmtQ8_0, true>(dev, w, (int)n_out, P, xc, (int)ldx, mm, yc, (int)ldy, stream)
+                    : launch_rows_mfma_m<FmtQ8_0, false>(dev, w, (int)n_out, P, xc, (int)ldx, mm, yc, (int)ldy, stream);
+        else
+            e = silu_pairs ? launch_r<2>(dev, w, (int)n_out, P, log2S, xc, (int)ldx, mm, yc, (int)ldy, stream)
+                           : launch_r<1>(dev, w, (int)n_out, P, log2S, xc, (int)ldx, mm, yc, (int)ldy, stream);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

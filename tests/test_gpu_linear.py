@@ -191,6 +191,35 @@ def test_batch_invariance_and_determinism(q8, n, k):
     assert np.max(np.abs(h1[0] - h40[5])) / np.max(np.abs(href)) <= 1e-5
 
 
+@pytest.mark.parametrize("n,k", [(300, 20480), (64, 4096), (1000, 16640), (6144, 4096)])
+def test_rows_kernels_agree_bit_for_bit(q8, n, k):
+    """9..16 activation rows run the matrix-core form of the float32 rows kernel (one fused
+    multiply-add per weight and activation row in the same order, the same butterfly and
+    group sum), up to 8 rows the rows kernel itself (and one row with K past the one-row
+    kernel): the rows agree bit for bit, plain and fused, also with the activation rows
+    padded to 12 or 16."""
+    lib, torch, dev = q8
+    wb, _, _ = wl.q8_weight(2300 + n, n, k)
+    x = wl.activations(2301, 16, k)
+    wd, xd = to_dev(wb, dev), to_dev(x, dev)
+    say(f"rows kernels agree n={n} k={k}")
+    y16 = lib.q8_linear(wd, n, k, xd).cpu().numpy()
+    for m in (13, 10, 5):
+        ym = lib.q8_linear(wd, n, k, xd[:m].contiguous()).cpu().numpy()
+        assert np.array_equal(ym, y16[:m]), m
+    f = n // 2
+    h16 = lib.q8_linear_fused_gate_up_silu(wd, f, k, xd).cpu().numpy()
+    for m in (11, 7):
+        hm = lib.q8_linear_fused_gate_up_silu(wd, f, k, xd[:m].contiguous()).cpu().numpy()
+        assert np.array_equal(hm, h16[:m]), m
+    if k > 16384:  # one row past the one-row kernel: the float32 rows kernel
+        for r in (0, 9, 15):
+            y1 = lib.q8_linear(wd, n, k, xd[r:r + 1].contiguous()).cpu().numpy()
+            assert np.array_equal(y1[0], y16[r]), r
+            h1 = lib.q8_linear_fused_gate_up_silu(wd, f, k, xd[r:r + 1].contiguous()).cpu().numpy()
+            assert np.array_equal(h1[0], h16[r]), r
+
+
 def test_scale_doubling_sign_and_zero_blocks(q8):
     lib, torch, dev = q8
     n, k, m = 2048, 2048, 4
