@@ -79,9 +79,11 @@ const char* q8_last_error(void);
  *   n >= 0 outputs, k > 0 a multiple of 256, m >= 0 rows, ldx >= k, ldy >= n.
  * Arithmetic by batch size (the m-dependent kernel classes of section 14.2):
  *   m == 1      float32: w = d*q exactly, per-block chains, fixed butterfly;
- *   2..255      float32 (8-row launches): exact fp32 dequantization, one fma per weight
- *               and row; every row is bit-identical whatever the other rows are (for
- *               any m in 2..255), and agrees with the m == 1 result to reassociation;
+ *   2..255      float32 in 16-row launches: exact fp32 dequantization, one fma per
+ *               weight and row in a fixed order (9..16 rows on the fp32 matrix cores,
+ *               whose 4x4x1 form rounds once per fma, fewer on the VALU: the same bits);
+ *               every row is bit-identical whatever the other rows are (for any m in
+ *               2..255), and agrees with the m == 1 result to reassociation;
  *   m >= 256    bf16 matrix cores (dense prefill): weights d*q and activations rounded
  *               to bf16 (nearest even), float32 accumulation and output.
  */
