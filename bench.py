@@ -539,11 +539,14 @@ def kernel_driver(which, m, q8act, fmt="q8_0"):
         dn = torch.cat([torch.from_numpy(dn_h).to(dev)] * (e // 8))
         x = torch.from_numpy(wl.activations(cfg.seed + 11, m, hd)).to(dev)
         wr = torch.from_numpy(wl.router_weight(cfg.seed + 12, e, hd, cfg.router_std)).to(dev)
+        used = []
         for _ in range(4):
             idx, wts = q8.moe_route_topk(x, wr, kk, True, workspace=True)
             q8.q8_moe_grouped_linear(gu, dn, e, f, hd, x, idx, wts)
+            used.append(int(torch.unique(idx).numel()))  # experts whose weights the call reads
         torch.cuda.synchronize()
-        log(f"kernel driver: moe tokens={m} done")
+        log(f"kernel driver: moe tokens={m} done; experts used per call: {used}; "
+            f"gate_up / down bytes per expert: {2 * f * hd * 17 // 16} / {hd * f * 17 // 16}")
         return
     n, k, fused = PROFILE_LINEARS[which]
     gen = {"q8_0": wl.q8_weight, "q4_0": wl.q4_0_weight, "q4_k": wl.q4_k_weight, "q5_k": wl.q5_k_weight,
