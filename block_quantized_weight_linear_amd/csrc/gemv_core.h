@@ -173,7 +173,9 @@ __host__ __device__ inline int slots_log2(int P) {
 // One wave walks row groups first, first+stride, ... < end (G = 64/S rows each) of a
 // Q8_0 matrix.  For R = 2 the lane also multiplies row n + r_off (gate/up pairs).
 // out(n, acc) is called on the lane with slot 0 of each valid row n < n_out.
-template <int M, int R, class X, class Out>
+// NRC: the rounds per row when known at compile time (1: a row fits the S lanes once),
+// 0 = computed from P (the per-item index arithmetic then divides by it).
+template <int M, int R, int NRC, class X, class Out>
 __device__ __forceinline__ void wave_rows(const uint8_t* __restrict__ w, int n_out, int r_off, int P, int log2S,
                                           const X& xs, int first, int stride, int end, Out&& out) {
     if (first >= end) return;
@@ -183,7 +185,7 @@ __device__ __forceinline__ void wave_rows(const uint8_t* __restrict__ w, int n_o
     const int j = lane & (S - 1);
     const int g = lane >> log2S;
     const size_t row_bytes = (size_t)P * 68;
-    const int n_rounds = (P + S - 1) / S;
+    const int n_rounds = NRC ? NRC : (P + S - 1) / S;
     const int n_items = ((end - 1 - first) / stride + 1) * n_rounds;
 
     auto item = [&](int it, int& n, int& p) {

@@ -189,7 +189,9 @@ __global__ __launch_bounds__(64 * kPlanWaves) void moe_plan_kernel(const int32_t
 // Computing the gate and up rows as separate rows keeps one weight row per lane (the
 // fused two-row form needs twice the registers); SiLU(gate) * up is formed from the
 // same two row sums, with the same function, as in the dense fused call.
-template <bool GATE_UP>
+// ONE_ROUND: every row fits the S lanes of its group once (P <= S), so the per-item
+// indexing needs no division.
+template <bool GATE_UP, bool ONE_ROUND>
 __global__ __launch_bounds__(kMoeThreads) void moe_expert_kernel(const uint8_t* __restrict__ w_stack,
                                                                  size_t expert_bytes, int n_out, int P, int log2S,
                                                                  const float* __restrict__ x, int ldx,
@@ -252,7 +254,7 @@ __global__ __launch_bounds__(kMoeThreads) void moe_expert_kernel(const uint8_t* 
             float* o = out + (size_t)(pos0 + c0) * ldo;
             auto run = [&](auto mtag) {
                 constexpr int MT = decltype(mtag)::value;
-                wave_rows<MT, 1>(w, n_out, n_out, P, log2S, xs, g_begin + wave, kMoeWaves, g_end,
+                wave_rows<MT, 1, ONE_ROUND ? 1 : 0>(w, n_out, n_out, P, log2S, xs, g_begin + wave, kMoeWaves, g_end,
                                  [&](int n, const float(&acc)[1][MT]) {
 #pragma unroll
                                      for (int m = 0; m < MT; ++m)
@@ -311,13 +313,13 @@ static int staged_rows(int P) {
 }
 
 // Blocks of moe_expert_kernel resident per CU for an LDS size (queried once per size).
-template <bool GATE_UP>
+template <bool GATE_UP, bool ONE_ROUND>
 static int moe_blocks_per_cu(size_t lds) {
     static thread_local size_t cached_lds = (size_t)-1;
     static thread_local int per_cu = 1;
     if (cached_lds != lds) {
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, moe_expert_kernel<GATE_UP>, kMoeThreads, lds) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, moe_expert_kernel<GATE_UP, ONE_ROUND>, kMoeThreads, lds) !=
                 hipSuccess ||
             n < 1)
             n = 1;
@@ -325,6 +327,20 @@ static int moe_blocks_per_cu(size_t lds) {
         cached_lds = lds;
     }
     return per_cu;
+}
+
+template <bool GATE_UP, bool ONE_ROUND>
+static hipError_t launch_expert_pass(const DeviceInfo& dev, const uint8_t* w, size_t expert_bytes, int rows_out,
+                                     int P, int log2S, const float* x, int ldx, const int32_t* offsets,
+                                     const int32_t* sorted, const int32_t* active, int n_exp, int k, float* out,
+                                     int ldo, int rows, int tiles, size_t lds, hipStream_t stream) {
+    const int64_t max_units = n_exp * (int64_t)tiles;
+    const int64_t slots = (int64_t)dev.cu_count * moe_blocks_per_cu<GATE_UP, ONE_ROUND>(lds);
+    const unsigned grid = (unsigned)(max_units < slots ? max_units : slots);
+    hipLaunchKernelGGL((moe_expert_kernel<GATE_UP, ONE_ROUND>), dim3(grid), dim3(kMoeThreads), lds, stream, w,
+                       expert_bytes, rows_out, P, log2S, x, ldx, offsets, sorted, active, n_exp, k, out, ldo, rows,
+                       tiles);
+    return hipGetLastError();
 }
 
 hipError_t launch_moe_grouped(const DeviceInfo& dev, const uint8_t* wgu, const uint8_t* wdn, int64_t n_exp, int64_t f,
@@ -383,19 +399,21 @@ hipError_t launch_moe_grouped(const DeviceInfo& dev, const uint8_t* wgu, const u
         const int rows = staged_rows(P);
         const size_t lds = (size_t)rows * P * 256;
         const size_t expert_bytes = (size_t)rows_out * (size_t)(K / 32) * 34;
-        const int64_t max_units = n_exp * (int64_t)tiles;
-        const int per_cu = gate_up ? moe_blocks_per_cu<true>(lds) : moe_blocks_per_cu<false>(lds);
-        const int64_t slots = (int64_t)dev.cu_count * per_cu;
-        const unsigned grid = (unsigned)(max_units < slots ? max_units : slots);
+        const bool one = P <= (1 << log2S);
         if (gate_up)
-            hipLaunchKernelGGL((moe_expert_kernel<true>), dim3(grid), dim3(kMoeThreads), lds, stream, wgu, expert_bytes,
-                               rows_out, P, log2S, x, (int)ldx, offsets, sorted, active, (int)n_exp, k, hidden,
-                               (int)(2 * f), rows, tiles);
+            e = one ? launch_expert_pass<true, true>(dev, wgu, expert_bytes, rows_out, P, log2S, x, (int)ldx, offsets,
+                                                     sorted, active, (int)n_exp, k, hidden, (int)(2 * f), rows, tiles,
+                                                     lds, stream)
+                    : launch_expert_pass<true, false>(dev, wgu, expert_bytes, rows_out, P, log2S, x, (int)ldx, offsets,
+                                                      sorted, active, (int)n_exp, k, hidden, (int)(2 * f), rows, tiles,
+                                                      lds, stream);
         else
-            hipLaunchKernelGGL((moe_expert_kernel<false>), dim3(grid), dim3(kMoeThreads), lds, stream, wdn,
-                               expert_bytes, rows_out, P, log2S, hidden, (int)(2 * f), offsets, sorted, active,
-                               (int)n_exp, k, outp, (int)h, rows, tiles);
-        e = hipGetLastError();
+            e = one ? launch_expert_pass<false, true>(dev, wdn, expert_bytes, rows_out, P, log2S, hidden, (int)(2 * f),
+                                                      offsets, sorted, active, (int)n_exp, k, outp, (int)h, rows, tiles,
+                                                      lds, stream)
+                    : launch_expert_pass<false, false>(dev, wdn, expert_bytes, rows_out, P, log2S, hidden,
+                                                       (int)(2 * f), offsets, sorted, active, (int)n_exp, k, outp,
+                                                       (int)h, rows, tiles, lds, stream);
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)m, (unsigned)((h + 255) / 256)), dim3(256), 0, stream, outp,
