@@ -178,6 +178,93 @@ __global__ __launch_bounds__(64 * kPlanWaves) void moe_plan_kernel(const int32_t
 
 // ------------------------------------------------------- 2./3. expert GEMV passes
 
+// Activation access: the 4 values of activation row m at k = 64*p + 4*c .. +3.
+// LDS copy in slot-major order: float4 index ((m*16 + c) * P + p), so the lanes of a
+// wave (consecutive p) read consecutive 16-byte vectors.
+struct XLds {
+    const float4* base;
+    int P;
+    __device__ __forceinline__ float4 get(int m, int p, int c) const { return base[(m * 16 + c) * P + p]; }
+};
+// One wave walks row groups first, first+stride, ... < end (G = 64/S rows each) of a
+// Q8_0 matrix (the lane layout and order of gemv_core.h).  For R = 2 the lane also multiplies row n + r_off (gate/up pairs).
+// out(n, acc) is called on the lane with slot 0 of each valid row n < n_out.
+// NRC: the rounds per row when known at compile time (1: a row fits the S lanes once),
+// 0 = computed from P (the per-item index arithmetic then divides by it).
+template <int M, int R, int NRC, class X, class Out>
+__device__ __forceinline__ void wave_rows(const uint8_t* __restrict__ w, int n_out, int r_off, int P, int log2S,
+                                          const X& xs, int first, int stride, int end, Out&& out) {
+    if (first >= end) return;
+    const int S = 1 << log2S;
+    const int G = 64 >> log2S;
+    const int lane = threadIdx.x & 63;
+    const int j = lane & (S - 1);
+    const int g = lane >> log2S;
+    const size_t row_bytes = (size_t)P * 68;
+    const int n_rounds = NRC ? NRC : (P + S - 1) / S;
+    const int n_items = ((end - 1 - first) / stride + 1) * n_rounds;
+
+    auto item = [&](int it, int& n, int& p) {
+        const int rg = first + (it / n_rounds) * stride;
+        n = rg * G + g;
+        p = j + S * (it % n_rounds);
+    };
+    // Loads are unconditional so the compiler keeps the next item's loads in flight
+    // (a load inside a branch makes it wait for all of them): a row past the matrix
+    // loads the last row, a pair past the row loads a pair of the same row; neither is
+    // multiplied or stored under its own index.
+    auto load_item = [&](int it, uint32_t(&wr)[R][17]) __attribute__((always_inline)) {
+        int n, p;
+        item(it, n, p);
+        const int nc = n < n_out ? n : n_out - 1;
+        const int pc = p < P ? p : p % P;
+#pragma unroll
+        for (int r = 0; r < R; ++r) load_pair(w + (size_t)(nc + r * r_off) * row_bytes + 68 * (size_t)pc, wr[r]);
+    };
+
+    float acc[R][M];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+
+    auto finish_item = [&](int it, const uint32_t(&wr)[R][17]) __attribute__((always_inline)) {
+        int n, p;
+        item(it, n, p);
+        const int nc = n < n_out ? n : n_out - 1;
+        if (p < P) mac_pair<M, R>(wr, xs, p, acc);
+        if (it % n_rounds == n_rounds - 1) {
+            for (int off = S >> 1; off >= 1; off >>= 1) {
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int m = 0; m < M; ++m) acc[r][m] += __shfl_xor(acc[r][m], off, 64);
+            }
+            // after the butterfly every lane of the row holds the same bits: all store
+            // (a lane past the matrix multiplies the last row and stores what its owner
+            // stores)
+            out(nc, acc);
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+        }
+    };
+
+    // Two register buffers, alternating: load item it+1 while multiplying item it.
+    uint32_t wa[R][17], wb[R][17];
+    load_item(0, wa);
+    int it = 0;
+    for (; it + 1 < n_items; it += 2) {
+        load_item(it + 1, wb);
+        finish_item(it, wa);
+        load_item(it + 2 < n_items ? it + 2 : it + 1, wa);  // past the end: a reload, unused
+        finish_item(it + 1, wb);
+    }
+    if (it < n_items) finish_item(it, wa);
+}
+
+
 // One pass of the experts' rows, one row per lane group (the lane layout and per-row
 // order of the one-row dense kernel: S lanes per row, lane j takes the pairs j, j + S,
 // ..., block chains in mac_pair, then the xor butterfly).
