@@ -132,10 +132,12 @@ def test_exact_arithmetic_bit_identical(q8, n, k, m, fused):
         assert_close(h, oracle.silu_ref(ref[:, :n]) * ref[:, n:], f"exact fused f={n} m={m}")
 
 
-# Many more row tiles than resident blocks with a short K: the rows kernel's persistent
-# walk over many tiles per block, every output against the oracle.
+# Many more row tiles than resident blocks with a short K: the persistent walk over many
+# tiles per block of the rows kernel and of its matrix-core form (9..16 rows), every output
+# against the oracle.
 @pytest.mark.parametrize("n,k,m,fused", [(40000, 256, 8, False), (40000, 256, 16, False), (20000, 512, 8, True),
-                                         (20000, 512, 3, True), (40000, 256, 1, False), (20000, 512, 1, True)])
+                                         (20000, 512, 3, True), (40000, 256, 1, False), (20000, 512, 1, True),
+                                         (20000, 512, 13, True), (30000, 1024, 10, False)])
 def test_many_tiles_vs_oracle(q8, n, k, m, fused):
     lib, torch, dev = q8
     w_rows = 2 * n if fused else n
