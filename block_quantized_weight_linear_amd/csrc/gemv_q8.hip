@@ -1057,6 +1057,220 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(MT
     }
 }
 
+// Several activation rows with K <= 4096, streamed (2..16 rows per launch).  One wave
+// per chunk of 16 pairs (up to four waves), each holding its lanes' activations for the
+// whole call in registers: lane (b, t) keeps pair 16w + b of activation rows t, 4 + t, ...
+// An item is a group of 4 weight rows (fused: 4 gate rows and their 4 up rows); each wave
+// copies its chunk of the item's rows (4 x 1088 bytes per weight row group) into its own
+// LDS ring with coalesced direct copies, D items ahead, reads its pair, and runs the
+// fp32 matrix-core form of the one-fma-per-weight arithmetic: v_mfma_f32_4x4x1_16b_f32
+// (one rounding per fma), block b of the instruction for pair b, four weight rows against
+// four activation rows, one instruction per input.  Per output: one chain per pair over
+// its 64 inputs in order, a fixed lane-exchange sum over the 16 pairs of the chunk (lane
+// swaps and row rotations, no LDS), then the chunks' sums added in chunk order.  The
+// matrix-core fp32 instructions and the VALU dequantization do not overlap on this chip,
+// so the per-item exchange and address work is kept to a few instructions; the copies of
+// a row group inside the matrix use one scalar base and fixed lane offsets.  The order
+// depends only on K, so every row of a call
+// with 2..255 rows is bit-identical whatever the other rows are; it is the class of these
+// K (the float32 rows kernel serves larger K).  Each wave leaves its chunk sums of every
+// item in LDS and runs on without waiting for the others; one barrier at the end, then
+// the block adds the chunks and stores (so no store is counted by the copies' vmcnt
+// waits).
+constexpr int kStreamMaxChunks = 4;
+
+// Sum of v[0..3] over the 16 lane groups of four (lane >> 2), each lane keeping one of the
+// four values: across the wave halves (v[0] with v[2], v[1] with v[3]: each half keeps one
+// of each pair), across row pairs (keeping one of the two), then within each row of 16
+// lanes (rotations by 8 and 4).  Which value a lane ends with follows from the exchanges
+// alone; reduce_scatter_tag runs them on the value indices.  Eight VALU instructions, no
+// LDS; the order of the additions is fixed.
+__device__ __forceinline__ float reduce_scatter_pairs(float v0, float v1, float v2, float v3) {
+    const auto s0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v0), __float_as_uint(v2), false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v1), __float_as_uint(v3), false, false);
+    const float u0 = __uint_as_float(s0[0]) + __uint_as_float(s0[1]);
+    const float u1 = __uint_as_float(s1[0]) + __uint_as_float(s1[1]);
+    const auto s2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(u0), __float_as_uint(u1), false, false);
+    float z = __uint_as_float(s2[0]) + __uint_as_float(s2[1]);
+    z += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(z), 0x128, 0xF, 0xF, false));  // row_ror:8
+    z += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(z), 0x124, 0xF, 0xF, false));  // row_ror:4
+    return z;
+}
+__device__ __forceinline__ float reduce_scatter_tag(const float (&v)[4]) {
+    const auto s0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[0]), __float_as_uint(v[2]), false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[1]), __float_as_uint(v[3]), false, false);
+    const auto s2 = __builtin_amdgcn_permlane16_swap(s0[0], s1[0], false, false);
+    return __uint_as_float(s2[0]);
+}
+
+template <int MT, bool SILU, int D>
+__global__ __launch_bounds__(64 * kStreamMaxChunks) __attribute__((amdgpu_waves_per_eu(MT <= 8 ? 2 : 1, 2)))
+void gemv_rows_stream_kernel(const uint8_t* __restrict__ w, int n_out, int P, const float* __restrict__ x, int ldx,
+                             int m_rows, float* __restrict__ y, int ldy) {
+    static_assert(MT % 4 == 0 && MT <= 16, "activation rows in groups of four, at most 16");
+    constexpr int QG = MT / 4;
+    constexpr int RG = SILU ? 2 : 1;  // weight row groups per item
+    static_assert(D * 5 * RG < 64, "copies in flight must fit the vmcnt counter");
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    extern __shared__ float4 smem4[];
+    uint8_t* smem = reinterpret_cast<uint8_t*>(smem4);
+    const int nc = (int)(blockDim.x >> 6);  // waves = chunks of the row
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lane = (int)(threadIdx.x & 63);
+    const int b = lane >> 2, t = lane & 3;
+    const int p = 16 * wv + b;
+    const bool live = p < P;
+    const int pc = live ? p : P - 1;
+    const size_t row_bytes = (size_t)P * 68;
+    const int seg = ((P - 16 * wv) < 16 ? (P - 16 * wv) : 16) * 68;  // bytes of the wave's chunk per row
+    const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(smem + (size_t)wv * (D * RG * kLdsItemBytes)));
+    const uint32_t* ring32 = reinterpret_cast<const uint32_t*>(smem + (size_t)wv * (D * RG * kLdsItemBytes));
+    constexpr int kPart = RG * 4 * MT;  // partial sums of a wave per item
+    float* part = reinterpret_cast<float*>(smem + (size_t)nc * D * RG * kLdsItemBytes);  // [items][nc][kPart]
+    const int row_groups = (n_out + 3) >> 2;
+    const int n_items = (row_groups - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+
+    // the lane's activations (rows past m_rows repeat the last one; a pair past the row: zeros)
+    float4 xr[QG][16];
+#pragma unroll
+    for (int q = 0; q < QG; ++q) {
+        const int m = 4 * q + t < m_rows ? 4 * q + t : m_rows - 1;
+        const float4* src = reinterpret_cast<const float4*>(x + (size_t)m * ldx + 64 * (size_t)pc);
+#pragma unroll
+        for (int c = 0; c < 16; ++c) xr[q][c] = src[c];
+    }
+    // the compiler's own wait (vmcnt 0, the other counters untouched): its wait insertion
+    // then knows the activations have landed and puts no vmcnt wait into the loop, where
+    // one would also drain the next item's copies
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    if (!live) {
+#pragma unroll
+        for (int q = 0; q < QG; ++q)
+#pragma unroll
+            for (int c = 0; c < 16; ++c) xr[q][c] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+
+    // the weight row (0..3) whose pair sum reduce_scatter_pairs leaves in this lane: the
+    // same exchanges applied once to the row numbers themselves
+    const int row_of_lane = [&] {
+        const float tags[4] = {0.0f, 1.0f, 2.0f, 3.0f};
+        return (int)reduce_scatter_tag(tags);
+    }();
+    const bool own = ((lane >> 2) & 3) == 0;  // one lane per (row, activation row) writes
+
+    // item i's rows of the wave's chunk into ring slot `slot`: 5 * RG vmcnt events.  LDS byte
+    // o of a row group's 4352 is byte o % 1088 of row o / 1088's chunk.  A short last chunk
+    // (a multiple of 4 pairs: seg a multiple of 272 bytes) repeats its own pairs past its
+    // end (byte o % 1088 % seg), so a lane past the row reads a whole real pair of its row
+    // (finite scale; multiplied by zero activations); rows past the matrix: the last row.
+    int crow[5], coff[5];  // the lane's row and byte of each copy (the same for every item)
+    uint32_t cbyte[5];     // ... as one offset from the row group's first row
+#pragma unroll
+    for (int c = 0; c < 5; ++c) {
+        const int o = c < 4 ? 1024 * c + 16 * lane : 4096 + 4 * lane;
+        crow[c] = o / 1088;
+        const int off = o - 1088 * crow[c];
+        coff[c] = 1088 * wv + (off < seg ? off : off % seg);
+        cbyte[c] = (uint32_t)(crow[c] * row_bytes) + (uint32_t)coff[c];
+    }
+    auto issue = [&](int i, int slot) __attribute__((always_inline)) {
+        const int rg = (int)blockIdx.x + i * (int)gridDim.x;
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+            const uint32_t dst = ring_lds + (uint32_t)((slot * RG + r) * kLdsItemBytes);
+            if (4 * rg + 3 < n_out) {  // all four rows in the matrix: one base, lane offsets
+                lds_copy_4352_gather_s<true>(w + (size_t)(4 * rg + r * n_out) * row_bytes, cbyte, dst);
+            } else {
+                const uint8_t* src[5];
+#pragma unroll
+                for (int c = 0; c < 5; ++c) {
+                    int n = 4 * rg + crow[c];
+                    n = n < n_out ? n : n_out - 1;
+                    src[c] = w + (size_t)(n + r * n_out) * row_bytes + coff[c];
+                }
+                lds_copy_4352_gather<true>(src, dst);
+            }
+        }
+    };
+
+    const int n_pro = n_items < D ? n_items : D;
+    static_for<D>([&](auto sc) __attribute__((always_inline)) {
+        constexpr int s0 = decltype(sc)::value;
+        if (s0 < n_pro) issue(s0, s0);
+    });
+    for (int i = 0; i < n_items; ++i) {
+        const int slot = i % D;
+        // items i+1 .. min(i+D-1, n_items-1) may stay in flight
+        const int rem = n_items - 1 - i;
+        if (rem >= D - 1) {
+            wait_vmcnt_mem<(D - 1) * 5 * RG>();
+        } else {
+            static_for<D - 1>([&](auto kc) __attribute__((always_inline)) {
+                constexpr int k = decltype(kc)::value;
+                if (rem == k) wait_vmcnt_mem<k * 5 * RG>();
+            });
+        }
+        uint32_t wr[RG][17];
+#pragma unroll
+        for (int r = 0; r < RG; ++r)
+#pragma unroll
+            for (int k = 0; k < 17; ++k) wr[r][k] = ring32[(slot * RG + r) * (kLdsItemBytes / 4) + t * 272 + b * 17 + k];
+        wait_lgkmcnt_mem<0>();
+        if (i + D < n_items) issue(i + D, slot);  // refill the slot just read
+
+        f32x4 acc[RG][QG];
+#pragma unroll
+        for (int r = 0; r < RG; ++r)
+#pragma unroll
+            for (int q = 0; q < QG; ++q) acc[r][q] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+        static_for<2>([&](auto hc) __attribute__((always_inline)) {
+            constexpr int HALF = decltype(hc)::value;
+#pragma unroll
+            for (int cc = 0; cc < 8; ++cc) {
+                float wf[RG][4];
+#pragma unroll
+                for (int r = 0; r < RG; ++r) FmtQ8_0::template weights<HALF>(wr[r], cc, wf[r], pc);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int r = 0; r < RG; ++r)
+#pragma unroll
+                        for (int q = 0; q < QG; ++q) {
+                            const float4 xv = xr[q][8 * HALF + cc];
+                            const float xe = e == 0 ? xv.x : e == 1 ? xv.y : e == 2 ? xv.z : xv.w;
+                            acc[r][q] = __builtin_amdgcn_mfma_f32_4x4x1f32(wf[r][e], xe, acc[r][q], 0, 0, 0);
+                        }
+            }
+        });
+        // register e of (r, q) holds weight row e of group r against activation row 4q + t
+        // for pair b; sum over the 16 pairs, scattering the four rows over the lanes
+#pragma unroll
+        for (int r = 0; r < RG; ++r)
+#pragma unroll
+            for (int q = 0; q < QG; ++q) {
+                const float v = reduce_scatter_pairs(acc[r][q][0], acc[r][q][1], acc[r][q][2], acc[r][q][3]);
+                if (own) part[(i * nc + wv) * kPart + (r * 4 + row_of_lane) * MT + 4 * q + t] = v;
+            }
+    }
+    __syncthreads();
+    // output (item i, weight row j / MT of its group, activation row j % MT)
+    for (int o = (int)threadIdx.x; o < n_items * 4 * MT; o += (int)blockDim.x) {
+        const int i = o / (4 * MT), j = o - i * (4 * MT);
+        const float* pi = part + (size_t)i * nc * kPart + j;
+        float s = pi[0];
+        for (int c = 1; c < nc; ++c) s += pi[c * kPart];
+        if constexpr (SILU) {
+            float u = pi[4 * MT];
+            for (int c = 1; c < nc; ++c) u += pi[c * kPart + 4 * MT];
+            s = silu_mul(s, u);
+        }
+        const int n = 4 * ((int)blockIdx.x + i * (int)gridDim.x) + j / MT;
+        const int m = j % MT;
+        if (n < n_out && m < m_rows) y[(size_t)m * ldy + n] = s;
+    }
+}
+
 namespace {
 
 template <class Fmt, int R, int NR, int D, int NW, bool NT = false>
@@ -1251,6 +1465,70 @@ hipError_t launch_rows_mfma_m(const DeviceInfo& dev, const uint8_t* w, int n_out
     return launch_rows_mfma<Fmt, 16, SILU>(dev, w, n_out, P, x, ldx, m, y, ldy, stream);
 }
 
+// Streaming rows form (K <= 4096): dynamic LDS = the rings and the chunk sums of every
+// item of the block.
+constexpr int kStreamSlots = 2;
+inline size_t stream_lds_bytes(int n_out, int P, int mt, bool silu, int64_t grid) {
+    const int nc = (P + 15) >> 4, rg = silu ? 2 : 1;
+    const int64_t row_groups = (n_out + 3) >> 2;
+    const int64_t items = (row_groups + grid - 1) / grid;
+    return (size_t)nc * kStreamSlots * rg * kLdsItemBytes + (size_t)(items * nc * rg * 4 * mt) * 4;
+}
+constexpr size_t kStreamLdsMax = 160 * 1024;
+
+// The form applies to one call when K <= 4096 and, for 16 activation rows on a grid of one
+// block per CU, its LDS fits (the chunk sums of every item of a block wait there).
+inline bool stream_fits(const DeviceInfo& dev, int64_t n_out, int P, bool silu) {
+    if (P > 16 * kStreamMaxChunks || n_out > (int64_t)1 << 28) return false;
+    return stream_lds_bytes((int)n_out, P, 16, silu, dev.cu_count) <= kStreamLdsMax;
+}
+
+template <int MT, bool SILU>
+hipError_t launch_rows_stream_mt(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, const float* x, int ldx,
+                                 int m_rows, float* y, int ldy, hipStream_t stream) {
+    auto kernel = gemv_rows_stream_kernel<MT, SILU, kStreamSlots>;
+    const int threads = 64 * ((P + 15) >> 4);
+    const int64_t row_groups = (n_out + 3) >> 2;
+    static thread_local int attr_dev = -1;
+    struct Occ { int dev, threads, lds, per_cu; };
+    static thread_local Occ occ[4] = {{-1, 0, 0, 1}, {-1, 0, 0, 1}, {-1, 0, 0, 1}, {-1, 0, 0, 1}};
+    static thread_local int occ_next = 0;
+    if (attr_dev != dev.device) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kStreamLdsMax);
+        if (e != hipSuccess) return e;
+        attr_dev = dev.device;
+    }
+    // two blocks per CU when the LDS of that grid (fewer items per block) lets two stay
+    // resident, else one
+    const int64_t g2 = row_groups < 2 * dev.cu_count ? row_groups : 2 * dev.cu_count;
+    const int lds2 = (int)stream_lds_bytes(n_out, P, MT, SILU, g2);
+    int per_cu = 0;
+    for (const Occ& o : occ)
+        if (o.dev == dev.device && o.threads == threads && o.lds == lds2) per_cu = o.per_cu;
+    if (per_cu == 0) {
+        int fit = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&fit, kernel, threads, lds2) != hipSuccess) fit = 0;
+        per_cu = fit >= 2 ? 2 : 1;
+        occ[occ_next] = {dev.device, threads, lds2, per_cu};
+        occ_next = (occ_next + 1) & 3;
+    }
+    const int64_t slots = (int64_t)dev.cu_count * per_cu;
+    const int grid = (int)(row_groups < slots ? row_groups : slots);
+    const size_t lds = stream_lds_bytes(n_out, P, MT, SILU, grid);
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), lds, stream, w, n_out, P, x, ldx, m_rows, y, ldy);
+    return hipGetLastError();
+}
+
+template <bool SILU>
+hipError_t launch_rows_stream(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, const float* x, int ldx,
+                              int m, float* y, int ldy, hipStream_t stream) {
+    if (m <= 4) return launch_rows_stream_mt<4, SILU>(dev, w, n_out, P, x, ldx, m, y, ldy, stream);
+    if (m <= 8) return launch_rows_stream_mt<8, SILU>(dev, w, n_out, P, x, ldx, m, y, ldy, stream);
+    if (m <= 12) return launch_rows_stream_mt<12, SILU>(dev, w, n_out, P, x, ldx, m, y, ldy, stream);
+    return launch_rows_stream_mt<16, SILU>(dev, w, n_out, P, x, ldx, m, y, ldy, stream);
+}
+
 template <int M, int R>
 hipError_t launch_m(const DeviceInfo& dev, const uint8_t* w, int n_out, int P, int log2S, const float* x, int ldx,
                     float* y, int ldy, hipStream_t stream) {
@@ -1386,6 +1664,18 @@ hipError_t launch_gemv_q8(const DeviceInfo& dev, const uint8_t* w, int64_t n_out
     if (m == 1)  // one row with K beyond the one-row kernel: the float32 rows kernel
         return silu_pairs ? launch_r<2>(dev, w, (int)n_out, P, log2S, x, (int)ldx, 1, y, (int)ldy, stream)
                           : launch_r<1>(dev, w, (int)n_out, P, log2S, x, (int)ldx, 1, y, (int)ldy, stream);
+    // Several rows with K <= 4096: the streaming form, in launches of up to 16 rows.
+    if (stream_fits(dev, n_out, P, silu_pairs)) {
+        for (int64_t m0 = 0; m0 < m; m0 += 16) {
+            const int mm = (int)((m - m0) < 16 ? (m - m0) : 16);
+            hipError_t e = silu_pairs ? launch_rows_stream<true>(dev, w, (int)n_out, P, x + m0 * ldx, (int)ldx, mm,
+                                                                 y + m0 * ldy, (int)ldy, stream)
+                                      : launch_rows_stream<false>(dev, w, (int)n_out, P, x + m0 * ldx, (int)ldx, mm,
+                                                                  y + m0 * ldy, (int)ldy, stream);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
     // Several rows, in launches of up to 16: 9..16 rows on the matrix-core form (one pass
     // over the weights), up to 8 on the float32 rows kernel, which is faster there; both
     // give the same bits.  Measured on the Qwen3-8B linears at 16 rows (one matrix-core

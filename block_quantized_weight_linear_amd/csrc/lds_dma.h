@@ -93,4 +93,76 @@ __device__ __forceinline__ void lds_copy_4352(const uint8_t* src, int len, uint3
 #undef Q8K_LDS_COPY_4352
 }
 
+// 4352 bytes into lds .. lds + 4351 from per-lane sources, as the same five direct-to-LDS
+// loads (five vmcnt events): copy c < 4 moves 16 bytes from p[c] to lds + 1024c + 16*lane,
+// copy 4 moves 4 bytes from p[4] to lds + 4096 + 4*lane.  The caller maps each destination
+// to its source (a gather: the bytes may come from different rows).
+template <bool NT = false>
+__device__ __forceinline__ void lds_copy_4352_gather(const uint8_t* const (&p)[5], uint32_t lds) {
+    uint32_t saved;
+#define Q8K_LDS_GATHER_4352(H)                                                                               \
+    asm volatile(                                                                                              \
+        "s_mov_b32 %0, m0\n\t"                                                                                 \
+        "s_mov_b32 m0, %6\n\t"                                                                                 \
+        "s_nop 0\n\t"                                                                                          \
+        "global_load_lds_dwordx4 %1, off" H "\n\t"                                                             \
+        "s_mov_b32 m0, %7\n\t"                                                                                 \
+        "s_nop 0\n\t"                                                                                          \
+        "global_load_lds_dwordx4 %2, off" H "\n\t"                                                             \
+        "s_mov_b32 m0, %8\n\t"                                                                                 \
+        "s_nop 0\n\t"                                                                                          \
+        "global_load_lds_dwordx4 %3, off" H "\n\t"                                                             \
+        "s_mov_b32 m0, %9\n\t"                                                                                 \
+        "s_nop 0\n\t"                                                                                          \
+        "global_load_lds_dwordx4 %4, off" H "\n\t"                                                             \
+        "s_mov_b32 m0, %10\n\t"                                                                                \
+        "s_nop 0\n\t"                                                                                          \
+        "global_load_lds_dword %5, off" H "\n\t"                                                               \
+        "s_mov_b32 m0, %0"                                                                                     \
+        : "=&s"(saved)                                                                                         \
+        : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "s"(lds), "s"(lds + 1024), "s"(lds + 2048),    \
+          "s"(lds + 3072), "s"(lds + 4096)                                                                     \
+        : "memory")
+    if constexpr (NT)
+        Q8K_LDS_GATHER_4352(" nt");
+    else
+        Q8K_LDS_GATHER_4352("");
+#undef Q8K_LDS_GATHER_4352
+}
+
+// The gather above with the source given as one wave-uniform base (an SGPR pair) and five
+// 32-bit per-lane byte offsets from it: no per-lane 64-bit address arithmetic.
+template <bool NT = false>
+__device__ __forceinline__ void lds_copy_4352_gather_s(const uint8_t* base, const uint32_t (&off)[5], uint32_t lds) {
+    uint32_t saved;
+#define Q8K_LDS_GATHER_4352_S(H)                                                                             \
+    asm volatile(                                                                                              \
+        "s_mov_b32 %0, m0\n\t"                                                                                 \
+        "s_mov_b32 m0, %7\n\t"                                                                                 \
+        "s_nop 0\n\t"                                                                                          \
+        "global_load_lds_dwordx4 %1, %6" H "\n\t"                                                              \
+        "s_mov_b32 m0, %8\n\t"                                                                                 \
+        "s_nop 0\n\t"                                                                                          \
+        "global_load_lds_dwordx4 %2, %6" H "\n\t"                                                              \
+        "s_mov_b32 m0, %9\n\t"                                                                                 \
+        "s_nop 0\n\t"                                                                                          \
+        "global_load_lds_dwordx4 %3, %6" H "\n\t"                                                              \
+        "s_mov_b32 m0, %10\n\t"                                                                                \
+        "s_nop 0\n\t"                                                                                          \
+        "global_load_lds_dwordx4 %4, %6" H "\n\t"                                                              \
+        "s_mov_b32 m0, %11\n\t"                                                                                \
+        "s_nop 0\n\t"                                                                                          \
+        "global_load_lds_dword %5, %6" H "\n\t"                                                                \
+        "s_mov_b32 m0, %0"                                                                                     \
+        : "=&s"(saved)                                                                                         \
+        : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "v"(off[4]), "s"(base), "s"(lds), "s"(lds + 1024), \
+          "s"(lds + 2048), "s"(lds + 3072), "s"(lds + 4096)                                                    \
+        : "memory")
+    if constexpr (NT)
+        Q8K_LDS_GATHER_4352_S(" nt");
+    else
+        Q8K_LDS_GATHER_4352_S("");
+#undef Q8K_LDS_GATHER_4352_S
+}
+
 }  // namespace q8k
