@@ -1228,9 +1228,13 @@ void gemv_rows_stream_kernel(const uint8_t* __restrict__ w, int n_out, int P, co
             constexpr int HALF = decltype(hc)::value;
 #pragma unroll
             for (int cc = 0; cc < 8; ++cc) {
+                // the step's weights as one batch of VALU work, then its MFMAs back to back:
+                // switching between the two costs cycles, so the compiler's interleaving
+                // (one weight, then the MFMAs that read it) is held off
                 float wf[RG][4];
 #pragma unroll
                 for (int r = 0; r < RG; ++r) FmtQ8_0::template weights<HALF>(wr[r], cc, wf[r], pc);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
 #pragma unroll
@@ -1241,6 +1245,7 @@ void gemv_rows_stream_kernel(const uint8_t* __restrict__ w, int n_out, int P, co
                             const float xe = e == 0 ? xv.x : e == 1 ? xv.y : e == 2 ? xv.z : xv.w;
                             acc[r][q] = __builtin_amdgcn_mfma_f32_4x4x1f32(wf[r][e], xe, acc[r][q], 0, 0, 0);
                         }
+                __builtin_amdgcn_sched_barrier(0);
             }
         });
         // register e of (r, q) holds weight row e of group r against activation row 4q + t
