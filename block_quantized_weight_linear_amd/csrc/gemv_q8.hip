@@ -920,9 +920,10 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(MT
         constexpr int HALF = decltype(half)::value;
         const int ch = h + 2 * st;
         // a chunk past the row's end (partial: some pairs missing) masks its dead pairs.
-        // Per quant dword: the activations of the 4 inputs, then row group by row group
-        // its 4 weights and the MFMAs that use them (short register lives; every
-        // accumulator still sees its inputs in increasing order).
+        // Per quant dword: the activations of the 4 inputs and the 4 weights of every row
+        // group as one batch, then all the MFMAs that use them back to back (the fp32
+        // matrix-core instructions and VALU work do not overlap, and alternating them
+        // costs cycles); every accumulator still sees its inputs in increasing order.
         auto body = [&](auto partial) __attribute__((always_inline)) {
             constexpr bool PARTIAL = decltype(partial)::value;
             const bool live = 16 * ch + b < P;
@@ -936,22 +937,26 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(MT
                         if (!live) xv[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
                     }
                 }
+                float wf[RR][4];
 #pragma unroll
                 for (int g = 0; g < RR; ++g) {
-                    float wf[4];
-                    Fmt::template weights<HALF>(wc[g], cc, wf, 16 * ch + b);
+                    Fmt::template weights<HALF>(wc[g], cc, wf[g], 16 * ch + b);
                     if constexpr (PARTIAL) {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) wf[e] = live ? wf[e] : 0.0f;
+                        for (int e = 0; e < 4; ++e) wf[g][e] = live ? wf[g][e] : 0.0f;
                     }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int g = 0; g < RR; ++g)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
 #pragma unroll
                         for (int q = 0; q < QG; ++q) {
                             const float xe = e == 0 ? xv[q].x : e == 1 ? xv[q].y : e == 2 ? xv[q].z : xv[q].w;
-                            acc[g][q] = __builtin_amdgcn_mfma_f32_4x4x1f32(wf[e], xe, acc[g][q], 0, 0, 0);
+                            acc[g][q] = __builtin_amdgcn_mfma_f32_4x4x1f32(wf[g][e], xe, acc[g][q], 0, 0, 0);
                         }
-                }
+                __builtin_amdgcn_sched_barrier(0);
             }
         };
         if (ch < nch) {  // wave-uniform
