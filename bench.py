@@ -35,6 +35,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix cores
 # float32 VALU lane operations per second without packed instructions (the build disables
 # packed float32): 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
 VALU_LANE_OPS_PER_S = 256 * 64 * 2.4e9
+# dense float32 matrix cores (v_mfma_f32_4x4x1_16b_f32: 512 flops per 8 cycles per SIMD)
+MFMA_FP32_PEAK_FLOPS = 157.3e12
 METRIC = "effective weight GB/s & % of HBM peak for Q8_0 linear at M=1/8/16; decode tok/s"
 
 
@@ -245,12 +247,15 @@ def bench_block(args, torch, dev, q8, spec, m_values):
         res["gate_up_avg_us"] = round(avg_ms * 1e3, 3)
         res["gate_up_gbps"] = round(gate_up_bytes / (avg_ms * 1e-3) / 1e9, 2)
         if m > 1:
-            # VALU roofline of the float32 rows kernel: per weight one int8 -> float32
-            # conversion and one scale multiply (shared by the rows) plus one fma per
-            # activation row, against the non-packed float32 lane rate of the chip
+            # compute floor of the streaming rows form that runs this gate_up (K = 4096): per
+            # weight one int8 -> float32 conversion and one scale multiply on the VALU, and
+            # the fp32 matrix cores over the activation rows rounded up to four; the two
+            # engines do not overlap, so the floor is the sum of both times
             weights = gu.n * gu.k
-            lane_ops = weights * (2 + m)
-            res["gate_up_valu_frac"] = round(lane_ops / (avg_ms * 1e-3) / VALU_LANE_OPS_PER_S, 4)
+            rows_mfma = 4 * ((m + 3) // 4)
+            floor_s = weights * 2 / VALU_LANE_OPS_PER_S + 2.0 * weights * rows_mfma / MFMA_FP32_PEAK_FLOPS
+            res["gate_up_compute_floor_us"] = round(floor_s * 1e6, 3)
+            res["gate_up_compute_frac"] = round(floor_s / (avg_ms * 1e-3), 4)
         out[m] = res
         log(f"M={m}: {res}")
     return stack, out, gate_up_bytes
