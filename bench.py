@@ -247,13 +247,15 @@ def bench_block(args, torch, dev, q8, spec, m_values):
         res["gate_up_avg_us"] = round(avg_ms * 1e3, 3)
         res["gate_up_gbps"] = round(gate_up_bytes / (avg_ms * 1e-3) / 1e9, 2)
         if m > 1:
-            # compute floor of the streaming rows form that runs this gate_up (K = 4096): per
-            # weight one int8 -> float32 conversion and one scale multiply on the VALU, and
-            # the fp32 matrix cores over the activation rows rounded up to four; the two
-            # engines do not overlap, so the floor is the sum of both times
+            # compute floor of the streaming rows form that runs this gate_up (K = 4096): on
+            # the VALU one int8 -> float32 conversion per weight and, per 32-weight block and
+            # lane, four scale broadcasts and one fma per group of four activation rows and
+            # weight row (acc = fma(d, t, acc)); on the fp32 matrix cores the activation rows
+            # rounded up to four; the two engines do not overlap, so the floor is the sum
             weights = gu.n * gu.k
             rows_mfma = 4 * ((m + 3) // 4)
-            floor_s = weights * 2 / VALU_LANE_OPS_PER_S + 2.0 * weights * rows_mfma / MFMA_FP32_PEAK_FLOPS
+            lane_ops = weights * (1.0 + (1 + rows_mfma // 4) / 8.0)
+            floor_s = lane_ops / VALU_LANE_OPS_PER_S + 2.0 * weights * rows_mfma / MFMA_FP32_PEAK_FLOPS
             res["gate_up_compute_floor_us"] = round(floor_s * 1e6, 3)
             res["gate_up_compute_frac"] = round(floor_s / (avg_ms * 1e-3), 4)
         out[m] = res

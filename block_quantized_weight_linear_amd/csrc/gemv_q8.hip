@@ -1068,11 +1068,13 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(MT
 // An item is a group of 4 weight rows (fused: 4 gate rows and their 4 up rows); each wave
 // copies its chunk of the item's rows (4 x 1088 bytes per weight row group) into its own
 // LDS ring with coalesced direct copies, D items ahead, reads its pair, and runs the
-// fp32 matrix-core form of the one-fma-per-weight arithmetic: v_mfma_f32_4x4x1_16b_f32
-// (one rounding per fma), block b of the instruction for pair b, four weight rows against
-// four activation rows, one instruction per input.  Per output: one chain per pair over
-// its 64 inputs in order, a fixed lane-exchange sum over the 16 pairs of the chunk (lane
-// swaps and row rotations, no LDS), then the chunks' sums added in chunk order.  The
+// per-block arithmetic of the one-row kernel on the fp32 matrix cores: per Q8_0 block
+// t = sum q*x as a chain of v_mfma_f32_4x4x1_16b_f32 (the quants exact in float32, one
+// rounding per fma; block b of the instruction for pair b, four weight rows against four
+// activation rows, one instruction per input), then acc = fma(d, t, acc) on the VALU
+// (block 0, then block 1 of the pair).  Per output: that chain per pair, a fixed
+// lane-exchange sum over the 16 pairs of the chunk (lane swaps and row rotations, no
+// LDS), then the chunks' sums added in chunk order.  The
 // matrix-core fp32 instructions and the VALU dequantization do not overlap on this chip,
 // so the per-item exchange and address work is kept to a few instructions; the copies of
 // a row group inside the matrix use one scalar base and fixed lane offsets.  The order
@@ -1229,16 +1231,45 @@ void gemv_rows_stream_kernel(const uint8_t* __restrict__ w, int n_out, int P, co
         for (int r = 0; r < RG; ++r)
 #pragma unroll
             for (int q = 0; q < QG; ++q) acc[r][q] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+        // per block (half of the pair): t = sum q*x over its 32 inputs on the matrix cores
+        // (the quants exact in float32), then acc = fma(d, t, acc) on the VALU
         static_for<2>([&](auto hc) __attribute__((always_inline)) {
             constexpr int HALF = decltype(hc)::value;
+            // register e holds weight row e, whose scale lane 4b + e holds (its own row)
+            float dr[RG][4];
+#pragma unroll
+            for (int r = 0; r < RG; ++r) {
+                const float dl = HALF == 0 ? half_lo(wr[r][0]) : half_hi(wr[r][8]);
+                static_for<4>([&](auto ec) __attribute__((always_inline)) {  // quad_perm [e, e, e, e]
+                    constexpr int e = decltype(ec)::value;
+                    dr[r][e] = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(dl), 0x55 * e, 0xF, 0xF, false));
+                });
+            }
+            f32x4 blk[RG][QG];
+#pragma unroll
+            for (int r = 0; r < RG; ++r)
+#pragma unroll
+                for (int q = 0; q < QG; ++q) blk[r][q] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int cc = 0; cc < 8; ++cc) {
-                // the step's weights as one batch of VALU work, then its MFMAs back to back:
+                // the step's quants as one batch of VALU work, then its MFMAs back to back:
                 // switching between the two costs cycles, so the compiler's interleaving
                 // (one weight, then the MFMAs that read it) is held off
-                float wf[RG][4];
+                float wq[RG][4];
 #pragma unroll
-                for (int r = 0; r < RG; ++r) FmtQ8_0::template weights<HALF>(wr[r], cc, wf[r], pc);
+                for (int r = 0; r < RG; ++r) {
+                    if constexpr (HALF == 0) {  // quants at bytes 2..33 of the pair
+                        wq[r][0] = sbyte<2>(wr[r][cc]);
+                        wq[r][1] = sbyte<3>(wr[r][cc]);
+                        wq[r][2] = sbyte<0>(wr[r][cc + 1]);
+                        wq[r][3] = sbyte<1>(wr[r][cc + 1]);
+                    } else {  // quants in dwords 9..16
+                        wq[r][0] = sbyte<0>(wr[r][9 + cc]);
+                        wq[r][1] = sbyte<1>(wr[r][9 + cc]);
+                        wq[r][2] = sbyte<2>(wr[r][9 + cc]);
+                        wq[r][3] = sbyte<3>(wr[r][9 + cc]);
+                    }
+                }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
@@ -1248,10 +1279,16 @@ void gemv_rows_stream_kernel(const uint8_t* __restrict__ w, int n_out, int P, co
                         for (int q = 0; q < QG; ++q) {
                             const float4 xv = xr[q][8 * HALF + cc];
                             const float xe = e == 0 ? xv.x : e == 1 ? xv.y : e == 2 ? xv.z : xv.w;
-                            acc[r][q] = __builtin_amdgcn_mfma_f32_4x4x1f32(wf[r][e], xe, acc[r][q], 0, 0, 0);
+                            blk[r][q] = __builtin_amdgcn_mfma_f32_4x4x1f32(wq[r][e], xe, blk[r][q], 0, 0, 0);
                         }
                 __builtin_amdgcn_sched_barrier(0);
             }
+#pragma unroll
+            for (int r = 0; r < RG; ++r)
+#pragma unroll
+                for (int q = 0; q < QG; ++q)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[r][q][e] = __builtin_fmaf(dr[r][e], blk[r][q][e], acc[r][q][e]);
         });
         // register e of (r, q) holds weight row e of group r against activation row 4q + t
         // for pair b; sum over the 16 pairs, scattering the four rows over the lanes
