@@ -80,6 +80,23 @@ struct FmtQ8_0 {  // 68 bytes: [d0 | 32 q] [d1 | 32 q]
                                                    const float (&)[2], float (&acc)[R][1], int);
 };
 
+// The 4 quants (exact in float32, no scale) of inputs 4*cc .. 4*cc+3 of block HALF of a
+// Q8_0 pair held as 17 dwords (the layout FmtQ8_0::weights reads).
+template <int HALF>
+__device__ __forceinline__ void q8_quants(const uint32_t (&w)[17], int cc, float (&wq)[4]) {
+    if constexpr (HALF == 0) {  // quants at bytes 2..33
+        wq[0] = sbyte<2>(w[cc]);
+        wq[1] = sbyte<3>(w[cc]);
+        wq[2] = sbyte<0>(w[cc + 1]);
+        wq[3] = sbyte<1>(w[cc + 1]);
+    } else {  // quants in dwords 9..16
+        wq[0] = sbyte<0>(w[9 + cc]);
+        wq[1] = sbyte<1>(w[9 + cc]);
+        wq[2] = sbyte<2>(w[9 + cc]);
+        wq[3] = sbyte<3>(w[9 + cc]);
+    }
+}
+
 // GGUF Q4_0: 36 bytes a pair, [d0 | 16 bytes] [d1 | 16 bytes]; weight j < 16 of a block is
 // the low nibble of its byte j, weight j + 16 the high nibble; w = d * (nibble - 8), exact
 // in float32 (a 4-bit integer times an 11-bit scale).
@@ -625,15 +642,16 @@ __global__ __launch_bounds__(64 * NW) void gemv_one_row_kernel(const uint8_t* __
 // rows (or row pairs) per lane, so each activation value read from LDS feeds R (or 2R)
 // rows.  Each step copies both groups' activation chunks into slot-major LDS with
 // direct-to-LDS loads (no register round trip); the weights of the step after next are
-// loaded while a step is multiplied (a ring of two steps in registers).  Weights are
-// dequantized exactly (fp32(d) * q needs at most 19 significant bits), one fma per
-// weight and activation row.
+// loaded while a step is multiplied (a ring of two steps in registers).  Q8_0: per block
+// t = fma chain of q_k * x_k (the quants exact in float32), then acc = fma(d, t, acc);
+// the other formats: weights dequantized exactly in float32, one fma per weight and
+// activation row.
 //
-// Per-output order: acc = fma(w_k, x_k, acc) over the lane's weights (its pair of each
-// of the group's chunks in increasing order, inputs in increasing order), the xor
-// butterfly over the 16 lanes (8, 4, 2, 1), then group 0's sum + group 1's sum.  It
-// depends only on K, never on M or R, so every row of a 2..255-row call is bit-identical
-// to the same row in any other such call.
+// Per-output order: over the lane's weights (its pair of each of the group's chunks in
+// increasing order, blocks and inputs in increasing order), the xor butterfly over the
+// 16 lanes (8, 4, 2, 1), then group 0's sum + group 1's sum.  It depends only on K,
+// never on M or R, so every row of a 2..255-row call is bit-identical to the same row in
+// any other such call.
 constexpr int kRowsThreads = 256;
 
 template <class Fmt, int M, int R, bool SILU>
@@ -717,20 +735,53 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(1,
         constexpr int HALF = decltype(half)::value;
         const int ch = h + 2 * st;
         if (ch < nch && 16 * ch + j < P) {
+            if constexpr (std::is_same<Fmt, FmtQ8_0>::value) {
+                // Q8_0: per block t = sum q*x (the quants exact in float32), then
+                // acc = fma(d, t, acc); d is the lane's own (its pair's block HALF)
+                float t[RR][M];
 #pragma unroll
-            for (int cc = 0; cc < 8; ++cc) {
-                float wf[RR][4];
+                for (int r = 0; r < RR; ++r)
 #pragma unroll
-                for (int r = 0; r < RR; ++r) Fmt::template weights<HALF>(wc[r], cc, wf[r], 16 * ch + j);
+                    for (int m = 0; m < M; ++m) t[r][m] = 0.0f;
 #pragma unroll
-                for (int m = 0; m < M; ++m) {
-                    const float4 xv = xs[(m * 8 + cc) * 16 + j];
+                for (int cc = 0; cc < 8; ++cc) {
+                    float wq[RR][4];
 #pragma unroll
-                    for (int r = 0; r < RR; ++r) {
-                        acc[r][m] = __builtin_fmaf(wf[r][0], xv.x, acc[r][m]);
-                        acc[r][m] = __builtin_fmaf(wf[r][1], xv.y, acc[r][m]);
-                        acc[r][m] = __builtin_fmaf(wf[r][2], xv.z, acc[r][m]);
-                        acc[r][m] = __builtin_fmaf(wf[r][3], xv.w, acc[r][m]);
+                    for (int r = 0; r < RR; ++r) q8_quants<HALF>(wc[r], cc, wq[r]);
+#pragma unroll
+                    for (int m = 0; m < M; ++m) {
+                        const float4 xv = xs[(m * 8 + cc) * 16 + j];
+#pragma unroll
+                        for (int r = 0; r < RR; ++r) {
+                            t[r][m] = __builtin_fmaf(wq[r][0], xv.x, t[r][m]);
+                            t[r][m] = __builtin_fmaf(wq[r][1], xv.y, t[r][m]);
+                            t[r][m] = __builtin_fmaf(wq[r][2], xv.z, t[r][m]);
+                            t[r][m] = __builtin_fmaf(wq[r][3], xv.w, t[r][m]);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < RR; ++r) {
+                    const float d = HALF == 0 ? half_lo(wc[r][0]) : half_hi(wc[r][8]);
+#pragma unroll
+                    for (int m = 0; m < M; ++m) acc[r][m] = __builtin_fmaf(d, t[r][m], acc[r][m]);
+                }
+            } else {
+#pragma unroll
+                for (int cc = 0; cc < 8; ++cc) {
+                    float wf[RR][4];
+#pragma unroll
+                    for (int r = 0; r < RR; ++r) Fmt::template weights<HALF>(wc[r], cc, wf[r], 16 * ch + j);
+#pragma unroll
+                    for (int m = 0; m < M; ++m) {
+                        const float4 xv = xs[(m * 8 + cc) * 16 + j];
+#pragma unroll
+                        for (int r = 0; r < RR; ++r) {
+                            acc[r][m] = __builtin_fmaf(wf[r][0], xv.x, acc[r][m]);
+                            acc[r][m] = __builtin_fmaf(wf[r][1], xv.y, acc[r][m]);
+                            acc[r][m] = __builtin_fmaf(wf[r][2], xv.z, acc[r][m]);
+                            acc[r][m] = __builtin_fmaf(wf[r][3], xv.w, acc[r][m]);
+                        }
                     }
                 }
             }
@@ -927,6 +978,18 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(MT
         auto body = [&](auto partial) __attribute__((always_inline)) {
             constexpr bool PARTIAL = decltype(partial)::value;
             const bool live = 16 * ch + b < P;
+            // Q8_0: per block t = sum q*x on the matrix cores (the quants exact in float32),
+            // then acc = fma(d, t, acc), as the rows kernel; other formats: the exact weights,
+            // one fma per weight.  Either way register e holds weight row slot e, whose
+            // block scale lane 4b + e holds (its own row).
+            constexpr bool kBlockScale = std::is_same<Fmt, FmtQ8_0>::value;
+            f32x4 blk[RR][QG];
+            if constexpr (kBlockScale) {
+#pragma unroll
+                for (int g = 0; g < RR; ++g)
+#pragma unroll
+                    for (int q = 0; q < QG; ++q) blk[g][q] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+            }
 #pragma unroll
             for (int cc = 0; cc < 8; ++cc) {
                 float4 xv[QG];
@@ -940,7 +1003,10 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(MT
                 float wf[RR][4];
 #pragma unroll
                 for (int g = 0; g < RR; ++g) {
-                    Fmt::template weights<HALF>(wc[g], cc, wf[g], 16 * ch + b);
+                    if constexpr (kBlockScale)
+                        q8_quants<HALF>(wc[g], cc, wf[g]);
+                    else
+                        Fmt::template weights<HALF>(wc[g], cc, wf[g], 16 * ch + b);
                     if constexpr (PARTIAL) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e) wf[g][e] = live ? wf[g][e] : 0.0f;
@@ -954,9 +1020,27 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(MT
 #pragma unroll
                         for (int q = 0; q < QG; ++q) {
                             const float xe = e == 0 ? xv[q].x : e == 1 ? xv[q].y : e == 2 ? xv[q].z : xv[q].w;
-                            acc[g][q] = __builtin_amdgcn_mfma_f32_4x4x1f32(wf[g][e], xe, acc[g][q], 0, 0, 0);
+                            if constexpr (kBlockScale)
+                                blk[g][q] = __builtin_amdgcn_mfma_f32_4x4x1f32(wf[g][e], xe, blk[g][q], 0, 0, 0);
+                            else
+                                acc[g][q] = __builtin_amdgcn_mfma_f32_4x4x1f32(wf[g][e], xe, acc[g][q], 0, 0, 0);
                         }
                 __builtin_amdgcn_sched_barrier(0);
+            }
+            if constexpr (kBlockScale) {
+#pragma unroll
+                for (int g = 0; g < RR; ++g) {
+                    const float dl = HALF == 0 ? half_lo(wc[g][0]) : half_hi(wc[g][8]);
+                    float dr[4];
+                    static_for<4>([&](auto ec) __attribute__((always_inline)) {  // quad_perm [e, e, e, e]
+                        constexpr int e = decltype(ec)::value;
+                        dr[e] = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(dl), 0x55 * e, 0xF, 0xF, false));
+                    });
+#pragma unroll
+                    for (int q = 0; q < QG; ++q)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[g][q][e] = __builtin_fmaf(dr[e], blk[g][q][e], acc[g][q][e]);
+                }
             }
         };
         if (ch < nch) {  // wave-uniform
@@ -1257,19 +1341,7 @@ void gemv_rows_stream_kernel(const uint8_t* __restrict__ w, int n_out, int P, co
                 // (one weight, then the MFMAs that read it) is held off
                 float wq[RG][4];
 #pragma unroll
-                for (int r = 0; r < RG; ++r) {
-                    if constexpr (HALF == 0) {  // quants at bytes 2..33 of the pair
-                        wq[r][0] = sbyte<2>(wr[r][cc]);
-                        wq[r][1] = sbyte<3>(wr[r][cc]);
-                        wq[r][2] = sbyte<0>(wr[r][cc + 1]);
-                        wq[r][3] = sbyte<1>(wr[r][cc + 1]);
-                    } else {  // quants in dwords 9..16
-                        wq[r][0] = sbyte<0>(wr[r][9 + cc]);
-                        wq[r][1] = sbyte<1>(wr[r][9 + cc]);
-                        wq[r][2] = sbyte<2>(wr[r][9 + cc]);
-                        wq[r][3] = sbyte<3>(wr[r][9 + cc]);
-                    }
-                }
+                for (int r = 0; r < RG; ++r) q8_quants<HALF>(wr[r], cc, wq[r]);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)

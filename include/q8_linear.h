@@ -78,17 +78,16 @@ const char* q8_last_error(void);
  *   w_q8 : Q8_0 [n][k]          x : float32 [m][ldx]          y : float32 [m][ldy]
  *   n >= 0 outputs, k > 0 a multiple of 256, m >= 0 rows, ldx >= k, ldy >= n.
  * Arithmetic by batch size (the m-dependent kernel classes of section 14.2):
- *   m == 1      float32: w = d*q exactly, per-block chains, fixed butterfly;
- *   2..255      float32 in 16-row launches (the fp32 matrix cores' 4x4x1 form rounds
- *               once per fma), in an order that depends only on k and n: k <= 4096
- *               streams the weights once per launch on the matrix cores when its LDS
- *               fits (at k = 4096 on 256 CUs: n <= 129,024, fused f <= 47,104): per
- *               block t = sum q*x, acc = fma(d, t, acc), a fixed sum over 16 pairs, then
- *               the 16-pair chunks in order; other calls run the float32 rows kernel
- *               (w = d*q exact, one fma per weight and row; 9..16 rows on its
- *               matrix-core form, the same bits); every row is bit-identical whatever
- *               the other rows are (for any m in 2..255), and agrees with the m == 1
- *               result to reassociation;
+ *   m == 1      float32: per block t = sum q*x, acc = fma(d, t, acc), fixed butterfly;
+ *   2..255      float32 in 16-row launches, per block t = sum q*x (the quants exact,
+ *               one rounding per fma; the fp32 matrix cores' 4x4x1 form rounds like an
+ *               fma), acc = fma(d, t, acc), in an order that depends only on k and n:
+ *               k <= 4096 streams the weights once per launch on the matrix cores when
+ *               its LDS fits (at k = 4096 on 256 CUs: n <= 129,024, fused f <= 47,104),
+ *               a fixed sum over 16 pairs, then the 16-pair chunks in order; other calls
+ *               run the float32 rows kernel (9..16 rows on its matrix-core form, the same
+ *               bits); every row is bit-identical whatever the other rows are (for any m
+ *               in 2..255), and agrees with the m == 1 result to reassociation;
  *   m >= 256    bf16 matrix cores (dense prefill): weights d*q and activations rounded
  *               to bf16 (nearest even), float32 accumulation and output.
  */
