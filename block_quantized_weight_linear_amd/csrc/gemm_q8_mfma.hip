@@ -71,11 +71,11 @@ struct WStage {
     static constexpr int kDwords = kCopies * 256;
 };
 
-constexpr size_t kXf32Bytes = (size_t)kBM * kBK * 4;      // float32 activation stage
-constexpr size_t kXbfBytes = (size_t)kBM * kXStride * 2;   // bf16 activation tile
+constexpr int kXbfElems = kBM * kXStride;                  // one bf16 activation tile
+constexpr size_t kXbfBytes = (size_t)kXbfElems * 2;
 template <int WN>
 constexpr size_t mfma_lds_bytes() {
-    return kXf32Bytes + kXbfBytes + (size_t)kMfWaves * kWRing * WStage<WN>::kDwords * 4;
+    return 2 * kXbfBytes + (size_t)kMfWaves * kWRing * WStage<WN>::kDwords * 4;
 }
 
 __device__ __forceinline__ float mf_half_lo(uint32_t v) {
@@ -102,21 +102,6 @@ __device__ __forceinline__ void lds_copy16_sbase(const uint8_t* base, uint32_t o
         : "memory");
 }
 
-// One wave-wide direct-to-LDS 16-byte copy: lane l copies 16 bytes from src to
-// lds + 16*l (lds wave-uniform, through M0 as above).
-__device__ __forceinline__ void lds_copy16_mf(const void* src, uint32_t lds) {
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %2\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, off\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(src), "s"(lds)
-        : "memory");
-}
-
 template <int N>
 __device__ __forceinline__ void mf_wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -137,10 +122,17 @@ struct GroupArgs {
     bool gather;
 };
 
-// Four bf16 weights d*q from the quant bytes of dword v (byte b: weight b).
-__device__ __forceinline__ void dq4(uint32_t v, float d, bf16x8& o, int at) {
-#pragma unroll
-    for (int b = 0; b < 4; ++b) o[at + b] = (__bf16)(mf_sbyte(v, b) * d);
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+// Four bf16 weights d*q from the quant bytes of dword v (byte b: weight b), each rounded
+// to nearest even once; converted as one vector so the pairs pack directly.
+__device__ __forceinline__ bf16x4 dq4(uint32_t v, float d) {
+    const f32x4v f = {mf_sbyte(v, 0) * d, mf_sbyte(v, 1) * d, mf_sbyte(v, 2) * d, mf_sbyte(v, 3) * d};
+    return __builtin_convertvector(f, bf16x4);
+}
+__device__ __forceinline__ bf16x8 join4(bf16x4 lo, bf16x4 hi) {
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 template <int WN, bool SILU, bool GROUPED>
@@ -153,9 +145,8 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(1, 1
     static_assert(WN % 32 == 0, "whole 32-column fragments per wave");
     static_assert(L < 64, "copies of a stage must fit the vmcnt counter");
     extern __shared__ __attribute__((aligned(16))) uint8_t mf_smem[];
-    float* xf = reinterpret_cast<float*>(mf_smem);                          // [kBM][kBK] float32
-    __bf16* xs = reinterpret_cast<__bf16*>(mf_smem + kXf32Bytes);           // [kBM][kXStride] bf16
-    uint32_t* wr = reinterpret_cast<uint32_t*>(mf_smem + kXf32Bytes + kXbfBytes);  // [waves][ring][stage]
+    __bf16* xs = reinterpret_cast<__bf16*>(mf_smem);                          // [2][kBM][kXStride] bf16
+    uint32_t* wr = reinterpret_cast<uint32_t*>(mf_smem + 2 * kXbfBytes);     // [waves][ring][stage]
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -209,44 +200,47 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(1, 1
         woff[j] = (uint32_t)w_row(r) * row_bytes + 16u * (uint32_t)c;
     }
     const uint32_t wr_lds = (uint32_t)(uintptr_t)wr + (uint32_t)(wave * kWRing * WStage<WN>::kDwords * 4);
-    auto issue_w = [&](int s, int slot) __attribute__((always_inline)) {
+    auto copy_w = [&](int s, int slot, int j) __attribute__((always_inline)) {
         const uint8_t* base = w + (size_t)s * 68 - 4 * (s & 3);  // 16-byte aligned within the row
         const uint32_t lds = __builtin_amdgcn_readfirstlane(wr_lds + (uint32_t)(slot * WStage<WN>::kDwords * 4));
+        lds_copy16_sbase(base, woff[j], lds + 1024u * j);
+    };
+    auto issue_w = [&](int s, int slot) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < L; ++j) lds_copy16_sbase(base, woff[j], lds + 1024u * j);
+        for (int j = 0; j < L; ++j) copy_w(s, slot, j);
     };
 
-    // Activation copies: copy j of wave w moves tile rows 32w + 4j .. 32w + 4j + 3 of a
-    // step (256 bytes each, lane l: row 32w + 4j + l/16, bytes 16*(l%16) ..); past the
-    // call's rows a lane re-reads the last row.
-    const float* xsrc[8];
+    // Activations: thread t loads inputs 4xc .. 4xc + 3 of a step (xc = t % 16) of the tile
+    // rows t/16 + 16q (q = 0..7) into registers one step ahead; past the call's rows a
+    // thread re-reads the last row.  They are rounded to bf16 into the tile buffer of their
+    // step (two buffers, steps alternate), where within each 32-input block the groups of
+    // 8 inputs are stored in the order 0, 2, 1, 3.
+    const int xc = tid & 15;
+    const float* xrow[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        int r = mt * kBM + 32 * wave + 4 * j + (lane >> 4);
+    for (int q = 0; q < 8; ++q) {
+        int r = mt * kBM + (tid >> 4) + 16 * q;
         r = r < M ? r : M - 1;
         size_t ri = (size_t)r;
         if constexpr (GROUPED) ri = g.gather ? (size_t)(g.sorted[mbase + r] / g.k) : (size_t)(mbase + r);
-        xsrc[j] = x + ri * (size_t)ldx + 4 * (lane & 15);
+        xrow[q] = x + ri * (size_t)ldx + 4 * xc;
     }
-    const uint32_t xf_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)xf + (uint32_t)(wave * 32 * kBK * 4));
-    auto issue_x = [&](int s) __attribute__((always_inline)) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) lds_copy16_mf(xsrc[j] + (size_t)kBK * s, xf_lds + 1024u * j);
+    float4 xr[8];
+    auto load_xq = [&](int s, int q) __attribute__((always_inline)) {
+        xr[q] = *reinterpret_cast<const float4*>(xrow[q] + (size_t)kBK * s);
     };
-    // float32 stage -> bf16 tile: thread t rounds chunk t%16 (4 inputs) of rows t/16 + 16q.
-    // Within each 32-input block the groups of 8 inputs are stored in the order 0, 2, 1, 3.
-    const int xc = tid & 15;                       // chunk: inputs 4xc .. 4xc + 3 of the step
-    const int xgrp = (xc >> 1) & 3;                // its group of 8 within the block
+    auto load_x = [&](int s) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) load_xq(s, q);
+    };
+    const int xgrp = (xc >> 1) & 3;                // the chunk's group of 8 within its block
     const int xpos = 32 * (xc >> 3) + 8 * ((xgrp == 1) ? 2 : (xgrp == 2) ? 1 : xgrp) + 4 * (xc & 1);
-    auto round_x = [&]() __attribute__((always_inline)) {
+    auto store_x = [&](int buf) __attribute__((always_inline)) {
+        __bf16* t = xs + buf * kXbfElems + (tid >> 4) * kXStride + xpos;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            const int r = (tid >> 4) + 16 * q;
-            const float4 v = *reinterpret_cast<const float4*>(xf + r * kBK + 4 * xc);
-            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-            bf16x4 o;
-            o[0] = (__bf16)v.x; o[1] = (__bf16)v.y; o[2] = (__bf16)v.z; o[3] = (__bf16)v.w;
-            *reinterpret_cast<bf16x4*>(xs + r * kXStride + xpos) = o;
+            const f32x4v v = {xr[q].x, xr[q].y, xr[q].z, xr[q].w};
+            *reinterpret_cast<bf16x4*>(t + 16 * q * kXStride) = __builtin_convertvector(v, bf16x4);
         }
     };
 
@@ -259,91 +253,135 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(1, 1
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][f][e] = 0.f;
 
-    // B operands of block hb of a step whose stage is `stage` and whose pair starts at dword
-    // U of its 20-dword stage row: bq[sub][f] holds quants 16h + 8sub .. +7 of the block.
+    // The weight side of block HB of a pair that starts at dword U of its 20-dword stage row:
+    // the three 16-byte chunks a lane reads (scale chunk, then the two chunks holding its
+    // quants 16h .. 16h + 15), the scale, and four-weight piece (sub, half) of its B operand
+    // (quants 16h + 8sub + 4half .. + 3).  HB 0: scale in the low half of dword U, quants at
+    // bytes 2 + 16h .. of the pair (dwords U + 4h .. U + 4h + 4, chunks h and h + 1); HB 1:
+    // scale in the high half of dword U + 8 (chunk 2), quants at dwords U + 9 + 4h .. U + 12
+    // + 4h (chunks 2 + h and 3 + h).
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    auto read_chunks = [&](auto hbc, const uint32_t* stage, int f, u32x4 (&ch)[3]) __attribute__((always_inline)) {
+        constexpr int HB = decltype(hbc)::value;
+        const u32x4* row = reinterpret_cast<const u32x4*>(stage + (32 * f + c32) * WStage<WN>::kRowDwords);
+        ch[0] = row[2 * HB];
+        ch[1] = row[2 * HB + h];
+        ch[2] = row[2 * HB + h + 1];
+    };
+    auto scale_of = [&](auto uc, auto hbc, const u32x4 (&ch)[3]) __attribute__((always_inline)) {
+        constexpr int U = decltype(uc)::value, HB = decltype(hbc)::value;
+        return HB == 0 ? mf_half_lo(ch[0][U]) : mf_half_hi(ch[0][U]);
+    };
+    auto piece = [&](auto uc, auto hbc, const u32x4 (&ch)[3], float d, int sub, int half)
+                     __attribute__((always_inline)) {
+        constexpr int U = decltype(uc)::value, HB = decltype(hbc)::value;
+        const int k = 2 * sub + half;
+        auto qw = [&](int j) {  // dword j of the lane's quant run
+            const int at = (HB == 0 ? U : U + 1) + j;
+            return at < 4 ? ch[1][at] : ch[2][at - 4];
+        };
+        const uint32_t v = HB == 0 ? __builtin_amdgcn_alignbyte(qw(k + 1), qw(k), 2) : qw(k);
+        return dq4(v, d);
+    };
+    // Block HB of the pair in `stage` into B operands bq[sub][f] (quants 16h + 8sub .. + 7).
     auto dequant_block = [&](auto uc, auto hbc, const uint32_t* stage, bf16x8 (&bq)[2][NF])
                              __attribute__((always_inline)) {
-        constexpr int U = decltype(uc)::value, HB = decltype(hbc)::value;
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
-            const u32x4* row = reinterpret_cast<const u32x4*>(stage + (32 * f + c32) * WStage<WN>::kRowDwords);
-            if constexpr (HB == 0) {
-                // scale: dword U (low half); quants 16h.. at bytes 2 + 16h .. 17 + 16h of the
-                // pair = dwords U + 4h .. U + 4h + 4, i.e. in chunks h and h + 1
-                const u32x4 sc = row[0], x = row[h], y = row[h + 1];
-                const float d = mf_half_lo(sc[U]);
-                uint32_t q[5];
+            u32x4 ch[3];
+            read_chunks(hbc, stage, f, ch);
+            const float d = scale_of(uc, hbc, ch);
 #pragma unroll
-                for (int k = 0; k < 5; ++k) q[k] = (U + k < 4) ? x[U + k] : y[U + k - 4];
-#pragma unroll
-                for (int sub = 0; sub < 2; ++sub) {
-                    dq4(__builtin_amdgcn_alignbyte(q[2 * sub + 1], q[2 * sub], 2), d, bq[sub][f], 0);
-                    dq4(__builtin_amdgcn_alignbyte(q[2 * sub + 2], q[2 * sub + 1], 2), d, bq[sub][f], 4);
-                }
-            } else {
-                // scale: dword U + 8 (high half, chunk 2); quants 16h.. at dwords U + 9 + 4h ..
-                // U + 12 + 4h, i.e. in chunks 2 + h and 3 + h
-                const u32x4 sc = row[2], x = row[2 + h], y = row[3 + h];
-                const float d = mf_half_hi(sc[U]);
-                uint32_t q[4];
-#pragma unroll
-                for (int k = 0; k < 4; ++k) q[k] = (U + 1 + k < 4) ? x[U + 1 + k] : y[U + 1 + k - 4];
-#pragma unroll
-                for (int sub = 0; sub < 2; ++sub) {
-                    dq4(q[2 * sub], d, bq[sub][f], 0);
-                    dq4(q[2 * sub + 1], d, bq[sub][f], 4);
-                }
-            }
+            for (int sub = 0; sub < 2; ++sub)
+                bq[sub][f] = join4(piece(uc, hbc, ch, d, sub, 0), piece(uc, hbc, ch, d, sub, 1));
         }
     };
-    // MFMAs of block hb (LDS positions 32hb .. 32hb + 31 of the tile rows)
-    auto mma_block = [&](int hb, const bf16x8 (&bq)[2][NF]) __attribute__((always_inline)) {
+    // The MFMAs of block hb of a step (B operands bq, activations of tile buffer buf: LDS
+    // positions 32hb .. 32hb + 31 of its rows), with block HB of the pair in `stage`
+    // dequantized into bn in between: one four-weight piece after every second MFMA, in
+    // this order (scheduling fences), so the conversions issue while the matrix cores work.
+    auto mma_dq = [&](auto uc, auto hbc, int buf, int hb, const bf16x8 (&bq)[2][NF], const uint32_t* stage,
+                      bf16x8 (&bn)[2][NF], auto&& side) __attribute__((always_inline)) {
+        const __bf16* xb = xs + buf * kXbfElems + c32 * kXStride + 32 * hb + 8 * h;
+        bf16x8 af[2][4];
+        u32x4 ch[NF][3];
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-            bf16x8 af[4];
+        for (int i = 0; i < 4; ++i) af[0][i] = *reinterpret_cast<const bf16x8*>(xb + 32 * i * kXStride);
+        read_chunks(hbc, stage, 0, ch[0]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                af[i] = *reinterpret_cast<const bf16x8*>(xs + (32 * i + c32) * kXStride + 32 * hb + 16 * sub + 8 * h);
+        for (int i = 0; i < 4; ++i) af[1][i] = *reinterpret_cast<const bf16x8*>(xb + 32 * i * kXStride + 16);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+        for (int f = 1; f < NF; ++f) read_chunks(hbc, stage, f, ch[f]);
+        float d[NF];
+        bf16x4 lo;
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int f = 0; f < NF; ++f)
-                    acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bq[sub][f], acc[i][f], 0, 0, 0);
+        for (int j = 0; j < 8 * NF; ++j) {
+            const int sub = j / (4 * NF), i = (j / NF) & 3, f = j % NF;
+            acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[sub][i], bq[sub][f], acc[i][f], 0, 0, 0);
+            if (j & 1) {
+                const int p = j >> 1, pf = p >> 2;
+                if ((p & 3) == 0) d[pf] = scale_of(uc, hbc, ch[pf]);
+                const bf16x4 part = piece(uc, hbc, ch[pf], d[pf], (p >> 1) & 1, p & 1);
+                if ((p & 1) == 0) {
+                    lo = part;
+                } else {
+                    bn[(p >> 1) & 1][pf] = join4(lo, part);
+                    // keep the finished operand here: otherwise its conversions may sink to
+                    // the code that uses it, past the next step's start
+                    asm volatile("" : "+v"(bn[(p >> 1) & 1][pf]));
+                }
+            }
+            side(j);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
     auto stage_of = [&](int t) __attribute__((always_inline)) {
         return wr + (size_t)(wave * kWRing + t % kWRing) * WStage<WN>::kDwords;
     };
 
-    // prologue: X(0), W(0), W(1) in flight, in that order; block 0 of step 0 dequantized
+    // The next step's loads (8 activation loads, L weight copies) go out one or two after
+    // each MFMA of a step's second run, so the vector-memory queue drains while the matrix
+    // cores work instead of stalling the wave in one burst.
+    constexpr int kNM = 8 * NF, kItems = 8 + L, kPairs = L < 8 ? L : 8;
+    auto vmem_item = [&](int t, int sn, int slot) __attribute__((always_inline)) {
+        if (t < 2 * kPairs) {
+            if (t & 1) copy_w(sn, slot, t >> 1);
+            else load_xq(sn, t >> 1);
+        } else {
+            load_xq(sn, t - kPairs);
+        }
+    };
+    auto no_side = [](int) __attribute__((always_inline)) {};
+
+    // prologue: X(0) to tile 0; X(1) and W(1) in flight; block 0 of step 0 dequantized
     bf16x8 b0[2][NF], b1[2][NF];
-    issue_x(0);
+    load_x(0);
     issue_w(0, 0);
+    store_x(0);  // X(0) arrived, and W(0), issued after it
+    load_x(1);
     issue_w(1, 1);  // P >= 4
-    mf_wait_vmcnt<L>();  // X(0), W(0)
+    mf_wait_vmcnt<8 + L>();  // W(0)
     dequant_block(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, stage_of(0), b0);
     auto step = [&](int s, auto uc) __attribute__((always_inline)) {
         constexpr int U = decltype(uc)::value;  // s % 4
-        // X(s) and W(s) have arrived: only W(s+1), the newest L copies, may be in flight
-        if (s + 1 < P)
-            mf_wait_vmcnt<L>();
-        else
-            mf_wait_vmcnt<0>();
-        __syncthreads();  // every wave's copies of X(s) are in; all waves are done with step s-1
-        round_x();
-        __syncthreads();  // the bf16 tile is complete; the float32 stage is free
-        const bool more = s + 1 < P;
-        if (more) issue_x(s + 1);
-        if (s + 2 < P) issue_w(s + 2, (s + 2) % kWRing);
-        dequant_block(uc, std::integral_constant<int, 1>{}, stage_of(s), b1);
-        mma_block(0, b0);
-        if (more) {
-            // W(s+1) is older than the 8 + L copies just issued
-            if (s + 2 < P) mf_wait_vmcnt<8 + L>(); else mf_wait_vmcnt<8>();
-            dequant_block(std::integral_constant<int, (U + 1) & 3>{}, std::integral_constant<int, 0>{}, stage_of(s + 1), b0);
-        }
-        mma_block(1, b1);
+        __syncthreads();  // tile s % 2 is complete; every wave is done with tile (s + 1) % 2
+        mma_dq(uc, std::integral_constant<int, 1>{}, s & 1, 0, b0, stage_of(s), b1, no_side);
+        // X(s+1) arrived, and W(s+1), issued with it.  Unconditional (past the end: step
+        // P - 1 again, into the tile no wave reads any more) so that no branch lets the
+        // compiler sink the loads of X(s+1) from where they are issued to here.
+        store_x((s + 1) & 1);
+        mf_wait_vmcnt<0>();
+        // X(s+2) and W(s+2) (past the end: step P - 1 again, never used) during the second
+        // run; W(s+2) goes to the stage of W(s-1), free since the previous step's first run.
+        // Past the end the run dequantizes a stale stage, never used.
+        const int sn = s + 2 < P ? s + 2 : P - 1;
+        const int slot = (s + 2) % kWRing;
+        mma_dq(std::integral_constant<int, (U + 1) & 3>{}, std::integral_constant<int, 0>{}, s & 1, 1, b1,
+               stage_of(s + 1), b0, [&](int j) __attribute__((always_inline)) {
+#pragma unroll
+                   for (int t = j * kItems / kNM; t < (j + 1) * kItems / kNM; ++t) vmem_item(t, sn, slot);
+               });
     };
     for (int s = 0; s < P; s += 4) {  // P is a multiple of 4
         step(s, std::integral_constant<int, 0>{});
@@ -351,6 +389,7 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(1, 1
         step(s + 2, std::integral_constant<int, 2>{});
         step(s + 3, std::integral_constant<int, 3>{});
     }
+    mf_wait_vmcnt<0>();  // the last run's copies (of step P - 1 again) have landed
 
     // epilogue: register e of fragment (i, f) holds row 32i + 8(e/4) + 4h + e%4, column
     // 32f + c32 of the wave's tile
