@@ -225,21 +225,21 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(1, 1
         if constexpr (GROUPED) ri = g.gather ? (size_t)(g.sorted[mbase + r] / g.k) : (size_t)(mbase + r);
         xrow[q] = x + ri * (size_t)ldx + 4 * xc;
     }
-    float4 xr[8];
-    auto load_xq = [&](int s, int q) __attribute__((always_inline)) {
-        xr[q] = *reinterpret_cast<const float4*>(xrow[q] + (size_t)kBK * s);
+    float4 xr[2][8];  // X(t) in set t % 2
+    auto load_xq = [&](int set, int s, int q) __attribute__((always_inline)) {
+        xr[set][q] = *reinterpret_cast<const float4*>(xrow[q] + (size_t)kBK * s);
     };
-    auto load_x = [&](int s) __attribute__((always_inline)) {
+    auto load_x = [&](int set, int s) __attribute__((always_inline)) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) load_xq(s, q);
+        for (int q = 0; q < 8; ++q) load_xq(set, s, q);
     };
     const int xgrp = (xc >> 1) & 3;                // the chunk's group of 8 within its block
     const int xpos = 32 * (xc >> 3) + 8 * ((xgrp == 1) ? 2 : (xgrp == 2) ? 1 : xgrp) + 4 * (xc & 1);
-    auto store_x = [&](int buf) __attribute__((always_inline)) {
+    auto store_x = [&](int set, int buf) __attribute__((always_inline)) {
         __bf16* t = xs + buf * kXbfElems + (tid >> 4) * kXStride + xpos;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            const f32x4v v = {xr[q].x, xr[q].y, xr[q].z, xr[q].w};
+            const f32x4v v = {xr[set][q].x, xr[set][q].y, xr[set][q].z, xr[set][q].w};
             *reinterpret_cast<bf16x4*>(t + 16 * q * kXStride) = __builtin_convertvector(v, bf16x4);
         }
     };
@@ -340,47 +340,46 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(1, 1
         return wr + (size_t)(wave * kWRing + t % kWRing) * WStage<WN>::kDwords;
     };
 
-    // The next step's loads (8 activation loads, L weight copies) go out one or two after
-    // each MFMA of a step's second run, so the vector-memory queue drains while the matrix
-    // cores work instead of stalling the wave in one burst.
-    constexpr int kNM = 8 * NF, kItems = 8 + L, kPairs = L < 8 ? L : 8;
-    auto vmem_item = [&](int t, int sn, int slot) __attribute__((always_inline)) {
-        if (t < 2 * kPairs) {
-            if (t & 1) copy_w(sn, slot, t >> 1);
-            else load_xq(sn, t >> 1);
-        } else {
-            load_xq(sn, t - kPairs);
-        }
+    // Loads for later steps go out one at a time between the MFMAs, so the vector-memory
+    // queue drains while the matrix cores work instead of stalling the wave in one burst:
+    // the activations of step s+2 during step s's first run (into the register set X(s)
+    // used), the weights of step s+2 during its second run.  In issue order X(s+1), W(s+1),
+    // X(s+2), so waiting for X(s+1) in the middle of step s leaves X(s+2) in flight and
+    // also completes W(s+1), which the second run needs.
+    constexpr int kNM = 8 * NF;
+    auto spread = [&](int j, int items, auto&& item) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = j * items / kNM; t < (j + 1) * items / kNM; ++t) item(t);
     };
-    auto no_side = [](int) __attribute__((always_inline)) {};
 
-    // prologue: X(0) to tile 0; X(1) and W(1) in flight; block 0 of step 0 dequantized
+    // prologue: X(0) to tile 0; W(1) and X(1) in flight; block 0 of step 0 dequantized
     bf16x8 b0[2][NF], b1[2][NF];
-    load_x(0);
+    load_x(0, 0);
     issue_w(0, 0);
-    store_x(0);  // X(0) arrived, and W(0), issued after it
-    load_x(1);
+    store_x(0, 0);  // X(0) arrived, and W(0), issued after it
     issue_w(1, 1);  // P >= 4
-    mf_wait_vmcnt<8 + L>();  // W(0)
+    load_x(1, 1);
     dequant_block(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, stage_of(0), b0);
     auto step = [&](int s, auto uc) __attribute__((always_inline)) {
         constexpr int U = decltype(uc)::value;  // s % 4
-        __syncthreads();  // tile s % 2 is complete; every wave is done with tile (s + 1) % 2
-        mma_dq(uc, std::integral_constant<int, 1>{}, s & 1, 0, b0, stage_of(s), b1, no_side);
-        // X(s+1) arrived, and W(s+1), issued with it.  Unconditional (past the end: step
-        // P - 1 again, into the tile no wave reads any more) so that no branch lets the
-        // compiler sink the loads of X(s+1) from where they are issued to here.
-        store_x((s + 1) & 1);
-        mf_wait_vmcnt<0>();
-        // X(s+2) and W(s+2) (past the end: step P - 1 again, never used) during the second
-        // run; W(s+2) goes to the stage of W(s-1), free since the previous step's first run.
-        // Past the end the run dequantizes a stale stage, never used.
+        // past the end the loads fetch step P - 1 again and the runs dequantize a stale
+        // stage; neither is used
         const int sn = s + 2 < P ? s + 2 : P - 1;
+        __syncthreads();  // tile s % 2 is complete; every wave is done with tile (s + 1) % 2
+        mma_dq(uc, std::integral_constant<int, 1>{}, s & 1, 0, b0, stage_of(s), b1,
+               [&](int j) __attribute__((always_inline)) {
+                   spread(j, 8, [&](int q) __attribute__((always_inline)) { load_xq(U & 1, sn, q); });
+               });
+        // X(s+1) arrived, and W(s+1), issued before X(s+2).  Unconditional (past the end:
+        // into the tile no wave reads any more) so that no branch lets the compiler sink
+        // the loads of X(s+1) from where they are issued to here.
+        store_x((U + 1) & 1, (s + 1) & 1);
+        mf_wait_vmcnt<8>();  // W(s+1): older than the 8 loads of X(s+2)
+        // W(s+2) goes to the stage of W(s-1), free since the previous step's first run
         const int slot = (s + 2) % kWRing;
         mma_dq(std::integral_constant<int, (U + 1) & 3>{}, std::integral_constant<int, 0>{}, s & 1, 1, b1,
                stage_of(s + 1), b0, [&](int j) __attribute__((always_inline)) {
-#pragma unroll
-                   for (int t = j * kItems / kNM; t < (j + 1) * kItems / kNM; ++t) vmem_item(t, sn, slot);
+                   spread(j, L, [&](int c) __attribute__((always_inline)) { copy_w(sn, slot, c); });
                });
     };
     for (int s = 0; s < P; s += 4) {  // P is a multiple of 4
@@ -389,7 +388,7 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(1, 1
         step(s + 2, std::integral_constant<int, 2>{});
         step(s + 3, std::integral_constant<int, 3>{});
     }
-    mf_wait_vmcnt<0>();  // the last run's copies (of step P - 1 again) have landed
+    mf_wait_vmcnt<0>();  // the last loads and copies (of step P - 1 again) have landed
 
     // epilogue: register e of fragment (i, f) holds row 32i + 8(e/4) + 4h + e%4, column
     // 32f + c32 of the wave's tile
