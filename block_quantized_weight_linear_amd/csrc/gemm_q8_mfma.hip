@@ -272,17 +272,18 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(1, 1
         constexpr int U = decltype(uc)::value, HB = decltype(hbc)::value;
         return HB == 0 ? mf_half_lo(ch[0][U]) : mf_half_hi(ch[0][U]);
     };
-    auto piece = [&](auto uc, auto hbc, const u32x4 (&ch)[3], float d, int sub, int half)
-                     __attribute__((always_inline)) {
+    auto piece_word = [&](auto uc, auto hbc, const u32x4 (&ch)[3], int sub, int half)
+                          __attribute__((always_inline)) {
         constexpr int U = decltype(uc)::value, HB = decltype(hbc)::value;
         const int k = 2 * sub + half;
         auto qw = [&](int j) {  // dword j of the lane's quant run
             const int at = (HB == 0 ? U : U + 1) + j;
             return at < 4 ? ch[1][at] : ch[2][at - 4];
         };
-        const uint32_t v = HB == 0 ? __builtin_amdgcn_alignbyte(qw(k + 1), qw(k), 2) : qw(k);
-        return dq4(v, d);
+        return HB == 0 ? __builtin_amdgcn_alignbyte(qw(k + 1), qw(k), 2) : qw(k);
     };
+    auto piece = [&](auto uc, auto hbc, const u32x4 (&ch)[3], float d, int sub, int half)
+                     __attribute__((always_inline)) { return dq4(piece_word(uc, hbc, ch, sub, half), d); };
     // Block HB of the pair in `stage` into B operands bq[sub][f] (quants 16h + 8sub .. + 7).
     auto dequant_block = [&](auto uc, auto hbc, const uint32_t* stage, bf16x8 (&bq)[2][NF])
                              __attribute__((always_inline)) {
@@ -314,15 +315,24 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(1, 1
         for (int f = 1; f < NF; ++f) read_chunks(hbc, stage, f, ch[f]);
         float d[NF];
         bf16x4 lo;
+        f32x4v wf;
+        uint32_t pv;
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < 8 * NF; ++j) {
             const int sub = j / (4 * NF), i = (j / NF) & 3, f = j % NF;
             acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[sub][i], bq[sub][f], acc[i][f], 0, 0, 0);
-            if (j & 1) {
-                const int p = j >> 1, pf = p >> 2;
+            // piece p = j / 2: two of its four weights after each MFMA
+            const int p = j >> 1, pf = p >> 2;
+            if ((j & 1) == 0) {
                 if ((p & 3) == 0) d[pf] = scale_of(uc, hbc, ch[pf]);
-                const bf16x4 part = piece(uc, hbc, ch[pf], d[pf], (p >> 1) & 1, p & 1);
+                pv = piece_word(uc, hbc, ch[pf], (p >> 1) & 1, p & 1);
+                wf[0] = mf_sbyte(pv, 0) * d[pf];
+                wf[1] = mf_sbyte(pv, 1) * d[pf];
+            } else {
+                wf[2] = mf_sbyte(pv, 2) * d[pf];
+                wf[3] = mf_sbyte(pv, 3) * d[pf];
+                const bf16x4 part = __builtin_convertvector(wf, bf16x4);
                 if ((p & 1) == 0) {
                     lo = part;
                 } else {
