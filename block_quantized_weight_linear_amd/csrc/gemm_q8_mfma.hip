@@ -14,24 +14,26 @@
 // own LDS ring by direct-to-LDS 16-byte copies (a lane's 32-bit offset into the matrix is
 // fixed for the whole K loop, the step is a scalar base), and the wave turns them into
 // MFMA B operands in registers (bf16(fp32(d) * q), one rounding; d*q needs at most 19
-// significant bits).  The activations of a K step (128 x 64 float32) reach LDS by direct
-// 16-byte copies and are rounded to bf16 (nearest even) once per block into the tile the
-// four waves share.  Per wave a K step is 4 x 4 x WN/32 v_mfma_f32_32x32x16_bf16 on a 128 x
-// WN accumulator tile (on gfx950 this shape keeps the matrix cores busy from one wave per
-// SIMD; 16x16x32 with as many accumulators does not).
+// significant bits).  The activations of a K step (128 x 64 float32) come into registers
+// one step ahead and are rounded to bf16 (nearest even) once per block into one of two
+// tiles the four waves share (steps alternate), so a step needs one barrier.  Per wave a K
+// step is 4 x 4 x WN/32 v_mfma_f32_32x32x16_bf16 on a 128 x WN accumulator tile (on gfx950
+// this shape keeps the matrix cores busy from one wave per SIMD; 16x16x32 with as many
+// accumulators does not).
 //
 // Inputs of a Q8_0 block are multiplied in a permuted order: the four groups of 8 inputs
 // run as groups 0, 2, 1, 3 (both operands alike, so the products and sums are those of
 // the block): then the 16 quants a lane needs are contiguous in the block, and the lane
 // reads them as whole 16-byte LDS chunks (conflict-free across the 32 rows of a fragment).
 //
-// Pipeline: weight bytes are copied two steps ahead into a ring of three stages per wave,
-// float32 activations one step ahead into one stage; every vector-memory load of the loop
-// is such a copy, so the waits are explicit counts of them.  Per K step: wait, barrier,
-// round the activations, barrier, issue the next copies, then the MFMAs of block 0 of the
-// pair while block 1 is dequantized and the MFMAs of block 1 while the next step's block 0
-// is (the dequantization runs under the matrix cores).  The step loop is unrolled by four,
-// the period of a pair's position inside its 16-byte chunks.
+// Pipeline: weight bytes go to a ring of three stages per wave, activations to two
+// register sets.  A K step is two runs of MFMAs, one per block of the pair; after every
+// MFMA of a run come two weights of the other block's dequantization (block 1 of this
+// step in the first run, block 0 of the next step in the second), in fixed program order,
+// and the loads for two steps ahead go out one at a time between the MFMAs (activations in
+// the first run, weight copies in the second) so the vector-memory queue drains while the
+// matrix cores work.  The step loop is unrolled by four, the period of a pair's position
+// inside its 16-byte chunks.
 //
 // Dense grids map tiles to blocks so that the 128-row tiles sharing a weight tile land
 // on the same XCD (blocks are handed to the 8 XCDs in turn), where they share its L2.
