@@ -1,8 +1,9 @@
 """GPU parity of q8_linear and q8_linear_fused_gate_up_silu against the CPU oracle.
 
-Small shapes (many tiles and ragged tails) are compared element by element with the
-full oracle; the Qwen3 layer shapes at their real sizes are compared on sampled
-output rows the oracle computes one by one.  Exact-arithmetic inputs (every partial
+Small shapes (many tiles and ragged tails) and the Qwen3 layer shapes at their real
+sizes (the oracle run in row chunks) are compared element by element with the full
+oracle; only the matrices too tall for the streaming form are compared on sampled
+output rows.  Exact-arithmetic inputs (every partial
 sum representable in float32) must match bit for bit.  Invariants: batch invariance,
 run-to-run determinism, scale doubling, sign symmetry, zero blocks, one-hot gathers.
 """

@@ -3,8 +3,8 @@ q8_linear_fused_gate_up_silu_q8act) against the CPU oracle.
 
 Codes and scales are integers decided in float32 on both sides: bit-exact.  The
 linears are compared element by element on small shapes (many tiles, ragged tails,
-row counts that are not a launch size) and on sampled outputs of the Qwen3 layer
-shapes; inputs whose partial sums are all exact in float32 must match bit for bit.
+row counts that are not a launch size) and on every output of the Qwen3 layer shapes;
+inputs whose partial sums are all exact in float32 must match bit for bit.
 Invariants: batch invariance and run-to-run determinism.
 """
 
