@@ -438,7 +438,8 @@ PREFILL_TOL = 2e-2   # bf16 operands, float32 accumulation
 # 128 x 256 tiles: (32768, 256, 256) and the ragged (33000, 256, 300) take that path there;
 # the smaller shapes take the 4-wave 128 x 128 / 128 x 64 tiles.
 @pytest.mark.parametrize("n,k,m", [(300, 1024, 256), (129, 512, 300), (1024, 4096, 512), (77, 3072, 257),
-                                   (520, 256, 1000), (32768, 256, 256), (33000, 256, 300)])
+                                   (520, 256, 1000), (32768, 256, 256), (33000, 256, 300),
+                                   (1024, 12288, 256)])  # the 8B down's K, 32-column waves
 def test_prefill_vs_oracle(q8, n, k, m):
     lib, torch, dev = q8
     wb, _, _ = wl.q8_weight(91 + n, n, k)
