@@ -213,8 +213,8 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(1, 1
     };
 
     // Activations: thread t loads inputs 4xc .. 4xc + 3 of a step (xc = t % 16) of the tile
-    // rows t/16 + 16q (q = 0..7) into registers one step ahead; past the call's rows a
-    // thread re-reads the last row.  They are rounded to bf16 into the tile buffer of their
+    // rows t/16 + 16q (q = 0..7) into registers two steps ahead (two register sets); past
+    // the call's rows a thread re-reads the last row.  They are rounded to bf16 into the tile buffer of their
     // step (two buffers, steps alternate), where within each 32-input block the groups of
     // 8 inputs are stored in the order 0, 2, 1, 3.
     const int xc = tid & 15;
@@ -301,8 +301,9 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(1, 1
     };
     // The MFMAs of block hb of a step (B operands bq, activations of tile buffer buf: LDS
     // positions 32hb .. 32hb + 31 of its rows), with block HB of the pair in `stage`
-    // dequantized into bn in between: one four-weight piece after every second MFMA, in
-    // this order (scheduling fences), so the conversions issue while the matrix cores work.
+    // dequantized into bn in between: two weights after every MFMA (a four-weight piece per
+    // two MFMAs), in this order (scheduling fences), so the conversions issue while the
+    // matrix cores work.  side(j) issues the loads that go out after MFMA j.
     auto mma_dq = [&](auto uc, auto hbc, int buf, int hb, const bf16x8 (&bq)[2][NF], const uint32_t* stage,
                       bf16x8 (&bn)[2][NF], auto&& side) __attribute__((always_inline)) {
         const __bf16* xb = xs + buf * kXbfElems + c32 * kXStride + 32 * hb + 8 * h;
