@@ -406,26 +406,51 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(1, 1
     // epilogue: register e of fragment (i, f) holds row 32i + 8(e/4) + 4h + e%4, column
     // 32f + c32 of the wave's tile
     if constexpr (GROUPED) y += (size_t)mbase * ldy;
+    // the lane's outputs: columns c0 + step * f; a tile inside the call's rows and columns
+    // (block-uniform) stores without per-element checks
+    auto store_tile = [&](int c0, int step, bool cols_inside) __attribute__((always_inline)) {
+        const int m0 = mt * kBM + 4 * h;
+        if (mt * kBM + kBM <= M && cols_inside) {
+            float* yl = y + (size_t)m0 * ldy + c0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int m = mt * kBM + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
+                for (int e = 0; e < 16; ++e)
 #pragma unroll
-            for (int f = 0; f < NF; ++f) {
-                if constexpr (SILU) {
-                    // columns 0..15 of a fragment are gate rows, 16..31 the up rows of the same
-                    // outputs: the up value comes from lane ^ 16
-                    const float v = acc[i][f][e];
-                    const float other = __shfl_xor(v, 16, 64);
-                    const int o = nt * (BN / 2) + wave * (WN / 2) + 16 * f + c32;
-                    if (c32 < 16 && m < M && o < n_out) y[(size_t)m * ldy + o] = v / (1.0f + __expf(-v)) * other;
-                } else {
-                    const int n = nt * BN + wave * WN + 32 * f + c32;
-                    if (m < M && n < n_out) y[(size_t)m * ldy + n] = acc[i][f][e];
+                    for (int f = 0; f < NF; ++f)
+                        yl[(size_t)(32 * i + 8 * (e >> 2) + (e & 3)) * ldy + step * f] = acc[i][f][e];
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int m = m0 + 32 * i + 8 * (e >> 2) + (e & 3);
+#pragma unroll
+                    for (int f = 0; f < NF; ++f) {
+                        const int c = c0 + step * f;
+                        if (m < M && c < n_out) y[(size_t)m * ldy + c] = acc[i][f][e];
+                    }
                 }
-            }
         }
+    };
+    if constexpr (SILU) {
+        // Columns 0..15 of a fragment are gate rows, 16..31 the up rows of the same outputs:
+        // swapping the 16-lane rows of each half wave brings a gate lane (c32 < 16) its up
+        // value; SiLU(gate) * up is formed in place (every lane, the up lanes' results
+        // unused), then the gate lanes store.
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int f = 0; f < NF; ++f)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const float v = acc[i][f][e];
+                    const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+                    acc[i][f][e] = v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)) * __uint_as_float(sw[1]);
+                }
+        if (c32 < 16) store_tile(nt * (BN / 2) + wave * (WN / 2) + c32, 16, nt * (BN / 2) + BN / 2 <= n_out);
+    } else {
+        store_tile(nt * BN + wave * WN + c32, 32, nt * BN + BN <= n_out);
     }
 }
 
