@@ -600,8 +600,8 @@ def main():
         kernel_driver(args.kernel_driver[0], int(args.kernel_driver[1]), args.q8act, args.fmt)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the sharding plan is described in the design notes, not built)", file=sys.stderr)
+        print(f"bench.py: runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the sharded path is not implemented)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -21,7 +21,7 @@ Every step is the plain definition written out in float64: parse the blocks,
 dequantize exactly, multiply with a library matmul, apply the elementwise
 epilogue.  No blocking, fusion or reordering.
 
-Readings taken where the pages are silent (each also listed in the design notes):
+Readings taken where the pages are silent:
 
 * Q8_0 byte layout: the GGUF Q8_0 block -- one little-endian IEEE binary16 scale
   ``d`` followed by 32 signed 8-bit quants ``q``, 34 bytes; blocks run along K and
